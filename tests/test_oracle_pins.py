@@ -1,0 +1,331 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle against a library routine (torch / numpy
+softmax), a closed form, an invariant of the method, a worked number printed
+on the pages, or brute force on tiny inputs.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from attention_reuse_amd import workload as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _softmax_attend(q, K, V, scale):
+    """Library reference: torch softmax over logits, then a weighted sum."""
+    qt = torch.as_tensor(np.asarray(q, np.float64))
+    Kt = torch.as_tensor(wl.from_storage(K))
+    Vt = torch.as_tensor(wl.from_storage(V))
+    logits = (Kt @ qt) * scale
+    w = torch.softmax(logits, dim=0)
+    return (w @ Vt).numpy(), torch.logsumexp(logits, 0).item()
+
+
+def _rand_kv(rng, T, d, dtype):
+    K = rng.standard_normal((T, d)).astype(np.float32)
+    V = rng.standard_normal((T, d)).astype(np.float32)
+    return wl.to_storage(K, dtype), wl.to_storage(V, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_summary_matches_library_softmax(oracle_lib, dtype):
+    rng = np.random.default_rng(1)
+    for d in (4, 16, 64):
+        K, V = _rand_kv(rng, 50, d, dtype)
+        for (a, e) in ((0, 49), (3, 17), (10, 10), (-5, 2)):
+            q = rng.standard_normal(d) * 2
+            o, lse = oracle_lib.summary(q, K, V, a, e)
+            lo = max(a, 0)
+            ref_o, ref_l = _softmax_attend(q, K[lo:e + 1], V[lo:e + 1],
+                                           1 / math.sqrt(d))
+            np.testing.assert_allclose(o, ref_o, rtol=1e-12, atol=1e-12)
+            assert abs(lse - ref_l) < 1e-12
+
+
+def test_summary_closed_forms(oracle_lib):
+    rng = np.random.default_rng(2)
+    d = 8
+    K, V = _rand_kv(rng, 20, d, "f32")
+    q = rng.standard_normal(d)
+    # A single token: the output is that token's value.
+    o, lse = oracle_lib.summary(q, K, V, 7, 7)
+    np.testing.assert_allclose(o, V[7].astype(np.float64), rtol=0, atol=1e-15)
+    assert abs(lse - float(q @ K[7].astype(np.float64)) / math.sqrt(d)) < 1e-12
+    # All keys equal: uniform weights, the output is the mean value.
+    Ke = np.repeat(K[:1], 20, axis=0)
+    o, lse = oracle_lib.summary(q, Ke, V, 0, 19)
+    np.testing.assert_allclose(o, V.astype(np.float64).mean(0), atol=1e-14)
+    assert abs(lse - (float(q @ K[0]) / math.sqrt(d) + math.log(20))) < 1e-12
+    # One dominant logit: the output is that token's value.
+    Kd = np.zeros_like(K)
+    Kd[5] = 1000.0 * q / np.linalg.norm(q)
+    o, _ = oracle_lib.summary(q, Kd, V, 0, 19)
+    np.testing.assert_allclose(o, V[5].astype(np.float64), atol=1e-12)
+    # Empty range: the empty summary.
+    o, lse = oracle_lib.summary(q, K, V, 9, 8)
+    assert lse == -math.inf and not o.any()
+
+
+def test_merge_prefix_suffix_equals_whole(oracle_lib):
+    """Summaries of disjoint sets merge into the summary of the union; the
+    split point p = m-1 is the online-normaliser identity (MAC-Attention
+    blog, "Decomposable representation of attention")."""
+    rng = np.random.default_rng(3)
+    d = 16
+    K, V = _rand_kv(rng, 64, d, "bf16")
+    for _ in range(20):
+        q = rng.standard_normal(d) * 3
+        m = int(rng.integers(1, 64))
+        p = int(rng.integers(0, m + 1))
+        whole = oracle_lib.summary(q, K, V, 0, m)
+        pre = oracle_lib.summary(q, K, V, 0, p - 1)
+        suf = oracle_lib.summary(q, K, V, p, m)
+        o, l = oracle_lib.merge(*pre, *suf)
+        np.testing.assert_allclose(o, whole[0], atol=1e-13)
+        assert abs(l - whole[1]) < 1e-12
+    # Online identity at p = m - 1, and associativity of a three-way split.
+    q = rng.standard_normal(d)
+    m = 40
+    a = oracle_lib.summary(q, K, V, 0, m - 1)
+    b = oracle_lib.summary(q, K, V, m, m)
+    o, l = oracle_lib.merge(*a, *b)
+    ref = oracle_lib.summary(q, K, V, 0, m)
+    np.testing.assert_allclose(o, ref[0], atol=1e-13)
+    x, y, z = (oracle_lib.summary(q, K, V, 0, 9), oracle_lib.summary(q, K, V, 10, 29),
+               oracle_lib.summary(q, K, V, 30, 50))
+    left = oracle_lib.merge(*oracle_lib.merge(*x, *y), *z)
+    right = oracle_lib.merge(*x, *oracle_lib.merge(*y, *z))
+    np.testing.assert_allclose(left[0], right[0], atol=1e-14)
+    assert abs(left[1] - right[1]) < 1e-13
+
+
+def test_merge_empty_is_identity_bitwise(oracle_lib):
+    rng = np.random.default_rng(4)
+    o = rng.standard_normal(8)
+    e = np.zeros(8)
+    r1 = oracle_lib.merge(o, 1.25, e, -math.inf)
+    r2 = oracle_lib.merge(e, -math.inf, o, 1.25)
+    assert np.array_equal(r1[0], o) and r1[1] == 1.25
+    assert np.array_equal(r2[0], o) and r2[1] == 1.25
+
+
+def test_unmerge_inverts_merge(oracle_lib):
+    rng = np.random.default_rng(5)
+    d = 16
+    K, V = _rand_kv(rng, 64, d, "f32")
+    q = rng.standard_normal(d)
+    whole = oracle_lib.summary(q, K, V, 0, 50)
+    tail = oracle_lib.summary(q, K, V, 30, 50)
+    head = oracle_lib.summary(q, K, V, 0, 29)
+    o, l = oracle_lib.unmerge(*whole, *tail)
+    np.testing.assert_allclose(o, head[0], atol=1e-12)
+    assert abs(l - head[1]) < 1e-12
+    o, l = oracle_lib.unmerge(*whole, np.zeros(d), -math.inf)
+    assert np.array_equal(o, whole[0]) and l == whole[1]
+    o, l = oracle_lib.unmerge(*whole, *whole)
+    assert l == -math.inf
+
+
+def test_threshold_worked_example(oracle_lib):
+    """d = 128, tau = 0.45 gives an acceptance distance of 8.8."""
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "threshold_worked_example.txt"))
+            if ln.strip() and not ln.startswith("#")]
+    for d, tau, chance, thr in rows:
+        d, tau, chance, thr = int(d), float(tau), float(chance), float(thr)
+        assert math.sqrt(2 * d) == chance
+        t2 = oracle_lib.threshold2(d, tau, mode=0)
+        assert abs(math.sqrt(t2) - thr) < 1e-5
+        # The other reading of the threshold (tau * sqrt(2d)) gives 7.2.
+        assert abs(math.sqrt(oracle_lib.threshold2(d, tau, mode=1)) - tau * chance) < 1e-5
+
+
+# ----------------------------------------------------------------------------
+# MAC stream pins.
+
+def _small(**kw):
+    base = dict(name="pin", batch=1, n_q_heads=2, n_kv_heads=1, head_dim=16,
+                dtype="f32", ctx=40, steps=30, ring_k=8, band_r=4, tau=0.6,
+                rope_base=1e4, n_protos=3, switch_p=0.2, sigma=(0.05, 0.05),
+                seed=7)
+    base.update(kw)
+    return wl.Workload(**base)
+
+
+def _stream(oracle_lib, cfg, h=0, thresh2=None, q_override=None, W=None, **kw):
+    K, V = wl.gen_kv(cfg)
+    qt, q, picks, _ = wl.gen_queries(cfg)
+    if q_override is not None:
+        q = q_override(qt, q)
+    W = cfg.n_warm if W is None else W
+    nw = cfg.n_warm
+    t2 = oracle_lib.threshold2(cfg.head_dim, cfg.tau) if thresh2 is None else thresh2
+    res = oracle_lib.run_stream(
+        K[0, h // cfg.group], V[0, h // cfg.group], qt[0, h, nw - W:nw],
+        q[0, h, nw - W:nw], qt[0, h, nw:], q[0, h, nw:], ctx_len=cfg.ctx,
+        ring_k=cfg.ring_k, band_r=cfg.band_r, thresh2=t2, **kw)
+    return res, K[0, h // cfg.group], V[0, h // cfg.group], qt[0, h], q[0, h]
+
+
+def test_forced_miss_is_full_attention(oracle_lib):
+    """Threshold 0: every step misses and the output is full attention over
+    [0, m], exactly as the baseline (MAC-Attention blog, "Match (1)": a miss
+    falls back to full attention, identical to the baseline)."""
+    cfg = _small()
+    res, K, V, qt, q = _stream(oracle_lib, cfg, thresh2=0.0, want_ring=True)
+    assert not res["hit"].any() and (res["p"] == -1).all()
+    d = cfg.head_dim
+    for s in range(cfg.steps):
+        m = cfg.ctx + s
+        ref, ref_l = _softmax_attend(q[cfg.n_warm + s], K[:m + 1], V[:m + 1], 1 / math.sqrt(d))
+        np.testing.assert_allclose(res["out"][s], ref, atol=1e-12)
+        assert abs(res["lse"][s] - ref_l) < 1e-12
+    # The rectified summary written at each slot is full attention over
+    # [0, m - r], rounded to fp32.
+    for k in range(cfg.ring_k):
+        m = int(res["ring_pos"][k])
+        s = m - cfg.ctx
+        ref, ref_l = _softmax_attend(q[cfg.n_warm + s], K[:m - cfg.band_r + 1],
+                                     V[:m - cfg.band_r + 1], 1 / math.sqrt(d))
+        np.testing.assert_allclose(res["ring_o"][k], ref, atol=1e-6)
+        assert abs(res["ring_lse"][k] - ref_l) < 1e-5
+
+
+def test_exact_reuse_invariant(oracle_lib):
+    """Identity RoPE, no noise, one prototype: every cached summary is exact
+    for the current query, so every step hits the most recent position
+    (ties go to the larger position) and the output equals full attention,
+    through arbitrarily long chains of reuse."""
+    cfg = _small(n_protos=1, sigma=(0.0, 0.0), steps=40, switch_p=0.0)
+    res, K, V, qt, q = _stream(
+        oracle_lib, cfg, q_override=lambda qt, q: wl.from_storage(qt).astype(np.float32))
+    assert res["hit"].all()
+    m = cfg.ctx + np.arange(cfg.steps)
+    assert (res["p"] == m - 1).all()
+    qv = wl.from_storage(qt)
+    for s in range(cfg.steps):
+        ref, ref_l = _softmax_attend(qv[cfg.n_warm + s], K[:m[s] + 1], V[:m[s] + 1],
+                                     1 / math.sqrt(cfg.head_dim))
+        np.testing.assert_allclose(res["out"][s], ref, atol=2e-6)
+
+
+def test_band_covering_everything_is_full(oracle_lib):
+    """r >= m + 1: the cached prefix is empty and the fresh band covers
+    [0, m], so a hit equals full attention."""
+    cfg = _small(band_r=200, sigma=(0.01, 0.01))
+    res, K, V, qt, q = _stream(oracle_lib, cfg)
+    assert res["hit"].mean() > 0.5
+    for s in range(cfg.steps):
+        m = cfg.ctx + s
+        ref, _ = _softmax_attend(q[cfg.n_warm + s], K[:m + 1], V[:m + 1],
+                                 1 / math.sqrt(cfg.head_dim))
+        np.testing.assert_allclose(res["out"][s], ref, atol=1e-12)
+
+
+def _owner_closed_form(cfg, res, q, K, V):
+    """Expected MAC outputs as single softmaxes over piecewise logits.
+
+    Every summary is a sum over disjoint token sets, so the output at m is
+    exact softmax attention in which position t's logit comes from the query
+    of the step that computed t's contribution: a hit at p takes positions
+    [0, p-r] from p's rectified summary and computes [p-r+1, m] with q_m; a
+    miss computes [0, m] with q_m; the rectified summary of m keeps [0, m-r]
+    ("MAC-Attention" blog, "Reuse" and "Paper version").
+    """
+    L, r, W = cfg.ctx, cfg.band_r, cfg.n_warm
+    qpos = {L - W + j: q[j].astype(np.float64) for j in range(q.shape[0])}
+    rect = {t: [t] * max(0, t - r + 1) for t in range(L - W, L)}
+    outs = []
+    for s in range(cfg.steps):
+        m = L + s
+        if res["hit"][s]:
+            p = int(res["p"][s])
+            pre = rect[p]
+            owner = pre + [m] * (m + 1 - len(pre))
+        else:
+            owner = [m] * (m + 1)
+        rect[m] = owner[:max(0, m - r + 1)]
+        Qo = np.stack([qpos[o] for o in owner])
+        Kf, Vf = wl.from_storage(K[:m + 1]), wl.from_storage(V[:m + 1])
+        logits = torch.as_tensor((Qo * Kf).sum(1) / math.sqrt(cfg.head_dim))
+        outs.append((torch.softmax(logits, 0) @ torch.as_tensor(Vf)).numpy())
+    return np.stack(outs)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(dtype="bf16", band_r=3, ring_k=5),
+                                dict(switch_p=0.5, n_protos=4, ring_k=16, band_r=8),
+                                dict(ctx=6, ring_k=8, band_r=4, steps=30)])
+def test_hit_path_piecewise_closed_form(oracle_lib, kw):
+    cfg = _small(**kw)
+    for h in range(cfg.n_q_heads):
+        res, K, V, qt, q = _stream(oracle_lib, cfg, h=h)
+        assert res["hit"].any() and (~res["hit"]).any() or res["hit"].all()
+        ref = _owner_closed_form(cfg, res, q, K, V)
+        # Summaries are stored in fp32 in the ring: allow for that rounding.
+        np.testing.assert_allclose(res["out"], ref, atol=2e-6, rtol=0)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(dtype="bf16", ring_k=5),
+                                dict(n_protos=2, sigma=(0.3, 0.3), ring_k=12)])
+def test_match_decisions_brute_force(oracle_lib, kw):
+    """Nearest pre-RoPE query among the last K positions, ties to the larger
+    position, accepted when the squared distance is below the threshold."""
+    cfg = _small(**kw)
+    t2 = oracle_lib.threshold2(cfg.head_dim, cfg.tau)
+    for h in range(cfg.n_q_heads):
+        res, K, V, qt, q = _stream(oracle_lib, cfg, h=h)
+        qv = wl.from_storage(qt)
+        W, L = cfg.n_warm, cfg.ctx
+        for s in range(cfg.steps):
+            m = L + s
+            cand = [t for t in range(max(L - W, m - cfg.ring_k), m)]
+            D = {t: float(((qv[W + s] - qv[t - (L - W)]) ** 2).sum()) for t in cand}
+            best = min(cand, key=lambda t: (D[t], -t))
+            hit = D[best] < t2
+            assert bool(res["hit"][s]) == hit
+            assert res["p"][s] == (best if hit else -1)
+            assert abs(res["dist"][s] - math.sqrt(D[best])) < 1e-12
+
+
+def _ring_trace_rows():
+    rows = {}
+    for ln in open(os.path.join(GOLDEN, "ring_trace_k4.txt")):
+        if not ln.strip() or ln.startswith("#"):
+            continue
+        f = ln.split()
+        rows[(f[0], f[1])] = [int(x) for x in f[2:]]
+    return rows
+
+
+@pytest.mark.parametrize("mode", ["warm", "cold"])
+def test_ring_addressing_trace(oracle_lib, mode):
+    rows = _ring_trace_rows()
+    cfg = _small(ctx=6, ring_k=4, band_r=1, steps=12)
+    W = cfg.n_warm if mode == "warm" else 0
+    res, *_ = _stream(oracle_lib, cfg, W=W, n_steps=0, want_ring=True)
+    assert list(res["ring_pos"]) == rows[(mode, "init")]
+    for n in range(1, 13):
+        res, *_ = _stream(oracle_lib, cfg, W=W, n_steps=n, want_ring=True)
+        assert list(res["ring_pos"]) == rows[(mode, str(cfg.ctx + n - 1))], n
+
+
+def test_nan_slot_never_selected(oracle_lib):
+    cfg = _small(n_protos=1, sigma=(0.0, 0.0), switch_p=0.0, steps=3)
+    K, V = wl.gen_kv(cfg)
+    qt, q, _, _ = wl.gen_queries(cfg)
+    W = cfg.n_warm
+    warm = qt[0, 0, :W].copy()
+    warm[-1, 3] = np.float32(np.nan)          # poison the most recent slot
+    res = oracle_lib.run_stream(K[0, 0], V[0, 0], warm, q[0, 0, :W], qt[0, 0, W:],
+                                q[0, 0, W:], ctx_len=cfg.ctx, ring_k=cfg.ring_k,
+                                band_r=cfg.band_r, thresh2=1e9, n_steps=1)
+    assert res["hit"][0] and res["p"][0] == cfg.ctx - 2
+    warm[:, 0] = np.float32(np.nan)           # every candidate poisoned
+    res = oracle_lib.run_stream(K[0, 0], V[0, 0], warm, q[0, 0, :W], qt[0, 0, W:],
+                                q[0, 0, W:], ctx_len=cfg.ctx, ring_k=cfg.ring_k,
+                                band_r=cfg.band_r, thresh2=1e9, n_steps=1)
+    assert not res["hit"][0] and res["dist"][0] == math.inf
