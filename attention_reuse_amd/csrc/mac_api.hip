@@ -1,0 +1,479 @@
+// C ABI of libmac_attention.so: argument validation, workspace layout,
+// stream/event ordering of the decode step.  Declared in mac_attention.h.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "mac_attention.h"
+#include "mac_internal.h"
+
+namespace mac {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(int B, int Hq, int Hkv, int D, int K, int T)
+{
+    WsLayout L;
+    const int G = Hq / Hkv;
+    L.nsplit = (K + kSlotsPerSplit - 1) / kSlotsPerSplit;
+    L.max_items = (int64_t)B * Hkv * ((int64_t)T / kChunk + 3);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    const size_t BH = (size_t)B * Hq, BG = (size_t)B * Hkv;
+    L.keys = take(BH * L.nsplit * sizeof(unsigned long long));
+    L.dec_start = take(BH * 4);
+    L.dec_slot = take(BH * 4);
+    L.grp_begin = take(BG * 4);
+    L.grp_count = take(BG * 4);
+    L.ctrl = take(64);
+    L.items = take((size_t)L.max_items * sizeof(WorkItem));
+    L.part_o = take((size_t)L.max_items * G * D * 4);
+    L.part_l = take((size_t)L.max_items * G * 4);
+    L.rect_o = take(BH * D * 4);
+    L.rect_l = take(BH * 4);
+    L.total = off;
+    return L;
+}
+
+WsPtrs ws_ptrs(void *base, const WsLayout &L)
+{
+    char *c = (char *)base;
+    WsPtrs w;
+    w.keys = (unsigned long long *)(c + L.keys);
+    w.dec_start = (int32_t *)(c + L.dec_start);
+    w.dec_slot = (int32_t *)(c + L.dec_slot);
+    w.grp_begin = (int32_t *)(c + L.grp_begin);
+    w.grp_count = (int32_t *)(c + L.grp_count);
+    w.ctrl = (int32_t *)(c + L.ctrl);
+    w.items = (WorkItem *)(c + L.items);
+    w.part_o = (float *)(c + L.part_o);
+    w.part_l = (float *)(c + L.part_l);
+    w.rect_o = (float *)(c + L.rect_o);
+    w.rect_l = (float *)(c + L.rect_l);
+    return w;
+}
+
+}  // namespace mac
+
+using namespace mac;
+
+constexpr int kStages = 5;
+
+struct mac_handle {
+    mac_params p;
+    Shape s;
+    WsLayout L;
+    WsPtrs w;
+    void *ws;
+    mac_rings rings;
+    hipEvent_t ev_main = nullptr, ev_aux = nullptr;
+    // Per-stage timing events: prof[(step * kStages + stage) * 2 + {0,1}].
+    std::vector<hipEvent_t> prof;
+    int32_t prof_cap = 0, prof_n = 0;
+};
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+static int elem_bytes(int32_t dtype) { return dtype == MAC_DTYPE_F32 ? 4 : 2; }
+
+// Host-side validation of the parameter block; fills the kernel shape.
+static mac_status check_params(const mac_params *p, Shape *s)
+{
+    if (!p)
+        return MAC_ERR_INVALID_ARG;
+    if (p->batch < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1 ||
+        p->n_q_heads % p->n_kv_heads != 0 || p->ring_k < 1 ||
+        p->band_r < 0 || p->kv_capacity < 1 || p->reserved != 0 ||
+        !isfinite(p->tau) || !isfinite(p->sm_scale) || p->sm_scale < 0.f ||
+        (p->thresh_mode != MAC_THRESH_ONE_MINUS_TAU &&
+         p->thresh_mode != MAC_THRESH_TAU))
+        return MAC_ERR_INVALID_ARG;
+    const int G = p->n_q_heads / p->n_kv_heads;
+    if ((p->head_dim != 64 && p->head_dim != 128) ||
+        (p->kv_dtype != MAC_DTYPE_F32 && p->kv_dtype != MAC_DTYPE_BF16) ||
+        (G != 1 && G != 2 && G != 4 && G != 8))
+        return MAC_ERR_UNSUPPORTED;
+    // Sizes are addressed with 32-bit work items and head indices.
+    if ((int64_t)p->batch * p->n_q_heads > (1 << 24) ||
+        (int64_t)p->kv_capacity > (1 << 30) || p->ring_k > (1 << 24))
+        return MAC_ERR_INVALID_ARG;
+    int64_t st = p->kv_stride_t, sh = p->kv_stride_h, sb = p->kv_stride_b;
+    if (st == 0 && sh == 0 && sb == 0) {
+        st = p->head_dim;
+        sh = st * p->kv_capacity;
+        sb = sh * p->n_kv_heads;
+    }
+    if (st < p->head_dim || sh < 0 || sb < 0)
+        return MAC_ERR_INVALID_ARG;
+    const int eb = elem_bytes(p->kv_dtype);
+    if ((st * eb) % 16 || (sh * eb) % 16 || (sb * eb) % 16)
+        return MAC_ERR_MISALIGNED;
+    if (s) {
+        const int d = p->head_dim;
+        const double scale = p->sm_scale != 0.f ? (double)p->sm_scale
+                                                : 1.0 / sqrt((double)d);
+        const double f = p->thresh_mode == MAC_THRESH_TAU
+                             ? (double)p->tau
+                             : 1.0 - (double)p->tau;
+        s->B = p->batch;
+        s->Hq = p->n_q_heads;
+        s->Hkv = p->n_kv_heads;
+        s->G = G;
+        s->D = d;
+        s->dtype = p->kv_dtype;
+        s->K = p->ring_k;
+        s->r = p->band_r;
+        s->T = p->kv_capacity;
+        s->kv_sb = sb;
+        s->kv_sh = sh;
+        s->kv_st = st;
+        s->qscale = (float)(scale * 1.4426950408889634);
+        s->thresh2 = (float)(2.0 * d * f * f);
+    }
+    return MAC_OK;
+}
+
+extern "C" {
+
+size_t mac_workspace_bytes(const mac_params *p)
+{
+    Shape s;
+    if (check_params(p, &s) != MAC_OK)
+        return 0;
+    return ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T).total;
+}
+
+mac_status mac_ring_bytes(const mac_params *p, size_t out[4])
+{
+    Shape s;
+    const mac_status st = check_params(p, &s);
+    if (st != MAC_OK)
+        return st;
+    if (!out)
+        return MAC_ERR_INVALID_ARG;
+    const size_t n = (size_t)s.B * s.Hq * s.K;
+    out[0] = n * s.D * elem_bytes(s.dtype);
+    out[1] = n * s.D * 4;
+    out[2] = n * 4;
+    out[3] = (size_t)s.B * s.K * 4;
+    return MAC_OK;
+}
+
+const char *mac_status_string(mac_status s)
+{
+    switch (s) {
+    case MAC_OK:
+        return "ok";
+    case MAC_ERR_INVALID_ARG:
+        return "invalid argument";
+    case MAC_ERR_UNSUPPORTED:
+        return "unsupported head_dim / dtype / GQA group";
+    case MAC_ERR_HIP:
+        return "HIP runtime error";
+    case MAC_ERR_WORKSPACE_TOO_SMALL:
+        return "workspace too small";
+    case MAC_ERR_MISALIGNED:
+        return "buffer or row not 16-byte aligned";
+    }
+    return "unknown status";
+}
+
+int32_t mac_chunk_tokens(void) { return kChunk; }
+
+int32_t mac_partition(int32_t s, int32_t e, int32_t r, int32_t *t0,
+                      int32_t *t1, int32_t cap)
+{
+    if (s < 0 || e < s || r < 0 || cap < 0)
+        return -1;
+    const RangeSplit rs(s, e, r);
+    for (int i = 0; i < rs.n && i < cap; ++i)
+        rs.item(i, t0[i], t1[i]);
+    return rs.n;
+}
+
+#define MAC_HIP(call)                      \
+    do {                                   \
+        if ((call) != hipSuccess)          \
+            return MAC_ERR_HIP;            \
+    } while (0)
+
+static mac_status full_engine(const Shape &s, const WsLayout &L,
+                              const WsPtrs &w, int32_t mode, int32_t offset,
+                              const float *q, int64_t q_sb, int64_t q_sh,
+                              const void *k, const void *v,
+                              const int32_t *pos, float *out, float *out_lse,
+                              hipStream_t st)
+{
+    MAC_HIP(launch_plan(s, mode, offset, pos, w, L.nsplit, L.max_items,
+                        nullptr, nullptr, st));
+    MAC_HIP(launch_attend(s, q, q_sb, q_sh, k, v, w, L.max_items, st));
+    MAC_HIP(launch_combine(s, offset, mode == kPlanInit, pos, w, nullptr,
+                           nullptr, out, out_lse, st));
+    return MAC_OK;
+}
+
+mac_status mac_full_decode(const mac_params *p, const float *q,
+                           const void *k_cache, const void *v_cache,
+                           const int32_t *pos, float *out, float *out_lse,
+                           void *workspace, size_t ws_bytes, void *stream)
+{
+    Shape s;
+    mac_status rc = check_params(p, &s);
+    if (rc != MAC_OK)
+        return rc;
+    if (!q || !k_cache || !v_cache || !pos || !out || !workspace)
+        return MAC_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        !aligned16(workspace))
+        return MAC_ERR_MISALIGNED;
+    const WsLayout L = ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T);
+    if (ws_bytes < L.total)
+        return MAC_ERR_WORKSPACE_TOO_SMALL;
+    const WsPtrs w = ws_ptrs(workspace, L);
+    return full_engine(s, L, w, kPlanFull, 0, q, (int64_t)s.Hq * s.D, s.D,
+                       k_cache, v_cache, pos, out, out_lse,
+                       (hipStream_t)stream);
+}
+
+mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
+                          void *workspace, size_t ws_bytes,
+                          const void *warm_qtilde, const float *warm_q,
+                          int32_t n_warm, const int32_t *ctx_len,
+                          const void *k_cache, const void *v_cache,
+                          void *stream, mac_handle **out)
+{
+    Shape s;
+    mac_status rc = check_params(p, &s);
+    if (rc != MAC_OK)
+        return rc;
+    if (!rings || !out || !workspace || !rings->q_ring || !rings->o_ring ||
+        !rings->lse_ring || !rings->pos_ring)
+        return MAC_ERR_INVALID_ARG;
+    if (!aligned16(rings->q_ring) || !aligned16(rings->o_ring) ||
+        !aligned16(workspace))
+        return MAC_ERR_MISALIGNED;
+    const WsLayout L = ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T);
+    if (ws_bytes < L.total)
+        return MAC_ERR_WORKSPACE_TOO_SMALL;
+    if (n_warm < 0 || n_warm > s.K)
+        return MAC_ERR_INVALID_ARG;
+    if (n_warm > 0) {
+        if (!warm_qtilde || !warm_q || !ctx_len || !k_cache || !v_cache)
+            return MAC_ERR_INVALID_ARG;
+        if (!aligned16(warm_qtilde) || !aligned16(warm_q) ||
+            !aligned16(k_cache) || !aligned16(v_cache))
+            return MAC_ERR_MISALIGNED;
+        for (int b = 0; b < s.B; ++b)
+            if (ctx_len[b] < n_warm || ctx_len[b] > s.T)
+                return MAC_ERR_INVALID_ARG;
+    }
+    hipStream_t st = (hipStream_t)stream;
+    const WsPtrs w = ws_ptrs(workspace, L);
+
+    mac_handle *h = new (std::nothrow) mac_handle();
+    if (!h)
+        return MAC_ERR_INVALID_ARG;
+    h->p = *p;
+    h->s = s;
+    h->L = L;
+    h->w = w;
+    h->ws = workspace;
+    h->rings = *rings;
+    if (hipEventCreateWithFlags(&h->ev_main, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_aux, hipEventDisableTiming) != hipSuccess) {
+        mac_release(h);
+        return MAC_ERR_HIP;
+    }
+    if (launch_ring_reset(s, rings->q_ring, rings->o_ring, rings->lse_ring,
+                          rings->pos_ring, w.ctrl, st) != hipSuccess) {
+        mac_release(h);
+        return MAC_ERR_HIP;
+    }
+    if (n_warm > 0) {
+        // Prompt lengths are staged in the match-key region, which the
+        // init path (plan in kPlanInit mode) never reads.
+        int32_t *d_ctx = (int32_t *)w.keys;
+        if (hipMemcpyAsync(d_ctx, ctx_len, sizeof(int32_t) * s.B,
+                           hipMemcpyHostToDevice, st) != hipSuccess ||
+            hipStreamSynchronize(st) != hipSuccess) {
+            mac_release(h);
+            return MAC_ERR_HIP;
+        }
+        Shape s0 = s;
+        s0.r = 0;  // the warm summary covers all of [0, t - r]
+        const int64_t wq_sh = (int64_t)n_warm * s.D;
+        const int64_t wq_sb = (int64_t)s.Hq * wq_sh;
+        for (int wi = 0; wi < n_warm; ++wi) {
+            // Warm position t = ctx_len - W + wi; summary of [0, t - r].
+            const int32_t t_off = wi - n_warm;
+            rc = full_engine(s0, L, w, kPlanInit, t_off - s.r,
+                             warm_q + (int64_t)wi * s.D, wq_sb, wq_sh,
+                             k_cache, v_cache, d_ctx, nullptr, nullptr, st);
+            if (rc == MAC_OK &&
+                launch_append(s, t_off, d_ctx,
+                              (const char *)warm_qtilde +
+                                  (int64_t)wi * s.D * elem_bytes(s.dtype),
+                              wq_sb, wq_sh, w, rings->q_ring, rings->o_ring,
+                              rings->lse_ring, rings->pos_ring,
+                              st) != hipSuccess)
+                rc = MAC_ERR_HIP;
+            if (rc != MAC_OK) {
+                mac_release(h);
+                return rc;
+            }
+        }
+    }
+    *out = h;
+    return MAC_OK;
+}
+
+mac_status mac_decode_step(mac_handle *h, const void *qtilde, const float *q,
+                           const void *k_cache, const void *v_cache,
+                           const int32_t *pos, float *out, float *out_lse,
+                           int32_t *match_p, float *match_d2,
+                           void *main_stream, void *aux_stream)
+{
+    if (!h || !qtilde || !q || !k_cache || !v_cache || !pos || !out)
+        return MAC_ERR_INVALID_ARG;
+    if (!aligned16(qtilde) || !aligned16(q) || !aligned16(k_cache) ||
+        !aligned16(v_cache))
+        return MAC_ERR_MISALIGNED;
+    const Shape &s = h->s;
+    const WsLayout &L = h->L;
+    const WsPtrs &w = h->w;
+    hipStream_t ms = (hipStream_t)main_stream;
+    hipStream_t as = aux_stream ? (hipStream_t)aux_stream : ms;
+    const bool split = as != ms;
+    const int64_t q_sh = s.D, q_sb = (int64_t)s.Hq * s.D;
+
+    const bool prof = h->prof_n < h->prof_cap;
+    hipEvent_t *pe = prof ? &h->prof[(size_t)h->prof_n * kStages * 2] : nullptr;
+#define MAC_STAGE(idx, stream_, launch)                         \
+    do {                                                        \
+        if (pe)                                                 \
+            MAC_HIP(hipEventRecord(pe[2 * (idx)], stream_));    \
+        MAC_HIP(launch);                                        \
+        if (pe)                                                 \
+            MAC_HIP(hipEventRecord(pe[2 * (idx) + 1], stream_)); \
+    } while (0)
+
+    // The previous rectify-append of this handle must have finished before
+    // the rings are read and the workspace is reused.
+    if (split)
+        MAC_HIP(hipStreamWaitEvent(ms, h->ev_aux, 0));
+    MAC_STAGE(0, ms,
+              launch_match(s, qtilde, q_sb, q_sh, h->rings.q_ring,
+                           h->rings.pos_ring, pos, w, L.nsplit, ms));
+    MAC_STAGE(1, ms,
+              launch_plan(s, kPlanMatch, 0, pos, w, L.nsplit, L.max_items,
+                          match_p, match_d2, ms));
+    MAC_STAGE(2, ms,
+              launch_attend(s, q, q_sb, q_sh, k_cache, v_cache, w,
+                            L.max_items, ms));
+    MAC_STAGE(3, ms,
+              launch_combine(s, 0, 0, pos, w, h->rings.o_ring,
+                             h->rings.lse_ring, out, out_lse, ms));
+    if (split) {
+        MAC_HIP(hipEventRecord(h->ev_main, ms));
+        MAC_HIP(hipStreamWaitEvent(as, h->ev_main, 0));
+    }
+    MAC_STAGE(4, as,
+              launch_append(s, 0, pos, qtilde, q_sb, q_sh, w, h->rings.q_ring,
+                            h->rings.o_ring, h->rings.lse_ring,
+                            h->rings.pos_ring, as));
+    if (split)
+        MAC_HIP(hipEventRecord(h->ev_aux, as));
+#undef MAC_STAGE
+    if (prof)
+        ++h->prof_n;
+    return MAC_OK;
+}
+
+mac_status mac_join_aux(mac_handle *h, void *stream)
+{
+    if (!h)
+        return MAC_ERR_INVALID_ARG;
+    MAC_HIP(hipStreamWaitEvent((hipStream_t)stream, h->ev_aux, 0));
+    return MAC_OK;
+}
+
+mac_status mac_read_device_status(const mac_params *p, void *workspace,
+                                  void *stream, int32_t *flags)
+{
+    Shape s;
+    mac_status rc = check_params(p, &s);
+    if (rc != MAC_OK)
+        return rc;
+    if (!workspace || !flags)
+        return MAC_ERR_INVALID_ARG;
+    const WsLayout L = ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T);
+    int32_t *ctrl = ws_ptrs(workspace, L).ctrl;
+    hipStream_t st = (hipStream_t)stream;
+    int32_t v = 0;
+    static const int32_t zero = 0;
+    MAC_HIP(hipMemcpyAsync(&v, ctrl + 1, sizeof v, hipMemcpyDeviceToHost, st));
+    MAC_HIP(hipStreamSynchronize(st));
+    MAC_HIP(hipMemcpyAsync(ctrl + 1, &zero, sizeof zero, hipMemcpyHostToDevice, st));
+    MAC_HIP(hipStreamSynchronize(st));
+    *flags = v;
+    return MAC_OK;
+}
+
+mac_status mac_profile_start(mac_handle *h, int32_t n_steps)
+{
+    if (!h || n_steps < 0)
+        return MAC_ERR_INVALID_ARG;
+    for (hipEvent_t e : h->prof)
+        (void)hipEventDestroy(e);
+    h->prof.assign((size_t)n_steps * kStages * 2, nullptr);
+    for (auto &e : h->prof)
+        MAC_HIP(hipEventCreate(&e));
+    h->prof_cap = n_steps;
+    h->prof_n = 0;
+    return MAC_OK;
+}
+
+mac_status mac_profile_read(mac_handle *h, double ms[5], int32_t *n)
+{
+    if (!h || !ms || !n)
+        return MAC_ERR_INVALID_ARG;
+    for (int k = 0; k < kStages; ++k)
+        ms[k] = 0.0;
+    for (int i = 0; i < h->prof_n; ++i)
+        for (int k = 0; k < kStages; ++k) {
+            hipEvent_t a = h->prof[((size_t)i * kStages + k) * 2];
+            hipEvent_t b = h->prof[((size_t)i * kStages + k) * 2 + 1];
+            float t = 0.f;
+            MAC_HIP(hipEventSynchronize(b));
+            MAC_HIP(hipEventElapsedTime(&t, a, b));
+            ms[k] += t;
+        }
+    *n = h->prof_n;
+    h->prof_cap = 0;
+    h->prof_n = 0;
+    return MAC_OK;
+}
+
+mac_status mac_release(mac_handle *h)
+{
+    if (!h)
+        return MAC_ERR_INVALID_ARG;
+    if (h->ev_main)
+        (void)hipEventDestroy(h->ev_main);
+    if (h->ev_aux)
+        (void)hipEventDestroy(h->ev_aux);
+    for (hipEvent_t e : h->prof)
+        if (e)
+            (void)hipEventDestroy(e);
+    delete h;
+    return MAC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,336 @@
+"""Decode-attention throughput of the MAC-Attention step on one MI355X.
+
+One step = one MAC decode step (match, plan, attention, merge,
+rectify-append) at one position m over NL independent copies of the
+attention layer (the layers of a model), each with its own K/V cache and
+rings, so the per-step working set is far larger than the 256 MB Infinity
+Cache.  Inputs are seeded synthetic data resident in HBM before timing.
+
+Prints one JSON line:  value = B * Hq * NL / t_step  (heads*layers per s).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from attention_reuse_amd import workload as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+STAGES = ("match", "plan", "attend", "combine", "append")
+KERNEL_NAMES = {"match": "match_kernel", "attend": "attend_kernel",
+                "combine": "combine_kernel", "plan": "plan_kernel",
+                "append": "append_kernel"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--config", type=int, default=2, choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layer copies per step (0 = enough to overflow the Infinity Cache)")
+    ap.add_argument("--mode", choices=("mac", "full"), default="mac")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--json-out", default="")
+    return ap.parse_args()
+
+
+def default_layers(cfg):
+    """Enough layer copies that one step touches >= 3x the 256 MB Infinity
+    Cache (rings plus a band+tail estimate per layer), so a layer's data is
+    evicted before the next step returns to it."""
+    e = cfg.elem_bytes
+    est = (cfg.batch * cfg.n_q_heads * cfg.ring_k * cfg.head_dim * e
+           + cfg.batch * cfg.n_kv_heads * (2 * cfg.band_r + 512) * cfg.head_dim * e * 2)
+    return int(max(1, min(64, math.ceil(768 * 2 ** 20 / est))))
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("mac_kernels.hip", "mac_api.hip", "mac_internal.h"):
+        h.update(open(os.path.join(ROOT, "attention_reuse_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload_name, kernel):
+    """HBM traffic per launch from committed rocprofv3 PMC summaries, if they
+    were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    want = source_hash()
+    for ln in open(path):
+        f = ln.split()
+        if len(f) >= 4 and not ln.startswith("#") and f[0] == workload_name and f[1] == kernel:
+            return float(f[2]) if f[3] == want else None
+    return None
+
+
+def algorithmic_bytes(cfg, match_p, m):
+    """Bytes the method must move per layer-step, by stage.
+
+    match_p: [B, Hq] matched position (-1 miss); m: [B] positions."""
+    B, H, Hkv, G, d = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.group, cfg.head_dim
+    e = cfg.elem_bytes
+    K_valid = min(cfg.ring_k, cfg.ctx)
+    match = B * H * K_valid * d * e + B * K_valid * 4 + B * H * d * e
+    start = np.where(match_p >= 0, np.maximum(0, match_p - cfg.band_r + 1), 0)
+    s_g = start.reshape(B, Hkv, G).min(axis=2)
+    span = (m[:, None] - s_g + 1).astype(np.int64)
+    kv = int(span.sum()) * d * e * 2
+    attend = kv + B * H * d * 4
+    hits = int((match_p >= 0).sum())
+    combine = hits * (d + 1) * 4 + B * H * (d + 1) * 4
+    append = B * H * (d * e + (d + 1) * 4) + B * 4
+    full_kv = int((m + 1).sum()) * Hkv * d * e * 2
+    return dict(match=match, attend=attend, combine=combine, append=append, plan=0,
+                kv=kv, full_kv=full_kv, hits=hits, group_miss=int(
+                    (match_p.reshape(B, Hkv, G) < 0).any(axis=2).sum()))
+
+
+def cpu_baseline(cfg, K, V, qt, q, budget_s):
+    """The CPU oracle, as is, on a bounded sample of the same workload."""
+    from oracle import oracle as orc
+
+    orc.build()
+    threads = min(16, os.cpu_count() or 1)
+    t2 = orc.threshold2(cfg.head_dim, cfg.tau)
+    W = cfg.n_warm
+    # Calibrate on one stream and a few steps, then size the sample.
+    probe_steps = min(8, cfg.steps)
+
+    def run(heads, n_steps):
+        res = orc.run_streams(K, V, qt, q, heads, ctx_len=cfg.ctx, n_warm=W,
+                              ring_k=cfg.ring_k, band_r=cfg.band_r, thresh2=t2,
+                              n_steps=n_steps, threads=threads)
+        warm = sum(r["warm_seconds"] for r in res.values())
+        return res, warm
+
+    t0 = time.perf_counter()
+    _, warm = run([(0, 0)], probe_steps)
+    per_step = max(1e-6, (time.perf_counter() - t0 - warm) / probe_steps)
+    all_heads = [(b, h) for b in range(cfg.batch) for h in range(cfg.n_q_heads)]
+    n_steps = int(min(cfg.steps, max(4, budget_s * threads / per_step / len(all_heads))))
+    heads = all_heads
+    if n_steps == 4 and per_step * 4 * len(all_heads) > budget_s * threads:
+        nh = max(threads, int(budget_s * threads / (per_step * 4)))
+        heads = all_heads[::max(1, len(all_heads) // nh)][:nh]
+    t0 = time.perf_counter()
+    res, warm = run(heads, n_steps)
+    wall = time.perf_counter() - t0
+    # Warm-summary evaluation (lazy, off the per-step path) is excluded,
+    # spread over the threads that ran it.
+    step_time = max(1e-9, wall - warm / threads)
+    value = len(heads) * n_steps / step_time
+    return dict(value=value, unit="heads*layers/s", cores=threads, kind="oracle",
+                sample="%d (request, head) streams x %d decode steps of %s, fp64 C "
+                       "oracle, %d threads, lazy warm summaries (%.1f s) excluded"
+                % (len(heads), n_steps, cfg.name, threads, warm))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from attention_reuse_amd import mac
+
+    mac.load()
+    dev = "cuda:0"
+    cfg = wl.WORKLOADS[args.config]
+    NL = args.layers or default_layers(cfg)
+    if args.warmup + args.steps > cfg.steps:
+        sys.exit("warmup + steps exceeds the %d decode steps of the workload" % cfg.steps)
+    B, H, Hkv, d, R, W = (cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim,
+                          cfg.ring_k, cfg.n_warm)
+    t_gen = time.perf_counter()
+    K, V = wl.gen_kv(cfg)
+    qt, q, _, _ = wl.gen_queries(cfg)
+    print("[bench] %s: inputs generated in %.1fs, %d layers" % (
+        cfg.name, time.perf_counter() - t_gen, NL), file=sys.stderr, flush=True)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    K0, V0 = to_dev(K), to_dev(V)
+    dec_qt = to_dev(np.moveaxis(qt[:, :, W:], 2, 0))   # [S, B, H, d]
+    dec_q = to_dev(np.moveaxis(q[:, :, W:], 2, 0))
+    pos_np = wl.decode_positions(cfg)
+    pos = to_dev(pos_np)
+    p = mac.make_params(B, H, Hkv, d, mac.MAC_DTYPE_F32 if cfg.dtype == "f32" else mac.MAC_DTYPE_BF16,
+                        R, cfg.band_r, cfg.capacity, cfg.tau)
+    wsb = mac.mac_workspace_bytes(p)
+    stream = torch.cuda.current_stream()
+    st = stream.cuda_stream
+    aux = torch.cuda.Stream()
+
+    layers = []
+    for li in range(NL):
+        L = dict(K=K0 if li == 0 else K0.clone(), V=V0 if li == 0 else V0.clone(),
+                 q_ring=torch.zeros((B, H, R, d), dtype=K0.dtype, device=dev),
+                 o_ring=torch.zeros((B, H, R, d), device=dev),
+                 lse_ring=torch.zeros((B, H, R), device=dev),
+                 pos_ring=torch.zeros((B, R), dtype=torch.int32, device=dev),
+                 ws=torch.empty(wsb, dtype=torch.uint8, device=dev),
+                 out=torch.empty((B, H, d), device=dev))
+        layers.append(L)
+    # Warm the rings of layer 0 from the prompt tail; the other layers copy them.
+    L0 = layers[0]
+    h0 = mac.mac_init_rings(p, L0["q_ring"], L0["o_ring"], L0["lse_ring"], L0["pos_ring"],
+                            L0["ws"], wsb, to_dev(qt[:, :, :W]), to_dev(q[:, :, :W]), W,
+                            [cfg.ctx] * B, L0["K"], L0["V"], st)
+    torch.cuda.synchronize()
+    warm_state = [L0[k].clone() for k in ("q_ring", "o_ring", "lse_ring", "pos_ring")]
+    mac.mac_release(h0)
+
+    def reset_rings():
+        for L in layers:
+            if L.get("h"):
+                mac.mac_release(L["h"])
+            L["h"] = mac.mac_init_rings(p, L["q_ring"], L["o_ring"], L["lse_ring"],
+                                        L["pos_ring"], L["ws"], wsb, None, None, 0,
+                                        [cfg.ctx] * B, L["K"], L["V"], st)
+            for k, src in zip(("q_ring", "o_ring", "lse_ring", "pos_ring"), warm_state):
+                L[k].copy_(src)
+        torch.cuda.synchronize()
+
+    match_rec = torch.full((cfg.steps, NL, B, H), -1, dtype=torch.int32, device=dev)
+
+    def step(s, record=True):
+        for li, L in enumerate(layers):
+            if args.mode == "mac":
+                mac.mac_decode_step(L["h"], dec_qt[s], dec_q[s], L["K"], L["V"], pos[s],
+                                    L["out"], None, match_rec[s, li] if record else None,
+                                    None, st, aux.cuda_stream)
+            else:
+                mac.mac_full_decode(p, dec_q[s], L["K"], L["V"], pos[s], L["out"], None,
+                                    L["ws"], wsb, st)
+
+    reset_rings()
+    for s in range(args.warmup):
+        step(s)
+    for L in layers:
+        mac.mac_join_aux(L["h"], st)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(args.warmup, args.warmup + args.steps):
+        step(s)
+    for L in layers:
+        mac.mac_join_aux(L["h"], st)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / args.steps
+    print("[bench] timed %d steps: %.3f ms/step" % (args.steps, ms_per_step),
+          file=sys.stderr, flush=True)
+
+    # Algorithmic bytes of the timed steps (from the recorded decisions).
+    mrec = match_rec.cpu().numpy()
+    per = {k: 0.0 for k in ("match", "attend", "combine", "append", "plan", "kv", "full_kv",
+                            "hits", "group_miss")}
+    timed = range(args.warmup, args.warmup + args.steps)
+    for s in timed:
+        for li in range(NL):
+            mp = mrec[s, li] if args.mode == "mac" else np.full((B, H), -1, np.int32)
+            ab = algorithmic_bytes(cfg, mp, pos_np[s].astype(np.int64))
+            for k in per:
+                per[k] += ab[k]
+    n_ls = args.steps * NL
+    per_launch = {k: v / n_ls for k, v in per.items()}
+
+    # Per-stage kernel durations with HIP events, on the stream each stage
+    # runs on, over a second pass of the same steps.
+    stage_ms = None
+    if not args.no_profile and args.mode == "mac":
+        reset_rings()
+        for s in range(args.warmup):
+            step(s, record=False)
+        for L in layers:
+            mac.mac_join_aux(L["h"], st)
+            mac.mac_profile_start(L["h"], args.steps)
+        for s in timed:
+            step(s, record=False)
+        tot = {k: 0.0 for k in STAGES}
+        cnt = 0
+        for L in layers:
+            mac.mac_join_aux(L["h"], st)
+            ms, n = mac.mac_profile_read(L["h"])
+            cnt += n
+            for k in STAGES:
+                tot[k] += ms[k]
+        stage_ms = {k: tot[k] / max(cnt, 1) for k in STAGES}
+
+    roofline = None
+    if stage_ms:
+        dom = max(("match", "attend"), key=lambda k: stage_ms[k])
+        ach = per_launch[dom] / (stage_ms[dom] * 1e-3) / 1e9
+        roofline = dict(bound="hbm", kernel=KERNEL_NAMES[dom], achieved=round(ach, 1),
+                        peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4),
+                        traffic=read_traffic(cfg.name, KERNEL_NAMES[dom]),
+                        alg_bytes_per_launch=int(per_launch[dom]),
+                        avg_launch_us=round(stage_ms[dom] * 1e3, 2))
+    elif args.mode == "full":
+        ach = per_launch["attend"] / (ms_per_step / NL * 1e-3) / 1e9
+        roofline = dict(bound="hbm", kernel="full decode step", achieved=round(ach, 1),
+                        peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4),
+                        traffic=None)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(cfg, K, V, qt, q, args.cpu_seconds)
+
+    alg_step = sum(per[k] for k in ("match", "attend", "combine", "append")) / args.steps
+    value = B * H * NL / (ms_per_step * 1e-3)
+    line = {
+        "metric": "decode attention steps/sec (heads*layers) + KV GB read/step + % HBM roofline",
+        "value": round(value, 1),
+        "unit": "heads*layers/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 in / fp32 accumulate" if cfg.dtype == "bf16" else "fp32",
+        "data": "synthetic (seeded N(0,1) K/V, prototype+noise query stream)",
+        "config": {"workload": cfg.name, "mode": args.mode, "layers": NL,
+                   "batch": B, "q_heads": H, "kv_heads": Hkv, "head_dim": d,
+                   "context": cfg.ctx, "ring_k": R, "band_r": cfg.band_r, "tau": cfg.tau,
+                   "parallelism": "1 GPU"},
+        "kv_gb_per_step": round(per["kv"] / args.steps / 1e9, 4),
+        "full_kv_gb_per_step": round(per["full_kv"] / args.steps / 1e9, 4),
+        "alg_gb_per_step": round(alg_step / 1e9, 4),
+        "step_hbm_frac": round(alg_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "hit_rate": round(per["hits"] / (n_ls * B * H), 4),
+        "group_miss_rate": round(per["group_miss"] / (n_ls * B * Hkv), 4),
+        "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()} if stage_ms else None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(s + "\n")
+    for L in layers:
+        mac.mac_release(L["h"])
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+/*
+ * mac_attention.h -- C ABI of the MI355X (gfx950) MAC-Attention decode step.
+ *
+ * MAC-Attention (Match-Amend-Complete) reuses attention across decode steps
+ * of one request: the current pre-RoPE query is matched against a ring of the
+ * last K pre-RoPE queries; on a hit at position p the cached, rectified
+ * attention summary of [0, p-r] is merged with fresh attention over
+ * [p-r+1, m]; on a miss the step is exact full attention; afterwards the new
+ * query and its rectified summary of [0, m-r] are appended to the rings.
+ *
+ * Sources: "MAC-Attention: Match-Amend-Complete attention reuse, up to 99%
+ * less KV reading in long-context decoding (MLSys 2026)" (blog post),
+ * sections "Decomposable representation of attention", "Reuse", "Match
+ * (1)-(3)", "Amend", "Complete" and "Paper version: the K1/K2/K3
+ * micro-pipeline"; "Attention Cache and Sequence Parallelism", section "MHA:
+ * per-token K/V" for the baseline decode semantics.
+ *
+ * Conventions for every entry point:
+ *  - All buffers are DEVICE pointers owned by the caller, unless noted.  The
+ *    library never allocates device memory; mac_init_rings allocates one
+ *    small host-side handle holding two HIP events.
+ *  - Streams are hipStream_t passed as void* (NULL = the null stream).
+ *  - Positions are 0-indexed.  At decode position m the query attends the
+ *    cached positions [0, m] (the caller has already written K_m, V_m).
+ *  - GQA: query head h reads KV head h / G with G = n_q_heads / n_kv_heads.
+ *  - Logits are scale * <q, K_t>, scale = 1/sqrt(d) unless sm_scale != 0.
+ *  - Summaries are (o, lse): the normalised output o = S/Z and lse = ln Z.
+ *  - Every call validates its arguments on the host first and returns an
+ *    error code without launching anything if they are invalid.  Calls
+ *    return without a host synchronisation; device-side errors (positions
+ *    out of range) of the latest call on a workspace are recorded in it and
+ *    read with mac_read_device_status().  No call aborts the process.
+ */
+#ifndef MAC_ATTENTION_H
+#define MAC_ATTENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mac_status {
+    MAC_OK = 0,
+    MAC_ERR_INVALID_ARG = -1,         /* null pointer, bad size or stride   */
+    MAC_ERR_UNSUPPORTED = -2,         /* head_dim / dtype / group not built */
+    MAC_ERR_HIP = -3,                 /* a HIP runtime call failed          */
+    MAC_ERR_WORKSPACE_TOO_SMALL = -4, /* ws_bytes < mac_workspace_bytes()   */
+    MAC_ERR_MISALIGNED = -5           /* a buffer or row not 16-B aligned   */
+} mac_status;
+
+/* Element type of the K/V cache, of the pre-RoPE queries and of the query
+ * ring.  Post-RoPE queries, outputs and summaries are always fp32. */
+enum { MAC_DTYPE_F32 = 0, MAC_DTYPE_BF16 = 1 };
+
+/* Acceptance rule of a match with squared L2 distance D (blog, "Match (2)"):
+ *   MAC_THRESH_ONE_MINUS_TAU: D < 2d (1-tau)^2   -- the blog's worked
+ *       example (d=128, tau=0.45 -> distance 8.8) and its pseudocode;
+ *   MAC_THRESH_TAU:           D < 2d tau^2       -- the paper summary's form.
+ * The squared threshold is computed in fp64 from the fp32 tau and rounded
+ * once to fp32. */
+enum { MAC_THRESH_ONE_MINUS_TAU = 0, MAC_THRESH_TAU = 1 };
+
+/* Device status flags latched in the workspace. */
+enum { MAC_DEV_BAD_POSITION = 1 /* some m outside [0, kv_capacity) */ };
+
+typedef struct mac_params {
+    int32_t batch;        /* B requests                                      */
+    int32_t n_q_heads;    /* Hq                                              */
+    int32_t n_kv_heads;   /* Hkv; G = Hq / Hkv must be 1, 2, 4 or 8          */
+    int32_t head_dim;     /* d: 64 or 128                                    */
+    int32_t kv_dtype;     /* MAC_DTYPE_*                                     */
+    int32_t ring_k;       /* K >= 1: ring capacity = match window            */
+    int32_t band_r;       /* r >= 0: rectification band                      */
+    int32_t kv_capacity;  /* T: positions held per (request, KV head)        */
+    float tau;            /* threshold parameter                             */
+    int32_t thresh_mode;  /* MAC_THRESH_*                                    */
+    float sm_scale;       /* logit scale; 0 means 1/sqrt(d)                  */
+    int32_t reserved;     /* must be 0                                       */
+    /* K/V cache strides in elements; all 0 means dense [B, Hkv, T, d].
+     * Row t of (b, g) starts at b*kv_stride_b + g*kv_stride_h + t*kv_stride_t
+     * and must be 16-byte aligned. */
+    int64_t kv_stride_b, kv_stride_h, kv_stride_t;
+} mac_params;
+
+/* Ring buffers of one attention layer, caller-allocated device memory:
+ *   q_ring   [B, Hq, K, d] kv_dtype  pre-RoPE queries of the last K positions
+ *   o_ring   [B, Hq, K, d] fp32      rectified summaries: normalised output
+ *   lse_ring [B, Hq, K]    fp32      rectified summaries: ln Z (-inf = empty)
+ *   pos_ring [B, K]        int32     position held by each slot (-1 = empty)
+ * Slot of position t is t mod K.  Sizes: mac_ring_bytes(). */
+typedef struct mac_rings {
+    void *q_ring;
+    float *o_ring;
+    float *lse_ring;
+    int32_t *pos_ring;
+} mac_rings;
+
+typedef struct mac_handle mac_handle;
+
+/* Bytes of device workspace the decode and full-decode calls need. */
+size_t mac_workspace_bytes(const mac_params *p);
+
+/* Bytes of each ring buffer: out[0..3] = q_ring, o_ring, lse_ring, pos_ring. */
+mac_status mac_ring_bytes(const mac_params *p, size_t out[4]);
+
+/*
+ * mac_init_rings -- reset one layer's rings and bind them to a handle.
+ *
+ * Every slot is emptied (pos -1, lse -inf).  With n_warm = W > 0 the last W
+ * prompt positions t = ctx_len[b] - W + w (w = 0..W-1) are pre-filled: slot
+ * t mod K receives the pre-RoPE query warm_qtilde[b, h, w, :], the summary of
+ * full attention of the post-RoPE query warm_q[b, h, w, :] over [0, t-r]
+ * (empty when t < r) and pos t.  W must not exceed K, and ctx_len[b] >= W.
+ *   warm_qtilde [B, Hq, W, d] kv_dtype   (device; ignored when W = 0)
+ *   warm_q      [B, Hq, W, d] fp32       (device; ignored when W = 0)
+ *   ctx_len     [B] int32 on the HOST: the prompt length of each request.
+ *   k_cache, v_cache: the layer's cache laid out as described in mac_params.
+ *   workspace: >= mac_workspace_bytes(p) device bytes, kept by the handle and
+ *   used by every later mac_decode_step on it (one workspace per handle).
+ * The rings and workspace must stay valid until mac_release().  On success
+ * *out receives a new handle; the work is enqueued on `stream`.
+ */
+mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
+                          void *workspace, size_t ws_bytes,
+                          const void *warm_qtilde, const float *warm_q,
+                          int32_t n_warm, const int32_t *ctx_len,
+                          const void *k_cache, const void *v_cache,
+                          void *stream, mac_handle **out);
+
+/*
+ * mac_decode_step -- one Match-Amend-Complete decode step of one layer.
+ *   qtilde  [B, Hq, d] kv_dtype  pre-RoPE query at position m
+ *   q       [B, Hq, d] fp32      post-RoPE query at position m
+ *   pos     [B] int32 (device)   m per request, 0 <= m < kv_capacity
+ *   out     [B, Hq, d] fp32      attention output
+ *   out_lse [B, Hq] fp32 or NULL ln Z of the output
+ *   match_p [B, Hq] int32 or NULL  matched position, -1 on a miss
+ *   match_d2[B, Hq] fp32 or NULL   squared distance of the nearest candidate
+ *                                  (+inf when the window is empty)
+ * Match, amend and complete run on main_stream; the rectify-append of the
+ * rings runs on aux_stream (main_stream if NULL or equal), ordered after the
+ * merge by an event; the next call on the same handle waits for it.  Returns
+ * without a host synchronisation, so a steady-state step can be captured
+ * into a HIP graph (join aux_stream back with mac_join_aux first).
+ */
+mac_status mac_decode_step(mac_handle *h, const void *qtilde, const float *q,
+                           const void *k_cache, const void *v_cache,
+                           const int32_t *pos, float *out, float *out_lse,
+                           int32_t *match_p, float *match_d2,
+                           void *main_stream, void *aux_stream);
+
+/* Make `stream` wait for the last rectify-append enqueued on the handle. */
+mac_status mac_join_aux(mac_handle *h, void *stream);
+
+/*
+ * mac_full_decode -- exact split-KV decode attention over [0, pos[b]] for
+ * every (request, query head); the miss path of mac_decode_step runs the
+ * same kernels on the same partition, so a forced miss gives bitwise the
+ * same output.  Arguments as in mac_decode_step; needs a workspace of
+ * mac_workspace_bytes(p) (not shared with a concurrently running handle).
+ */
+mac_status mac_full_decode(const mac_params *p, const float *q,
+                           const void *k_cache, const void *v_cache,
+                           const int32_t *pos, float *out, float *out_lse,
+                           void *workspace, size_t ws_bytes, void *stream);
+
+/* Read (with a synchronisation of `stream`) and clear the device status
+ * flags (MAC_DEV_*) of the latest call on a workspace laid out for p. */
+mac_status mac_read_device_status(const mac_params *p, void *workspace,
+                                  void *stream, int32_t *flags);
+
+/* Per-stage timing with HIP events (diagnostics).  mac_profile_start arms
+ * recording for the next `n_steps` decode steps of the handle; stages are
+ * 0 match, 1 plan, 2 attention, 3 merge, 4 rectify-append.
+ * mac_profile_read synchronises, returns the summed milliseconds per stage
+ * in ms[5] and the number of recorded steps in *n, and disarms. */
+mac_status mac_profile_start(mac_handle *h, int32_t n_steps);
+mac_status mac_profile_read(mac_handle *h, double ms[5], int32_t *n);
+
+/* Free the handle and its events (not the caller's buffers). */
+mac_status mac_release(mac_handle *h);
+
+const char *mac_status_string(mac_status s);
+
+/* Tokens per attention work item (the fixed split-KV partition). */
+int32_t mac_chunk_tokens(void);
+
+/* The split-KV partition the kernels use for a KV group whose heads attend
+ * [s, e] with band r (host mirror of the device planner): item i covers
+ * [t0[i], t1[i]); boundaries are s, the multiples of mac_chunk_tokens() in
+ * (s, e], the rectify split e - r + 1 when inside (s, e], and e + 1.
+ * Writes min(n, cap) items (host arrays) and returns n, or -1 on bad input. */
+int32_t mac_partition(int32_t s, int32_t e, int32_t r, int32_t *t0,
+                      int32_t *t1, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MAC_ATTENTION_H */

@@ -1,0 +1,135 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before touching a device (runs without a GPU)."""
+import ctypes
+import subprocess
+
+import pytest
+
+from attention_reuse_amd import mac
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mac.load()
+
+
+def _params(**kw):
+    base = dict(batch=2, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                kv_dtype=mac.MAC_DTYPE_BF16, ring_k=1024, band_r=256,
+                kv_capacity=4096, tau=0.6)
+    base.update(kw)
+    return mac.make_params(**base)
+
+
+def test_exports_every_declared_function(lib):
+    names = mac.header_functions()
+    assert len(names) >= 12
+    out = subprocess.check_output(["nm", "-D", "--defined-only", mac.LIB_PATH]).decode()
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(mac.mac_params) == 72
+    assert mac.mac_params.kv_stride_b.offset == 48
+    assert ctypes.sizeof(mac.mac_rings) == 32
+
+
+def test_status_strings_and_chunk(lib):
+    assert mac.mac_status_string(0) == "ok"
+    assert "workspace" in mac.mac_status_string(-4)
+    assert mac.mac_chunk_tokens() == 128
+
+
+def test_workspace_and_ring_sizes(lib):
+    p = _params()
+    ws = mac.mac_workspace_bytes(p)
+    assert ws > 0
+    # 2 x 32 heads x 1024 slots x 128 dims: bf16 query ring, fp32 summaries.
+    assert mac.mac_ring_bytes(p) == (2 * 32 * 1024 * 128 * 2, 2 * 32 * 1024 * 128 * 4,
+                                     2 * 32 * 1024 * 4, 2 * 1024 * 4)
+    # The workspace grows with the KV capacity (split-KV partials).
+    assert mac.mac_workspace_bytes(_params(kv_capacity=65536)) > ws
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), -2), (dict(kv_dtype=7), -2), (dict(n_q_heads=48, n_kv_heads=3), -2),
+    (dict(n_q_heads=30), -1), (dict(ring_k=0), -1), (dict(band_r=-1), -1),
+    (dict(batch=0), -1), (dict(kv_capacity=0), -1), (dict(tau=float("nan")), -1),
+    (dict(thresh_mode=2), -1), (dict(strides=(0, 0, 100)), -1),
+    (dict(strides=(1 << 20, 4096 * 136, 136)), 0), (dict(strides=(1 << 20, 4096 * 132, 132)), -5),
+])
+def test_param_validation(lib, kw, status):
+    p = _params(**kw)
+    rc = lib.mac_full_decode(ctypes.byref(p), 0x1000, 0x2000, 0x3000, 0x4000,
+                             None, None, None, 0, None)
+    # Valid parameters then fail on the NULL output / workspace pointers.
+    assert rc == (status if status != 0 else -1)
+    assert (mac.mac_workspace_bytes(p) > 0) == (status == 0)
+
+
+def test_pointer_validation_happens_before_any_device_call(lib):
+    p = _params()
+    ws = mac.mac_workspace_bytes(p)
+    # Misaligned query pointer.
+    rc = lib.mac_full_decode(ctypes.byref(p), 0x1004, 0x2000, 0x3000, 0x4000,
+                             0x5000, None, 0x6000, ws, None)
+    assert rc == -5
+    # Workspace too small.
+    rc = lib.mac_full_decode(ctypes.byref(p), 0x1000, 0x2000, 0x3000, 0x4000,
+                             0x5000, None, 0x6000, ws - 1, None)
+    assert rc == -4
+    # Decode step with a NULL handle.
+    assert lib.mac_decode_step(None, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000,
+                               0x1000, None, None, None, None, None) == -1
+    # Init: more warm positions than ring slots, and a prompt shorter than W.
+    rings = mac.mac_rings(0x1000, 0x2000, 0x3000, 0x4000)
+    h = ctypes.c_void_p()
+    ctx = (ctypes.c_int32 * 2)(4096, 4096)
+    rc = lib.mac_init_rings(ctypes.byref(p), ctypes.byref(rings), 0x6000, ws,
+                            0x7000, 0x8000, 1025, ctx, 0x9000, 0xa000, None,
+                            ctypes.byref(h))
+    assert rc == -1
+    ctx = (ctypes.c_int32 * 2)(4096, 100)
+    rc = lib.mac_init_rings(ctypes.byref(p), ctypes.byref(rings), 0x6000, ws,
+                            0x7000, 0x8000, 512, ctx, 0x9000, 0xa000, None,
+                            ctypes.byref(h))
+    assert rc == -1
+    assert lib.mac_release(None) == -1
+    assert lib.mac_profile_start(None, 3) == -1
+    f = ctypes.c_int32()
+    assert lib.mac_read_device_status(ctypes.byref(p), None, None, ctypes.byref(f)) == -1
+
+
+def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
+    monkeypatch.setattr(mac, "_lib", None)
+    monkeypatch.setattr(mac, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        mac.load()
+
+
+@pytest.mark.parametrize("s,e,r", [(0, 0, 0), (0, 127, 32), (0, 128, 32), (5, 1000, 256),
+                                   (300, 1000, 256), (900, 1000, 256), (0, 262399, 256),
+                                   (1000, 1000, 0), (0, 500, 1000), (640, 1000, 361)])
+def test_partition_covers_range_on_the_grid(lib, s, e, r):
+    """Items tile [s, e] in order; every interior boundary is a multiple of the
+    chunk or the rectify split e - r + 1; no item crosses either."""
+    C = mac.mac_chunk_tokens()
+    items = mac.mac_partition(s, e, r)
+    assert items[0][0] == s and items[-1][1] == e + 1
+    for (a0, a1), (b0, _) in zip(items, items[1:]):
+        assert a1 == b0
+    sp = e - r + 1
+    for t0, t1 in items:
+        assert t0 < t1 <= t0 + C
+        assert (t0 // C) == ((t1 - 1) // C)                  # inside one grid chunk
+        assert not (t0 < sp < t1)                            # never straddles the split
+        if t0 != s:
+            assert t0 % C == 0 or t0 == sp
+    # A miss head (s = 0) gets the same items as a full decode.
+    if s == 0:
+        assert items == mac.mac_partition(0, e, r)
+    assert lib.mac_partition(5, 4, 0, None, None, 0) == -1

@@ -1,0 +1,223 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs, at sizes the oracle finishes in seconds that still span
+several 128-token work items and a ragged tail."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from attention_reuse_amd import mac
+from attention_reuse_amd import workload as wl
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from mac_harness import (DEV, Layer, lockstep_compare, params_for, run_steps,
+                             to_dev, tolerance_check)
+
+
+def _cfg(**kw):
+    base = dict(name="t", batch=2, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                dtype="bf16", ctx=3000, steps=40, ring_k=256, band_r=64, tau=0.6,
+                rope_base=5e5, n_protos=16, switch_p=0.1, sigma=(0.05, 0.05), seed=0)
+    base.update(kw)
+    return wl.Workload(**base)
+
+
+def _inputs(cfg):
+    K, V = wl.gen_kv(cfg)
+    qt, q, _, _ = wl.gen_queries(cfg)
+    return K, V, qt, q
+
+
+@pytest.mark.parametrize("shape", [
+    dict(batch=1, n_q_heads=4, n_kv_heads=1, head_dim=64, dtype="f32", ctx=2048, steps=64),
+    dict(batch=3, n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16", ctx=1000, steps=8),
+    dict(batch=2, n_q_heads=4, n_kv_heads=4, head_dim=64, dtype="bf16", ctx=700, steps=4),
+    dict(batch=1, n_q_heads=16, n_kv_heads=2, head_dim=128, dtype="f32", ctx=500, steps=4),
+    dict(batch=2, n_q_heads=8, n_kv_heads=4, head_dim=128, dtype="bf16", ctx=300, steps=4),
+])
+def test_full_decode_matches_oracle(oracle_lib, shape):
+    cfg = _cfg(**shape)
+    print("full decode", shape, flush=True)
+    K, V, qt, q = _inputs(cfg)
+    p = params_for(cfg)
+    ws_b = mac.mac_workspace_bytes(p)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=DEV)
+    Kd, Vd = to_dev(K), to_dev(V)
+    # Ragged positions per request, including m = 0, a chunk boundary and a
+    # chunk tail.
+    choices = [[0, 127, 128, 129, cfg.capacity - 1], [cfg.capacity - 1, 5, 255, 256, 1000 % cfg.capacity]]
+    for pos_list in choices:
+        m = np.array([pos_list[b % len(pos_list)] for b in range(cfg.batch)], np.int32)
+        qq = q[:, :, cfg.n_warm]
+        out = torch.empty((cfg.batch, cfg.n_q_heads, cfg.head_dim), device=DEV)
+        lse = torch.empty((cfg.batch, cfg.n_q_heads), device=DEV)
+        mac.mac_full_decode(p, to_dev(qq), Kd, Vd, to_dev(m), out, lse, ws, ws_b,
+                            torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        ref_o, ref_l = oracle_lib.full_decode(qq, K, V, m)
+        ok, err = tolerance_check(cfg, out.cpu().numpy(), ref_o)
+        assert ok, err
+        np.testing.assert_allclose(lse.cpu().numpy(), ref_l, atol=1e-4)
+        assert mac.mac_read_device_status(p, ws) == 0
+
+
+def _lockstep(oracle_lib, cfg, layer=None, heads=None, n_warm=None, want_ring=True):
+    K, V, qt, q = _inputs(cfg)
+    layer = layer or Layer(cfg, K, V, qt, q, n_warm=n_warm)
+    layer.init()
+    aux = torch.cuda.Stream()
+    gpu = run_steps(layer, cfg.steps, aux=aux)
+    heads = heads or [(b, h) for b in range(cfg.batch) for h in range(cfg.n_q_heads)]
+    W = layer.n_warm
+    nw = cfg.n_warm
+    t2 = oracle_lib.threshold2(cfg.head_dim, cfg.tau)
+    res = {}
+    for (b, h) in heads:
+        g = h // cfg.group
+        res[(b, h)] = oracle_lib.run_stream(
+            K[b, g], V[b, g], qt[b, h, nw - W:nw], q[b, h, nw - W:nw], qt[b, h, nw:],
+            q[b, h, nw:], ctx_len=cfg.ctx, ring_k=cfg.ring_k, band_r=cfg.band_r,
+            thresh2=t2, want_ring=want_ring)
+    stats = dict(hits=0, steps=0, exempt=0, diverged=0)
+    qr = layer.q_ring.cpu().float().numpy() if want_ring else None
+    orr = layer.o_ring.cpu().numpy() if want_ring else None
+    lr = layer.lse_ring.cpu().numpy() if want_ring else None
+    pr = layer.pos_ring.cpu().numpy() if want_ring else None
+    for (b, h), o in res.items():
+        n, ex, div = lockstep_compare(cfg, gpu, o, b, h, cfg.steps)
+        stats["steps"] += n
+        stats["exempt"] += ex
+        stats["hits"] += int(o["hit"][:n].sum())
+        if div is not None:
+            stats["diverged"] += 1
+            continue
+        if want_ring:
+            assert np.array_equal(pr[b], o["ring_pos"]), (b, h)
+            np.testing.assert_array_equal(qr[b, h], o["ring_q"])
+            fin = np.isfinite(o["ring_lse"])
+            assert np.array_equal(np.isfinite(lr[b, h]), fin)
+            np.testing.assert_allclose(lr[b, h][fin], o["ring_lse"][fin], atol=1e-3)
+            ok, err = tolerance_check(cfg, orr[b, h], o["ring_o"])
+            assert ok, err
+    print(cfg.name, stats, flush=True)
+    return gpu, res, stats, layer
+
+
+def test_lockstep_tiny_f32_config(oracle_lib):
+    """The tiny CPU-checkable configuration at full size: 1 request, 4 query
+    heads on 1 KV head, d=64 fp32, 2048 context, 64 steps, K=64, r=32."""
+    cfg = wl.WORKLOADS[1]
+    _, _, st, _ = _lockstep(oracle_lib, cfg)
+    assert st["diverged"] == 0 and st["hits"] > 0.8 * st["steps"]
+
+
+def test_lockstep_gqa_bf16(oracle_lib):
+    cfg = _cfg()
+    _, _, st, _ = _lockstep(oracle_lib, cfg)
+    assert st["hits"] > 0.9 * st["steps"]
+
+
+def test_lockstep_mixed_hit_miss(oracle_lib):
+    """Per-head noise U[0.02, 0.5]: hits and misses mix inside GQA groups."""
+    cfg = _cfg(batch=2, ctx=2000, steps=40, ring_k=128, band_r=64, sigma=(0.02, 0.5), seed=3)
+    gpu, res, st, _ = _lockstep(oracle_lib, cfg)
+    rate = st["hits"] / st["steps"]
+    assert 0.3 < rate < 0.97, rate
+
+
+def test_lockstep_cold_ring_and_edges(oracle_lib):
+    # Cold ring: the first step has no candidate.
+    cfg = _cfg(batch=1, n_q_heads=8, n_kv_heads=2, ctx=600, steps=30, ring_k=16, band_r=8)
+    gpu, res, st, _ = _lockstep(oracle_lib, cfg, n_warm=0)
+    assert (gpu["p"][0] == -1).all()
+    # r = 0 (nothing recomputed before the match), K = 1 (only m-1 is a candidate),
+    # r larger than the context (hits are full attention).
+    for kw in (dict(band_r=0), dict(ring_k=1, band_r=3), dict(band_r=5000, ctx=200)):
+        _lockstep(oracle_lib, cfg.replace(**kw))
+
+
+def test_forced_miss_is_bitwise_full_decode():
+    """tau = 1 makes the threshold 0: every step misses and must equal the
+    full decode bit for bit (same partition, same fold order)."""
+    cfg = _cfg(steps=6)
+    K, V, qt, q = _inputs(cfg)
+    p = params_for(cfg, tau=1.0)
+    layer = Layer(cfg, K, V, qt, q, params=p).init()
+    gpu = run_steps(layer, cfg.steps, aux=torch.cuda.Stream())
+    assert (gpu["p"] == -1).all()
+    ws_b = mac.mac_workspace_bytes(p)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=DEV)
+    pos = wl.decode_positions(cfg)
+    for s in range(cfg.steps):
+        out = torch.empty((cfg.batch, cfg.n_q_heads, cfg.head_dim), device=DEV)
+        mac.mac_full_decode(p, layer.dec_q[s], layer.K, layer.V, to_dev(pos[s]), out, None,
+                            ws, ws_b, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), gpu["out"][s]), s
+
+
+def test_run_to_run_deterministic_and_aux_stream_invariant():
+    cfg = _cfg(steps=12, sigma=(0.02, 0.5))
+    K, V, qt, q = _inputs(cfg)
+    layer = Layer(cfg, K, V, qt, q)
+    a = run_steps(layer.init(), cfg.steps, aux=torch.cuda.Stream())
+    b = run_steps(layer.init(), cfg.steps, aux=None)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_exact_reuse_on_gpu():
+    """Identity RoPE, no noise, one prototype: every step hits p = m - 1 (the
+    tie goes to the most recent position) and equals full attention."""
+    cfg = _cfg(batch=1, n_protos=1, sigma=(0.0, 0.0), switch_p=0.0, steps=20)
+    K, V, qt, _ = _inputs(cfg)
+    q = wl.from_storage(qt).astype(np.float32)
+    layer = Layer(cfg, K, V, qt, q).init()
+    gpu = run_steps(layer, cfg.steps)
+    m = wl.decode_positions(cfg)[:, 0]
+    assert (gpu["p"] == (m - 1)[:, None, None]).all()
+    p = params_for(cfg)
+    ws_b = mac.mac_workspace_bytes(p)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=DEV)
+    for s in (0, 10, 19):
+        out = torch.empty((1, cfg.n_q_heads, cfg.head_dim), device=DEV)
+        mac.mac_full_decode(p, layer.dec_q[s], layer.K, layer.V, to_dev(np.array([m[s]], np.int32)),
+                            out, None, ws, ws_b, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert np.abs(out.cpu().numpy() - gpu["out"][s]).max() < 1e-4
+
+
+def test_nan_ring_slot_never_selected():
+    cfg = _cfg(batch=1, n_protos=1, sigma=(0.0, 0.0), switch_p=0.0, steps=1)
+    K, V, qt, _ = _inputs(cfg)
+    q = wl.from_storage(qt).astype(np.float32)
+    layer = Layer(cfg, K, V, qt, q).init()
+    torch.cuda.synchronize()
+    slot = (cfg.ctx - 1) % cfg.ring_k
+    layer.q_ring[0, :, slot, 5] = float("nan")        # poison position m-1
+    gpu = run_steps(layer, 1)
+    assert (gpu["p"][0] == cfg.ctx - 2).all()
+    layer.init()
+    torch.cuda.synchronize()
+    layer.q_ring[0, 3, :, 0] = float("nan")           # every candidate of head 3
+    gpu = run_steps(layer, 1)
+    assert gpu["p"][0, 0, 3] == -1 and np.isinf(gpu["d2"][0, 0, 3])
+    assert (gpu["p"][0, 0, :3] >= 0).all()
+
+
+def test_bad_position_is_flagged_not_faulted():
+    cfg = _cfg(batch=2, steps=1)
+    K, V, qt, q = _inputs(cfg)
+    layer = Layer(cfg, K, V, qt, q).init()
+    torch.cuda.synchronize()
+    before = layer.pos_ring.cpu().numpy().copy()
+    pos = torch.tensor([[cfg.ctx, cfg.capacity]], dtype=torch.int32, device=DEV)
+    gpu = run_steps(layer, 1, pos=pos)
+    assert mac.mac_read_device_status(layer.p, layer.ws) == mac.MAC_DEV_BAD_POSITION
+    assert np.isnan(gpu["out"][0, 1]).all() and np.isfinite(gpu["out"][0, 0]).all()
+    after = layer.pos_ring.cpu().numpy()
+    assert np.array_equal(after[1], before[1])          # no append for request 1
+    assert mac.mac_read_device_status(layer.p, layer.ws) == 0
