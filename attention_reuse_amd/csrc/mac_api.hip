@@ -19,7 +19,7 @@ WsLayout ws_layout(int B, int Hq, int Hkv, int D, int K, int T)
     WsLayout L;
     const int G = Hq / Hkv;
     L.nsplit = (K + kSlotsPerSplit - 1) / kSlotsPerSplit;
-    L.max_items = (int64_t)B * Hkv * ((int64_t)T / kChunk + 3);
+    L.max_items = (int64_t)B * Hkv * (kMaxItemsPerGroup + 2);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -28,12 +28,11 @@ WsLayout ws_layout(int B, int Hq, int Hkv, int D, int K, int T)
     };
     const size_t BH = (size_t)B * Hq, BG = (size_t)B * Hkv;
     L.keys = take(BH * L.nsplit * sizeof(unsigned long long));
-    L.dec_start = take(BH * 4);
     L.dec_slot = take(BH * 4);
     L.grp_begin = take(BG * 4);
     L.grp_count = take(BG * 4);
+    L.grp_start = take(BG * 4);
     L.ctrl = take(64);
-    L.items = take((size_t)L.max_items * sizeof(WorkItem));
     L.part_o = take((size_t)L.max_items * G * D * 4);
     L.part_l = take((size_t)L.max_items * G * 4);
     L.rect_o = take(BH * D * 4);
@@ -47,12 +46,11 @@ WsPtrs ws_ptrs(void *base, const WsLayout &L)
     char *c = (char *)base;
     WsPtrs w;
     w.keys = (unsigned long long *)(c + L.keys);
-    w.dec_start = (int32_t *)(c + L.dec_start);
     w.dec_slot = (int32_t *)(c + L.dec_slot);
     w.grp_begin = (int32_t *)(c + L.grp_begin);
     w.grp_count = (int32_t *)(c + L.grp_count);
+    w.grp_start = (int32_t *)(c + L.grp_start);
     w.ctrl = (int32_t *)(c + L.ctrl);
-    w.items = (WorkItem *)(c + L.items);
     w.part_o = (float *)(c + L.part_o);
     w.part_l = (float *)(c + L.part_l);
     w.rect_o = (float *)(c + L.rect_o);
@@ -64,7 +62,7 @@ WsPtrs ws_ptrs(void *base, const WsLayout &L)
 
 using namespace mac;
 
-constexpr int kStages = 5;
+constexpr int kStages = 4;  // match, attend (+plan), merge, append
 
 struct mac_handle {
     mac_params p;
@@ -73,6 +71,7 @@ struct mac_handle {
     WsPtrs w;
     void *ws;
     mac_rings rings;
+    bool fused_append;
     hipEvent_t ev_main = nullptr, ev_aux = nullptr;
     // Per-stage timing events: prof[(step * kStages + stage) * 2 + {0,1}].
     std::vector<hipEvent_t> prof;
@@ -90,7 +89,8 @@ static mac_status check_params(const mac_params *p, Shape *s)
         return MAC_ERR_INVALID_ARG;
     if (p->batch < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1 ||
         p->n_q_heads % p->n_kv_heads != 0 || p->ring_k < 1 ||
-        p->band_r < 0 || p->kv_capacity < 1 || p->reserved != 0 ||
+        p->band_r < 0 || p->kv_capacity < 1 ||
+        (p->flags & ~MAC_FLAG_FUSED_APPEND) != 0 ||
         !isfinite(p->tau) || !isfinite(p->sm_scale) || p->sm_scale < 0.f ||
         (p->thresh_mode != MAC_THRESH_ONE_MINUS_TAU &&
          p->thresh_mode != MAC_THRESH_TAU))
@@ -100,10 +100,13 @@ static mac_status check_params(const mac_params *p, Shape *s)
         (p->kv_dtype != MAC_DTYPE_F32 && p->kv_dtype != MAC_DTYPE_BF16) ||
         (G != 1 && G != 2 && G != 4 && G != 8))
         return MAC_ERR_UNSUPPORTED;
-    // Sizes are addressed with 32-bit work items and head indices.
-    if ((int64_t)p->batch * p->n_q_heads > (1 << 24) ||
-        (int64_t)p->kv_capacity > (1 << 30) || p->ring_k > (1 << 24))
+    // Sizes are addressed with 32-bit work items and head indices; the
+    // planner keeps its per-head and per-group tables in LDS.
+    if ((int64_t)p->kv_capacity > (1 << 30) || p->ring_k > (1 << 24))
         return MAC_ERR_INVALID_ARG;
+    if ((int64_t)p->batch * p->n_q_heads > 8192 ||
+        plan_lds_bytes(p->batch, p->n_q_heads, p->n_kv_heads) > 48 * 1024)
+        return MAC_ERR_UNSUPPORTED;
     int64_t st = p->kv_stride_t, sh = p->kv_stride_h, sb = p->kv_stride_b;
     if (st == 0 && sh == 0 && sb == 0) {
         st = p->head_dim;
@@ -185,7 +188,10 @@ const char *mac_status_string(mac_status s)
     return "unknown status";
 }
 
-int32_t mac_chunk_tokens(void) { return kChunk; }
+int32_t mac_chunk_tokens(int32_t s, int32_t e)
+{
+    return (s < 0 || e < s) ? -1 : RangeSplit::chunk_for(s, e);
+}
 
 int32_t mac_partition(int32_t s, int32_t e, int32_t r, int32_t *t0,
                       int32_t *t1, int32_t cap)
@@ -204,19 +210,16 @@ int32_t mac_partition(int32_t s, int32_t e, int32_t r, int32_t *t0,
             return MAC_ERR_HIP;            \
     } while (0)
 
-static mac_status full_engine(const Shape &s, const WsLayout &L,
-                              const WsPtrs &w, int32_t mode, int32_t offset,
-                              const float *q, int64_t q_sb, int64_t q_sh,
-                              const void *k, const void *v,
-                              const int32_t *pos, float *out, float *out_lse,
-                              hipStream_t st)
+// Kernel arguments common to every call on a shape and workspace.
+static StepArgs base_args(const Shape &s, const WsLayout &L, const WsPtrs &w)
 {
-    MAC_HIP(launch_plan(s, mode, offset, pos, w, L.nsplit, L.max_items,
-                        nullptr, nullptr, st));
-    MAC_HIP(launch_attend(s, q, q_sb, q_sh, k, v, w, L.max_items, st));
-    MAC_HIP(launch_combine(s, offset, mode == kPlanInit, pos, w, nullptr,
-                           nullptr, out, out_lse, st));
-    return MAC_OK;
+    StepArgs a;
+    memset(&a, 0, sizeof a);
+    a.s = s;
+    a.w = w;
+    a.max_items = L.max_items;
+    a.nsplit = L.nsplit;
+    return a;
 }
 
 mac_status mac_full_decode(const mac_params *p, const float *q,
@@ -236,10 +239,20 @@ mac_status mac_full_decode(const mac_params *p, const float *q,
     const WsLayout L = ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T);
     if (ws_bytes < L.total)
         return MAC_ERR_WORKSPACE_TOO_SMALL;
-    const WsPtrs w = ws_ptrs(workspace, L);
-    return full_engine(s, L, w, kPlanFull, 0, q, (int64_t)s.Hq * s.D, s.D,
-                       k_cache, v_cache, pos, out, out_lse,
-                       (hipStream_t)stream);
+    StepArgs a = base_args(s, L, ws_ptrs(workspace, L));
+    a.mode = kPlanFull;
+    a.pos = pos;
+    a.q = q;
+    a.q_sh = s.D;
+    a.q_sb = (int64_t)s.Hq * s.D;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.out = out;
+    a.out_lse = out_lse;
+    hipStream_t st = (hipStream_t)stream;
+    MAC_HIP(launch_attend(a, st));
+    MAC_HIP(launch_merge(a, st));
+    return MAC_OK;
 }
 
 mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
@@ -286,6 +299,7 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
     h->w = w;
     h->ws = workspace;
     h->rings = *rings;
+    h->fused_append = (p->flags & MAC_FLAG_FUSED_APPEND) != 0;
     if (hipEventCreateWithFlags(&h->ev_main, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&h->ev_aux, hipEventDisableTiming) != hipSuccess) {
         mac_release(h);
@@ -297,8 +311,8 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
         return MAC_ERR_HIP;
     }
     if (n_warm > 0) {
-        // Prompt lengths are staged in the match-key region, which the
-        // init path (plan in kPlanInit mode) never reads.
+        // Prompt lengths are staged in the match-key region, which the warm
+        // path (plan in kPlanInit mode) never reads.
         int32_t *d_ctx = (int32_t *)w.keys;
         if (hipMemcpyAsync(d_ctx, ctx_len, sizeof(int32_t) * s.B,
                            hipMemcpyHostToDevice, st) != hipSuccess ||
@@ -306,28 +320,35 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
             mac_release(h);
             return MAC_ERR_HIP;
         }
-        Shape s0 = s;
-        s0.r = 0;  // the warm summary covers all of [0, t - r]
-        const int64_t wq_sh = (int64_t)n_warm * s.D;
-        const int64_t wq_sb = (int64_t)s.Hq * wq_sh;
-        for (int wi = 0; wi < n_warm; ++wi) {
-            // Warm position t = ctx_len - W + wi; summary of [0, t - r].
+        StepArgs a = base_args(s, L, w);
+        a.s.r = 0;  // the warm summary covers all of [0, t - r]
+        a.mode = kPlanInit;
+        a.pos = d_ctx;
+        a.k = k_cache;
+        a.v = v_cache;
+        a.q_sh = (int64_t)n_warm * s.D;
+        a.q_sb = (int64_t)s.Hq * a.q_sh;
+        a.qt_sh = a.q_sh;
+        a.qt_sb = a.q_sb;
+        a.q_ring = rings->q_ring;
+        a.o_ring = rings->o_ring;
+        a.lse_ring = rings->lse_ring;
+        a.pos_ring = rings->pos_ring;
+        for (int wi = 0; wi < n_warm && rc == MAC_OK; ++wi) {
+            // Warm position t = ctx_len - W + wi; its summary covers [0, t - r].
             const int32_t t_off = wi - n_warm;
-            rc = full_engine(s0, L, w, kPlanInit, t_off - s.r,
-                             warm_q + (int64_t)wi * s.D, wq_sb, wq_sh,
-                             k_cache, v_cache, d_ctx, nullptr, nullptr, st);
-            if (rc == MAC_OK &&
-                launch_append(s, t_off, d_ctx,
-                              (const char *)warm_qtilde +
-                                  (int64_t)wi * s.D * elem_bytes(s.dtype),
-                              wq_sb, wq_sh, w, rings->q_ring, rings->o_ring,
-                              rings->lse_ring, rings->pos_ring,
-                              st) != hipSuccess)
+            a.end_offset = t_off - s.r;
+            a.q = warm_q + (int64_t)wi * s.D;
+            a.qtilde = (const char *)warm_qtilde +
+                       (int64_t)wi * s.D * elem_bytes(s.dtype);
+            if (launch_attend(a, st) != hipSuccess ||
+                launch_merge(a, st) != hipSuccess ||
+                launch_append(a, t_off, st) != hipSuccess)
                 rc = MAC_ERR_HIP;
-            if (rc != MAC_OK) {
-                mac_release(h);
-                return rc;
-            }
+        }
+        if (rc != MAC_OK) {
+            mac_release(h);
+            return rc;
         }
     }
     *out = h;
@@ -346,21 +367,39 @@ mac_status mac_decode_step(mac_handle *h, const void *qtilde, const float *q,
         !aligned16(v_cache))
         return MAC_ERR_MISALIGNED;
     const Shape &s = h->s;
-    const WsLayout &L = h->L;
-    const WsPtrs &w = h->w;
     hipStream_t ms = (hipStream_t)main_stream;
     hipStream_t as = aux_stream ? (hipStream_t)aux_stream : ms;
-    const bool split = as != ms;
-    const int64_t q_sh = s.D, q_sb = (int64_t)s.Hq * s.D;
+    const bool split = as != ms && !h->fused_append;
+
+    StepArgs a = base_args(s, h->L, h->w);
+    a.mode = kPlanMatch;
+    a.pos = pos;
+    a.qtilde = qtilde;
+    a.qt_sh = s.D;
+    a.qt_sb = (int64_t)s.Hq * s.D;
+    a.q = q;
+    a.q_sh = s.D;
+    a.q_sb = (int64_t)s.Hq * s.D;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.out = out;
+    a.out_lse = out_lse;
+    a.match_p = match_p;
+    a.match_d2 = match_d2;
+    a.q_ring = h->rings.q_ring;
+    a.o_ring = h->rings.o_ring;
+    a.lse_ring = h->rings.lse_ring;
+    a.pos_ring = h->rings.pos_ring;
+    a.append_fused = h->fused_append ? 1 : 0;
 
     const bool prof = h->prof_n < h->prof_cap;
     hipEvent_t *pe = prof ? &h->prof[(size_t)h->prof_n * kStages * 2] : nullptr;
-#define MAC_STAGE(idx, stream_, launch)                         \
-    do {                                                        \
-        if (pe)                                                 \
-            MAC_HIP(hipEventRecord(pe[2 * (idx)], stream_));    \
-        MAC_HIP(launch);                                        \
-        if (pe)                                                 \
+#define MAC_STAGE(idx, stream_, launch)                          \
+    do {                                                         \
+        if (pe)                                                  \
+            MAC_HIP(hipEventRecord(pe[2 * (idx)], stream_));     \
+        MAC_HIP(launch);                                         \
+        if (pe)                                                  \
             MAC_HIP(hipEventRecord(pe[2 * (idx) + 1], stream_)); \
     } while (0)
 
@@ -368,28 +407,21 @@ mac_status mac_decode_step(mac_handle *h, const void *qtilde, const float *q,
     // the rings are read and the workspace is reused.
     if (split)
         MAC_HIP(hipStreamWaitEvent(ms, h->ev_aux, 0));
-    MAC_STAGE(0, ms,
-              launch_match(s, qtilde, q_sb, q_sh, h->rings.q_ring,
-                           h->rings.pos_ring, pos, w, L.nsplit, ms));
-    MAC_STAGE(1, ms,
-              launch_plan(s, kPlanMatch, 0, pos, w, L.nsplit, L.max_items,
-                          match_p, match_d2, ms));
-    MAC_STAGE(2, ms,
-              launch_attend(s, q, q_sb, q_sh, k_cache, v_cache, w,
-                            L.max_items, ms));
-    MAC_STAGE(3, ms,
-              launch_combine(s, 0, 0, pos, w, h->rings.o_ring,
-                             h->rings.lse_ring, out, out_lse, ms));
-    if (split) {
-        MAC_HIP(hipEventRecord(h->ev_main, ms));
-        MAC_HIP(hipStreamWaitEvent(as, h->ev_main, 0));
+    MAC_STAGE(0, ms, launch_match(a, ms));
+    MAC_STAGE(1, ms, launch_attend(a, ms));
+    MAC_STAGE(2, ms, launch_merge(a, ms));
+    if (!h->fused_append) {
+        if (split) {
+            MAC_HIP(hipEventRecord(h->ev_main, ms));
+            MAC_HIP(hipStreamWaitEvent(as, h->ev_main, 0));
+        }
+        MAC_STAGE(3, as, launch_append(a, 0, as));
+        if (split)
+            MAC_HIP(hipEventRecord(h->ev_aux, as));
+    } else if (pe) {
+        MAC_HIP(hipEventRecord(pe[6], ms));
+        MAC_HIP(hipEventRecord(pe[7], ms));
     }
-    MAC_STAGE(4, as,
-              launch_append(s, 0, pos, qtilde, q_sb, q_sh, w, h->rings.q_ring,
-                            h->rings.o_ring, h->rings.lse_ring,
-                            h->rings.pos_ring, as));
-    if (split)
-        MAC_HIP(hipEventRecord(h->ev_aux, as));
 #undef MAC_STAGE
     if (prof)
         ++h->prof_n;
@@ -440,7 +472,7 @@ mac_status mac_profile_start(mac_handle *h, int32_t n_steps)
     return MAC_OK;
 }
 
-mac_status mac_profile_read(mac_handle *h, double ms[5], int32_t *n)
+mac_status mac_profile_read(mac_handle *h, double ms[4], int32_t *n)
 {
     if (!h || !ms || !n)
         return MAC_ERR_INVALID_ARG;

@@ -7,41 +7,45 @@
 
 namespace mac {
 
-// Tokens per attention work item.  Item boundaries sit at absolute multiples
-// of this (plus the rectify split m-r+1), so a head's partition depends only
-// on its own range: a miss and a full decode see the same items.
-constexpr int kChunk = 128;
+// Work items: a KV group's token range [s, e] is cut on an absolute grid of
+// C tokens, C = kChunkMin * 2^k the smallest such that the range spans at
+// most kMaxItemsPerGroup grid cells.  C depends only on the group's own
+// range, so a head that misses sees exactly the items of a full decode.
+constexpr int kChunkMin = 128;
+constexpr int kMaxItemsPerGroup = 128;
 // Ring slots scanned by one match workgroup.
 constexpr int kSlotsPerSplit = 64;
 // Workgroup size of the match and attention kernels.
 constexpr int kBlock = 256;
 
-struct WorkItem {
-    int32_t bg;  // b * Hkv + g
-    int32_t t0;  // first position (inclusive)
-    int32_t t1;  // last position (exclusive)
-    int32_t pad;
-};
-
 // Plan: work-item partition of one group's token range [s, e].
-// Boundaries: s, the multiples of kChunk in (s, e], the rectify split
+// Boundaries: s, the multiples of C in (s, e], the rectify split
 // sp = e - r + 1 when it falls strictly inside (s, e], and e + 1.
 struct RangeSplit {
-    int s, e, c_first, n_grid, sp, has_sp, j_sp, n;
+    int s, e, C, c_first, n_grid, sp, has_sp, j_sp, n;
+    __host__ __device__ static int chunk_for(int s_, int e_)
+    {
+        const int span = e_ - s_ + 1;
+        int c = kChunkMin;
+        while ((span + c - 1) / c > kMaxItemsPerGroup)
+            c *= 2;
+        return c;
+    }
     __host__ __device__ RangeSplit(int s_, int e_, int r)
     {
         s = s_;
         e = e_;
-        c_first = s / kChunk + 1;
-        const int c_last = e / kChunk;
+        C = chunk_for(s_, e_);
+        c_first = s / C + 1;
+        const int c_last = e / C;
         n_grid = c_last - c_first + 1;
         if (n_grid < 0)
             n_grid = 0;
         sp = e - r + 1;
-        has_sp = (sp > s && sp <= e && (sp % kChunk) != 0) ? 1 : 0;
+        has_sp = (sp > s && sp <= e && (sp % C) != 0) ? 1 : 0;
         j_sp = 0;
         if (has_sp) {
-            j_sp = (sp - 1) / kChunk - c_first + 1;
+            j_sp = (sp - 1) / C - c_first + 1;
             j_sp = j_sp < 0 ? 0 : (j_sp > n_grid ? n_grid : j_sp);
         }
         n = 1 + n_grid + has_sp;
@@ -50,24 +54,33 @@ struct RangeSplit {
     {
         if (has_sp) {
             if (j < j_sp)
-                return (c_first + j) * kChunk;
+                return (c_first + j) * C;
             if (j == j_sp)
                 return sp;
-            return (c_first + j - 1) * kChunk;
+            return (c_first + j - 1) * C;
         }
-        return (c_first + j) * kChunk;
+        return (c_first + j) * C;
     }
     __host__ __device__ void item(int i, int &t0, int &t1) const
     {
         t0 = (i == 0) ? s : boundary(i - 1);
         t1 = (i == n - 1) ? e + 1 : boundary(i);
     }
+    // Number of leading items that lie before the rectify split sp.
+    __host__ __device__ int n_before_split() const
+    {
+        if (sp <= s)
+            return 0;
+        if (sp > e)
+            return n;
+        return (has_sp ? j_sp : sp / C - c_first) + 1;
+    }
 };
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WsLayout {
-    size_t keys, dec_start, dec_slot, grp_begin, grp_count, ctrl, items,
-        part_o, part_l, rect_o, rect_l, total;
+    size_t keys, dec_slot, grp_begin, grp_count, grp_start, ctrl, part_o,
+        part_l, rect_o, rect_l, total;
     int64_t max_items;
     int32_t nsplit;
 };
@@ -79,6 +92,9 @@ enum PlanMode : int32_t {
     kPlanInit = 2,   // full, end = pos[b] + end_offset, a negative end is empty
 };
 
+// ctrl words: [0] work items of the latest call, [1] its status flags.
+enum { kCtrlItems = 0, kCtrlStatus = 1 };
+
 struct Shape {
     int32_t B, Hq, Hkv, G, D, dtype, K, r, T;
     int64_t kv_sb, kv_sh, kv_st;  // elements
@@ -89,39 +105,56 @@ struct Shape {
 // Device pointers into the workspace.
 struct WsPtrs {
     unsigned long long *keys;
-    int32_t *dec_start, *dec_slot, *grp_begin, *grp_count, *ctrl;
-    WorkItem *items;
+    int32_t *dec_slot, *grp_begin, *grp_count, *grp_start, *ctrl;
     float *part_o, *part_l, *rect_o, *rect_l;
 };
+
+// Everything the kernels of one call read or write.
+struct StepArgs {
+    Shape s;
+    WsPtrs w;
+    int64_t max_items;
+    int32_t nsplit;
+    int32_t mode;        // PlanMode
+    int32_t end_offset;  // kPlanInit: end = pos[b] + end_offset
+    const int32_t *pos;  // [B] device
+    // queries (element strides per request and head)
+    const void *qtilde;
+    int64_t qt_sb, qt_sh;
+    const float *q;
+    int64_t q_sb, q_sh;
+    const void *k, *v;
+    // outputs (any may be null except where noted)
+    float *out, *out_lse;
+    int32_t *match_p;
+    float *match_d2;
+    // rings: read for the cached summary, written when append_fused
+    void *q_ring;
+    float *o_ring, *lse_ring;
+    int32_t *pos_ring;
+    int32_t append_fused;
+};
+
+// Bytes of dynamic LDS the planner needs.
+size_t plan_lds_bytes(int B, int Hq, int Hkv);
 
 WsLayout ws_layout(int B, int Hq, int Hkv, int D, int K, int T);
 WsPtrs ws_ptrs(void *base, const WsLayout &L);
 
-// Kernel launchers (mac_kernels.hip).  Each returns the hipError_t of its
-// launch.  q pointers carry (batch, head) strides in elements.
-hipError_t launch_match(const Shape &s, const void *qtilde, int64_t qt_sb,
-                        int64_t qt_sh, const void *q_ring,
-                        const int32_t *pos_ring, const int32_t *pos,
-                        const WsPtrs &w, int nsplit, hipStream_t st);
-hipError_t launch_plan(const Shape &s, int32_t mode, int32_t end_offset,
-                       const int32_t *pos, const WsPtrs &w, int nsplit,
-                       int64_t max_items, int32_t *match_p, float *match_d2,
-                       hipStream_t st);
-hipError_t launch_attend(const Shape &s, const float *q, int64_t q_sb,
-                         int64_t q_sh, const void *k, const void *v,
-                         const WsPtrs &w, int64_t max_items, hipStream_t st);
-hipError_t launch_combine(const Shape &s, int32_t end_offset,
-                          int32_t allow_negative, const int32_t *pos,
-                          const WsPtrs &w,
-                          const float *o_ring, const float *lse_ring,
-                          float *out, float *out_lse, hipStream_t st);
-hipError_t launch_append(const Shape &s, int32_t pos_offset,
-                         const int32_t *pos, const void *qtilde, int64_t qt_sb,
-                         int64_t qt_sh, const WsPtrs &w, void *q_ring,
-                         float *o_ring, float *lse_ring, int32_t *pos_ring,
-                         hipStream_t st);
+// Kernel launchers (mac_kernels.hip); each returns its launch status.
+hipError_t launch_match(const StepArgs &a, hipStream_t st);
+// Plan (in every workgroup) + split-KV attention: one partial per item and
+// head; workgroup 0 publishes the plan for the merge.
+hipError_t launch_attend(const StepArgs &a, hipStream_t st);
+// Per-group merge of the partials with the cached summaries; appends to
+// the rings itself when append_fused.
+hipError_t launch_merge(const StepArgs &a, hipStream_t st);
+// Rectify-append from the workspace staging into the rings; the position of
+// request b is pos[b] + pos_offset.
+hipError_t launch_append(const StepArgs &a, int32_t pos_offset, hipStream_t st);
 hipError_t launch_ring_reset(const Shape &s, void *q_ring, float *o_ring,
                              float *lse_ring, int32_t *pos_ring,
                              int32_t *ctrl, hipStream_t st);
+int device_cu_count();
 
 }  // namespace mac

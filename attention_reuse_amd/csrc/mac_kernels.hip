@@ -1,22 +1,35 @@
 // HIP kernels of the MAC-Attention decode step for gfx950 (MI355X).
 //
-// One kernel per stage of the step described in the MAC-Attention blog
-// ("MAC-Attention: Match-Amend-Complete attention reuse ... (MLSys 2026)"),
-// section "Paper version: the K1/K2/K3 micro-pipeline":
-//   match   -- L2 nearest neighbour of the pre-RoPE query in the query ring
-//              ("Match (1)-(3)"), one 64-slot split per workgroup;
-//   plan    -- final argmin, hit test, per-(request, KV group) token range
-//              and the device work list (the span-proportional allocator:
-//              every group gets one work item per kChunk tokens of its range);
-//   attend  -- split-KV decode attention over the work list: each item
-//              loads its K/V rows once for all G query heads of the group;
-//   combine -- fixed-order log-domain merge of the partials with the cached
-//              summary ("Complete"); also yields the rectified summary;
-//   append  -- writes the query and rectified summary into slot m mod K.
+// The step of the MAC-Attention blog ("MAC-Attention: Match-Amend-Complete
+// attention reuse ... (MLSys 2026)", section "Paper version: the K1/K2/K3
+// micro-pipeline") runs as three kernels on the main stream plus one on an
+// auxiliary stream:
 //
-// The path is HBM-bound (about 4 flop per KV byte for G = 4): attention and
-// match use VALU with 16-byte coalesced row loads, a K/V row (256 B for
-// d=128 bf16 or d=64 fp32) being spread over one 16-lane DPP row.
+//   match  -- L2 nearest neighbour of the pre-RoPE query among the last K
+//       ring entries ("Match (1)-(3)"), one 64-slot split per workgroup,
+//       emitting the split's smallest (distance, position) key.
+//   attend -- every workgroup first plans from the match keys (final argmin
+//       per head, threshold, token range [s_g, m] per (request, KV group);
+//       every range is cut into items on an absolute 128-token grid plus the
+//       rectify split m-r+1: the span-proportional allocator of "K2"), then
+//       runs persistent split-KV attention over the items.  A K/V row
+//       is loaded once (16 B per lane, one 16-lane DPP row per row) and
+//       serves the G query heads of the group from registers; each item
+//       leaves one partial (o, lse) per head.
+//   merge  -- one workgroup per KV group folds the partials in a fixed order
+//       with the cached summary ("Complete"), giving the output and the
+//       rectified summary of [0, m-r]; with append_fused it also writes the
+//       ring slot m mod K.
+//   append -- the rectify-append as its own kernel ("K3") on an auxiliary
+//       stream after the merge.
+//
+// Workgroups of one kernel never wait for or signal each other: on MI355X
+// the L2 caches of the eight XCDs are not coherent, and the device-scope
+// fence a cross-workgroup hand-off needs writes back a whole L2, so the
+// stages hand over at kernel boundaries instead.
+//
+// The path is HBM-bound (about 4 flop per KV byte for G = 4), so attention
+// and match run on VALU; MFMA tiles would be 3/4 padding at G = 4.
 #include <math.h>
 
 #include "mac_attention.h"
@@ -65,14 +78,37 @@ __device__ inline uint4 load16(const void *p)
     return *reinterpret_cast<const uint4 *>(p);
 }
 
-// Sum over the W consecutive lanes of a row (W a power of two <= 64); every
-// lane of the row receives the total.
+// v_exp_f32 / v_log_f32 (base 2) without library range wrappers; the
+// arguments here are <= 0 (exp) or >= 1 (log).
+__device__ inline float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float lg2(float x) { return __builtin_amdgcn_logf(x); }
+
+// DPP lane permutations inside a 16-lane row.
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- 7-i within 8 lanes
+constexpr int kDppRowMirror = 0x140;   // lane i <- 15-i within 16 lanes
+
+template <int CTRL>
+__device__ inline float dpp(float v)
+{
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over W consecutive lanes (W = 8, 16 or 32); every lane of the group
+// receives the same bits (each step adds a symmetric pair).
 template <int W>
 __device__ inline float row_sum(float v)
 {
-#pragma unroll
-    for (int off = W / 2; off > 0; off >>= 1)
-        v += __shfl_xor(v, off, 64);
+    static_assert(W == 8 || W == 16 || W == 32, "row width");
+    v += dpp<kDppQuadXor1>(v);
+    v += dpp<kDppQuadXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    if (W >= 16)
+        v += dpp<kDppRowMirror>(v);
+    if (W == 32)
+        v += __shfl_xor(v, 16, 64);
     return v;
 }
 
@@ -89,54 +125,212 @@ __device__ inline unsigned long long umin64(unsigned long long a, unsigned long 
     return a < b ? a : b;
 }
 
-// Merge (l, o) <- (l, o) (+) (lb, ob) for log2-domain summaries; the empty
-// summary (-inf) is an exact identity.
-__device__ inline void merge_into(float &l, float &o, float lb, float ob)
+// (l, o[N]) <- (l, o) (+) (lb, ob) for log2-domain summaries of disjoint
+// token sets; the empty summary (l = -inf) is an exact identity.
+template <int N>
+__device__ inline void merge_into(float &l, float *o, float lb, const float *ob)
 {
     if (lb == -INFINITY)
         return;
     if (l == -INFINITY) {
         l = lb;
-        o = ob;
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            o[i] = ob[i];
         return;
     }
     const float M = fmaxf(l, lb);
-    const float ln = M + log2f(exp2f(l - M) + exp2f(lb - M));
-    o = exp2f(l - ln) * o + exp2f(lb - ln) * ob;
+    const float ln = M + lg2(ex2(l - M) + ex2(lb - M));
+    const float wa = ex2(l - ln), wb = ex2(lb - ln);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        o[i] = wa * o[i] + wb * ob[i];
     l = ln;
 }
 
+__device__ inline int32_t end_of(const StepArgs &a, int b)
+{
+    return a.pos[b] + (a.mode == kPlanInit ? a.end_offset : 0);
+}
+
+__device__ inline bool end_ok(const StepArgs &a, int e)
+{
+    return e < a.s.T && (a.mode == kPlanInit || e >= 0);
+}
+
 // ---------------------------------------------------------------------------
-// Match.  Grid (nsplit, B*Hq).  Each LPR-lane row of a wave computes the
-// squared distance of one ring slot; the workgroup keeps the smallest key
+// Planner, run redundantly by every attention workgroup from the match keys
+// (a few KiB, L2-resident): decision per (b, h), token range [s_g, e] and
+// item count per (b, g), and an exclusive scan of the counts, all in LDS.
+// Workgroup 0 also publishes what the merge kernel and the caller need.
+// LDS: ints [BH + 4*NG + 1 + nt + 1].
+struct PlanTables {
+    const int32_t *start, *gstart, *gend, *gcount, *gbegin;
+    int total;
+};
+
+__device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
+{
+    const Shape &s = a.s;
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int BH = s.B * s.Hq, NG = s.B * s.Hkv;
+    const int r_split = (a.mode == kPlanInit) ? 0 : s.r;
+    int32_t *s_start = lds;
+    int32_t *s_gstart = s_start + BH;
+    int32_t *s_gend = s_gstart + NG;
+    int32_t *s_gcount = s_gend + NG;
+    int32_t *s_gbegin = s_gcount + NG;  // NG + 1
+    int32_t *s_part = s_gbegin + NG + 1;
+    int32_t *s_flag = s_part + nt;
+    if (tid == 0)
+        s_flag[0] = 0;
+    __syncthreads();
+
+    // Decisions per (b, h).
+    for (int bh = tid; bh < BH; bh += nt) {
+        const int b = bh / s.Hq;
+        const int e = end_of(a, b);
+        const bool ok = end_ok(a, e);
+        if (!ok)
+            s_flag[0] = 1;
+        int start = 0, slot = -1;
+        if (a.mode == kPlanMatch) {
+            unsigned long long key = ~0ull;
+            const unsigned long long *kp = a.w.keys + (int64_t)bh * a.nsplit;
+#pragma unroll 4
+            for (int i = 0; i < a.nsplit; ++i)
+                key = umin64(key, kp[i]);
+            const bool any = key != ~0ull;
+            const float d2 = any ? __uint_as_float((uint32_t)(key >> 32)) : INFINITY;
+            const int p = any ? (int)(0xffffffffu - (uint32_t)key) : -1;
+            const bool hit = ok && any && d2 < s.thresh2;
+            if (hit) {
+                start = p - s.r + 1 > 0 ? p - s.r + 1 : 0;
+                slot = p % s.K;
+            }
+            if (publish && a.match_p)
+                a.match_p[bh] = hit ? p : -1;
+            if (publish && a.match_d2)
+                a.match_d2[bh] = d2;
+        }
+        s_start[bh] = start;
+        if (publish)
+            a.w.dec_slot[bh] = slot;
+    }
+    __syncthreads();
+
+    // Token range and item count per (b, g).
+    for (int grp = tid; grp < NG; grp += nt) {
+        const int b = grp / s.Hkv, g = grp - b * s.Hkv;
+        const int e = end_of(a, b);
+        int st = 0, cnt = 0;
+        if (e >= 0 && e < s.T) {
+            st = e;
+            for (int j = 0; j < s.G; ++j) {
+                const int v = s_start[b * s.Hq + g * s.G + j];
+                st = v < st ? v : st;
+            }
+            cnt = RangeSplit(st, e, r_split).n;
+        }
+        s_gstart[grp] = st;
+        s_gend[grp] = e;
+        s_gcount[grp] = cnt;
+    }
+    __syncthreads();
+
+    // Exclusive scan of the counts: contiguous runs per thread, then a
+    // Hillis-Steele scan of the run totals.
+    const int per = (NG + nt - 1) / nt;
+    const int lo = tid * per, hi = lo + per < NG ? lo + per : NG;
+    int run = 0;
+    for (int i = lo; i < hi; ++i)
+        run += s_gcount[i];
+    s_part[tid] = run;
+    __syncthreads();
+    for (int o = 1; o < nt; o <<= 1) {
+        const int v = tid >= o ? s_part[tid - o] : 0;
+        __syncthreads();
+        s_part[tid] += v;
+        __syncthreads();
+    }
+    int acc = s_part[tid] - run;
+    for (int i = lo; i < hi; ++i) {
+        s_gbegin[i] = acc;
+        acc += s_gcount[i];
+    }
+    if (tid == nt - 1)
+        s_gbegin[NG] = s_part[nt - 1];
+    __syncthreads();
+    int total = s_gbegin[NG];
+    if (total > a.max_items)
+        total = (int)a.max_items;
+
+    if (publish) {
+        for (int grp = tid; grp < NG; grp += nt) {
+            a.w.grp_begin[grp] = s_gbegin[grp];
+            a.w.grp_count[grp] = s_gcount[grp];
+            a.w.grp_start[grp] = s_gstart[grp];
+            if (s_gcount[grp] == 0) {
+                // No item, so no merge will run: the outputs are written here.
+                const int b = grp / s.Hkv, g = grp - b * s.Hkv;
+                const bool bad = !end_ok(a, s_gend[grp]);
+                for (int j = 0; j < s.G; ++j) {
+                    const int bh = b * s.Hq + g * s.G + j;
+                    for (int d = 0; d < s.D; ++d) {
+                        if (a.out)
+                            a.out[(int64_t)bh * s.D + d] = bad ? NAN : 0.f;
+                        a.w.rect_o[(int64_t)bh * s.D + d] = 0.f;
+                    }
+                    if (a.out_lse)
+                        a.out_lse[bh] = bad ? NAN : -INFINITY;
+                    a.w.rect_l[bh] = -INFINITY;
+                }
+            }
+        }
+        if (tid == 0) {
+            a.w.ctrl[kCtrlItems] = total;
+            a.w.ctrl[kCtrlStatus] = s_flag[0] ? MAC_DEV_BAD_POSITION : 0;
+        }
+    }
+    PlanTables t;
+    t.start = s_start;
+    t.gstart = s_gstart;
+    t.gend = s_gend;
+    t.gcount = s_gcount;
+    t.gbegin = s_gbegin;
+    t.total = total;
+    return t;
+}
+
+// ---------------------------------------------------------------------------
+// Match.  Grid (nsplit, B*Hq).  Each LPR-lane row of a wave computes
+// the squared distance of one ring slot; the workgroup keeps the smallest
 //   key = float_bits(D) << 32 | (0xffffffff - p)
 // (non-negative floats order like their bits; equal D prefers larger p).
 template <class T, int D>
-__global__ __launch_bounds__(kBlock) void match_kernel(
-    const typename T::S *__restrict__ qt, int64_t qt_sb, int64_t qt_sh,
-    const typename T::S *__restrict__ q_ring, const int32_t *__restrict__ pos_ring,
-    const int32_t *__restrict__ pos, int Hq, int K, int T_cap, int nsplit,
-    unsigned long long *__restrict__ keys)
+__global__ __launch_bounds__(kBlock) void match_kernel(StepArgs a)
 {
     constexpr int EPL = T::EPL, LPR = D / EPL, RPB = kBlock / LPR;
     constexpr int U = kSlotsPerSplit / RPB;
     static_assert(U >= 1 && U * RPB == kSlotsPerSplit, "split shape");
-    const int bh = blockIdx.y, b = bh / Hq, h = bh - b * Hq;
+    using S = typename T::S;
+    const Shape &s = a.s;
+    const int bh = blockIdx.y, b = bh / s.Hq, h = bh - b * s.Hq;
     const int lane = threadIdx.x % LPR, row = threadIdx.x / LPR;
-    const int m = pos[b];
-    const bool m_ok = m >= 0 && m < T_cap;
+    const int m = a.pos[b];
+    const bool m_ok = m >= 0 && m < s.T;
 
     float qv[EPL];
-    unpack<T>(load16(qt + b * qt_sb + h * qt_sh + lane * EPL), qv);
-    const typename T::S *ring = q_ring + (int64_t)bh * K * D + lane * EPL;
-    const int32_t *pr = pos_ring + (int64_t)b * K;
+    unpack<T>(load16((const S *)a.qtilde + b * a.qt_sb + h * a.qt_sh + lane * EPL), qv);
+    const S *ring = (const S *)a.q_ring + (int64_t)bh * s.K * D + lane * EPL;
+    const int32_t *pr = a.pos_ring + (int64_t)b * s.K;
 
     uint4 raw[U];
     int p[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int k = blockIdx.x * kSlotsPerSplit + u * RPB + row;
-        if (k < K) {
+        if (k < s.K) {
             raw[u] = load16(ring + (int64_t)k * D);
             p[u] = pr[k];
         } else {
@@ -147,17 +341,17 @@ __global__ __launch_bounds__(kBlock) void match_kernel(
     unsigned long long best = ~0ull;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        float r[EPL];
-        unpack<T>(raw[u], r);
+        float rv[EPL];
+        unpack<T>(raw[u], rv);
         float acc = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-            const float df = qv[e] - r[e];
+            const float df = qv[e] - rv[e];
             acc = fmaf(df, df, acc);
         }
         acc = row_sum<LPR>(acc);
         const int pu = p[u];
-        const bool valid = m_ok && pu >= 0 && pu >= m - K && pu <= m - 1;
+        const bool valid = m_ok && pu >= 0 && pu >= m - s.K && pu <= m - 1;
         uint32_t bits = __float_as_uint(acc);
         if (acc != acc)
             bits = 0x7f800000u;  // NaN distance counts as +inf
@@ -176,168 +370,338 @@ __global__ __launch_bounds__(kBlock) void match_kernel(
 #pragma unroll
         for (int i = 1; i < kBlock / 64; ++i)
             best = umin64(best, sm[i]);
-        keys[(int64_t)bh * nsplit + blockIdx.x] = best;
+        a.w.keys[(int64_t)bh * a.nsplit + blockIdx.x] = best;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Single workgroup.  Decision per (b, h), token range per (b, g), exclusive
-// scan of the per-group item counts, then the work list.
-__global__ __launch_bounds__(1024) void plan_kernel(
-    const unsigned long long *__restrict__ keys, int nsplit,
-    const int32_t *__restrict__ pos, int32_t mode, int32_t end_offset, int B,
-    int Hq, int Hkv, int G, int K, int r, int T_cap, float thresh2,
-    int32_t *__restrict__ dec_start, int32_t *__restrict__ dec_slot,
-    int32_t *__restrict__ grp_begin, int32_t *__restrict__ grp_count,
-    int32_t *__restrict__ ctrl, WorkItem *__restrict__ items,
-    int64_t max_items, int32_t *__restrict__ match_p, float *__restrict__ match_d2)
+// Merge of one KV group (one workgroup of kMergeBlock threads per group).
+// Fixed shape, so a head's result depends only on its own item list: the
+// list is cut into A = items before the rectify split and Bt = the rest;
+// each list into at most P equal segments folded left to right by separate
+// threads, then the segments in order.  R = C (+) A with C the cached summary
+// of the matched slot (empty on a miss); out = R (+) Bt.
+constexpr int kMergeBlock = 1024;
+
+template <class T, int D, int G>
+struct MergeShape {
+    static constexpr int P = 64 / G;                   // segments per list
+    static constexpr int DPT = D / 16;                 // dims per thread
+    static constexpr int TPS = 16;                     // threads per (head, segment)
+    static constexpr int SEG = D + 1;                  // floats per segment record
+    static constexpr int kFloats = G * P * SEG;
+    static constexpr int NPT = (G * D + kMergeBlock - 1) / kMergeBlock;
+    static_assert(G * P * TPS == kMergeBlock, "merge shape");
+};
+
+// Fold items [i0, i1) of head j into (l, o) for dims [d0, d0 + DPT), with
+// the loads of the next batch of four items in flight during each merge.
+template <int D, int G, int DPT>
+__device__ inline void fold_items(const StepArgs &a, int64_t begin, int i0, int i1, int j,
+                                  int d0, float &l, float *o)
 {
-    __shared__ int32_t s_scan[1024];
-    __shared__ int32_t s_bad;
-    const int tid = threadIdx.x, nt = blockDim.x;
-    const int off = (mode == kPlanInit) ? end_offset : 0;
-    if (tid == 0)
-        s_bad = 0;
-    __syncthreads();
-
-    for (int bh = tid; bh < B * Hq; bh += nt) {
-        const int b = bh / Hq;
-        const int e = pos[b] + off;
-        const bool ok = (mode == kPlanInit) ? (e < T_cap) : (e >= 0 && e < T_cap);
-        if (!ok)
-            s_bad = 1;
-        int start = 0, slot = -1;
-        if (mode == kPlanMatch) {
-            unsigned long long key = ~0ull;
-            for (int s = 0; s < nsplit; ++s)
-                key = umin64(key, keys[(int64_t)bh * nsplit + s]);
-            const bool any = key != ~0ull;
-            const float d2 = any ? __uint_as_float((uint32_t)(key >> 32)) : INFINITY;
-            const int p = any ? (int)(0xffffffffu - (uint32_t)key) : -1;
-            const bool hit = ok && any && d2 < thresh2;
-            if (hit) {
-                start = p - r + 1 > 0 ? p - r + 1 : 0;
-                slot = p % K;
-            }
-            if (match_p)
-                match_p[bh] = hit ? p : -1;
-            if (match_d2)
-                match_d2[bh] = d2;
-        }
-        dec_start[bh] = start;
-        dec_slot[bh] = slot;
-    }
-    __syncthreads();
-
-    int carry = 0;
-    const int n_grp = B * Hkv;
-    const int r_split = (mode == kPlanInit) ? 0 : r;
-    for (int base = 0; base < n_grp; base += nt) {
-        const int grp = base + tid;
-        int cnt = 0;
-        if (grp < n_grp) {
-            const int b = grp / Hkv, g = grp - b * Hkv;
-            const int e = pos[b] + off;
-            if (e >= 0 && e < T_cap) {
-                int s = e;
-                for (int j = 0; j < G; ++j) {
-                    const int st = dec_start[b * Hq + g * G + j];
-                    s = st < s ? st : s;
+    constexpr int NBUF = 4;
+    float lb[2][NBUF], ob[2][NBUF][DPT];
+    auto fetch = [&](int buf, int base) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+            const int i = base + u;
+            lb[buf][u] = -INFINITY;
+            if (i < i1) {
+                const int64_t ix = begin + i;
+                lb[buf][u] = a.w.part_l[ix * G + j];
+                const float *src = a.w.part_o + (ix * G + j) * D + d0;
+#pragma unroll
+                for (int k = 0; k < DPT; k += 4) {
+                    const float4 v = *reinterpret_cast<const float4 *>(src + k);
+                    ob[buf][u][k] = v.x;
+                    ob[buf][u][k + 1] = v.y;
+                    ob[buf][u][k + 2] = v.z;
+                    ob[buf][u][k + 3] = v.w;
                 }
-                cnt = RangeSplit(s, e, r_split).n;
             }
         }
-        s_scan[tid] = cnt;
+    };
+    fetch(0, i0);
+    int buf = 0;
+    for (int base = i0; base < i1; base += NBUF) {
+        if (base + NBUF < i1)
+            fetch(buf ^ 1, base + NBUF);
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u)
+            if (base + u < i1)
+                merge_into<DPT>(l, o, lb[buf][u], ob[buf][u]);
+        buf ^= 1;
+    }
+}
+
+template <class T, int D, int G>
+__global__ __launch_bounds__(kMergeBlock) void merge_kernel(StepArgs a)
+{
+    using M = MergeShape<T, D, G>;
+    constexpr int P = M::P, DPT = M::DPT, TPS = M::TPS, SEG = M::SEG, NPT = M::NPT;
+    using S = typename T::S;
+    __shared__ float lds[M::kFloats];
+    const Shape &s = a.s;
+    const int grp = blockIdx.x;
+    const int cnt = a.w.grp_count[grp];
+    if (cnt == 0)
+        return;  // the planner wrote this group's outputs
+    const int tid = threadIdx.x;
+    const int j = tid / (P * TPS), seg = (tid / TPS) % P, d0 = (tid % TPS) * DPT;
+    const int b = grp / s.Hkv, g = grp - b * s.Hkv;
+    const int64_t begin = a.w.grp_begin[grp];
+    const int e = end_of(a, b);
+    const int r_split = (a.mode == kPlanInit) ? 0 : s.r;
+    const int nA = RangeSplit(a.w.grp_start[grp], e, r_split).n_before_split();
+
+    // list 0 = A (items [0, nA)), list 1 = Bt (items [nA, cnt)); each folds
+    // into res[list][k] for this thread's (head, dim) outputs.
+    float res_l[2][NPT], res_o[2][NPT];
+#pragma unroll 1
+    for (int list = 0; list < 2; ++list) {
+        const int l0 = list == 0 ? 0 : nA;
+        const int L = list == 0 ? nA : cnt - nA;
+        const int Pe = L < P ? L : P;
+        float l = -INFINITY, o[DPT];
+#pragma unroll
+        for (int i = 0; i < DPT; ++i)
+            o[i] = 0.f;
+        if (seg < Pe)
+            fold_items<D, G, DPT>(a, begin, l0 + seg * L / Pe, l0 + (seg + 1) * L / Pe, j, d0, l, o);
+        float *rec = lds + (j * P + seg) * SEG;
+        if ((tid % TPS) == 0)
+            rec[D] = l;
+#pragma unroll
+        for (int i = 0; i < DPT; ++i)
+            rec[d0 + i] = o[i];
         __syncthreads();
-        for (int o = 1; o < nt; o <<= 1) {
-            const int v = tid >= o ? s_scan[tid - o] : 0;
-            __syncthreads();
-            s_scan[tid] += v;
-            __syncthreads();
+#pragma unroll
+        for (int k = 0; k < NPT; ++k) {
+            const int idx = tid + k * kMergeBlock;
+            float fl = -INFINITY, fo = 0.f;
+            if (idx < G * D) {
+                const int jj = idx / D, dim = idx - jj * D;
+                for (int sg = 0; sg < Pe; ++sg) {
+                    const float *r = lds + (jj * P + sg) * SEG;
+                    merge_into<1>(fl, &fo, r[D], r + dim);
+                }
+            }
+            res_l[list][k] = fl;
+            res_o[list][k] = fo;
         }
-        if (grp < n_grp) {
-            grp_begin[grp] = carry + s_scan[tid] - cnt;
-            grp_count[grp] = cnt;
-        }
-        carry += s_scan[nt - 1];
         __syncthreads();
     }
 
-    for (int grp = 0; grp < n_grp; ++grp) {
-        const int cnt = grp_count[grp];
-        if (cnt == 0)
+    // Results are held until every thread has read its cached summary, since
+    // the fused append may overwrite that slot.
+    float out_l[NPT], out_o[NPT], rec_l[NPT], rec_o[NPT];
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+        const int idx = tid + k * kMergeBlock;
+        out_l[k] = rec_l[k] = -INFINITY;
+        out_o[k] = rec_o[k] = 0.f;
+        if (idx >= G * D)
             continue;
-        const int begin = grp_begin[grp];
-        const int b = grp / Hkv, g = grp - b * Hkv;
-        const int e = pos[b] + off;
-        int s = e;
-        for (int j = 0; j < G; ++j) {
-            const int st = dec_start[b * Hq + g * G + j];
-            s = st < s ? st : s;
+        const int jj = idx / D, dim = idx - jj * D;
+        const int bh = b * s.Hq + g * G + jj;
+        float lr = -INFINITY, orr = 0.f;
+        const int slot = a.w.dec_slot[bh];
+        if (slot >= 0) {
+            lr = a.lse_ring[(int64_t)bh * s.K + slot] * kLog2e;
+            orr = a.o_ring[((int64_t)bh * s.K + slot) * D + dim];
         }
-        const RangeSplit rs(s, e, r_split);
-        for (int i = tid; i < cnt; i += nt) {
-            if (begin + i >= max_items)
-                break;
-            WorkItem w;
-            w.bg = grp;
-            rs.item(i, w.t0, w.t1);
-            w.pad = 0;
-            items[begin + i] = w;
-        }
+        merge_into<1>(lr, &orr, res_l[0][k], &res_o[0][k]);
+        float lo = lr, oo = orr;
+        merge_into<1>(lo, &oo, res_l[1][k], &res_o[1][k]);
+        out_l[k] = lo;
+        out_o[k] = oo;
+        rec_l[k] = lr;
+        rec_o[k] = orr;
     }
-    if (tid == 0) {
-        ctrl[0] = carry < max_items ? carry : (int32_t)max_items;
-        ctrl[1] = s_bad ? MAC_DEV_BAD_POSITION : 0;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+        const int idx = tid + k * kMergeBlock;
+        if (idx >= G * D)
+            continue;
+        const int jj = idx / D, dim = idx - jj * D;
+        const int h = g * G + jj, bh = b * s.Hq + h;
+        if (a.out)
+            a.out[(int64_t)bh * D + dim] = out_o[k];
+        if (a.out_lse && dim == 0)
+            a.out_lse[bh] = out_l[k] * kLn2;
+        if (a.append_fused) {
+            // Rectify-append into slot m mod K of this head's rings.
+            const int slot = e % s.K;
+            const int64_t ri = ((int64_t)bh * s.K + slot) * D + dim;
+            ((S *)a.q_ring)[ri] = ((const S *)a.qtilde)[b * a.qt_sb + h * a.qt_sh + dim];
+            a.o_ring[ri] = rec_o[k];
+            if (dim == 0)
+                a.lse_ring[(int64_t)bh * s.K + slot] = rec_l[k] * kLn2;
+            if (h == 0 && dim == 0)
+                a.pos_ring[(int64_t)b * s.K + slot] = e;
+        } else {
+            a.w.rect_o[(int64_t)bh * D + dim] = rec_o[k];
+            if (dim == 0)
+                a.w.rect_l[bh] = rec_l[k];
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // Attention over the work list.  Each workgroup loops over items; within an
-// item, LPR-lane row `row` handles tokens t0 + i*RPB + row.  A K/V row is
-// loaded once (16 B per lane) and serves the G query heads of the group from
-// registers.  Per-row online softmax in log2 units; the RPB row states are
-// combined in LDS in a fixed order into one partial (o, log2-lse) per head.
+// item, LPR-lane row `row` handles tokens t0 + i*RPB + row, NB tokens per
+// block, with the next block's K/V loads in flight while a block computes.
+// Per-row online softmax in log2 units; the RPB row states are combined in
+// LDS in a fixed order into one partial (o, log2-lse) per head.
 template <class T, int D, int G>
-__global__ __launch_bounds__(kBlock) void attend_kernel(
-    const WorkItem *__restrict__ items, const int32_t *__restrict__ ctrl,
-    const float *__restrict__ q, int64_t q_sb, int64_t q_sh,
-    const typename T::S *__restrict__ Kc, const typename T::S *__restrict__ Vc,
-    int64_t kv_sb, int64_t kv_sh, int64_t kv_st,
-    const int32_t *__restrict__ dec_start, int Hq, int Hkv, float qscale,
-    float *__restrict__ part_o, float *__restrict__ part_l)
+struct AttendShape {
+    static constexpr int EPL = T::EPL, LPR = D / EPL, RPB = kBlock / LPR;
+    static constexpr int NB = 4;  // tokens per row per block
+    static constexpr int kFloats = RPB * G * (D + 2);
+};
+
+template <class T, int G, int EPL, int NB>
+struct KvBlock {
+    uint4 k[NB], v[NB];
+    int t[NB];
+};
+
+template <class T, int D, int G, int LPR, int RPB, int NB>
+__device__ inline void load_block(KvBlock<T, G, T::EPL, NB> &kv, const typename T::S *kb,
+                                  const typename T::S *vb, int64_t kv_st, int base, int t1,
+                                  int row)
 {
-    constexpr int EPL = T::EPL, LPR = D / EPL, RPB = kBlock / LPR;
-    constexpr int NI = kChunk / RPB;
-    constexpr int NB = NI < 8 ? NI : 8;
-    static_assert(NI % NB == 0, "chunk shape");
-    __shared__ float sm_m[RPB][G];
-    __shared__ float sm_l[RPB][G];
-    __shared__ float sm_acc[RPB][G][D];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int t = base + i * RPB + row;
+        kv.t[i] = t;
+        if (t < t1) {
+            kv.k[i] = load16(kb + (int64_t)t * kv_st);
+            kv.v[i] = load16(vb + (int64_t)t * kv_st);
+        } else {
+            kv.k[i] = make_uint4(0, 0, 0, 0);
+            kv.v[i] = make_uint4(0, 0, 0, 0);
+        }
+    }
+}
+
+template <class T, int D, int G, int LPR, int NB>
+__device__ inline void compute_block(const KvBlock<T, G, T::EPL, NB> &kv,
+                                     const float (&qr)[G][T::EPL], const int (&st)[G], int t1,
+                                     float (&mrun)[G], float (&lrun)[G],
+                                     float (&acc)[G][T::EPL])
+{
+    constexpr int EPL = T::EPL;
+    float sc[NB][G];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        float kf[EPL];
+        unpack<T>(kv.k[i], kf);
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            float x = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+                x = fmaf(qr[j][e], kf[e], x);
+            sc[i][j] = x;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const float v = row_sum<LPR>(sc[i][j]);
+            sc[i][j] = (kv.t[i] < t1 && kv.t[i] >= st[j]) ? v : -INFINITY;
+        }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        float bm = sc[0][j];
+#pragma unroll
+        for (int i = 1; i < NB; ++i)
+            bm = fmaxf(bm, sc[i][j]);
+        const float mn = fmaxf(mrun[j], bm);
+        const bool live = mn != -INFINITY;
+        const float alpha = live ? ex2(mrun[j] - mn) : 1.f;
+        float lsum = lrun[j] * alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            acc[j][e] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const float pi = live ? ex2(sc[i][j] - mn) : 0.f;
+            sc[i][j] = pi;
+            lsum += pi;
+        }
+        lrun[j] = lsum;
+        mrun[j] = mn;
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        float vf[EPL];
+        unpack<T>(kv.v[i], vf);
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+                acc[j][e] = fmaf(sc[i][j], vf[e], acc[j][e]);
+    }
+}
+
+template <class T, int D, int G>
+__global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
+{
+    using L = AttendShape<T, D, G>;
+    constexpr int EPL = L::EPL, LPR = L::LPR, RPB = L::RPB, NB = L::NB;
+    constexpr int TPB = RPB * NB;  // tokens per block
+    using S = typename T::S;
+    __shared__ float lds[L::kFloats];
+    float *sm_m = lds;                  // [RPB][G]
+    float *sm_l = lds + RPB * G;        // [RPB][G]
+    float *sm_acc = lds + 2 * RPB * G;  // [RPB][G][D]
+    const Shape &s = a.s;
 
     const int lane = threadIdx.x % LPR, row = threadIdx.x / LPR;
-    const int n_items = ctrl[0];
-    for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
-        const WorkItem w = items[it];
-        const int b = w.bg / Hkv, g = w.bg - b * Hkv;
+    extern __shared__ int32_t plan_lds[];
+    const PlanTables pt = plan_tables(a, plan_lds, blockIdx.x == 0);
+    const int NG = s.B * s.Hkv;
+    const int r_split = (a.mode == kPlanInit) ? 0 : s.r;
+    for (int it = blockIdx.x; it < pt.total; it += gridDim.x) {
+        // Group of item `it`: the last group whose first item is <= it.
+        int lo = 0, hi = NG;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (pt.gbegin[mid] <= it)
+                lo = mid + 1;
+            else
+                hi = mid;
+        }
+        const int grp = lo - 1;
+        const int b = grp / s.Hkv, g = grp - b * s.Hkv;
+        int t0, t1;
+        RangeSplit(pt.gstart[grp], pt.gend[grp], r_split).item(it - pt.gbegin[grp], t0, t1);
+        const S *kb = (const S *)a.k + b * s.kv_sb + g * s.kv_sh + lane * EPL;
+        const S *vb = (const S *)a.v + b * s.kv_sb + g * s.kv_sh + lane * EPL;
+
+        KvBlock<T, G, EPL, NB> bufA, bufB;
+        load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, t0, t1, row);
 
         float qr[G][EPL];
         int st[G];
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-            const float *qp = q + b * q_sb + (int64_t)(g * G + j) * q_sh + lane * EPL;
+            const float *qp = a.q + b * a.q_sb + (int64_t)(g * G + j) * a.q_sh + lane * EPL;
 #pragma unroll
             for (int e4 = 0; e4 < EPL; e4 += 4) {
                 const float4 v = *reinterpret_cast<const float4 *>(qp + e4);
-                qr[j][e4 + 0] = v.x * qscale;
-                qr[j][e4 + 1] = v.y * qscale;
-                qr[j][e4 + 2] = v.z * qscale;
-                qr[j][e4 + 3] = v.w * qscale;
+                qr[j][e4 + 0] = v.x * s.qscale;
+                qr[j][e4 + 1] = v.y * s.qscale;
+                qr[j][e4 + 2] = v.z * s.qscale;
+                qr[j][e4 + 3] = v.w * s.qscale;
             }
-            st[j] = dec_start[b * Hq + g * G + j];
+            st[j] = pt.start[b * s.Hq + g * G + j];
         }
-        const typename T::S *kb = Kc + b * kv_sb + g * kv_sh + lane * EPL;
-        const typename T::S *vb = Vc + b * kv_sb + g * kv_sh + lane * EPL;
 
         float mrun[G], lrun[G], acc[G][EPL];
 #pragma unroll
@@ -348,223 +712,80 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
             for (int e = 0; e < EPL; ++e)
                 acc[j][e] = 0.f;
         }
-
-#pragma unroll 1
-        for (int blk = 0; blk < NI / NB; ++blk) {
-            uint4 kr[NB], vr[NB];
-            int tt[NB];
-#pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                const int t = w.t0 + (blk * NB + i) * RPB + row;
-                tt[i] = t;
-                if (t < w.t1) {
-                    kr[i] = load16(kb + (int64_t)t * kv_st);
-                    vr[i] = load16(vb + (int64_t)t * kv_st);
-                } else {
-                    kr[i] = make_uint4(0, 0, 0, 0);
-                    vr[i] = make_uint4(0, 0, 0, 0);
-                }
-            }
-            float s[NB][G];
-#pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                float kf[EPL];
-                unpack<T>(kr[i], kf);
-#pragma unroll
-                for (int j = 0; j < G; ++j) {
-                    float a = 0.f;
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e)
-                        a = fmaf(qr[j][e], kf[e], a);
-                    s[i][j] = a;
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < NB; ++i)
-#pragma unroll
-                for (int j = 0; j < G; ++j) {
-                    const float v = row_sum<LPR>(s[i][j]);
-                    s[i][j] = (tt[i] < w.t1 && tt[i] >= st[j]) ? v : -INFINITY;
-                }
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                float bm = s[0][j];
-#pragma unroll
-                for (int i = 1; i < NB; ++i)
-                    bm = fmaxf(bm, s[i][j]);
-                const float mn = fmaxf(mrun[j], bm);
-                const bool live = mn != -INFINITY;
-                const float alpha = live ? exp2f(mrun[j] - mn) : 1.f;
-                float lsum = lrun[j] * alpha;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e)
-                    acc[j][e] *= alpha;
-#pragma unroll
-                for (int i = 0; i < NB; ++i) {
-                    const float pi = live ? exp2f(s[i][j] - mn) : 0.f;
-                    s[i][j] = pi;
-                    lsum += pi;
-                }
-                lrun[j] = lsum;
-                mrun[j] = mn;
-            }
-#pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                float vf[EPL];
-                unpack<T>(vr[i], vf);
-#pragma unroll
-                for (int j = 0; j < G; ++j)
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e)
-                        acc[j][e] = fmaf(s[i][j], vf[e], acc[j][e]);
+        // Blocks alternate between the two buffers; the next block is
+        // always requested before the current one is consumed.
+        for (int base = t0; base < t1; base += 2 * TPB) {
+            if (base + TPB < t1)
+                load_block<T, D, G, LPR, RPB, NB>(bufB, kb, vb, s.kv_st, base + TPB, t1, row);
+            compute_block<T, D, G, LPR, NB>(bufA, qr, st, t1, mrun, lrun, acc);
+            if (base + TPB < t1) {
+                if (base + 2 * TPB < t1)
+                    load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, base + 2 * TPB, t1,
+                                                      row);
+                compute_block<T, D, G, LPR, NB>(bufB, qr, st, t1, mrun, lrun, acc);
             }
         }
 
         if (lane == 0) {
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                sm_m[row][j] = mrun[j];
-                sm_l[row][j] = lrun[j];
+                sm_m[row * G + j] = mrun[j];
+                sm_l[row * G + j] = lrun[j];
             }
         }
 #pragma unroll
         for (int j = 0; j < G; ++j)
 #pragma unroll
             for (int e = 0; e < EPL; ++e)
-                sm_acc[row][j][lane * EPL + e] = acc[j][e];
+                sm_acc[(row * G + j) * D + lane * EPL + e] = acc[j][e];
         __syncthreads();
         for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
             const int j = idx / D, dim = idx - j * D;
             float M = -INFINITY;
 #pragma unroll 8
             for (int rr = 0; rr < RPB; ++rr)
-                M = fmaxf(M, sm_m[rr][j]);
-            float o = 0.f, L = -INFINITY;
+                M = fmaxf(M, sm_m[rr * G + j]);
+            float o = 0.f, Lg = -INFINITY;
             if (M != -INFINITY) {
                 float ls = 0.f, os = 0.f;
 #pragma unroll 8
                 for (int rr = 0; rr < RPB; ++rr) {
-                    const float c = exp2f(sm_m[rr][j] - M);
-                    ls = fmaf(c, sm_l[rr][j], ls);
-                    os = fmaf(c, sm_acc[rr][j][dim], os);
+                    const float c = ex2(sm_m[rr * G + j] - M);
+                    ls = fmaf(c, sm_l[rr * G + j], ls);
+                    os = fmaf(c, sm_acc[(rr * G + j) * D + dim], os);
                 }
                 o = os / ls;
-                L = M + log2f(ls);
+                Lg = M + lg2(ls);
             }
-            part_o[((int64_t)it * G + j) * D + dim] = o;
+            a.w.part_o[((int64_t)it * G + j) * D + dim] = o;
             if (dim == 0)
-                part_l[(int64_t)it * G + j] = L;
+                a.w.part_l[(int64_t)it * G + j] = Lg;
         }
         __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------------------
-// Combine.  One workgroup of D threads per (b, h), thread = output dim.
-// Partials of the group's items are folded in item order into
-//   A  = items before the rectify split sp = e - r + 1,
-//   Bt = items from sp on,
-// then R = C (+) A with C the cached summary of the matched slot (empty on a
-// miss) and out = R (+) Bt.  R is the rectified summary of [0, e - r].
-template <int D>
-__global__ __launch_bounds__(D) void combine_kernel(
-    const WorkItem *__restrict__ items, const int32_t *__restrict__ grp_begin,
-    const int32_t *__restrict__ grp_count, const int32_t *__restrict__ pos,
-    int32_t end_offset, int32_t allow_negative, int Hq, int Hkv, int G, int K,
-    int r, int T_cap, const float *__restrict__ part_o,
-    const float *__restrict__ part_l, const int32_t *__restrict__ dec_slot,
-    const float *__restrict__ o_ring, const float *__restrict__ lse_ring,
-    float *__restrict__ out, float *__restrict__ out_lse,
-    float *__restrict__ rect_o, float *__restrict__ rect_l)
-{
-    const int bh = blockIdx.x, b = bh / Hq, h = bh - b * Hq;
-    const int g = h / G, j = h - g * G, grp = b * Hkv + g;
-    const int dim = threadIdx.x;
-    const int e = pos[b] + end_offset;
-    const bool ok = e < T_cap && (allow_negative || e >= 0);
-    if (!ok) {
-        if (out)
-            out[(int64_t)bh * D + dim] = NAN;
-        if (out_lse && dim == 0)
-            out_lse[bh] = NAN;
-        rect_o[(int64_t)bh * D + dim] = 0.f;
-        if (dim == 0)
-            rect_l[bh] = -INFINITY;
-        return;
-    }
-    const int sp = e - r + 1;
-    const int begin = grp_begin[grp], cnt = grp_count[grp];
-    float la = -INFINITY, oa = 0.f, lb = -INFINITY, ob = 0.f;
-    int i = 0;
-    for (; i + 4 <= cnt; i += 4) {
-        int t0[4];
-        float li[4], oi[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t ix = (int64_t)begin + i + u;
-            t0[u] = items[ix].t0;
-            li[u] = part_l[ix * G + j];
-            oi[u] = part_o[(ix * G + j) * D + dim];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (t0[u] < sp)
-                merge_into(la, oa, li[u], oi[u]);
-            else
-                merge_into(lb, ob, li[u], oi[u]);
-        }
-    }
-    for (; i < cnt; ++i) {
-        const int64_t ix = (int64_t)begin + i;
-        const float li = part_l[ix * G + j];
-        const float oi = part_o[(ix * G + j) * D + dim];
-        if (items[ix].t0 < sp)
-            merge_into(la, oa, li, oi);
-        else
-            merge_into(lb, ob, li, oi);
-    }
-    float lr = -INFINITY, orr = 0.f;
-    const int slot = dec_slot[bh];
-    if (slot >= 0) {
-        lr = lse_ring[(int64_t)bh * K + slot] * kLog2e;
-        orr = o_ring[((int64_t)bh * K + slot) * D + dim];
-    }
-    merge_into(lr, orr, la, oa);
-    float lo = lr, oo = orr;
-    merge_into(lo, oo, lb, ob);
-    if (out)
-        out[(int64_t)bh * D + dim] = oo;
-    if (out_lse && dim == 0)
-        out_lse[bh] = lo * kLn2;
-    rect_o[(int64_t)bh * D + dim] = orr;
-    if (dim == 0)
-        rect_l[bh] = lr;
-}
-
-// ---------------------------------------------------------------------------
 // Rectify-append: slot t mod K of every (b, h) receives the pre-RoPE query,
 // the rectified summary (natural-log lse) and pos t = pos[b] + pos_offset.
 template <class T, int D>
-__global__ __launch_bounds__(D) void append_kernel(
-    const int32_t *__restrict__ pos, int32_t pos_offset, int T_cap,
-    const typename T::S *__restrict__ qt, int64_t qt_sb, int64_t qt_sh,
-    const float *__restrict__ rect_o, const float *__restrict__ rect_l, int Hq,
-    int K, typename T::S *__restrict__ q_ring, float *__restrict__ o_ring,
-    float *__restrict__ lse_ring, int32_t *__restrict__ pos_ring)
+__global__ __launch_bounds__(D) void append_kernel(StepArgs a, int32_t pos_offset)
 {
-    const int bh = blockIdx.x, b = bh / Hq, h = bh - b * Hq;
+    using S = typename T::S;
+    const Shape &s = a.s;
+    const int bh = blockIdx.x, b = bh / s.Hq, h = bh - b * s.Hq;
     const int dim = threadIdx.x;
-    const int t = pos[b] + pos_offset;
-    if (t < 0 || t >= T_cap)
+    const int t = a.pos[b] + pos_offset;
+    if (t < 0 || t >= s.T)
         return;
-    const int slot = t % K;
-    const int64_t ri = ((int64_t)bh * K + slot) * D + dim;
-    q_ring[ri] = qt[b * qt_sb + h * qt_sh + dim];
-    o_ring[ri] = rect_o[(int64_t)bh * D + dim];
+    const int slot = t % s.K;
+    const int64_t ri = ((int64_t)bh * s.K + slot) * D + dim;
+    ((S *)a.q_ring)[ri] = ((const S *)a.qtilde)[b * a.qt_sb + h * a.qt_sh + dim];
+    a.o_ring[ri] = a.w.rect_o[(int64_t)bh * D + dim];
     if (dim == 0)
-        lse_ring[(int64_t)bh * K + slot] = rect_l[bh] * kLn2;
+        a.lse_ring[(int64_t)bh * s.K + slot] = a.w.rect_l[bh] * kLn2;
     if (h == 0 && dim == 0)
-        pos_ring[(int64_t)b * K + slot] = t;
+        a.pos_ring[(int64_t)b * s.K + slot] = t;
 }
 
 template <class S>
@@ -584,16 +805,8 @@ __global__ void ring_reset_kernel(int64_t n_q, S *__restrict__ q_ring,
         lse_ring[i] = -INFINITY;
     for (int64_t i = i0; i < n_p; i += stride)
         pos_ring[i] = -1;
-    if (i0 == 0) {
-        ctrl[0] = 0;
-        ctrl[1] = 0;
-    }
-}
-
-int attend_grid(int64_t max_items)
-{
-    const int64_t cap = 2048;
-    return (int)(max_items < cap ? (max_items > 0 ? max_items : 1) : cap);
+    if (i0 < 16)
+        ctrl[i0] = 0;
 }
 
 }  // namespace
@@ -601,54 +814,65 @@ int attend_grid(int64_t max_items)
 // ---------------------------------------------------------------------------
 // Launchers with (dtype, D, G) dispatch.
 
-hipError_t launch_match(const Shape &s, const void *qtilde, int64_t qt_sb,
-                        int64_t qt_sh, const void *q_ring,
-                        const int32_t *pos_ring, const int32_t *pos,
-                        const WsPtrs &w, int nsplit, hipStream_t st)
+size_t plan_lds_bytes(int B, int Hq, int Hkv)
 {
-    const dim3 grid(nsplit, s.B * s.Hq), block(kBlock);
-#define MAC_MATCH(TT, DD)                                                     \
-    hipLaunchKernelGGL((match_kernel<TT, DD>), grid, block, 0, st,            \
-                       (const TT::S *)qtilde, qt_sb, qt_sh,                   \
-                       (const TT::S *)q_ring, pos_ring, pos, s.Hq, s.K, s.T,  \
-                       nsplit, w.keys)
-    if (s.dtype == MAC_DTYPE_BF16 && s.D == 128)
-        MAC_MATCH(BF16, 128);
-    else if (s.dtype == MAC_DTYPE_BF16 && s.D == 64)
-        MAC_MATCH(BF16, 64);
-    else if (s.dtype == MAC_DTYPE_F32 && s.D == 128)
-        MAC_MATCH(F32, 128);
-    else
-        MAC_MATCH(F32, 64);
-#undef MAC_MATCH
-    return hipGetLastError();
+    const size_t BH = (size_t)B * Hq, NG = (size_t)B * Hkv;
+    return 4 * (BH + 4 * NG + 1 + kBlock + 1);
 }
 
-hipError_t launch_plan(const Shape &s, int32_t mode, int32_t end_offset,
-                       const int32_t *pos, const WsPtrs &w, int nsplit,
-                       int64_t max_items, int32_t *match_p, float *match_d2,
-                       hipStream_t st)
+int device_cu_count()
 {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, st, w.keys,
-                       nsplit, pos, mode, end_offset, s.B, s.Hq, s.Hkv, s.G,
-                       s.K, s.r, s.T, s.thresh2, w.dec_start, w.dec_slot,
-                       w.grp_begin, w.grp_count, w.ctrl, w.items, max_items,
-                       match_p, match_d2);
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+#define MAC_DISPATCH_TD(FN, ...)                             \
+    do {                                                     \
+        if (a.s.dtype == MAC_DTYPE_BF16 && a.s.D == 128)     \
+            FN<BF16, 128>(__VA_ARGS__);                      \
+        else if (a.s.dtype == MAC_DTYPE_BF16 && a.s.D == 64) \
+            FN<BF16, 64>(__VA_ARGS__);                       \
+        else if (a.s.dtype == MAC_DTYPE_F32 && a.s.D == 128) \
+            FN<F32, 128>(__VA_ARGS__);                       \
+        else                                                 \
+            FN<F32, 64>(__VA_ARGS__);                        \
+    } while (0)
+
+template <class T, int D>
+static void match_go(const StepArgs &a, hipStream_t st)
+{
+    hipLaunchKernelGGL((match_kernel<T, D>), dim3(a.nsplit, a.s.B * a.s.Hq), dim3(kBlock), 0,
+                       st, a);
+}
+
+hipError_t launch_match(const StepArgs &a, hipStream_t st)
+{
+    MAC_DISPATCH_TD(match_go, a, st);
     return hipGetLastError();
 }
 
 template <class T, int D>
-static void attend_g(const Shape &s, const float *q, int64_t q_sb,
-                     int64_t q_sh, const void *k, const void *v,
-                     const WsPtrs &w, int grid, hipStream_t st)
+static void attend_go(const StepArgs &a, hipStream_t st)
 {
-#define MAC_ATT(GG)                                                           \
-    hipLaunchKernelGGL((attend_kernel<T, D, GG>), dim3(grid), dim3(kBlock), 0, \
-                       st, w.items, w.ctrl, q, q_sb, q_sh,                    \
-                       (const typename T::S *)k, (const typename T::S *)v,    \
-                       s.kv_sb, s.kv_sh, s.kv_st, w.dec_start, s.Hq, s.Hkv,   \
-                       s.qscale, w.part_o, w.part_l)
-    switch (s.G) {
+    // Persistent grid: a few workgroups per CU, never more than items.
+    int64_t grid = (int64_t)device_cu_count() * 4;
+    if (grid > a.max_items)
+        grid = a.max_items > 0 ? a.max_items : 1;
+    const size_t lds = plan_lds_bytes(a.s.B, a.s.Hq, a.s.Hkv);
+#define MAC_ATT(GG)                                                                 \
+    hipLaunchKernelGGL((attend_kernel<T, D, GG>), dim3((int)grid), dim3(kBlock), lds, \
+                       st, a)
+    switch (a.s.G) {
     case 1:
         MAC_ATT(1);
         break;
@@ -665,62 +889,48 @@ static void attend_g(const Shape &s, const float *q, int64_t q_sb,
 #undef MAC_ATT
 }
 
-hipError_t launch_attend(const Shape &s, const float *q, int64_t q_sb,
-                         int64_t q_sh, const void *k, const void *v,
-                         const WsPtrs &w, int64_t max_items, hipStream_t st)
+hipError_t launch_attend(const StepArgs &a, hipStream_t st)
 {
-    const int grid = attend_grid(max_items);
-    if (s.dtype == MAC_DTYPE_BF16 && s.D == 128)
-        attend_g<BF16, 128>(s, q, q_sb, q_sh, k, v, w, grid, st);
-    else if (s.dtype == MAC_DTYPE_BF16 && s.D == 64)
-        attend_g<BF16, 64>(s, q, q_sb, q_sh, k, v, w, grid, st);
-    else if (s.dtype == MAC_DTYPE_F32 && s.D == 128)
-        attend_g<F32, 128>(s, q, q_sb, q_sh, k, v, w, grid, st);
-    else
-        attend_g<F32, 64>(s, q, q_sb, q_sh, k, v, w, grid, st);
+    MAC_DISPATCH_TD(attend_go, a, st);
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const Shape &s, int32_t end_offset,
-                          int32_t allow_neg, const int32_t *pos,
-                          const WsPtrs &w, const float *o_ring,
-                          const float *lse_ring, float *out, float *out_lse,
-                          hipStream_t st)
+template <class T, int D>
+static void merge_go(const StepArgs &a, hipStream_t st)
 {
-#define MAC_COMB(DD)                                                          \
-    hipLaunchKernelGGL((combine_kernel<DD>), dim3(s.B * s.Hq), dim3(DD), 0,   \
-                       st, w.items, w.grp_begin, w.grp_count, pos, end_offset, \
-                       allow_neg, s.Hq, s.Hkv, s.G, s.K, s.r, s.T, w.part_o,  \
-                       w.part_l, w.dec_slot, o_ring, lse_ring, out, out_lse,  \
-                       w.rect_o, w.rect_l)
-    if (s.D == 128)
-        MAC_COMB(128);
-    else
-        MAC_COMB(64);
-#undef MAC_COMB
+    const dim3 grid(a.s.B * a.s.Hkv), block(kMergeBlock);
+    switch (a.s.G) {
+    case 1:
+        hipLaunchKernelGGL((merge_kernel<T, D, 1>), grid, block, 0, st, a);
+        break;
+    case 2:
+        hipLaunchKernelGGL((merge_kernel<T, D, 2>), grid, block, 0, st, a);
+        break;
+    case 4:
+        hipLaunchKernelGGL((merge_kernel<T, D, 4>), grid, block, 0, st, a);
+        break;
+    default:
+        hipLaunchKernelGGL((merge_kernel<T, D, 8>), grid, block, 0, st, a);
+        break;
+    }
+}
+
+hipError_t launch_merge(const StepArgs &a, hipStream_t st)
+{
+    MAC_DISPATCH_TD(merge_go, a, st);
     return hipGetLastError();
 }
 
-hipError_t launch_append(const Shape &s, int32_t pos_offset,
-                         const int32_t *pos, const void *qtilde, int64_t qt_sb,
-                         int64_t qt_sh, const WsPtrs &w, void *q_ring,
-                         float *o_ring, float *lse_ring, int32_t *pos_ring,
-                         hipStream_t st)
+template <class T, int D>
+static void append_go(const StepArgs &a, int32_t pos_offset, hipStream_t st)
 {
-#define MAC_APP(TT, DD)                                                       \
-    hipLaunchKernelGGL((append_kernel<TT, DD>), dim3(s.B * s.Hq), dim3(DD), 0, \
-                       st, pos, pos_offset, s.T, (const TT::S *)qtilde, qt_sb, \
-                       qt_sh, w.rect_o, w.rect_l, s.Hq, s.K, (TT::S *)q_ring, \
-                       o_ring, lse_ring, pos_ring)
-    if (s.dtype == MAC_DTYPE_BF16 && s.D == 128)
-        MAC_APP(BF16, 128);
-    else if (s.dtype == MAC_DTYPE_BF16 && s.D == 64)
-        MAC_APP(BF16, 64);
-    else if (s.dtype == MAC_DTYPE_F32 && s.D == 128)
-        MAC_APP(F32, 128);
-    else
-        MAC_APP(F32, 64);
-#undef MAC_APP
+    hipLaunchKernelGGL((append_kernel<T, D>), dim3(a.s.B * a.s.Hq), dim3(D), 0, st, a,
+                       pos_offset);
+}
+
+hipError_t launch_append(const StepArgs &a, int32_t pos_offset, hipStream_t st)
+{
+    MAC_DISPATCH_TD(append_go, a, pos_offset, st);
     return hipGetLastError();
 }
 
@@ -735,13 +945,11 @@ hipError_t launch_ring_reset(const Shape &s, void *q_ring, float *o_ring,
     if (blocks > 4096)
         blocks = 4096;
     if (s.dtype == MAC_DTYPE_BF16)
-        hipLaunchKernelGGL(ring_reset_kernel<uint16_t>, dim3((int)blocks),
-                           dim3(256), 0, st, n_q, (uint16_t *)q_ring, o_ring,
-                           n_l, lse_ring, n_p, pos_ring, ctrl);
+        hipLaunchKernelGGL(ring_reset_kernel<uint16_t>, dim3((int)blocks), dim3(256), 0, st,
+                           n_q, (uint16_t *)q_ring, o_ring, n_l, lse_ring, n_p, pos_ring, ctrl);
     else
-        hipLaunchKernelGGL(ring_reset_kernel<float>, dim3((int)blocks),
-                           dim3(256), 0, st, n_q, (float *)q_ring, o_ring, n_l,
-                           lse_ring, n_p, pos_ring, ctrl);
+        hipLaunchKernelGGL(ring_reset_kernel<float>, dim3((int)blocks), dim3(256), 0, st, n_q,
+                           (float *)q_ring, o_ring, n_l, lse_ring, n_p, pos_ring, ctrl);
     return hipGetLastError();
 }
 

@@ -21,10 +21,11 @@ MAC_DTYPE_BF16 = 1
 MAC_THRESH_ONE_MINUS_TAU = 0
 MAC_THRESH_TAU = 1
 MAC_DEV_BAD_POSITION = 1
+MAC_FLAG_FUSED_APPEND = 1
 STATUS = {0: "MAC_OK", -1: "MAC_ERR_INVALID_ARG", -2: "MAC_ERR_UNSUPPORTED",
           -3: "MAC_ERR_HIP", -4: "MAC_ERR_WORKSPACE_TOO_SMALL",
           -5: "MAC_ERR_MISALIGNED"}
-STAGES = ("match", "plan", "attend", "combine", "append")
+STAGES = ("match", "attend", "merge", "append")
 
 
 class MacError(RuntimeError):
@@ -40,7 +41,7 @@ class mac_params(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32), ("ring_k", ctypes.c_int32),
         ("band_r", ctypes.c_int32), ("kv_capacity", ctypes.c_int32),
         ("tau", ctypes.c_float), ("thresh_mode", ctypes.c_int32),
-        ("sm_scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float), ("flags", ctypes.c_int32),
         ("kv_stride_b", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64),
         ("kv_stride_t", ctypes.c_int64),
     ]
@@ -84,7 +85,7 @@ def load():
                                             ctypes.POINTER(ctypes.c_int32)]),
         "mac_release": (ctypes.c_int, [_vp]),
         "mac_status_string": (ctypes.c_char_p, [ctypes.c_int]),
-        "mac_chunk_tokens": (ctypes.c_int32, []),
+        "mac_chunk_tokens": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32]),
         "mac_partition": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32,
                                            ctypes.POINTER(ctypes.c_int32),
@@ -121,9 +122,9 @@ def _check(fn, rc):
 
 def make_params(batch, n_q_heads, n_kv_heads, head_dim, kv_dtype, ring_k,
                 band_r, kv_capacity, tau, thresh_mode=MAC_THRESH_ONE_MINUS_TAU,
-                sm_scale=0.0, strides=(0, 0, 0)) -> mac_params:
+                sm_scale=0.0, strides=(0, 0, 0), flags=0) -> mac_params:
     return mac_params(batch, n_q_heads, n_kv_heads, head_dim, kv_dtype, ring_k,
-                      band_r, kv_capacity, tau, thresh_mode, sm_scale, 0,
+                      band_r, kv_capacity, tau, thresh_mode, sm_scale, flags,
                       *strides)
 
 
@@ -184,7 +185,7 @@ def mac_profile_start(handle, n_steps):
 
 def mac_profile_read(handle):
     """Summed milliseconds per stage (dict) and the number of steps."""
-    ms = (ctypes.c_double * 5)()
+    ms = (ctypes.c_double * 4)()
     n = ctypes.c_int32()
     _check("mac_profile_read", load().mac_profile_read(handle, ms, ctypes.byref(n)))
     return dict(zip(STAGES, list(ms))), n.value
@@ -198,8 +199,8 @@ def mac_status_string(status: int) -> str:
     return load().mac_status_string(status).decode()
 
 
-def mac_chunk_tokens() -> int:
-    return int(load().mac_chunk_tokens())
+def mac_chunk_tokens(s: int, e: int) -> int:
+    return int(load().mac_chunk_tokens(s, e))
 
 
 def mac_partition(s: int, e: int, r: int):

@@ -26,10 +26,9 @@ sys.path.insert(0, ROOT)
 from attention_reuse_amd import workload as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-STAGES = ("match", "plan", "attend", "combine", "append")
+STAGES = ("match", "attend", "merge", "append")
 KERNEL_NAMES = {"match": "match_kernel", "attend": "attend_kernel",
-                "combine": "combine_kernel", "plan": "plan_kernel",
-                "append": "append_kernel"}
+                "merge": "merge_kernel", "append": "append_kernel"}
 
 
 def parse():
@@ -41,6 +40,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=0,
                     help="layer copies per step (0 = enough to overflow the Infinity Cache)")
     ap.add_argument("--mode", choices=("mac", "full"), default="mac")
+    ap.add_argument("--append", choices=("aux", "fused"), default="aux",
+                    help="rectify-append on the auxiliary stream or fused into the merge")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--no-profile", action="store_true")
@@ -93,12 +94,14 @@ def algorithmic_bytes(cfg, match_p, m):
     kv = int(span.sum()) * d * e * 2
     attend = kv + B * H * d * 4
     hits = int((match_p >= 0).sum())
-    combine = hits * (d + 1) * 4 + B * H * (d + 1) * 4
+    # The merge reads the cached summary of every hit head and writes the
+    # output and its lse (split-KV partials are overhead, not credited).
+    merge = hits * (d + 1) * 4 + B * H * (d + 1) * 4
     append = B * H * (d * e + (d + 1) * 4) + B * 4
     full_kv = int((m + 1).sum()) * Hkv * d * e * 2
-    return dict(match=match, attend=attend, combine=combine, append=append, plan=0,
-                kv=kv, full_kv=full_kv, hits=hits, group_miss=int(
-                    (match_p.reshape(B, Hkv, G) < 0).any(axis=2).sum()))
+    return dict(match=match, plan=0, attend=attend, merge=merge, append=append, kv=kv,
+                full_kv=full_kv,
+                hits=hits, group_miss=int((match_p.reshape(B, Hkv, G) < 0).any(axis=2).sum()))
 
 
 def cpu_baseline(cfg, K, V, qt, q, budget_s):
@@ -176,7 +179,8 @@ def main():
     pos_np = wl.decode_positions(cfg)
     pos = to_dev(pos_np)
     p = mac.make_params(B, H, Hkv, d, mac.MAC_DTYPE_F32 if cfg.dtype == "f32" else mac.MAC_DTYPE_BF16,
-                        R, cfg.band_r, cfg.capacity, cfg.tau)
+                        R, cfg.band_r, cfg.capacity, cfg.tau,
+                        flags=mac.MAC_FLAG_FUSED_APPEND if args.append == "fused" else 0)
     wsb = mac.mac_workspace_bytes(p)
     stream = torch.cuda.current_stream()
     st = stream.cuda_stream
@@ -245,7 +249,7 @@ def main():
 
     # Algorithmic bytes of the timed steps (from the recorded decisions).
     mrec = match_rec.cpu().numpy()
-    per = {k: 0.0 for k in ("match", "attend", "combine", "append", "plan", "kv", "full_kv",
+    per = {k: 0.0 for k in ("match", "plan", "attend", "merge", "append", "kv", "full_kv",
                             "hits", "group_miss")}
     timed = range(args.warmup, args.warmup + args.steps)
     for s in timed:
@@ -298,7 +302,7 @@ def main():
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(cfg, K, V, qt, q, args.cpu_seconds)
 
-    alg_step = sum(per[k] for k in ("match", "attend", "combine", "append")) / args.steps
+    alg_step = sum(per[k] for k in ("match", "attend", "merge", "append")) / args.steps
     value = B * H * NL / (ms_per_step * 1e-3)
     line = {
         "metric": "decode attention steps/sec (heads*layers) + KV GB read/step + % HBM roofline",
@@ -309,7 +313,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16 in / fp32 accumulate" if cfg.dtype == "bf16" else "fp32",
         "data": "synthetic (seeded N(0,1) K/V, prototype+noise query stream)",
-        "config": {"workload": cfg.name, "mode": args.mode, "layers": NL,
+        "config": {"workload": cfg.name, "mode": args.mode, "append": args.append,
+                   "layers": NL,
                    "batch": B, "q_heads": H, "kv_heads": Hkv, "head_dim": d,
                    "context": cfg.ctx, "ring_k": R, "band_r": cfg.band_r, "tau": cfg.tau,
                    "parallelism": "1 GPU"},

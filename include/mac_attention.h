@@ -62,6 +62,11 @@ enum { MAC_DTYPE_F32 = 0, MAC_DTYPE_BF16 = 1 };
  * once to fp32. */
 enum { MAC_THRESH_ONE_MINUS_TAU = 0, MAC_THRESH_TAU = 1 };
 
+/* mac_params.flags bits.
+ *   MAC_FLAG_FUSED_APPEND: the rectify-append is done by the merge inside the
+ *   attention kernel instead of a separate kernel on the auxiliary stream. */
+enum { MAC_FLAG_FUSED_APPEND = 1 };
+
 /* Device status flags latched in the workspace. */
 enum { MAC_DEV_BAD_POSITION = 1 /* some m outside [0, kv_capacity) */ };
 
@@ -77,7 +82,7 @@ typedef struct mac_params {
     float tau;            /* threshold parameter                             */
     int32_t thresh_mode;  /* MAC_THRESH_*                                    */
     float sm_scale;       /* logit scale; 0 means 1/sqrt(d)                  */
-    int32_t reserved;     /* must be 0                                       */
+    int32_t flags;        /* MAC_FLAG_* bits, 0 for the defaults             */
     /* K/V cache strides in elements; all 0 means dense [B, Hkv, T, d].
      * Row t of (b, g) starts at b*kv_stride_b + g*kv_stride_h + t*kv_stride_t
      * and must be 16-byte aligned. */
@@ -139,11 +144,14 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
  *   match_p [B, Hq] int32 or NULL  matched position, -1 on a miss
  *   match_d2[B, Hq] fp32 or NULL   squared distance of the nearest candidate
  *                                  (+inf when the window is empty)
- * Match, amend and complete run on main_stream; the rectify-append of the
- * rings runs on aux_stream (main_stream if NULL or equal), ordered after the
- * merge by an event; the next call on the same handle waits for it.  Returns
- * without a host synchronisation, so a steady-state step can be captured
- * into a HIP graph (join aux_stream back with mac_join_aux first).
+ * Match, amend and complete run on main_stream as three kernels (match,
+ * plan + attention, merge).  The rectify-append of the rings runs as a third
+ * kernel on aux_stream (main_stream if NULL or equal), ordered after the
+ * merge by an event; the next call on the same handle waits for it.  With
+ * MAC_FLAG_FUSED_APPEND the merge writes the rings itself and aux_stream is
+ * unused.  Returns without a host synchronisation, so a steady-state step
+ * can be captured into a HIP graph (join aux_stream back with mac_join_aux
+ * first).  Calls on one handle must not overlap; handles are independent.
  */
 mac_status mac_decode_step(mac_handle *h, const void *qtilde, const float *q,
                            const void *k_cache, const void *v_cache,
@@ -171,26 +179,28 @@ mac_status mac_full_decode(const mac_params *p, const float *q,
 mac_status mac_read_device_status(const mac_params *p, void *workspace,
                                   void *stream, int32_t *flags);
 
-/* Per-stage timing with HIP events (diagnostics).  mac_profile_start arms
+/* Per-kernel timing with HIP events (diagnostics).  mac_profile_start arms
  * recording for the next `n_steps` decode steps of the handle; stages are
- * 0 match, 1 plan, 2 attention, 3 merge, 4 rectify-append.
+ * 0 match, 1 plan + attention, 2 merge, 3 rectify-append (0 when fused).
  * mac_profile_read synchronises, returns the summed milliseconds per stage
- * in ms[5] and the number of recorded steps in *n, and disarms. */
+ * in ms[4] and the number of recorded steps in *n, and disarms. */
 mac_status mac_profile_start(mac_handle *h, int32_t n_steps);
-mac_status mac_profile_read(mac_handle *h, double ms[5], int32_t *n);
+mac_status mac_profile_read(mac_handle *h, double ms[4], int32_t *n);
 
 /* Free the handle and its events (not the caller's buffers). */
 mac_status mac_release(mac_handle *h);
 
 const char *mac_status_string(mac_status s);
 
-/* Tokens per attention work item (the fixed split-KV partition). */
-int32_t mac_chunk_tokens(void);
+/* Grid of the split-KV partition for a KV group attending [s, e]: the
+ * smallest C = 128 * 2^k with at most 128 grid cells over the range (-1 on
+ * bad input). */
+int32_t mac_chunk_tokens(int32_t s, int32_t e);
 
 /* The split-KV partition the kernels use for a KV group whose heads attend
  * [s, e] with band r (host mirror of the device planner): item i covers
- * [t0[i], t1[i]); boundaries are s, the multiples of mac_chunk_tokens() in
- * (s, e], the rectify split e - r + 1 when inside (s, e], and e + 1.
+ * [t0[i], t1[i]); boundaries are s, the multiples of mac_chunk_tokens(s, e)
+ * in (s, e], the rectify split e - r + 1 when inside (s, e], and e + 1.
  * Writes min(n, cap) items (host arrays) and returns n, or -1 on bad input. */
 int32_t mac_partition(int32_t s, int32_t e, int32_t r, int32_t *t0,
                       int32_t *t1, int32_t cap);

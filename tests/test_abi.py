@@ -41,7 +41,13 @@ def test_struct_layout_matches_header():
 def test_status_strings_and_chunk(lib):
     assert mac.mac_status_string(0) == "ok"
     assert "workspace" in mac.mac_status_string(-4)
-    assert mac.mac_chunk_tokens() == 128
+    assert mac.mac_chunk_tokens(0, 63) == 128
+    assert mac.mac_chunk_tokens(0, 128 * 128 - 1) == 128
+    assert mac.mac_chunk_tokens(0, 128 * 128) == 256
+    assert mac.mac_chunk_tokens(0, 65536) == 1024
+    assert mac.mac_chunk_tokens(100, 65536) == 512
+    assert mac.mac_chunk_tokens(0, 262399) == 4096
+    assert mac.mac_chunk_tokens(5, 4) == -1
 
 
 def test_workspace_and_ring_sizes(lib):
@@ -51,15 +57,17 @@ def test_workspace_and_ring_sizes(lib):
     # 2 x 32 heads x 1024 slots x 128 dims: bf16 query ring, fp32 summaries.
     assert mac.mac_ring_bytes(p) == (2 * 32 * 1024 * 128 * 2, 2 * 32 * 1024 * 128 * 4,
                                      2 * 32 * 1024 * 4, 2 * 1024 * 4)
-    # The workspace grows with the KV capacity (split-KV partials).
-    assert mac.mac_workspace_bytes(_params(kv_capacity=65536)) > ws
+    # The split-KV partials are bounded per KV group, so the workspace does
+    # not grow with the KV capacity.
+    assert mac.mac_workspace_bytes(_params(kv_capacity=65536)) == ws
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), -2), (dict(kv_dtype=7), -2), (dict(n_q_heads=48, n_kv_heads=3), -2),
     (dict(n_q_heads=30), -1), (dict(ring_k=0), -1), (dict(band_r=-1), -1),
     (dict(batch=0), -1), (dict(kv_capacity=0), -1), (dict(tau=float("nan")), -1),
-    (dict(thresh_mode=2), -1), (dict(strides=(0, 0, 100)), -1),
+    (dict(thresh_mode=2), -1), (dict(strides=(0, 0, 100)), -1), (dict(flags=2), -1),
+    (dict(flags=1), 0), (dict(batch=300), -2),
     (dict(strides=(1 << 20, 4096 * 136, 136)), 0), (dict(strides=(1 << 20, 4096 * 132, 132)), -5),
 ])
 def test_param_validation(lib, kw, status):
@@ -117,8 +125,9 @@ def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
 def test_partition_covers_range_on_the_grid(lib, s, e, r):
     """Items tile [s, e] in order; every interior boundary is a multiple of the
     chunk or the rectify split e - r + 1; no item crosses either."""
-    C = mac.mac_chunk_tokens()
+    C = mac.mac_chunk_tokens(s, e)
     items = mac.mac_partition(s, e, r)
+    assert len(items) <= 130
     assert items[0][0] == s and items[-1][1] == e + 1
     for (a0, a1), (b0, _) in zip(items, items[1:]):
         assert a1 == b0

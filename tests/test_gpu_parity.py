@@ -159,14 +159,33 @@ def test_forced_miss_is_bitwise_full_decode():
         assert np.array_equal(out.cpu().numpy(), gpu["out"][s]), s
 
 
-def test_run_to_run_deterministic_and_aux_stream_invariant():
+def test_run_to_run_deterministic_and_append_mode_invariant():
+    """Outputs and rings are bitwise identical run to run, with the
+    rectify-append on an auxiliary stream, on the main stream, or fused into
+    the merge."""
     cfg = _cfg(steps=12, sigma=(0.02, 0.5))
     K, V, qt, q = _inputs(cfg)
-    layer = Layer(cfg, K, V, qt, q)
-    a = run_steps(layer.init(), cfg.steps, aux=torch.cuda.Stream())
-    b = run_steps(layer.init(), cfg.steps, aux=None)
-    for k in a:
-        assert np.array_equal(a[k], b[k]), k
+    runs = []
+    for flags, aux in ((0, torch.cuda.Stream()), (0, None),
+                       (mac.MAC_FLAG_FUSED_APPEND, torch.cuda.Stream()), (0, torch.cuda.Stream())):
+        layer = Layer(cfg, K, V, qt, q, params=params_for(cfg, flags=flags))
+        res = run_steps(layer.init(), cfg.steps, aux=aux)
+        res["rings"] = [t.cpu().float().numpy() for t in
+                        (layer.q_ring, layer.o_ring, layer.lse_ring, layer.pos_ring)]
+        runs.append(res)
+        layer.release()
+    for r in runs[1:]:
+        for k in ("out", "lse", "p", "d2"):
+            assert np.array_equal(runs[0][k], r[k]), k
+        for x, y in zip(runs[0]["rings"], r["rings"]):
+            assert np.array_equal(x, y)
+
+
+def test_lockstep_fused_append(oracle_lib):
+    cfg = _cfg(batch=2, ctx=1500, steps=24, ring_k=128, band_r=32, sigma=(0.02, 0.5), seed=5)
+    K, V, qt, q = _inputs(cfg)
+    layer = Layer(cfg, K, V, qt, q, params=params_for(cfg, flags=mac.MAC_FLAG_FUSED_APPEND))
+    _lockstep(oracle_lib, cfg, layer=layer)
 
 
 def test_exact_reuse_on_gpu():
