@@ -27,7 +27,8 @@ WsLayout ws_layout(int B, int Hq, int Hkv, int D, int K, int T)
         return o;
     };
     const size_t BH = (size_t)B * Hq, BG = (size_t)B * Hkv;
-    L.keys = take(BH * L.nsplit * sizeof(unsigned long long));
+    L.keys = take(BH * sizeof(unsigned long long));
+    L.ctx = take((size_t)B * 4);
     L.dec_slot = take(BH * 4);
     L.grp_begin = take(BG * 4);
     L.grp_count = take(BG * 4);
@@ -46,6 +47,7 @@ WsPtrs ws_ptrs(void *base, const WsLayout &L)
     char *c = (char *)base;
     WsPtrs w;
     w.keys = (unsigned long long *)(c + L.keys);
+    w.ctx = (int32_t *)(c + L.ctx);
     w.dec_slot = (int32_t *)(c + L.dec_slot);
     w.grp_begin = (int32_t *)(c + L.grp_begin);
     w.grp_count = (int32_t *)(c + L.grp_count);
@@ -306,14 +308,12 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
         return MAC_ERR_HIP;
     }
     if (launch_ring_reset(s, rings->q_ring, rings->o_ring, rings->lse_ring,
-                          rings->pos_ring, w.ctrl, st) != hipSuccess) {
+                          rings->pos_ring, w, st) != hipSuccess) {
         mac_release(h);
         return MAC_ERR_HIP;
     }
     if (n_warm > 0) {
-        // Prompt lengths are staged in the match-key region, which the warm
-        // path (plan in kPlanInit mode) never reads.
-        int32_t *d_ctx = (int32_t *)w.keys;
+        int32_t *d_ctx = w.ctx;
         if (hipMemcpyAsync(d_ctx, ctx_len, sizeof(int32_t) * s.B,
                            hipMemcpyHostToDevice, st) != hipSuccess ||
             hipStreamSynchronize(st) != hipSuccess) {

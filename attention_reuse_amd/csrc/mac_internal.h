@@ -79,7 +79,7 @@ struct RangeSplit {
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WsLayout {
-    size_t keys, dec_slot, grp_begin, grp_count, grp_start, ctrl, part_o,
+    size_t keys, ctx, dec_slot, grp_begin, grp_count, grp_start, ctrl, part_o,
         part_l, rect_o, rect_l, total;
     int64_t max_items;
     int32_t nsplit;
@@ -104,7 +104,8 @@ struct Shape {
 
 // Device pointers into the workspace.
 struct WsPtrs {
-    unsigned long long *keys;
+    unsigned long long *keys;  // [B*Hq] per-head match key
+    int32_t *ctx;              // [B] prompt lengths during the warm-up
     int32_t *dec_slot, *grp_begin, *grp_count, *grp_start, *ctrl;
     float *part_o, *part_l, *rect_o, *rect_l;
 };
@@ -153,8 +154,8 @@ hipError_t launch_merge(const StepArgs &a, hipStream_t st);
 // request b is pos[b] + pos_offset.
 hipError_t launch_append(const StepArgs &a, int32_t pos_offset, hipStream_t st);
 hipError_t launch_ring_reset(const Shape &s, void *q_ring, float *o_ring,
-                             float *lse_ring, int32_t *pos_ring,
-                             int32_t *ctrl, hipStream_t st);
+                             float *lse_ring, int32_t *pos_ring, const WsPtrs &w,
+                             hipStream_t st);
 int device_cu_count();
 
 }  // namespace mac

@@ -32,6 +32,8 @@
 // and match run on VALU; MFMA tiles would be 3/4 padding at G = 4.
 #include <math.h>
 
+#include <utility>
+
 #include "mac_attention.h"
 #include "mac_internal.h"
 
@@ -110,6 +112,66 @@ __device__ inline float row_sum(float v)
     if (W == 32)
         v += __shfl_xor(v, 16, 64);
     return v;
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [0, N).
+template <class F, int... Is>
+__device__ inline void static_for_impl(F &&f, std::integer_sequence<int, Is...>)
+{
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ inline void static_for(F &&f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+constexpr int kDppRowRor = 0x120;       // + n: lane i <- lane (i - n) mod 16
+constexpr int kDppRowNewBcast = 0x150;  // + n: every lane <- lane n of its row
+
+// Reduce-scatter of 16 values over the 16 lanes of a row: lane L returns
+// the row sum of v[L].  Four exchange steps halve the values a lane holds
+// (partners: lane ^ 8, the mirror within 8 lanes, lane ^ 2, lane ^ 1).
+__device__ inline float row_reduce_scatter16(const float (&v)[16], int lane)
+{
+    const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
+    float a[8], c[4], d[2];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const float keep = b3 ? v[8 + m] : v[m];
+        const float send = b3 ? v[m] : v[8 + m];
+        a[m] = keep + dpp<kDppRowRor + 8>(send);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const float keep = b2 ? a[4 + m] : a[m];
+        const float send = b2 ? a[m] : a[4 + m];
+        c[m] = keep + dpp<kDppHalfMirror>(send);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const float keep = b1 ? c[2 + m] : c[m];
+        const float send = b1 ? c[m] : c[2 + m];
+        d[m] = keep + dpp<kDppQuadXor2>(send);
+    }
+    const float keep = b0 ? d[1] : d[0];
+    const float send = b0 ? d[0] : d[1];
+    return keep + dpp<kDppQuadXor1>(send);
+}
+
+// All-reduce (max or sum) over the lanes of a 16-lane row that are equal
+// modulo G, by rotations of G, 2G, ... 8 lanes.
+template <int G, bool kMax>
+__device__ inline float row_mod_reduce(float x)
+{
+    static_for<4>([&](auto S) {
+        constexpr int sh = 1 << S;
+        if constexpr (sh >= G) {
+            const float y = dpp<kDppRowRor + sh>(x);
+            x = kMax ? fmaxf(x, y) : x + y;
+        }
+    });
+    return x;
 }
 
 __device__ inline unsigned long long shfl_xor_u64(unsigned long long v, int off)
@@ -195,11 +257,7 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
             s_flag[0] = 1;
         int start = 0, slot = -1;
         if (a.mode == kPlanMatch) {
-            unsigned long long key = ~0ull;
-            const unsigned long long *kp = a.w.keys + (int64_t)bh * a.nsplit;
-#pragma unroll 4
-            for (int i = 0; i < a.nsplit; ++i)
-                key = umin64(key, kp[i]);
+            const unsigned long long key = a.w.keys[bh];
             const bool any = key != ~0ull;
             const float d2 = any ? __uint_as_float((uint32_t)(key >> 32)) : INFINITY;
             const int p = any ? (int)(0xffffffffu - (uint32_t)key) : -1;
@@ -306,7 +364,8 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
 // Match.  Grid (nsplit, B*Hq).  Each LPR-lane row of a wave computes
 // the squared distance of one ring slot; the workgroup keeps the smallest
 //   key = float_bits(D) << 32 | (0xffffffff - p)
-// (non-negative floats order like their bits; equal D prefers larger p).
+// (non-negative floats order like their bits; equal D prefers larger p)
+// and folds it into the head's key with a 64-bit atomic minimum.
 template <class T, int D>
 __global__ __launch_bounds__(kBlock) void match_kernel(StepArgs a)
 {
@@ -370,7 +429,11 @@ __global__ __launch_bounds__(kBlock) void match_kernel(StepArgs a)
 #pragma unroll
         for (int i = 1; i < kBlock / 64; ++i)
             best = umin64(best, sm[i]);
-        a.w.keys[(int64_t)bh * a.nsplit + blockIdx.x] = best;
+        // The head's key is the minimum over its splits; the minimum is
+        // exact and order-independent.  Read by the next kernel; reset to
+        // ~0 by the merge of the same step.
+        if (best != ~0ull)
+            atomicMin(&a.w.keys[bh], best);
     }
 }
 
@@ -444,6 +507,8 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(StepArgs a)
     __shared__ float lds[M::kFloats];
     const Shape &s = a.s;
     const int grp = blockIdx.x;
+    if (threadIdx.x < G)  // ready for the next step's match
+        a.w.keys[(int64_t)grp * G + threadIdx.x] = ~0ull;
     const int cnt = a.w.grp_count[grp];
     if (cnt == 0)
         return;  // the planner wrote this group's outputs
@@ -558,14 +623,17 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(StepArgs a)
 template <class T, int D, int G>
 struct AttendShape {
     static constexpr int EPL = T::EPL, LPR = D / EPL, RPB = kBlock / LPR;
-    static constexpr int NB = 4;  // tokens per row per block
+    // 16-lane rows use the reduce-scatter softmax (NB * G <= 16 values per
+    // lane); other row widths all-reduce every logit.
+    static constexpr bool kScatter = LPR == 16;
+    static constexpr int NB = kScatter ? (16 / G < 4 ? 16 / G : 4) : 4;  // tokens per row per block
     static constexpr int kFloats = RPB * G * (D + 2);
 };
 
 template <class T, int G, int EPL, int NB>
 struct KvBlock {
     uint4 k[NB], v[NB];
-    int t[NB];
+    int base;  // token of row 0, i = 0
 };
 
 template <class T, int D, int G, int LPR, int RPB, int NB>
@@ -573,10 +641,10 @@ __device__ inline void load_block(KvBlock<T, G, T::EPL, NB> &kv, const typename 
                                   const typename T::S *vb, int64_t kv_st, int base, int t1,
                                   int row)
 {
+    kv.base = base;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
         const int t = base + i * RPB + row;
-        kv.t[i] = t;
         if (t < t1) {
             kv.k[i] = load16(kb + (int64_t)t * kv_st);
             kv.v[i] = load16(vb + (int64_t)t * kv_st);
@@ -587,8 +655,8 @@ __device__ inline void load_block(KvBlock<T, G, T::EPL, NB> &kv, const typename 
     }
 }
 
-template <class T, int D, int G, int LPR, int NB>
-__device__ inline void compute_block(const KvBlock<T, G, T::EPL, NB> &kv,
+template <class T, int D, int G, int LPR, int RPB, int NB>
+__device__ inline void compute_block(const KvBlock<T, G, T::EPL, NB> &kv, int row,
                                      const float (&qr)[G][T::EPL], const int (&st)[G], int t1,
                                      float (&mrun)[G], float (&lrun)[G],
                                      float (&acc)[G][T::EPL])
@@ -613,7 +681,8 @@ __device__ inline void compute_block(const KvBlock<T, G, T::EPL, NB> &kv,
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             const float v = row_sum<LPR>(sc[i][j]);
-            sc[i][j] = (kv.t[i] < t1 && kv.t[i] >= st[j]) ? v : -INFINITY;
+            const int t = kv.base + i * RPB + row;
+            sc[i][j] = (t < t1 && t >= st[j]) ? v : -INFINITY;
         }
 #pragma unroll
     for (int j = 0; j < G; ++j) {
@@ -649,6 +718,64 @@ __device__ inline void compute_block(const KvBlock<T, G, T::EPL, NB> &kv,
     }
 }
 
+// One block with 16-lane rows: after the partial dot products each lane
+// holds NB*G (<= 16) partial logits; a reduce-scatter leaves lane k with
+// the logit of token k / G, head k % G, so the softmax of a block costs two
+// exponentials per lane.  The per-head running max and sum live in the
+// lanes of that head; probabilities and rescale factors reach the P*V
+// products through row broadcasts.
+template <class T, int G, int RPB, int NB>
+__device__ inline void compute_block_rs(const KvBlock<T, G, T::EPL, NB> &kv, int row, int lane,
+                                        const float (&qr)[G][T::EPL], int my_st, int t1,
+                                        float &mrun, float &lrun, float (&acc)[G][T::EPL])
+{
+    constexpr int EPL = T::EPL;
+    static_assert(NB * G <= 16, "values per row");
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        v[k] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        float kf[EPL];
+        unpack<T>(kv.k[i], kf);
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            float x = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+                x = fmaf(qr[j][e], kf[e], x);
+            v[i * G + j] = x;
+        }
+    }
+    float sv = row_reduce_scatter16(v, lane);
+    const int t = kv.base + (lane / G) * RPB + row;
+    sv = (lane < NB * G && t < t1 && t >= my_st) ? sv : -INFINITY;
+    const float bm = row_mod_reduce<G, true>(sv);
+    const float mn = fmaxf(mrun, bm);
+    const bool live = mn != -INFINITY;
+    const float alpha = live ? ex2(mrun - mn) : 1.f;
+    const float p = live ? ex2(sv - mn) : 0.f;
+    lrun = lrun * alpha + row_mod_reduce<G, false>(p);
+    mrun = mn;
+    static_for<G>([&](auto J) {
+        const float aj = dpp<kDppRowNewBcast + J>(alpha);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            acc[J][e] *= aj;
+    });
+    static_for<NB>([&](auto I) {
+        float vf[EPL];
+        unpack<T>(kv.v[I], vf);
+        static_for<G>([&](auto J) {
+            const float pb = dpp<kDppRowNewBcast + I * G + J>(p);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+                acc[J][e] = fmaf(pb, vf[e], acc[J][e]);
+        });
+    });
+}
+
 template <class T, int D, int G>
 __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
 {
@@ -677,10 +804,13 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
             else
                 hi = mid;
         }
-        const int grp = lo - 1;
+        // Workgroup-uniform values are moved to scalar registers.
+        const int grp = __builtin_amdgcn_readfirstlane(lo - 1);
         const int b = grp / s.Hkv, g = grp - b * s.Hkv;
         int t0, t1;
         RangeSplit(pt.gstart[grp], pt.gend[grp], r_split).item(it - pt.gbegin[grp], t0, t1);
+        t0 = __builtin_amdgcn_readfirstlane(t0);
+        t1 = __builtin_amdgcn_readfirstlane(t1);
         const S *kb = (const S *)a.k + b * s.kv_sb + g * s.kv_sh + lane * EPL;
         const S *vb = (const S *)a.v + b * s.kv_sb + g * s.kv_sh + lane * EPL;
 
@@ -700,7 +830,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
                 qr[j][e4 + 2] = v.z * s.qscale;
                 qr[j][e4 + 3] = v.w * s.qscale;
             }
-            st[j] = pt.start[b * s.Hq + g * G + j];
+            st[j] = __builtin_amdgcn_readfirstlane(pt.start[b * s.Hq + g * G + j]);
         }
 
         float mrun[G], lrun[G], acc[G][EPL];
@@ -712,25 +842,50 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
             for (int e = 0; e < EPL; ++e)
                 acc[j][e] = 0.f;
         }
-        // Blocks alternate between the two buffers; the next block is
-        // always requested before the current one is consumed.
-        for (int base = t0; base < t1; base += 2 * TPB) {
-            if (base + TPB < t1)
-                load_block<T, D, G, LPR, RPB, NB>(bufB, kb, vb, s.kv_st, base + TPB, t1, row);
-            compute_block<T, D, G, LPR, NB>(bufA, qr, st, t1, mrun, lrun, acc);
-            if (base + TPB < t1) {
-                if (base + 2 * TPB < t1)
-                    load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, base + 2 * TPB, t1,
-                                                      row);
-                compute_block<T, D, G, LPR, NB>(bufB, qr, st, t1, mrun, lrun, acc);
-            }
-        }
-
-        if (lane == 0) {
+        if constexpr (L::kScatter) {
+            // Lane k keeps the running max / sum of head k % G in mrun[0],
+            // lrun[0]; its token-start bound is that head's.
+            int my_st = st[0];
 #pragma unroll
-            for (int j = 0; j < G; ++j) {
-                sm_m[row * G + j] = mrun[j];
-                sm_l[row * G + j] = lrun[j];
+            for (int j = 1; j < G; ++j)
+                my_st = (lane % G == j) ? st[j] : my_st;
+            for (int base = t0; base < t1; base += 2 * TPB) {
+                if (base + TPB < t1)
+                    load_block<T, D, G, LPR, RPB, NB>(bufB, kb, vb, s.kv_st, base + TPB, t1, row);
+                compute_block_rs<T, G, RPB, NB>(bufA, row, lane, qr, my_st, t1, mrun[0], lrun[0],
+                                                acc);
+                if (base + TPB < t1) {
+                    if (base + 2 * TPB < t1)
+                        load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, base + 2 * TPB,
+                                                          t1, row);
+                    compute_block_rs<T, G, RPB, NB>(bufB, row, lane, qr, my_st, t1, mrun[0],
+                                                    lrun[0], acc);
+                }
+            }
+            if (lane < G) {
+                sm_m[row * G + lane] = mrun[0];
+                sm_l[row * G + lane] = lrun[0];
+            }
+        } else {
+            // Blocks alternate between the two buffers; the next block is
+            // always requested before the current one is consumed.
+            for (int base = t0; base < t1; base += 2 * TPB) {
+                if (base + TPB < t1)
+                    load_block<T, D, G, LPR, RPB, NB>(bufB, kb, vb, s.kv_st, base + TPB, t1, row);
+                compute_block<T, D, G, LPR, RPB, NB>(bufA, row, qr, st, t1, mrun, lrun, acc);
+                if (base + TPB < t1) {
+                    if (base + 2 * TPB < t1)
+                        load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, base + 2 * TPB,
+                                                          t1, row);
+                    compute_block<T, D, G, LPR, RPB, NB>(bufB, row, qr, st, t1, mrun, lrun, acc);
+                }
+            }
+            if (lane == 0) {
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    sm_m[row * G + j] = mrun[j];
+                    sm_l[row * G + j] = lrun[j];
+                }
             }
         }
 #pragma unroll
@@ -793,7 +948,8 @@ __global__ void ring_reset_kernel(int64_t n_q, S *__restrict__ q_ring,
                                   float *__restrict__ o_ring, int64_t n_l,
                                   float *__restrict__ lse_ring, int64_t n_p,
                                   int32_t *__restrict__ pos_ring,
-                                  int32_t *__restrict__ ctrl)
+                                  int32_t *__restrict__ ctrl, int64_t n_keys,
+                                  unsigned long long *__restrict__ keys)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -805,6 +961,8 @@ __global__ void ring_reset_kernel(int64_t n_q, S *__restrict__ q_ring,
         lse_ring[i] = -INFINITY;
     for (int64_t i = i0; i < n_p; i += stride)
         pos_ring[i] = -1;
+    for (int64_t i = i0; i < n_keys; i += stride)
+        keys[i] = ~0ull;
     if (i0 < 16)
         ctrl[i0] = 0;
 }
@@ -935,9 +1093,10 @@ hipError_t launch_append(const StepArgs &a, int32_t pos_offset, hipStream_t st)
 }
 
 hipError_t launch_ring_reset(const Shape &s, void *q_ring, float *o_ring,
-                             float *lse_ring, int32_t *pos_ring,
-                             int32_t *ctrl, hipStream_t st)
+                             float *lse_ring, int32_t *pos_ring, const WsPtrs &w,
+                             hipStream_t st)
 {
+    const int64_t n_keys = (int64_t)s.B * s.Hq;
     const int64_t n_q = (int64_t)s.B * s.Hq * s.K * s.D;
     const int64_t n_l = (int64_t)s.B * s.Hq * s.K;
     const int64_t n_p = (int64_t)s.B * s.K;
@@ -946,10 +1105,12 @@ hipError_t launch_ring_reset(const Shape &s, void *q_ring, float *o_ring,
         blocks = 4096;
     if (s.dtype == MAC_DTYPE_BF16)
         hipLaunchKernelGGL(ring_reset_kernel<uint16_t>, dim3((int)blocks), dim3(256), 0, st,
-                           n_q, (uint16_t *)q_ring, o_ring, n_l, lse_ring, n_p, pos_ring, ctrl);
+                           n_q, (uint16_t *)q_ring, o_ring, n_l, lse_ring, n_p, pos_ring, w.ctrl,
+                           n_keys, w.keys);
     else
         hipLaunchKernelGGL(ring_reset_kernel<float>, dim3((int)blocks), dim3(256), 0, st, n_q,
-                           (float *)q_ring, o_ring, n_l, lse_ring, n_p, pos_ring, ctrl);
+                           (float *)q_ring, o_ring, n_l, lse_ring, n_p, pos_ring, w.ctrl, n_keys,
+                           w.keys);
     return hipGetLastError();
 }
 
