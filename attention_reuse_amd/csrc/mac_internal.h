@@ -11,7 +11,8 @@ namespace mac {
 // C tokens, C = kChunkMin * 2^k the smallest such that the range spans at
 // most kMaxItemsPerGroup grid cells.  C depends only on the group's own
 // range, so a head that misses sees exactly the items of a full decode.
-constexpr int kChunkMin = 128;
+constexpr int kChunkMinShift = 7;
+constexpr int kChunkMin = 1 << kChunkMinShift;
 constexpr int kMaxItemsPerGroup = 128;
 // Ring slots scanned by one match workgroup.
 constexpr int kSlotsPerSplit = 64;
@@ -22,30 +23,32 @@ constexpr int kBlock = 256;
 // Boundaries: s, the multiples of C in (s, e], the rectify split
 // sp = e - r + 1 when it falls strictly inside (s, e], and e + 1.
 struct RangeSplit {
-    int s, e, C, c_first, n_grid, sp, has_sp, j_sp, n;
-    __host__ __device__ static int chunk_for(int s_, int e_)
+    // C = 1 << cs; divisions by C are shifts.
+    int s, e, cs, c_first, n_grid, sp, has_sp, j_sp, n;
+    __host__ __device__ static int chunk_shift_for(int s_, int e_)
     {
         const int span = e_ - s_ + 1;
-        int c = kChunkMin;
-        while ((span + c - 1) / c > kMaxItemsPerGroup)
-            c *= 2;
-        return c;
+        int cs = 0;
+        while ((kChunkMin << cs) < span && (((span - 1) >> cs) >> kChunkMinShift) + 1 > kMaxItemsPerGroup)
+            ++cs;
+        return cs + kChunkMinShift;
     }
+    __host__ __device__ static int chunk_for(int s_, int e_) { return 1 << chunk_shift_for(s_, e_); }
     __host__ __device__ RangeSplit(int s_, int e_, int r)
     {
         s = s_;
         e = e_;
-        C = chunk_for(s_, e_);
-        c_first = s / C + 1;
-        const int c_last = e / C;
+        cs = chunk_shift_for(s_, e_);
+        c_first = (s >> cs) + 1;
+        const int c_last = e >> cs;
         n_grid = c_last - c_first + 1;
         if (n_grid < 0)
             n_grid = 0;
         sp = e - r + 1;
-        has_sp = (sp > s && sp <= e && (sp % C) != 0) ? 1 : 0;
+        has_sp = (sp > s && sp <= e && (sp & ((1 << cs) - 1)) != 0) ? 1 : 0;
         j_sp = 0;
         if (has_sp) {
-            j_sp = (sp - 1) / C - c_first + 1;
+            j_sp = ((sp - 1) >> cs) - c_first + 1;
             j_sp = j_sp < 0 ? 0 : (j_sp > n_grid ? n_grid : j_sp);
         }
         n = 1 + n_grid + has_sp;
@@ -54,12 +57,12 @@ struct RangeSplit {
     {
         if (has_sp) {
             if (j < j_sp)
-                return (c_first + j) * C;
+                return (c_first + j) << cs;
             if (j == j_sp)
                 return sp;
-            return (c_first + j - 1) * C;
+            return (c_first + j - 1) << cs;
         }
-        return (c_first + j) * C;
+        return (c_first + j) << cs;
     }
     __host__ __device__ void item(int i, int &t0, int &t1) const
     {
@@ -73,7 +76,7 @@ struct RangeSplit {
             return 0;
         if (sp > e)
             return n;
-        return (has_sp ? j_sp : sp / C - c_first) + 1;
+        return (has_sp ? j_sp : (sp >> cs) - c_first) + 1;
     }
 };
 

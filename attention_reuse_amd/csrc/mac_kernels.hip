@@ -225,7 +225,7 @@ __device__ inline bool end_ok(const StepArgs &a, int e)
 // (a few KiB, L2-resident): decision per (b, h), token range [s_g, e] and
 // item count per (b, g), and an exclusive scan of the counts, all in LDS.
 // Workgroup 0 also publishes what the merge kernel and the caller need.
-// LDS: ints [BH + 4*NG + 1 + nt + 1].
+// LDS: ints [BH + 4*NG + 1 + nt/64].
 struct PlanTables {
     const int32_t *start, *gstart, *gend, *gcount, *gbegin;
     int total;
@@ -235,6 +235,7 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
 {
     const Shape &s = a.s;
     const int tid = threadIdx.x, nt = blockDim.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int BH = s.B * s.Hq, NG = s.B * s.Hkv;
     const int r_split = (a.mode == kPlanInit) ? 0 : s.r;
     int32_t *s_start = lds;
@@ -242,19 +243,15 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
     int32_t *s_gend = s_gstart + NG;
     int32_t *s_gcount = s_gend + NG;
     int32_t *s_gbegin = s_gcount + NG;  // NG + 1
-    int32_t *s_part = s_gbegin + NG + 1;
-    int32_t *s_flag = s_part + nt;
-    if (tid == 0)
-        s_flag[0] = 0;
-    __syncthreads();
+    int32_t *s_wave = s_gbegin + NG + 1;  // one per wave
 
     // Decisions per (b, h).
+    int bad = 0;
     for (int bh = tid; bh < BH; bh += nt) {
         const int b = bh / s.Hq;
         const int e = end_of(a, b);
         const bool ok = end_ok(a, e);
-        if (!ok)
-            s_flag[0] = 1;
+        bad |= !ok;
         int start = 0, slot = -1;
         if (a.mode == kPlanMatch) {
             const unsigned long long key = a.w.keys[bh];
@@ -275,10 +272,14 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
         if (publish)
             a.w.dec_slot[bh] = slot;
     }
-    __syncthreads();
+    bad = __syncthreads_or(bad);
 
-    // Token range and item count per (b, g).
-    for (int grp = tid; grp < NG; grp += nt) {
+    // Token range and item count per (b, g): a contiguous run of groups per
+    // thread, so the scan below needs one pass over the runs.
+    const int per = (NG + nt - 1) / nt;
+    const int lo = tid * per, hi = lo + per < NG ? lo + per : NG;
+    int run = 0;
+    for (int grp = lo; grp < hi; ++grp) {
         const int b = grp / s.Hkv, g = grp - b * s.Hkv;
         const int e = end_of(a, b);
         int st = 0, cnt = 0;
@@ -293,33 +294,34 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
         s_gstart[grp] = st;
         s_gend[grp] = e;
         s_gcount[grp] = cnt;
+        run += cnt;
     }
-    __syncthreads();
-
-    // Exclusive scan of the counts: contiguous runs per thread, then a
-    // Hillis-Steele scan of the run totals.
-    const int per = (NG + nt - 1) / nt;
-    const int lo = tid * per, hi = lo + per < NG ? lo + per : NG;
-    int run = 0;
-    for (int i = lo; i < hi; ++i)
-        run += s_gcount[i];
-    s_part[tid] = run;
-    __syncthreads();
-    for (int o = 1; o < nt; o <<= 1) {
-        const int v = tid >= o ? s_part[tid - o] : 0;
-        __syncthreads();
-        s_part[tid] += v;
-        __syncthreads();
+    // Exclusive scan of the counts: inclusive scan of the run totals within
+    // each wave, then across the waves.
+    int x = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o)
+            x += y;
     }
-    int acc = s_part[tid] - run;
-    for (int i = lo; i < hi; ++i) {
-        s_gbegin[i] = acc;
-        acc += s_gcount[i];
-    }
-    if (tid == nt - 1)
-        s_gbegin[NG] = s_part[nt - 1];
+    if (lane == 63)
+        s_wave[wave] = x;
     __syncthreads();
-    int total = s_gbegin[NG];
+    int before = 0, total = 0;
+    for (int w = 0; w < (nt >> 6); ++w) {
+        const int v = s_wave[w];
+        before += w < wave ? v : 0;
+        total += v;
+    }
+    int acc = before + x - run;
+    for (int grp = lo; grp < hi; ++grp) {
+        s_gbegin[grp] = acc;
+        acc += s_gcount[grp];
+    }
+    if (tid == 0)
+        s_gbegin[NG] = total;
+    __syncthreads();
     if (total > a.max_items)
         total = (int)a.max_items;
 
@@ -347,7 +349,7 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
         }
         if (tid == 0) {
             a.w.ctrl[kCtrlItems] = total;
-            a.w.ctrl[kCtrlStatus] = s_flag[0] ? MAC_DEV_BAD_POSITION : 0;
+            a.w.ctrl[kCtrlStatus] = bad ? MAC_DEV_BAD_POSITION : 0;
         }
     }
     PlanTables t;
@@ -445,6 +447,9 @@ __global__ __launch_bounds__(kBlock) void match_kernel(StepArgs a)
 // threads, then the segments in order.  R = C (+) A with C the cached summary
 // of the matched slot (empty on a miss); out = R (+) Bt.
 constexpr int kMergeBlock = 1024;
+// Groups with at most this many items are folded directly, one thread per
+// (head, dim) output; larger groups use the segmented fold.
+constexpr int kMergeDirect = 16;
 
 template <class T, int D, int G>
 struct MergeShape {
@@ -498,7 +503,7 @@ __device__ inline void fold_items(const StepArgs &a, int64_t begin, int i0, int 
     }
 }
 
-template <class T, int D, int G>
+template <class T, int D, int G, bool kWarm>
 __global__ __launch_bounds__(kMergeBlock) void merge_kernel(StepArgs a)
 {
     using M = MergeShape<T, D, G>;
@@ -523,39 +528,72 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(StepArgs a)
     // list 0 = A (items [0, nA)), list 1 = Bt (items [nA, cnt)); each folds
     // into res[list][k] for this thread's (head, dim) outputs.
     float res_l[2][NPT], res_o[2][NPT];
-#pragma unroll 1
-    for (int list = 0; list < 2; ++list) {
-        const int l0 = list == 0 ? 0 : nA;
-        const int L = list == 0 ? nA : cnt - nA;
-        const int Pe = L < P ? L : P;
-        float l = -INFINITY, o[DPT];
-#pragma unroll
-        for (int i = 0; i < DPT; ++i)
-            o[i] = 0.f;
-        if (seg < Pe)
-            fold_items<D, G, DPT>(a, begin, l0 + seg * L / Pe, l0 + (seg + 1) * L / Pe, j, d0, l, o);
-        float *rec = lds + (j * P + seg) * SEG;
-        if ((tid % TPS) == 0)
-            rec[D] = l;
-#pragma unroll
-        for (int i = 0; i < DPT; ++i)
-            rec[d0 + i] = o[i];
-        __syncthreads();
+    if (cnt <= kMergeDirect) {
+        // Few items: each thread folds its (head, dim) over the items in
+        // order, all loads issued first.
 #pragma unroll
         for (int k = 0; k < NPT; ++k) {
             const int idx = tid + k * kMergeBlock;
-            float fl = -INFINITY, fo = 0.f;
+            float la = -INFINITY, oa = 0.f, lb = -INFINITY, ob = 0.f;
             if (idx < G * D) {
                 const int jj = idx / D, dim = idx - jj * D;
-                for (int sg = 0; sg < Pe; ++sg) {
-                    const float *r = lds + (jj * P + sg) * SEG;
-                    merge_into<1>(fl, &fo, r[D], r + dim);
+                float li[kMergeDirect], oi[kMergeDirect];
+#pragma unroll
+                for (int i = 0; i < kMergeDirect; ++i) {
+                    if (i < cnt) {
+                        const int64_t ix = begin + i;
+                        li[i] = a.w.part_l[ix * G + jj];
+                        oi[i] = a.w.part_o[(ix * G + jj) * D + dim];
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < kMergeDirect; ++i) {
+                    if (i < nA)
+                        merge_into<1>(la, &oa, li[i], &oi[i]);
+                    else if (i < cnt)
+                        merge_into<1>(lb, &ob, li[i], &oi[i]);
                 }
             }
-            res_l[list][k] = fl;
-            res_o[list][k] = fo;
+            res_l[0][k] = la;
+            res_o[0][k] = oa;
+            res_l[1][k] = lb;
+            res_o[1][k] = ob;
         }
-        __syncthreads();
+    } else {
+#pragma unroll 1
+        for (int list = 0; list < 2; ++list) {
+            const int l0 = list == 0 ? 0 : nA;
+            const int L = list == 0 ? nA : cnt - nA;
+            const int Pe = L < P ? L : P;
+            float l = -INFINITY, o[DPT];
+#pragma unroll
+            for (int i = 0; i < DPT; ++i)
+                o[i] = 0.f;
+            if (seg < Pe)
+                fold_items<D, G, DPT>(a, begin, l0 + seg * L / Pe, l0 + (seg + 1) * L / Pe, j, d0, l, o);
+            float *rec = lds + (j * P + seg) * SEG;
+            if ((tid % TPS) == 0)
+                rec[D] = l;
+#pragma unroll
+            for (int i = 0; i < DPT; ++i)
+                rec[d0 + i] = o[i];
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < NPT; ++k) {
+                const int idx = tid + k * kMergeBlock;
+                float fl = -INFINITY, fo = 0.f;
+                if (idx < G * D) {
+                    const int jj = idx / D, dim = idx - jj * D;
+                    for (int sg = 0; sg < Pe; ++sg) {
+                        const float *r = lds + (jj * P + sg) * SEG;
+                        merge_into<1>(fl, &fo, r[D], r + dim);
+                    }
+                }
+                res_l[list][k] = fl;
+                res_o[list][k] = fo;
+            }
+            __syncthreads();
+        }
     }
 
     // Results are held until every thread has read its cached summary, since
@@ -776,7 +814,9 @@ __device__ inline void compute_block_rs(const KvBlock<T, G, T::EPL, NB> &kv, int
     });
 }
 
-template <class T, int D, int G>
+// kWarm only renames the instantiation used by the ring warm-up, so kernel
+// profiles separate it from decode steps.
+template <class T, int D, int G, bool kWarm>
 __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
 {
     using L = AttendShape<T, D, G>;
@@ -894,23 +934,43 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
             for (int e = 0; e < EPL; ++e)
                 sm_acc[(row * G + j) * D + lane * EPL + e] = acc[j][e];
         __syncthreads();
+        // Row weights: c[rr][j] = 2^(m[rr][j] - M_j) replaces m in LDS;
+        // sm_l[0][j] becomes head j's total sum and sm_l[RPB-1][j] its M.
+        float cw = 0.f, Ls = 0.f, Mj = -INFINITY;
+        const int wr = threadIdx.x / G, wj = threadIdx.x - wr * G;
+        if (threadIdx.x < RPB * G) {
+#pragma unroll 8
+            for (int q = 0; q < RPB; ++q)
+                Mj = fmaxf(Mj, sm_m[q * G + wj]);
+            if (Mj != -INFINITY) {
+                cw = ex2(sm_m[wr * G + wj] - Mj);
+                if (wr == 0) {
+#pragma unroll 8
+                    for (int q = 0; q < RPB; ++q)
+                        Ls = fmaf(ex2(sm_m[q * G + wj] - Mj), sm_l[q * G + wj], Ls);
+                }
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x < RPB * G) {
+            sm_m[wr * G + wj] = cw;
+            if (wr == 0) {
+                sm_l[wj] = Ls;
+                sm_l[(RPB - 1) * G + wj] = Mj;
+            }
+        }
+        __syncthreads();
         for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
             const int j = idx / D, dim = idx - j * D;
-            float M = -INFINITY;
-#pragma unroll 8
-            for (int rr = 0; rr < RPB; ++rr)
-                M = fmaxf(M, sm_m[rr * G + j]);
+            const float ls = sm_l[j];
             float o = 0.f, Lg = -INFINITY;
-            if (M != -INFINITY) {
-                float ls = 0.f, os = 0.f;
+            if (ls > 0.f) {
+                float os = 0.f;
 #pragma unroll 8
-                for (int rr = 0; rr < RPB; ++rr) {
-                    const float c = ex2(sm_m[rr * G + j] - M);
-                    ls = fmaf(c, sm_l[rr * G + j], ls);
-                    os = fmaf(c, sm_acc[(rr * G + j) * D + dim], os);
-                }
+                for (int rr = 0; rr < RPB; ++rr)
+                    os = fmaf(sm_m[rr * G + j], sm_acc[(rr * G + j) * D + dim], os);
                 o = os / ls;
-                Lg = M + lg2(ls);
+                Lg = sm_l[(RPB - 1) * G + j] + lg2(ls);
             }
             a.w.part_o[((int64_t)it * G + j) * D + dim] = o;
             if (dim == 0)
@@ -923,7 +983,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
 // ---------------------------------------------------------------------------
 // Rectify-append: slot t mod K of every (b, h) receives the pre-RoPE query,
 // the rectified summary (natural-log lse) and pos t = pos[b] + pos_offset.
-template <class T, int D>
+template <class T, int D, bool kWarm>
 __global__ __launch_bounds__(D) void append_kernel(StepArgs a, int32_t pos_offset)
 {
     using S = typename T::S;
@@ -975,7 +1035,7 @@ __global__ void ring_reset_kernel(int64_t n_q, S *__restrict__ q_ring,
 size_t plan_lds_bytes(int B, int Hq, int Hkv)
 {
     const size_t BH = (size_t)B * Hq, NG = (size_t)B * Hkv;
-    return 4 * (BH + 4 * NG + 1 + kBlock + 1);
+    return 4 * (BH + 4 * NG + 1 + kBlock / 64);
 }
 
 int device_cu_count()
@@ -1019,17 +1079,52 @@ hipError_t launch_match(const StepArgs &a, hipStream_t st)
     return hipGetLastError();
 }
 
+// Resident workgroups per CU of a kernel (cached per kernel and LDS size).
+static int resident_per_cu(const void *fn, size_t lds)
+{
+    struct Entry {
+        const void *fn;
+        size_t lds;
+        int dev, n;
+    };
+    static Entry cache[64];
+    static int used = 0;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    for (int i = 0; i < used; ++i)
+        if (cache[i].fn == fn && cache[i].lds == lds && cache[i].dev == dev)
+            return cache[i].n;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kBlock, lds) != hipSuccess || n < 1)
+        n = 1;
+    if (used < 64)
+        cache[used++] = Entry{fn, lds, dev, n};
+    return n;
+}
+
 template <class T, int D>
 static void attend_go(const StepArgs &a, hipStream_t st)
 {
-    // Persistent grid: a few workgroups per CU, never more than items.
-    int64_t grid = (int64_t)device_cu_count() * 4;
+    const size_t lds = plan_lds_bytes(a.s.B, a.s.Hq, a.s.Hkv);
+    // Persistent grid: exactly the workgroups that are resident at once, so
+    // no workgroup waits for a slot only to find no work; never more than
+    // the item bound.
+    const void *fn = a.s.G == 1   ? (const void *)attend_kernel<T, D, 1, false>
+                     : a.s.G == 2 ? (const void *)attend_kernel<T, D, 2, false>
+                     : a.s.G == 4 ? (const void *)attend_kernel<T, D, 4, false>
+                                  : (const void *)attend_kernel<T, D, 8, false>;
+    int64_t grid = (int64_t)device_cu_count() * resident_per_cu(fn, lds);
     if (grid > a.max_items)
         grid = a.max_items > 0 ? a.max_items : 1;
-    const size_t lds = plan_lds_bytes(a.s.B, a.s.Hq, a.s.Hkv);
-#define MAC_ATT(GG)                                                                 \
-    hipLaunchKernelGGL((attend_kernel<T, D, GG>), dim3((int)grid), dim3(kBlock), lds, \
-                       st, a)
+#define MAC_ATT(GG)                                                                       \
+    do {                                                                                  \
+        if (a.mode == kPlanInit)                                                          \
+            hipLaunchKernelGGL((attend_kernel<T, D, GG, true>), dim3((int)grid), dim3(kBlock), \
+                               lds, st, a);                                               \
+        else                                                                              \
+            hipLaunchKernelGGL((attend_kernel<T, D, GG, false>), dim3((int)grid), dim3(kBlock), \
+                               lds, st, a);                                               \
+    } while (0)
     switch (a.s.G) {
     case 1:
         MAC_ATT(1);
@@ -1053,24 +1148,33 @@ hipError_t launch_attend(const StepArgs &a, hipStream_t st)
     return hipGetLastError();
 }
 
-template <class T, int D>
-static void merge_go(const StepArgs &a, hipStream_t st)
+template <class T, int D, bool W>
+static void merge_go_w(const StepArgs &a, hipStream_t st)
 {
     const dim3 grid(a.s.B * a.s.Hkv), block(kMergeBlock);
     switch (a.s.G) {
     case 1:
-        hipLaunchKernelGGL((merge_kernel<T, D, 1>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((merge_kernel<T, D, 1, W>), grid, block, 0, st, a);
         break;
     case 2:
-        hipLaunchKernelGGL((merge_kernel<T, D, 2>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((merge_kernel<T, D, 2, W>), grid, block, 0, st, a);
         break;
     case 4:
-        hipLaunchKernelGGL((merge_kernel<T, D, 4>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((merge_kernel<T, D, 4, W>), grid, block, 0, st, a);
         break;
     default:
-        hipLaunchKernelGGL((merge_kernel<T, D, 8>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((merge_kernel<T, D, 8, W>), grid, block, 0, st, a);
         break;
     }
+}
+
+template <class T, int D>
+static void merge_go(const StepArgs &a, hipStream_t st)
+{
+    if (a.mode == kPlanInit)
+        merge_go_w<T, D, true>(a, st);
+    else
+        merge_go_w<T, D, false>(a, st);
 }
 
 hipError_t launch_merge(const StepArgs &a, hipStream_t st)
@@ -1082,8 +1186,12 @@ hipError_t launch_merge(const StepArgs &a, hipStream_t st)
 template <class T, int D>
 static void append_go(const StepArgs &a, int32_t pos_offset, hipStream_t st)
 {
-    hipLaunchKernelGGL((append_kernel<T, D>), dim3(a.s.B * a.s.Hq), dim3(D), 0, st, a,
-                       pos_offset);
+    if (a.mode == kPlanInit)
+        hipLaunchKernelGGL((append_kernel<T, D, true>), dim3(a.s.B * a.s.Hq), dim3(D), 0, st, a,
+                           pos_offset);
+    else
+        hipLaunchKernelGGL((append_kernel<T, D, false>), dim3(a.s.B * a.s.Hq), dim3(D), 0, st,
+                           a, pos_offset);
 }
 
 hipError_t launch_append(const StepArgs &a, int32_t pos_offset, hipStream_t st)
