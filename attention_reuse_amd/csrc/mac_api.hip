@@ -418,9 +418,6 @@ mac_status mac_decode_step(mac_handle *h, const void *qtilde, const float *q,
         MAC_STAGE(3, as, launch_append(a, 0, as));
         if (split)
             MAC_HIP(hipEventRecord(h->ev_aux, as));
-    } else if (pe) {
-        MAC_HIP(hipEventRecord(pe[6], ms));
-        MAC_HIP(hipEventRecord(pe[7], ms));
     }
 #undef MAC_STAGE
     if (prof)
@@ -465,8 +462,10 @@ mac_status mac_profile_start(mac_handle *h, int32_t n_steps)
     for (hipEvent_t e : h->prof)
         (void)hipEventDestroy(e);
     h->prof.assign((size_t)n_steps * kStages * 2, nullptr);
+    // Timing-only events: no system-scope fence (cache write-back) at
+    // record time, which would otherwise add microseconds to every stage.
     for (auto &e : h->prof)
-        MAC_HIP(hipEventCreate(&e));
+        MAC_HIP(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
     h->prof_cap = n_steps;
     h->prof_n = 0;
     return MAC_OK;
@@ -478,12 +477,13 @@ mac_status mac_profile_read(mac_handle *h, double ms[4], int32_t *n)
         return MAC_ERR_INVALID_ARG;
     for (int k = 0; k < kStages; ++k)
         ms[k] = 0.0;
+    MAC_HIP(hipDeviceSynchronize());
+    const int stages = h->fused_append ? kStages - 1 : kStages;  // fused: no append kernel
     for (int i = 0; i < h->prof_n; ++i)
-        for (int k = 0; k < kStages; ++k) {
+        for (int k = 0; k < stages; ++k) {
             hipEvent_t a = h->prof[((size_t)i * kStages + k) * 2];
             hipEvent_t b = h->prof[((size_t)i * kStages + k) * 2 + 1];
             float t = 0.f;
-            MAC_HIP(hipEventSynchronize(b));
             MAC_HIP(hipEventElapsedTime(&t, a, b));
             ms[k] += t;
         }

@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=0,
                     help="layer copies per step (0 = enough to overflow the Infinity Cache)")
     ap.add_argument("--mode", choices=("mac", "full"), default="mac")
-    ap.add_argument("--append", choices=("aux", "fused"), default="aux",
+    ap.add_argument("--append", choices=("aux", "fused"), default="fused",
                     help="rectify-append on the auxiliary stream or fused into the merge")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
@@ -63,8 +63,9 @@ def default_layers(cfg):
 
 
 def source_hash():
+    """Hash of the device-code sources the PMC counters were taken on."""
     h = hashlib.sha256()
-    for f in ("mac_kernels.hip", "mac_api.hip", "mac_internal.h"):
+    for f in ("mac_kernels.hip", "mac_internal.h"):
         h.update(open(os.path.join(ROOT, "attention_reuse_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -79,7 +80,7 @@ def read_traffic(workload_name, kernel):
     for ln in open(path):
         f = ln.split()
         if len(f) >= 4 and not ln.startswith("#") and f[0] == workload_name and f[1] == kernel:
-            return float(f[2]) if f[3] == want else None
+            return float(f[2]) if f[-1] == want else None
     return None
 
 
@@ -323,10 +324,10 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 in / fp32 accumulate" if cfg.dtype == "bf16" else "fp32",
+        "dtype": "f32",
         "data": "synthetic (seeded N(0,1) K/V, prototype+noise query stream)",
         "config": {"workload": cfg.name, "mode": args.mode, "append": args.append,
-                   "layers": NL,
+                   "layers": NL, "kv_dtype": cfg.dtype,
                    "batch": B, "q_heads": H, "kv_heads": Hkv, "head_dim": d,
                    "context": cfg.ctx, "ring_k": R, "band_r": cfg.band_r, "tau": cfg.tau,
                    "parallelism": "1 GPU"},
