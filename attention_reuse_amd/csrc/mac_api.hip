@@ -27,13 +27,15 @@ WsLayout ws_layout(int B, int Hq, int Hkv, int D, int K, int T)
         return o;
     };
     const size_t BH = (size_t)B * Hq, BG = (size_t)B * Hkv;
-    L.keys = take(BH * sizeof(unsigned long long));
+    L.keys = take(2 * BH * kKeyStride * sizeof(unsigned long long));
     L.ctx = take((size_t)B * 4);
     L.dec_slot = take(BH * 4);
     L.grp_begin = take(BG * 4);
     L.grp_count = take(BG * 4);
     L.grp_start = take(BG * 4);
     L.ctrl = take(64);
+    L.sync = take((size_t)kSyncWords * sizeof(unsigned long long));
+    L.grp_sync = take(BG * kGrpStride * sizeof(uint32_t));
     L.part_o = take((size_t)L.max_items * G * D * 4);
     L.part_l = take((size_t)L.max_items * G * 4);
     L.rect_o = take(BH * D * 4);
@@ -53,6 +55,8 @@ WsPtrs ws_ptrs(void *base, const WsLayout &L)
     w.grp_count = (int32_t *)(c + L.grp_count);
     w.grp_start = (int32_t *)(c + L.grp_start);
     w.ctrl = (int32_t *)(c + L.ctrl);
+    w.sync = (unsigned long long *)(c + L.sync);
+    w.grp_sync = (uint32_t *)(c + L.grp_sync);
     w.part_o = (float *)(c + L.part_o);
     w.part_l = (float *)(c + L.part_l);
     w.rect_o = (float *)(c + L.rect_o);
@@ -64,7 +68,8 @@ WsPtrs ws_ptrs(void *base, const WsLayout &L)
 
 using namespace mac;
 
-constexpr int kStages = 4;  // match, attend (+plan), merge, append
+// match, attend (+plan), merge, append, single launch
+constexpr int kStages = MAC_PROFILE_STAGES;
 
 struct mac_handle {
     mac_params p;
@@ -74,6 +79,7 @@ struct mac_handle {
     void *ws;
     mac_rings rings;
     bool fused_append;
+    bool split_stages;
     hipEvent_t ev_main = nullptr, ev_aux = nullptr;
     // Per-stage timing events: prof[(step * kStages + stage) * 2 + {0,1}].
     std::vector<hipEvent_t> prof;
@@ -92,7 +98,9 @@ static mac_status check_params(const mac_params *p, Shape *s)
     if (p->batch < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1 ||
         p->n_q_heads % p->n_kv_heads != 0 || p->ring_k < 1 ||
         p->band_r < 0 || p->kv_capacity < 1 ||
-        (p->flags & ~MAC_FLAG_FUSED_APPEND) != 0 ||
+        (p->flags & ~(MAC_FLAG_FUSED_APPEND | MAC_FLAG_SPLIT_STAGES |
+                      MAC_FLAG_SINGLE_LAUNCH)) != 0 ||
+        (p->flags & MAC_FLAG_SPLIT_STAGES && p->flags & MAC_FLAG_SINGLE_LAUNCH) ||
         !isfinite(p->tau) || !isfinite(p->sm_scale) || p->sm_scale < 0.f ||
         (p->thresh_mode != MAC_THRESH_ONE_MINUS_TAU &&
          p->thresh_mode != MAC_THRESH_TAU))
@@ -302,6 +310,9 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
     h->ws = workspace;
     h->rings = *rings;
     h->fused_append = (p->flags & MAC_FLAG_FUSED_APPEND) != 0;
+    h->split_stages = (p->flags & MAC_FLAG_SPLIT_STAGES) != 0 ||
+                      ((p->flags & MAC_FLAG_SINGLE_LAUNCH) == 0 &&
+                       s.B * s.Hkv > kSingleLaunchMaxGroups);
     if (hipEventCreateWithFlags(&h->ev_main, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&h->ev_aux, hipEventDisableTiming) != hipSuccess) {
         mac_release(h);
@@ -407,9 +418,13 @@ mac_status mac_decode_step(mac_handle *h, const void *qtilde, const float *q,
     // the rings are read and the workspace is reused.
     if (split)
         MAC_HIP(hipStreamWaitEvent(ms, h->ev_aux, 0));
-    MAC_STAGE(0, ms, launch_match(a, ms));
-    MAC_STAGE(1, ms, launch_attend(a, ms));
-    MAC_STAGE(2, ms, launch_merge(a, ms));
+    if (h->split_stages) {
+        MAC_STAGE(0, ms, launch_match(a, ms));
+        MAC_STAGE(1, ms, launch_attend(a, ms));
+        MAC_STAGE(2, ms, launch_merge(a, ms));
+    } else {
+        MAC_STAGE(4, ms, launch_step(a, ms));
+    }
     if (!h->fused_append) {
         if (split) {
             MAC_HIP(hipEventRecord(h->ev_main, ms));
@@ -443,15 +458,24 @@ mac_status mac_read_device_status(const mac_params *p, void *workspace,
     if (!workspace || !flags)
         return MAC_ERR_INVALID_ARG;
     const WsLayout L = ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T);
-    int32_t *ctrl = ws_ptrs(workspace, L).ctrl;
+    const WsPtrs w = ws_ptrs(workspace, L);
     hipStream_t st = (hipStream_t)stream;
     int32_t v = 0;
+    unsigned long long sy[3] = {0, 0, 0};
     static const int32_t zero = 0;
-    MAC_HIP(hipMemcpyAsync(&v, ctrl + 1, sizeof v, hipMemcpyDeviceToHost, st));
+    static const unsigned long long zero64 = 0;
+    MAC_HIP(hipMemcpyAsync(&v, w.ctrl + kCtrlStatus, sizeof v, hipMemcpyDeviceToHost, st));
+    MAC_HIP(hipMemcpyAsync(sy, w.sync, sizeof sy, hipMemcpyDeviceToHost, st));
     MAC_HIP(hipStreamSynchronize(st));
-    MAC_HIP(hipMemcpyAsync(ctrl + 1, &zero, sizeof zero, hipMemcpyHostToDevice, st));
+    MAC_HIP(hipMemcpyAsync(w.ctrl + kCtrlStatus, &zero, sizeof zero, hipMemcpyHostToDevice, st));
+    // The latched time-outs exist only on a workspace whose rings were
+    // initialised (a full-decode-only workspace never holds the marker).
+    const bool init = sy[kSyncMagicWord] == kSyncMagic;
+    if (init)
+        MAC_HIP(hipMemcpyAsync(w.sync + kSyncSticky, &zero64, sizeof zero64,
+                               hipMemcpyHostToDevice, st));
     MAC_HIP(hipStreamSynchronize(st));
-    *flags = v;
+    *flags = v | (init ? (int32_t)sy[kSyncSticky] : 0);
     return MAC_OK;
 }
 
@@ -471,16 +495,20 @@ mac_status mac_profile_start(mac_handle *h, int32_t n_steps)
     return MAC_OK;
 }
 
-mac_status mac_profile_read(mac_handle *h, double ms[4], int32_t *n)
+mac_status mac_profile_read(mac_handle *h, double ms[MAC_PROFILE_STAGES], int32_t *n)
 {
     if (!h || !ms || !n)
         return MAC_ERR_INVALID_ARG;
     for (int k = 0; k < kStages; ++k)
         ms[k] = 0.0;
     MAC_HIP(hipDeviceSynchronize());
-    const int stages = h->fused_append ? kStages - 1 : kStages;  // fused: no append kernel
+    // Stages that ran (and recorded their events) on this handle.
+    bool ran[kStages] = {h->split_stages, h->split_stages, h->split_stages, !h->fused_append,
+                         !h->split_stages};
     for (int i = 0; i < h->prof_n; ++i)
-        for (int k = 0; k < stages; ++k) {
+        for (int k = 0; k < kStages; ++k) {
+            if (!ran[k])
+                continue;
             hipEvent_t a = h->prof[((size_t)i * kStages + k) * 2];
             hipEvent_t b = h->prof[((size_t)i * kStages + k) * 2 + 1];
             float t = 0.f;

@@ -19,6 +19,30 @@ constexpr int kSlotsPerSplit = 64;
 // Workgroup size of the match and attention kernels.
 constexpr int kBlock = 256;
 
+// Single-launch step: cross-workgroup synchronisation words in the
+// workspace, 64-bit, one 128-byte line (kLineU64 words) each:
+//   line 0: [0] launch epoch, [1] kSyncMagic once the rings were
+//           initialised on the workspace, [2] latched time-outs;
+//   lines 1..kBarLines: grid-barrier arrival counters;
+//   line 1 + kBarLines: count of completed arrival lines;
+//   the kRelLines lines after it: the barrier's release word.
+// The per-group arrival counters are 32-bit, kGrpStride words apart.
+constexpr int kBarLines = 16;
+constexpr int kRelLines = 32;
+constexpr int kLineU64 = 16;
+constexpr int kSyncWords = kLineU64 * (2 + kBarLines + kRelLines);
+constexpr int kGrpStride = 16;
+// Default form of the decode step: one launch for at most this many KV
+// groups per layer (latency-bound steps), three kernels above (measured on
+// MI355X: one launch is ahead at 8 groups, behind at 64 and 128).
+constexpr int kSingleLaunchMaxGroups = 16;
+// Match keys are kKeyStride words apart (one 128-byte line per head): the
+// atomic minima of a head's splits serialise per line, so heads must not
+// share one.
+constexpr int kKeyStride = 16;
+constexpr unsigned long long kSyncMagic = 0x4d41432d53594e43ull;
+enum { kSyncEpoch = 0, kSyncMagicWord = 1, kSyncSticky = 2 };
+
 // Plan: work-item partition of one group's token range [s, e].
 // Boundaries: s, the multiples of C in (s, e], the rectify split
 // sp = e - r + 1 when it falls strictly inside (s, e], and e + 1.
@@ -82,8 +106,8 @@ struct RangeSplit {
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WsLayout {
-    size_t keys, ctx, dec_slot, grp_begin, grp_count, grp_start, ctrl, part_o,
-        part_l, rect_o, rect_l, total;
+    size_t keys, ctx, dec_slot, grp_begin, grp_count, grp_start, ctrl, sync,
+        grp_sync, part_o, part_l, rect_o, rect_l, total;
     int64_t max_items;
     int32_t nsplit;
 };
@@ -107,9 +131,13 @@ struct Shape {
 
 // Device pointers into the workspace.
 struct WsPtrs {
-    unsigned long long *keys;  // [B*Hq] per-head match key
-    int32_t *ctx;              // [B] prompt lengths during the warm-up
+    // [2][B*Hq * kKeyStride] per-head match keys; the three-kernel step
+    // uses the first half, the single-launch step alternates by epoch.
+    unsigned long long *keys;
+    int32_t *ctx;  // [B] prompt lengths during the warm-up
     int32_t *dec_slot, *grp_begin, *grp_count, *grp_start, *ctrl;
+    unsigned long long *sync;  // epoch + kBarLines arrival lines
+    uint32_t *grp_sync;        // [B*Hkv * kGrpStride] per-group arrivals
     float *part_o, *part_l, *rect_o, *rect_l;
 };
 
@@ -153,6 +181,10 @@ hipError_t launch_attend(const StepArgs &a, hipStream_t st);
 // Per-group merge of the partials with the cached summaries; appends to
 // the rings itself when append_fused.
 hipError_t launch_merge(const StepArgs &a, hipStream_t st);
+// The whole decode step (match, plan, attention, merge and, with
+// append_fused, the ring append) as one launch of a grid that is resident
+// at once.
+hipError_t launch_step(const StepArgs &a, hipStream_t st);
 // Rectify-append from the workspace staging into the rings; the position of
 // request b is pos[b] + pos_offset.
 hipError_t launch_append(const StepArgs &a, int32_t pos_offset, hipStream_t st);

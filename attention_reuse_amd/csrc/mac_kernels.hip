@@ -2,31 +2,40 @@
 //
 // The step of the MAC-Attention blog ("MAC-Attention: Match-Amend-Complete
 // attention reuse ... (MLSys 2026)", section "Paper version: the K1/K2/K3
-// micro-pipeline") runs as three kernels on the main stream plus one on an
-// auxiliary stream:
+// micro-pipeline") has four stages:
 //
 //   match  -- L2 nearest neighbour of the pre-RoPE query among the last K
-//       ring entries ("Match (1)-(3)"), one 64-slot split per workgroup,
-//       emitting the split's smallest (distance, position) key.
-//   attend -- every workgroup first plans from the match keys (final argmin
-//       per head, threshold, token range [s_g, m] per (request, KV group);
-//       every range is cut into items on an absolute 128-token grid plus the
-//       rectify split m-r+1: the span-proportional allocator of "K2"), then
-//       runs persistent split-KV attention over the items.  A K/V row
-//       is loaded once (16 B per lane, one 16-lane DPP row per row) and
+//       ring entries ("Match (1)-(3)"), one 64-slot split per unit of work,
+//       folded into a per-head (distance, position) key by an atomic min.
+//   plan + attend -- every workgroup plans from the match keys (final
+//       decision per head, threshold, token range [s_g, m] per (request, KV
+//       group); every range is cut into items on an absolute 128-token grid
+//       plus the rectify split m-r+1: the span-proportional allocator of
+//       "K2"), then runs persistent split-KV attention over the items.  A K/V
+//       row is loaded once (16 B per lane, one 16-lane DPP row per row) and
 //       serves the G query heads of the group from registers; each item
 //       leaves one partial (o, lse) per head.
-//   merge  -- one workgroup per KV group folds the partials in a fixed order
-//       with the cached summary ("Complete"), giving the output and the
-//       rectified summary of [0, m-r]; with append_fused it also writes the
-//       ring slot m mod K.
-//   append -- the rectify-append as its own kernel ("K3") on an auxiliary
-//       stream after the merge.
+//   merge  -- per KV group, the partials are folded in a fixed order with the
+//       cached summary ("Complete"), giving the output and the rectified
+//       summary of [0, m-r]; with append_fused the ring slot m mod K is
+//       written here too.
+//   append -- otherwise the rectify-append ("K3") runs as its own kernel on
+//       an auxiliary stream.
 //
-// Workgroups of one kernel never wait for or signal each other: on MI355X
-// the L2 caches of the eight XCDs are not coherent, and the device-scope
-// fence a cross-workgroup hand-off needs writes back a whole L2, so the
-// stages hand over at kernel boundaries instead.
+// The stages run either as one launch (step_kernel) or as one kernel each.
+// The separate kernels hand over at kernel boundaries.  Inside the single
+// launch, match -> plan is a grid barrier (the grid is sized to be resident
+// at once; the wait is bounded) and attention -> merge is a hand-off to the
+// workgroup that completes a group's last item.  The eight XCDs of MI355X
+// have private L2 caches that are not coherent with each other, and a
+// device-scope release fence writes a whole L2 back, which costs tens of
+// microseconds under load.  Data that crosses workgroups inside the launch
+// therefore travels with device-coherent loads and stores (agent-scope
+// atomic accesses, issued with the sc1 bit, which bypass the L2); a
+// producer waits for its stores to complete before it signals with an
+// atomic counter, and a consumer reads only after the counter says so.
+// Both forms run the same device functions in the same order, so their
+// results are bitwise identical.
 //
 // The path is HBM-bound (about 4 flop per KV byte for G = 4), so attention
 // and match run on VALU; MFMA tiles would be 3/4 padding at G = 4.
@@ -220,6 +229,89 @@ __device__ inline bool end_ok(const StepArgs &a, int e)
     return e < a.s.T && (a.mode == kPlanInit || e >= 0);
 }
 
+// Device-coherent accesses for data handed between workgroups of one
+// launch: relaxed agent-scope atomics, which gfx950 issues with the sc1
+// bit (write-through on stores, L2 bypass on loads).
+__device__ inline void st_wt(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_wt(unsigned long long *p, unsigned long long v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_wt(uint32_t *p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float ld_wt(const float *p)
+{
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline unsigned long long ld_wt(const unsigned long long *p)
+{
+    return __hip_atomic_load(const_cast<unsigned long long *>(p), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Plain or device-coherent load of one float / four floats.
+template <bool kWT>
+__device__ inline float ld_f(const float *p)
+{
+    if constexpr (kWT)
+        return ld_wt(p);
+    else
+        return *p;
+}
+template <bool kWT>
+__device__ inline float4 ld_f4(const float *p)
+{
+    if constexpr (kWT) {
+        const unsigned long long lo = ld_wt(reinterpret_cast<const unsigned long long *>(p));
+        const unsigned long long hi = ld_wt(reinterpret_cast<const unsigned long long *>(p) + 1);
+        return make_float4(__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                           __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32)));
+    } else {
+        return *reinterpret_cast<const float4 *>(p);
+    }
+}
+
+// s_waitcnt vmcnt(0): this wave's loads and stores have completed (a
+// write-through store is then visible to every XCD).  Encoding (gfx9):
+// vmcnt bits [3:0] and [15:14] = 0, expcnt [6:4] = 7, lgkmcnt [11:8] = 15.
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Decision of one head from its match key: hit iff a candidate exists, the
+// position is valid and D < threshold ("Match (2)"); a hit attends from
+// max(0, p - r + 1) and reuses the summary in slot p mod K.
+struct Decision {
+    int start, slot, p;
+    float d2;
+    bool hit;
+};
+
+__device__ inline Decision decide(const StepArgs &a, unsigned long long key, bool ok)
+{
+    Decision d;
+    const bool any = key != ~0ull;
+    d.d2 = any ? __uint_as_float((uint32_t)(key >> 32)) : INFINITY;
+    d.p = any ? (int)(0xffffffffu - (uint32_t)key) : -1;
+    d.hit = ok && any && d.d2 < a.s.thresh2;
+    d.start = d.hit ? (d.p - a.s.r + 1 > 0 ? d.p - a.s.r + 1 : 0) : 0;
+    d.slot = d.hit ? d.p % a.s.K : -1;
+    return d;
+}
+
+// Per-head code kept by the planner: p - r + 1 for a hit (may be negative),
+// kMissCode otherwise.  The head attends from max(0, code); a hit reuses
+// slot (code + r - 1) mod K = p mod K.
+constexpr int32_t kMissCode = INT32_MIN;
+__device__ inline int code_start(int32_t c) { return c > 0 ? c : 0; }
+__device__ inline int code_slot(int32_t c, int r, int K)
+{
+    return c == kMissCode ? -1 : (c + r - 1) % K;
+}
+
 // ---------------------------------------------------------------------------
 // Planner, run redundantly by every attention workgroup from the match keys
 // (a few KiB, L2-resident): decision per (b, h), token range [s_g, e] and
@@ -227,19 +319,23 @@ __device__ inline bool end_ok(const StepArgs &a, int e)
 // Workgroup 0 also publishes what the merge kernel and the caller need.
 // LDS: ints [BH + 4*NG + 1 + nt/64].
 struct PlanTables {
-    const int32_t *start, *gstart, *gend, *gcount, *gbegin;
+    const int32_t *code, *gstart, *gend, *gcount, *gbegin;
     int total;
 };
 
-__device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
+// keys: the per-head match keys to decide from (read device-coherently
+// when kWT: they were written by atomics of the same launch).
+template <bool kWT>
+__device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish,
+                                  const unsigned long long *keys)
 {
     const Shape &s = a.s;
     const int tid = threadIdx.x, nt = blockDim.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int BH = s.B * s.Hq, NG = s.B * s.Hkv;
     const int r_split = (a.mode == kPlanInit) ? 0 : s.r;
-    int32_t *s_start = lds;
-    int32_t *s_gstart = s_start + BH;
+    int32_t *s_code = lds;
+    int32_t *s_gstart = s_code + BH;
     int32_t *s_gend = s_gstart + NG;
     int32_t *s_gcount = s_gend + NG;
     int32_t *s_gbegin = s_gcount + NG;  // NG + 1
@@ -252,23 +348,18 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
         const int e = end_of(a, b);
         const bool ok = end_ok(a, e);
         bad |= !ok;
-        int start = 0, slot = -1;
+        int32_t code = kMissCode, slot = -1;
         if (a.mode == kPlanMatch) {
-            const unsigned long long key = a.w.keys[bh];
-            const bool any = key != ~0ull;
-            const float d2 = any ? __uint_as_float((uint32_t)(key >> 32)) : INFINITY;
-            const int p = any ? (int)(0xffffffffu - (uint32_t)key) : -1;
-            const bool hit = ok && any && d2 < s.thresh2;
-            if (hit) {
-                start = p - s.r + 1 > 0 ? p - s.r + 1 : 0;
-                slot = p % s.K;
-            }
+            const unsigned long long *kp = &keys[bh * kKeyStride];
+            const Decision dc = decide(a, kWT ? ld_wt(kp) : *kp, ok);
+            code = dc.hit ? dc.p - s.r + 1 : kMissCode;
+            slot = dc.slot;
             if (publish && a.match_p)
-                a.match_p[bh] = hit ? p : -1;
+                a.match_p[bh] = dc.hit ? dc.p : -1;
             if (publish && a.match_d2)
-                a.match_d2[bh] = d2;
+                a.match_d2[bh] = dc.d2;
         }
-        s_start[bh] = start;
+        s_code[bh] = code;
         if (publish)
             a.w.dec_slot[bh] = slot;
     }
@@ -286,7 +377,7 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
         if (e >= 0 && e < s.T) {
             st = e;
             for (int j = 0; j < s.G; ++j) {
-                const int v = s_start[b * s.Hq + g * s.G + j];
+                const int v = code_start(s_code[b * s.Hq + g * s.G + j]);
                 st = v < st ? v : st;
             }
             cnt = RangeSplit(st, e, r_split).n;
@@ -353,7 +444,7 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
         }
     }
     PlanTables t;
-    t.start = s_start;
+    t.code = s_code;
     t.gstart = s_gstart;
     t.gend = s_gend;
     t.gcount = s_gcount;
@@ -363,20 +454,22 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
 }
 
 // ---------------------------------------------------------------------------
-// Match.  Grid (nsplit, B*Hq).  Each LPR-lane row of a wave computes
-// the squared distance of one ring slot; the workgroup keeps the smallest
+// Match of one unit: ring slots [split * kSlotsPerSplit, +kSlotsPerSplit) of
+// head bh.  Each LPR-lane row of a wave computes the squared distance of one
+// slot; the workgroup keeps the smallest
 //   key = float_bits(D) << 32 | (0xffffffff - p)
-// (non-negative floats order like their bits; equal D prefers larger p)
-// and folds it into the head's key with a 64-bit atomic minimum.
+// (non-negative floats order like their bits; equal D prefers larger p).
+// The result is valid in thread 0; sm holds kBlock/64 words of LDS.
 template <class T, int D>
-__global__ __launch_bounds__(kBlock) void match_kernel(StepArgs a)
+__device__ inline unsigned long long match_unit(const StepArgs &a, int split, int bh,
+                                                unsigned long long *sm)
 {
     constexpr int EPL = T::EPL, LPR = D / EPL, RPB = kBlock / LPR;
     constexpr int U = kSlotsPerSplit / RPB;
     static_assert(U >= 1 && U * RPB == kSlotsPerSplit, "split shape");
     using S = typename T::S;
     const Shape &s = a.s;
-    const int bh = blockIdx.y, b = bh / s.Hq, h = bh - b * s.Hq;
+    const int b = bh / s.Hq, h = bh - b * s.Hq;
     const int lane = threadIdx.x % LPR, row = threadIdx.x / LPR;
     const int m = a.pos[b];
     const bool m_ok = m >= 0 && m < s.T;
@@ -390,7 +483,7 @@ __global__ __launch_bounds__(kBlock) void match_kernel(StepArgs a)
     int p[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int k = blockIdx.x * kSlotsPerSplit + u * RPB + row;
+        const int k = split * kSlotsPerSplit + u * RPB + row;
         if (k < s.K) {
             raw[u] = load16(ring + (int64_t)k * D);
             p[u] = pr[k];
@@ -423,7 +516,6 @@ __global__ __launch_bounds__(kBlock) void match_kernel(StepArgs a)
 #pragma unroll
     for (int off = LPR; off < 64; off <<= 1)
         best = umin64(best, shfl_xor_u64(best, off));
-    __shared__ unsigned long long sm[kBlock / 64];
     if ((threadIdx.x & 63) == 0)
         sm[threadIdx.x >> 6] = best;
     __syncthreads();
@@ -431,225 +523,294 @@ __global__ __launch_bounds__(kBlock) void match_kernel(StepArgs a)
 #pragma unroll
         for (int i = 1; i < kBlock / 64; ++i)
             best = umin64(best, sm[i]);
-        // The head's key is the minimum over its splits; the minimum is
-        // exact and order-independent.  Read by the next kernel; reset to
-        // ~0 by the merge of the same step.
-        if (best != ~0ull)
-            atomicMin(&a.w.keys[bh], best);
     }
+    return best;
+}
+
+// Match kernel.  Grid (nsplit, B*Hq).  The head's key is the minimum over
+// its splits (exact and order-independent), folded with a 64-bit atomic
+// minimum; read by the next kernel, reset to ~0 by the merge of the step.
+template <class T, int D>
+__global__ __launch_bounds__(kBlock) void match_kernel(StepArgs a)
+{
+    __shared__ unsigned long long sm[kBlock / 64];
+    const int bh = blockIdx.y;
+    const unsigned long long best = match_unit<T, D>(a, blockIdx.x, bh, sm);
+    if (threadIdx.x == 0 && best != ~0ull)
+        atomicMin(&a.w.keys[bh * kKeyStride], best);
 }
 
 // ---------------------------------------------------------------------------
-// Merge of one KV group (one workgroup of kMergeBlock threads per group).
-// Fixed shape, so a head's result depends only on its own item list: the
-// list is cut into A = items before the rectify split and Bt = the rest;
-// each list into at most P equal segments folded left to right by separate
-// threads, then the segments in order.  R = C (+) A with C the cached summary
-// of the matched slot (empty on a miss); out = R (+) Bt.
+// Merge of one KV group.  The fold has a fixed shape, so a head's result
+// depends only on its own item list (not on the thread count that runs it):
+// the list is cut into A = items before the rectify split and Bt = the
+// rest; with more than kMergeDirect items each list is cut into at most P
+// equal segments folded left to right, then the segments in order.
+// R = C (+) A with C the cached summary of the matched slot (empty on a
+// miss); out = R (+) Bt.
 constexpr int kMergeBlock = 1024;
-// Groups with at most this many items are folded directly, one thread per
+// Groups with at most this many items are folded directly, one task per
 // (head, dim) output; larger groups use the segmented fold.
 constexpr int kMergeDirect = 16;
 
 template <class T, int D, int G>
 struct MergeShape {
     static constexpr int P = 64 / G;                   // segments per list
-    static constexpr int DPT = D / 16;                 // dims per thread
-    static constexpr int TPS = 16;                     // threads per (head, segment)
+    static constexpr int DPT = D / 16;                 // dims per task
+    static constexpr int TPS = 16;                     // tasks per (head, segment)
     static constexpr int SEG = D + 1;                  // floats per segment record
     static constexpr int kFloats = G * P * SEG;
-    static constexpr int NPT = (G * D + kMergeBlock - 1) / kMergeBlock;
-    static_assert(G * P * TPS == kMergeBlock, "merge shape");
+    static constexpr int NTASK = G * P * TPS;
+    static_assert(NTASK == 1024, "merge shape");
 };
 
 // Fold items [i0, i1) of head j into (l, o) for dims [d0, d0 + DPT), with
 // the loads of the next batch of four items in flight during each merge.
-template <int D, int G, int DPT>
+template <int D, int G, int DPT, bool kWT>
 __device__ inline void fold_items(const StepArgs &a, int64_t begin, int i0, int i1, int j,
                                   int d0, float &l, float *o)
 {
     constexpr int NBUF = 4;
-    float lb[2][NBUF], ob[2][NBUF][DPT];
-    auto fetch = [&](int buf, int base) {
+    // Two register buffers with compile-time indices (no scratch).
+    float lb0[NBUF], ob0[NBUF][DPT], lb1[NBUF], ob1[NBUF][DPT];
+    auto fetch = [&](float(&lb)[NBUF], float(&ob)[NBUF][DPT], int base) {
 #pragma unroll
         for (int u = 0; u < NBUF; ++u) {
             const int i = base + u;
-            lb[buf][u] = -INFINITY;
+            lb[u] = -INFINITY;
             if (i < i1) {
                 const int64_t ix = begin + i;
-                lb[buf][u] = a.w.part_l[ix * G + j];
+                lb[u] = ld_f<kWT>(a.w.part_l + ix * G + j);
                 const float *src = a.w.part_o + (ix * G + j) * D + d0;
 #pragma unroll
                 for (int k = 0; k < DPT; k += 4) {
-                    const float4 v = *reinterpret_cast<const float4 *>(src + k);
-                    ob[buf][u][k] = v.x;
-                    ob[buf][u][k + 1] = v.y;
-                    ob[buf][u][k + 2] = v.z;
-                    ob[buf][u][k + 3] = v.w;
+                    const float4 v = ld_f4<kWT>(src + k);
+                    ob[u][k] = v.x;
+                    ob[u][k + 1] = v.y;
+                    ob[u][k + 2] = v.z;
+                    ob[u][k + 3] = v.w;
                 }
             }
         }
     };
-    fetch(0, i0);
-    int buf = 0;
-    for (int base = i0; base < i1; base += NBUF) {
-        if (base + NBUF < i1)
-            fetch(buf ^ 1, base + NBUF);
+    auto consume = [&](const float(&lb)[NBUF], const float(&ob)[NBUF][DPT], int base) {
 #pragma unroll
         for (int u = 0; u < NBUF; ++u)
             if (base + u < i1)
-                merge_into<DPT>(l, o, lb[buf][u], ob[buf][u]);
-        buf ^= 1;
+                merge_into<DPT>(l, o, lb[u], ob[u]);
+    };
+    fetch(lb0, ob0, i0);
+    for (int base = i0; base < i1; base += 2 * NBUF) {
+        if (base + NBUF < i1)
+            fetch(lb1, ob1, base + NBUF);
+        consume(lb0, ob0, base);
+        if (base + NBUF < i1) {
+            if (base + 2 * NBUF < i1)
+                fetch(lb0, ob0, base + 2 * NBUF);
+            consume(lb1, ob1, base + NBUF);
+        }
     }
 }
 
-template <class T, int D, int G, bool kWarm>
-__global__ __launch_bounds__(kMergeBlock) void merge_kernel(StepArgs a)
+// Merge of group grp by the NT threads of the calling workgroup: cnt items
+// from item index `begin`, the group's range starting at gstart.  Outputs
+// are handled in pair tasks (two adjacent dims of one head), the same for
+// every NT.  The partials are read device-coherently when kWT.  The matched
+// slot of each head comes from the planner's per-head codes (codes !=
+// nullptr) or from the published plan.  lds holds MergeShape::kFloats
+// floats.
+template <class T, int D, int G, int NT, bool kWT>
+__device__ void merge_group(const StepArgs &a, int grp, int cnt, int64_t begin, int gstart,
+                            float *lds, const int32_t *codes)
 {
     using M = MergeShape<T, D, G>;
-    constexpr int P = M::P, DPT = M::DPT, TPS = M::TPS, SEG = M::SEG, NPT = M::NPT;
+    constexpr int P = M::P, DPT = M::DPT, TPS = M::TPS, SEG = M::SEG, NTASK = M::NTASK;
+    constexpr int NPAIR = G * D / 2;                  // pair tasks
+    constexpr int NPK = (NPAIR + NT - 1) / NT;        // pair tasks per thread
     using S = typename T::S;
-    __shared__ float lds[M::kFloats];
     const Shape &s = a.s;
-    const int grp = blockIdx.x;
-    if (threadIdx.x < G)  // ready for the next step's match
-        a.w.keys[(int64_t)grp * G + threadIdx.x] = ~0ull;
-    const int cnt = a.w.grp_count[grp];
-    if (cnt == 0)
-        return;  // the planner wrote this group's outputs
     const int tid = threadIdx.x;
-    const int j = tid / (P * TPS), seg = (tid / TPS) % P, d0 = (tid % TPS) * DPT;
     const int b = grp / s.Hkv, g = grp - b * s.Hkv;
-    const int64_t begin = a.w.grp_begin[grp];
     const int e = end_of(a, b);
     const int r_split = (a.mode == kPlanInit) ? 0 : s.r;
-    const int nA = RangeSplit(a.w.grp_start[grp], e, r_split).n_before_split();
+    const int nA = RangeSplit(gstart, e, r_split).n_before_split();
 
-    // list 0 = A (items [0, nA)), list 1 = Bt (items [nA, cnt)); each folds
-    // into res[list][k] for this thread's (head, dim) outputs.
-    float res_l[2][NPT], res_o[2][NPT];
+    // The cached summary C of each pair, requested before the partials.
+    float c_l[NPK], c_o[NPK][2];
+#pragma unroll
+    for (int k = 0; k < NPK; ++k) {
+        const int pt = tid + k * NT;
+        c_l[k] = -INFINITY;
+        c_o[k][0] = c_o[k][1] = 0.f;
+        if (pt < NPAIR) {
+            const int jj = 2 * pt / D, dim = 2 * pt - jj * D;
+            const int bh = b * s.Hq + g * G + jj;
+            const int slot = codes ? code_slot(codes[bh], s.r, s.K) : a.w.dec_slot[bh];
+            if (slot >= 0) {
+                c_l[k] = a.lse_ring[(int64_t)bh * s.K + slot] * kLog2e;
+                const float2 v = *reinterpret_cast<const float2 *>(
+                    a.o_ring + ((int64_t)bh * s.K + slot) * D + dim);
+                c_o[k][0] = v.x;
+                c_o[k][1] = v.y;
+            }
+        }
+    }
+
+    // list 0 = A (items [0, nA)), list 1 = Bt (items [nA, cnt)); each pair
+    // folds into res[list][k].
+    float res_l[2][NPK], res_o[2][NPK][2];
     if (cnt <= kMergeDirect) {
-        // Few items: each thread folds its (head, dim) over the items in
-        // order, all loads issued first.
+        // Few items: each pair is folded over the items in order, with every
+        // load issued before the first merge.
+        float li[NPK][kMergeDirect], oi[NPK][kMergeDirect][2];
 #pragma unroll
-        for (int k = 0; k < NPT; ++k) {
-            const int idx = tid + k * kMergeBlock;
-            float la = -INFINITY, oa = 0.f, lb = -INFINITY, ob = 0.f;
-            if (idx < G * D) {
-                const int jj = idx / D, dim = idx - jj * D;
-                float li[kMergeDirect], oi[kMergeDirect];
+        for (int k = 0; k < NPK; ++k) {
+            const int pt = tid + k * NT;
+            const int jj = 2 * pt / D, dim = 2 * pt - jj * D;
 #pragma unroll
-                for (int i = 0; i < kMergeDirect; ++i) {
-                    if (i < cnt) {
-                        const int64_t ix = begin + i;
-                        li[i] = a.w.part_l[ix * G + jj];
-                        oi[i] = a.w.part_o[(ix * G + jj) * D + dim];
+            for (int i = 0; i < kMergeDirect; ++i) {
+                li[k][i] = -INFINITY;
+                oi[k][i][0] = oi[k][i][1] = 0.f;
+                if (pt < NPAIR && i < cnt) {
+                    const int64_t ix = begin + i;
+                    li[k][i] = ld_f<kWT>(a.w.part_l + ix * G + jj);
+                    const float *src = a.w.part_o + (ix * G + jj) * D + dim;
+                    if constexpr (kWT) {
+                        const unsigned long long w =
+                            ld_wt(reinterpret_cast<const unsigned long long *>(src));
+                        oi[k][i][0] = __uint_as_float((uint32_t)w);
+                        oi[k][i][1] = __uint_as_float((uint32_t)(w >> 32));
+                    } else {
+                        const float2 v = *reinterpret_cast<const float2 *>(src);
+                        oi[k][i][0] = v.x;
+                        oi[k][i][1] = v.y;
                     }
                 }
+            }
+        }
 #pragma unroll
-                for (int i = 0; i < kMergeDirect; ++i) {
-                    if (i < nA)
-                        merge_into<1>(la, &oa, li[i], &oi[i]);
-                    else if (i < cnt)
-                        merge_into<1>(lb, &ob, li[i], &oi[i]);
-                }
+        for (int k = 0; k < NPK; ++k) {
+            float la = -INFINITY, oa[2] = {0.f, 0.f}, lb = -INFINITY, ob[2] = {0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < kMergeDirect; ++i) {
+                if (i < nA)
+                    merge_into<2>(la, oa, li[k][i], oi[k][i]);
+                else if (i < cnt)
+                    merge_into<2>(lb, ob, li[k][i], oi[k][i]);
             }
             res_l[0][k] = la;
-            res_o[0][k] = oa;
+            res_o[0][k][0] = oa[0];
+            res_o[0][k][1] = oa[1];
             res_l[1][k] = lb;
-            res_o[1][k] = ob;
+            res_o[1][k][0] = ob[0];
+            res_o[1][k][1] = ob[1];
         }
     } else {
-#pragma unroll 1
+#pragma unroll
         for (int list = 0; list < 2; ++list) {
             const int l0 = list == 0 ? 0 : nA;
             const int L = list == 0 ? nA : cnt - nA;
             const int Pe = L < P ? L : P;
-            float l = -INFINITY, o[DPT];
+            for (int task = tid; task < NTASK; task += NT) {
+                const int j = task / (P * TPS), seg = (task / TPS) % P, d0 = (task % TPS) * DPT;
+                float l = -INFINITY, o[DPT];
 #pragma unroll
-            for (int i = 0; i < DPT; ++i)
-                o[i] = 0.f;
-            if (seg < Pe)
-                fold_items<D, G, DPT>(a, begin, l0 + seg * L / Pe, l0 + (seg + 1) * L / Pe, j, d0, l, o);
-            float *rec = lds + (j * P + seg) * SEG;
-            if ((tid % TPS) == 0)
-                rec[D] = l;
+                for (int i = 0; i < DPT; ++i)
+                    o[i] = 0.f;
+                if (seg < Pe)
+                    fold_items<D, G, DPT, kWT>(a, begin, l0 + seg * L / Pe,
+                                               l0 + (seg + 1) * L / Pe, j, d0, l, o);
+                float *rec = lds + (j * P + seg) * SEG;
+                if ((task % TPS) == 0)
+                    rec[D] = l;
 #pragma unroll
-            for (int i = 0; i < DPT; ++i)
-                rec[d0 + i] = o[i];
+                for (int i = 0; i < DPT; ++i)
+                    rec[d0 + i] = o[i];
+            }
             __syncthreads();
 #pragma unroll
-            for (int k = 0; k < NPT; ++k) {
-                const int idx = tid + k * kMergeBlock;
-                float fl = -INFINITY, fo = 0.f;
-                if (idx < G * D) {
-                    const int jj = idx / D, dim = idx - jj * D;
+            for (int k = 0; k < NPK; ++k) {
+                const int pt = tid + k * NT;
+                float fl = -INFINITY, fo[2] = {0.f, 0.f};
+                if (pt < NPAIR) {
+                    const int jj = 2 * pt / D, dim = 2 * pt - jj * D;
                     for (int sg = 0; sg < Pe; ++sg) {
                         const float *r = lds + (jj * P + sg) * SEG;
-                        merge_into<1>(fl, &fo, r[D], r + dim);
+                        merge_into<2>(fl, fo, r[D], r + dim);
                     }
                 }
                 res_l[list][k] = fl;
-                res_o[list][k] = fo;
+                res_o[list][k][0] = fo[0];
+                res_o[list][k][1] = fo[1];
             }
             __syncthreads();
         }
     }
 
-    // Results are held until every thread has read its cached summary, since
-    // the fused append may overwrite that slot.
-    float out_l[NPT], out_o[NPT], rec_l[NPT], rec_o[NPT];
+    // R = C (+) A, out = R (+) Bt.  Results are held until every thread has
+    // read its cached summary, since the fused append may overwrite it.
+    float out_l[NPK], out_o[NPK][2], rec_l[NPK], rec_o[NPK][2];
 #pragma unroll
-    for (int k = 0; k < NPT; ++k) {
-        const int idx = tid + k * kMergeBlock;
-        out_l[k] = rec_l[k] = -INFINITY;
-        out_o[k] = rec_o[k] = 0.f;
-        if (idx >= G * D)
-            continue;
-        const int jj = idx / D, dim = idx - jj * D;
-        const int bh = b * s.Hq + g * G + jj;
-        float lr = -INFINITY, orr = 0.f;
-        const int slot = a.w.dec_slot[bh];
-        if (slot >= 0) {
-            lr = a.lse_ring[(int64_t)bh * s.K + slot] * kLog2e;
-            orr = a.o_ring[((int64_t)bh * s.K + slot) * D + dim];
-        }
-        merge_into<1>(lr, &orr, res_l[0][k], &res_o[0][k]);
-        float lo = lr, oo = orr;
-        merge_into<1>(lo, &oo, res_l[1][k], &res_o[1][k]);
+    for (int k = 0; k < NPK; ++k) {
+        float lr = c_l[k], orr[2] = {c_o[k][0], c_o[k][1]};
+        merge_into<2>(lr, orr, res_l[0][k], res_o[0][k]);
+        float lo = lr, oo[2] = {orr[0], orr[1]};
+        merge_into<2>(lo, oo, res_l[1][k], res_o[1][k]);
         out_l[k] = lo;
-        out_o[k] = oo;
+        out_o[k][0] = oo[0];
+        out_o[k][1] = oo[1];
         rec_l[k] = lr;
-        rec_o[k] = orr;
+        rec_o[k][0] = orr[0];
+        rec_o[k][1] = orr[1];
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < NPT; ++k) {
-        const int idx = tid + k * kMergeBlock;
-        if (idx >= G * D)
+    for (int k = 0; k < NPK; ++k) {
+        const int pt = tid + k * NT;
+        if (pt >= NPAIR)
             continue;
-        const int jj = idx / D, dim = idx - jj * D;
+        const int jj = 2 * pt / D, dim = 2 * pt - jj * D;
         const int h = g * G + jj, bh = b * s.Hq + h;
         if (a.out)
-            a.out[(int64_t)bh * D + dim] = out_o[k];
+            *reinterpret_cast<float2 *>(a.out + (int64_t)bh * D + dim) =
+                make_float2(out_o[k][0], out_o[k][1]);
         if (a.out_lse && dim == 0)
             a.out_lse[bh] = out_l[k] * kLn2;
         if (a.append_fused) {
             // Rectify-append into slot m mod K of this head's rings.
             const int slot = e % s.K;
             const int64_t ri = ((int64_t)bh * s.K + slot) * D + dim;
-            ((S *)a.q_ring)[ri] = ((const S *)a.qtilde)[b * a.qt_sb + h * a.qt_sh + dim];
-            a.o_ring[ri] = rec_o[k];
+            const S *qs = (const S *)a.qtilde + b * a.qt_sb + h * a.qt_sh + dim;
+            ((S *)a.q_ring)[ri] = qs[0];
+            ((S *)a.q_ring)[ri + 1] = qs[1];
+            *reinterpret_cast<float2 *>(a.o_ring + ri) = make_float2(rec_o[k][0], rec_o[k][1]);
             if (dim == 0)
                 a.lse_ring[(int64_t)bh * s.K + slot] = rec_l[k] * kLn2;
             if (h == 0 && dim == 0)
                 a.pos_ring[(int64_t)b * s.K + slot] = e;
         } else {
-            a.w.rect_o[(int64_t)bh * D + dim] = rec_o[k];
+            *reinterpret_cast<float2 *>(a.w.rect_o + (int64_t)bh * D + dim) =
+                make_float2(rec_o[k][0], rec_o[k][1]);
             if (dim == 0)
                 a.w.rect_l[bh] = rec_l[k];
         }
     }
+}
+
+// Merge kernel: one workgroup of kMergeBlock threads per KV group, from the
+// plan that the attention kernel published.
+template <class T, int D, int G, bool kWarm>
+__global__ __launch_bounds__(kMergeBlock) void merge_kernel(StepArgs a)
+{
+    __shared__ float lds[MergeShape<T, D, G>::kFloats];
+    const int grp = blockIdx.x;
+    if (threadIdx.x < G)  // ready for the next step's match
+        a.w.keys[((int64_t)grp * G + threadIdx.x) * kKeyStride] = ~0ull;
+    const int cnt = a.w.grp_count[grp];
+    if (cnt == 0)
+        return;  // the planner wrote this group's outputs
+    merge_group<T, D, G, kMergeBlock, false>(a, grp, cnt, a.w.grp_begin[grp],
+                                             a.w.grp_start[grp], lds, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -814,167 +975,285 @@ __device__ inline void compute_block_rs(const KvBlock<T, G, T::EPL, NB> &kv, int
     });
 }
 
-// kWarm only renames the instantiation used by the ring warm-up, so kernel
-// profiles separate it from decode steps.
-template <class T, int D, int G, bool kWarm>
-__global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
+// Group of work item `it`: the last group whose first item is <= it,
+// moved to a scalar register (workgroup-uniform).
+__device__ inline int group_of(const PlanTables &pt, int it, int NG)
+{
+    int lo = 0, hi = NG;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (pt.gbegin[mid] <= it)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    return __builtin_amdgcn_readfirstlane(lo - 1);
+}
+
+// Attention of work item `it` (of group grp) by the whole workgroup, ending
+// with its partial (o, log2-lse) per head in the workspace (written
+// device-coherently when kWT).  lds holds AttendShape::kFloats floats.
+template <class T, int D, int G, bool kWT>
+__device__ inline void run_item(const StepArgs &a, const PlanTables &pt, int it, int grp,
+                                float *lds)
 {
     using L = AttendShape<T, D, G>;
     constexpr int EPL = L::EPL, LPR = L::LPR, RPB = L::RPB, NB = L::NB;
     constexpr int TPB = RPB * NB;  // tokens per block
     using S = typename T::S;
-    __shared__ float lds[L::kFloats];
     float *sm_m = lds;                  // [RPB][G]
     float *sm_l = lds + RPB * G;        // [RPB][G]
     float *sm_acc = lds + 2 * RPB * G;  // [RPB][G][D]
     const Shape &s = a.s;
-
     const int lane = threadIdx.x % LPR, row = threadIdx.x / LPR;
-    extern __shared__ int32_t plan_lds[];
-    const PlanTables pt = plan_tables(a, plan_lds, blockIdx.x == 0);
-    const int NG = s.B * s.Hkv;
     const int r_split = (a.mode == kPlanInit) ? 0 : s.r;
-    for (int it = blockIdx.x; it < pt.total; it += gridDim.x) {
-        // Group of item `it`: the last group whose first item is <= it.
-        int lo = 0, hi = NG;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (pt.gbegin[mid] <= it)
-                lo = mid + 1;
-            else
-                hi = mid;
-        }
-        // Workgroup-uniform values are moved to scalar registers.
-        const int grp = __builtin_amdgcn_readfirstlane(lo - 1);
-        const int b = grp / s.Hkv, g = grp - b * s.Hkv;
-        int t0, t1;
-        RangeSplit(pt.gstart[grp], pt.gend[grp], r_split).item(it - pt.gbegin[grp], t0, t1);
-        t0 = __builtin_amdgcn_readfirstlane(t0);
-        t1 = __builtin_amdgcn_readfirstlane(t1);
-        const S *kb = (const S *)a.k + b * s.kv_sb + g * s.kv_sh + lane * EPL;
-        const S *vb = (const S *)a.v + b * s.kv_sb + g * s.kv_sh + lane * EPL;
+    const int b = grp / s.Hkv, g = grp - b * s.Hkv;
+    int t0, t1;
+    RangeSplit(pt.gstart[grp], pt.gend[grp], r_split).item(it - pt.gbegin[grp], t0, t1);
+    t0 = __builtin_amdgcn_readfirstlane(t0);
+    t1 = __builtin_amdgcn_readfirstlane(t1);
+    const S *kb = (const S *)a.k + b * s.kv_sb + g * s.kv_sh + lane * EPL;
+    const S *vb = (const S *)a.v + b * s.kv_sb + g * s.kv_sh + lane * EPL;
 
-        KvBlock<T, G, EPL, NB> bufA, bufB;
-        load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, t0, t1, row);
+    KvBlock<T, G, EPL, NB> bufA, bufB;
+    load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, t0, t1, row);
 
-        float qr[G][EPL];
-        int st[G];
+    float qr[G][EPL];
+    int st[G];
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const float *qp = a.q + b * a.q_sb + (int64_t)(g * G + j) * a.q_sh + lane * EPL;
+    for (int j = 0; j < G; ++j) {
+        const float *qp = a.q + b * a.q_sb + (int64_t)(g * G + j) * a.q_sh + lane * EPL;
 #pragma unroll
-            for (int e4 = 0; e4 < EPL; e4 += 4) {
-                const float4 v = *reinterpret_cast<const float4 *>(qp + e4);
-                qr[j][e4 + 0] = v.x * s.qscale;
-                qr[j][e4 + 1] = v.y * s.qscale;
-                qr[j][e4 + 2] = v.z * s.qscale;
-                qr[j][e4 + 3] = v.w * s.qscale;
-            }
-            st[j] = __builtin_amdgcn_readfirstlane(pt.start[b * s.Hq + g * G + j]);
+        for (int e4 = 0; e4 < EPL; e4 += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(qp + e4);
+            qr[j][e4 + 0] = v.x * s.qscale;
+            qr[j][e4 + 1] = v.y * s.qscale;
+            qr[j][e4 + 2] = v.z * s.qscale;
+            qr[j][e4 + 3] = v.w * s.qscale;
         }
+        st[j] = __builtin_amdgcn_readfirstlane(code_start(pt.code[b * s.Hq + g * G + j]));
+    }
 
-        float mrun[G], lrun[G], acc[G][EPL];
+    float mrun[G], lrun[G], acc[G][EPL];
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            mrun[j] = -INFINITY;
-            lrun[j] = 0.f;
+    for (int j = 0; j < G; ++j) {
+        mrun[j] = -INFINITY;
+        lrun[j] = 0.f;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e)
-                acc[j][e] = 0.f;
-        }
-        if constexpr (L::kScatter) {
-            // Lane k keeps the running max / sum of head k % G in mrun[0],
-            // lrun[0]; its token-start bound is that head's.
-            int my_st = st[0];
+        for (int e = 0; e < EPL; ++e)
+            acc[j][e] = 0.f;
+    }
+    if constexpr (L::kScatter) {
+        // Lane k keeps the running max / sum of head k % G in mrun[0],
+        // lrun[0]; its token-start bound is that head's.
+        int my_st = st[0];
 #pragma unroll
-            for (int j = 1; j < G; ++j)
-                my_st = (lane % G == j) ? st[j] : my_st;
-            for (int base = t0; base < t1; base += 2 * TPB) {
-                if (base + TPB < t1)
-                    load_block<T, D, G, LPR, RPB, NB>(bufB, kb, vb, s.kv_st, base + TPB, t1, row);
-                compute_block_rs<T, G, RPB, NB>(bufA, row, lane, qr, my_st, t1, mrun[0], lrun[0],
-                                                acc);
-                if (base + TPB < t1) {
-                    if (base + 2 * TPB < t1)
-                        load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, base + 2 * TPB,
-                                                          t1, row);
-                    compute_block_rs<T, G, RPB, NB>(bufB, row, lane, qr, my_st, t1, mrun[0],
-                                                    lrun[0], acc);
-                }
-            }
-            if (lane < G) {
-                sm_m[row * G + lane] = mrun[0];
-                sm_l[row * G + lane] = lrun[0];
-            }
-        } else {
-            // Blocks alternate between the two buffers; the next block is
-            // always requested before the current one is consumed.
-            for (int base = t0; base < t1; base += 2 * TPB) {
-                if (base + TPB < t1)
-                    load_block<T, D, G, LPR, RPB, NB>(bufB, kb, vb, s.kv_st, base + TPB, t1, row);
-                compute_block<T, D, G, LPR, RPB, NB>(bufA, row, qr, st, t1, mrun, lrun, acc);
-                if (base + TPB < t1) {
-                    if (base + 2 * TPB < t1)
-                        load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, base + 2 * TPB,
-                                                          t1, row);
-                    compute_block<T, D, G, LPR, RPB, NB>(bufB, row, qr, st, t1, mrun, lrun, acc);
-                }
-            }
-            if (lane == 0) {
-#pragma unroll
-                for (int j = 0; j < G; ++j) {
-                    sm_m[row * G + j] = mrun[j];
-                    sm_l[row * G + j] = lrun[j];
-                }
+        for (int j = 1; j < G; ++j)
+            my_st = (lane % G == j) ? st[j] : my_st;
+        for (int base = t0; base < t1; base += 2 * TPB) {
+            if (base + TPB < t1)
+                load_block<T, D, G, LPR, RPB, NB>(bufB, kb, vb, s.kv_st, base + TPB, t1, row);
+            compute_block_rs<T, G, RPB, NB>(bufA, row, lane, qr, my_st, t1, mrun[0], lrun[0],
+                                            acc);
+            if (base + TPB < t1) {
+                if (base + 2 * TPB < t1)
+                    load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, base + 2 * TPB,
+                                                      t1, row);
+                compute_block_rs<T, G, RPB, NB>(bufB, row, lane, qr, my_st, t1, mrun[0],
+                                                lrun[0], acc);
             }
         }
+        if (lane < G) {
+            sm_m[row * G + lane] = mrun[0];
+            sm_l[row * G + lane] = lrun[0];
+        }
+    } else {
+        // Blocks alternate between the two buffers; the next block is
+        // always requested before the current one is consumed.
+        for (int base = t0; base < t1; base += 2 * TPB) {
+            if (base + TPB < t1)
+                load_block<T, D, G, LPR, RPB, NB>(bufB, kb, vb, s.kv_st, base + TPB, t1, row);
+            compute_block<T, D, G, LPR, RPB, NB>(bufA, row, qr, st, t1, mrun, lrun, acc);
+            if (base + TPB < t1) {
+                if (base + 2 * TPB < t1)
+                    load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, base + 2 * TPB,
+                                                      t1, row);
+                compute_block<T, D, G, LPR, RPB, NB>(bufB, row, qr, st, t1, mrun, lrun, acc);
+            }
+        }
+        if (lane == 0) {
 #pragma unroll
-        for (int j = 0; j < G; ++j)
+            for (int j = 0; j < G; ++j) {
+                sm_m[row * G + j] = mrun[j];
+                sm_l[row * G + j] = lrun[j];
+            }
+        }
+    }
 #pragma unroll
-            for (int e = 0; e < EPL; ++e)
-                sm_acc[(row * G + j) * D + lane * EPL + e] = acc[j][e];
-        __syncthreads();
-        // Row weights: c[rr][j] = 2^(m[rr][j] - M_j) replaces m in LDS;
-        // sm_l[0][j] becomes head j's total sum and sm_l[RPB-1][j] its M.
-        float cw = 0.f, Ls = 0.f, Mj = -INFINITY;
-        const int wr = threadIdx.x / G, wj = threadIdx.x - wr * G;
-        if (threadIdx.x < RPB * G) {
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            sm_acc[(row * G + j) * D + lane * EPL + e] = acc[j][e];
+    __syncthreads();
+    // Row weights: c[rr][j] = 2^(m[rr][j] - M_j) replaces m in LDS;
+    // sm_l[0][j] becomes head j's total sum and sm_l[RPB-1][j] its M.
+    float cw = 0.f, Ls = 0.f, Mj = -INFINITY;
+    const int wr = threadIdx.x / G, wj = threadIdx.x - wr * G;
+    if (threadIdx.x < RPB * G) {
 #pragma unroll 8
-            for (int q = 0; q < RPB; ++q)
-                Mj = fmaxf(Mj, sm_m[q * G + wj]);
-            if (Mj != -INFINITY) {
-                cw = ex2(sm_m[wr * G + wj] - Mj);
-                if (wr == 0) {
-#pragma unroll 8
-                    for (int q = 0; q < RPB; ++q)
-                        Ls = fmaf(ex2(sm_m[q * G + wj] - Mj), sm_l[q * G + wj], Ls);
-                }
-            }
-        }
-        __syncthreads();
-        if (threadIdx.x < RPB * G) {
-            sm_m[wr * G + wj] = cw;
+        for (int q = 0; q < RPB; ++q)
+            Mj = fmaxf(Mj, sm_m[q * G + wj]);
+        if (Mj != -INFINITY) {
+            cw = ex2(sm_m[wr * G + wj] - Mj);
             if (wr == 0) {
-                sm_l[wj] = Ls;
-                sm_l[(RPB - 1) * G + wj] = Mj;
+#pragma unroll 8
+                for (int q = 0; q < RPB; ++q)
+                    Ls = fmaf(ex2(sm_m[q * G + wj] - Mj), sm_l[q * G + wj], Ls);
             }
         }
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
-            const int j = idx / D, dim = idx - j * D;
-            const float ls = sm_l[j];
-            float o = 0.f, Lg = -INFINITY;
-            if (ls > 0.f) {
-                float os = 0.f;
+    }
+    __syncthreads();
+    if (threadIdx.x < RPB * G) {
+        sm_m[wr * G + wj] = cw;
+        if (wr == 0) {
+            sm_l[wj] = Ls;
+            sm_l[(RPB - 1) * G + wj] = Mj;
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
+        const int j = idx / D, dim = idx - j * D;
+        const float ls = sm_l[j];
+        float o = 0.f, Lg = -INFINITY;
+        if (ls > 0.f) {
+            float os = 0.f;
 #pragma unroll 8
-                for (int rr = 0; rr < RPB; ++rr)
-                    os = fmaf(sm_m[rr * G + j], sm_acc[(rr * G + j) * D + dim], os);
-                o = os / ls;
-                Lg = sm_l[(RPB - 1) * G + j] + lg2(ls);
-            }
+            for (int rr = 0; rr < RPB; ++rr)
+                os = fmaf(sm_m[rr * G + j], sm_acc[(rr * G + j) * D + dim], os);
+            o = os / ls;
+            Lg = sm_l[(RPB - 1) * G + j] + lg2(ls);
+        }
+        if constexpr (kWT) {
+            st_wt(a.w.part_o + ((int64_t)it * G + j) * D + dim, o);
+            if (dim == 0)
+                st_wt(a.w.part_l + (int64_t)it * G + j, Lg);
+        } else {
             a.w.part_o[((int64_t)it * G + j) * D + dim] = o;
             if (dim == 0)
                 a.w.part_l[(int64_t)it * G + j] = Lg;
+        }
+    }
+}
+
+// Plan + attention kernel.  kWarm only renames the instantiation used by
+// the ring warm-up, so kernel profiles separate it from decode steps.
+template <class T, int D, int G, bool kWarm>
+__global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
+{
+    __shared__ float lds[AttendShape<T, D, G>::kFloats];
+    extern __shared__ int32_t plan_lds[];
+    const PlanTables pt = plan_tables<false>(a, plan_lds, blockIdx.x == 0, a.w.keys);
+    const int NG = a.s.B * a.s.Hkv;
+    for (int it = blockIdx.x; it < pt.total; it += gridDim.x) {
+        run_item<T, D, G, false>(a, pt, it, group_of(pt, it, NG), lds);
+        __syncthreads();
+    }
+}
+
+// Bounded spin of the grid barrier (polls of about a microsecond each).
+constexpr int kSpinLimit = 1 << 18;
+
+// Grid barrier of one single-launch step, in two levels so that no line is
+// both counted on and polled by many workgroups (same-line accesses
+// serialise at the memory side).  Workgroup i arrives on line
+// i mod kBarLines with a returning atomic; the counters only grow, so the
+// arrival that brings line c to (epoch + 1) times its workgroup count is the
+// line's last, and counts the line as complete.  The arrival that completes
+// the last line writes epoch + 1 to every release line; each workgroup
+// polls release line i mod kRelLines.  Returns false (in every thread) if
+// the wait timed out.
+__device__ inline bool grid_barrier(unsigned long long *sync, unsigned long long epoch)
+{
+    int ok = 1;
+    if (threadIdx.x == 0) {
+        wait_vmem();  // this workgroup's match atomics have completed
+        const unsigned c = blockIdx.x % kBarLines;
+        const unsigned per = gridDim.x / kBarLines + (c < gridDim.x % kBarLines ? 1u : 0u);
+        const unsigned lines = gridDim.x < (unsigned)kBarLines ? gridDim.x : kBarLines;
+        const unsigned long long old = atomicAdd(&sync[kLineU64 * (1 + c)], 1ull);
+        if (old + 1 == (epoch + 1) * per) {
+            const unsigned long long done = atomicAdd(&sync[kLineU64 * (1 + kBarLines)], 1ull);
+            if (done + 1 == (epoch + 1) * lines)
+                for (int i = 0; i < kRelLines; ++i)
+                    st_wt(&sync[kLineU64 * (2 + kBarLines + i)], epoch + 1);
+        }
+        const unsigned long long *rel = &sync[kLineU64 * (2 + kBarLines + blockIdx.x % kRelLines)];
+        int it = 0;
+        while (ld_wt(rel) < epoch + 1 && ++it < kSpinLimit)
+            __builtin_amdgcn_s_sleep(1);
+        ok = it < kSpinLimit;
+    }
+    return __syncthreads_and(ok);
+}
+
+// The whole decode step in one launch; the grid must be resident at once.
+//   1. match units (split, head) strided over the grid, atomic-min into the
+//      key buffer of this launch's epoch; the other buffer is reset for the
+//      next launch;
+//   2. grid barrier; workgroup 0 advances the epoch;
+//   3. every workgroup plans from the keys; items strided over the grid;
+//   4. after its item's partials have completed, a workgroup counts the
+//      item on its group; the one that completes the group merges it (with
+//      the fused append) and resets the group's counter.
+template <class T, int D, int G>
+__global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
+{
+    using AS = AttendShape<T, D, G>;
+    using MS = MergeShape<T, D, G>;
+    constexpr int kFloats = AS::kFloats > MS::kFloats ? AS::kFloats : MS::kFloats;
+    __shared__ float lds[kFloats];
+    __shared__ int s_last;
+    extern __shared__ int32_t plan_lds[];
+    const Shape &s = a.s;
+    const int BH = s.B * s.Hq, NG = s.B * s.Hkv;
+    unsigned long long *sync = a.w.sync;
+    const unsigned long long epoch = ld_wt(&sync[kSyncEpoch]);
+    unsigned long long *keys = a.w.keys + (epoch & 1) * BH * kKeyStride;
+    unsigned long long *keys_next = a.w.keys + ((epoch + 1) & 1) * BH * kKeyStride;
+
+    const int units = a.nsplit * BH;
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+        const int bh = u / a.nsplit, split = u - bh * a.nsplit;
+        const unsigned long long best =
+            match_unit<T, D>(a, split, bh, reinterpret_cast<unsigned long long *>(lds));
+        if (threadIdx.x == 0) {
+            if (best != ~0ull)
+                atomicMin(&keys[bh * kKeyStride], best);
+            if (split == 0)
+                keys_next[bh * kKeyStride] = ~0ull;
+        }
+        __syncthreads();
+    }
+    if (!grid_barrier(sync, epoch) && threadIdx.x == 0)
+        atomicOr(&sync[kSyncSticky], (unsigned long long)MAC_DEV_SYNC_TIMEOUT);
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        st_wt(&sync[kSyncEpoch], epoch + 1);  // every workgroup read the epoch before arriving
+
+    const PlanTables pt = plan_tables<true>(a, plan_lds, blockIdx.x == 0, keys);
+    for (int it = blockIdx.x; it < pt.total; it += gridDim.x) {
+        const int grp = group_of(pt, it, NG);
+        run_item<T, D, G, true>(a, pt, it, grp, lds);
+        wait_vmem();  // this wave's partial stores have completed
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_last = atomicAdd(&a.w.grp_sync[(int64_t)grp * kGrpStride], 1u) ==
+                     (uint32_t)(pt.gcount[grp] - 1);
+        __syncthreads();
+        if (s_last) {
+            merge_group<T, D, G, kBlock, true>(a, grp, pt.gcount[grp], pt.gbegin[grp],
+                                               pt.gstart[grp], lds, pt.code);
+            if (threadIdx.x == 0)
+                st_wt(&a.w.grp_sync[(int64_t)grp * kGrpStride], 0u);
         }
         __syncthreads();
     }
@@ -1009,7 +1288,9 @@ __global__ void ring_reset_kernel(int64_t n_q, S *__restrict__ q_ring,
                                   float *__restrict__ lse_ring, int64_t n_p,
                                   int32_t *__restrict__ pos_ring,
                                   int32_t *__restrict__ ctrl, int64_t n_keys,
-                                  unsigned long long *__restrict__ keys)
+                                  unsigned long long *__restrict__ keys, int64_t n_sync,
+                                  unsigned long long *__restrict__ sync, int64_t n_gs,
+                                  uint32_t *__restrict__ grp_sync)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1022,7 +1303,11 @@ __global__ void ring_reset_kernel(int64_t n_q, S *__restrict__ q_ring,
     for (int64_t i = i0; i < n_p; i += stride)
         pos_ring[i] = -1;
     for (int64_t i = i0; i < n_keys; i += stride)
-        keys[i] = ~0ull;
+        keys[i * kKeyStride] = ~0ull;
+    for (int64_t i = i0; i < n_sync; i += stride)
+        sync[i] = i == kSyncMagicWord ? kSyncMagic : 0ull;
+    for (int64_t i = i0; i < n_gs; i += stride)
+        grp_sync[i] = 0;
     if (i0 < 16)
         ctrl[i0] = 0;
 }
@@ -1148,6 +1433,47 @@ hipError_t launch_attend(const StepArgs &a, hipStream_t st)
     return hipGetLastError();
 }
 
+// Grid of the single-launch step: the workgroups resident at once (the
+// grid barrier needs all of them running), never more than the larger of
+// the match units and the item bound.
+template <class T, int D, int G>
+static void step_go_g(const StepArgs &a, hipStream_t st)
+{
+    const size_t lds = plan_lds_bytes(a.s.B, a.s.Hq, a.s.Hkv);
+    const void *fn = (const void *)step_kernel<T, D, G>;
+    int64_t grid = (int64_t)device_cu_count() * resident_per_cu(fn, lds);
+    const int64_t units = (int64_t)a.nsplit * a.s.B * a.s.Hq;
+    const int64_t need = units > a.max_items ? units : a.max_items;
+    if (grid > need)
+        grid = need;
+    hipLaunchKernelGGL((step_kernel<T, D, G>), dim3((int)grid), dim3(kBlock), lds, st, a);
+}
+
+template <class T, int D>
+static void step_go(const StepArgs &a, hipStream_t st)
+{
+    switch (a.s.G) {
+    case 1:
+        step_go_g<T, D, 1>(a, st);
+        break;
+    case 2:
+        step_go_g<T, D, 2>(a, st);
+        break;
+    case 4:
+        step_go_g<T, D, 4>(a, st);
+        break;
+    default:
+        step_go_g<T, D, 8>(a, st);
+        break;
+    }
+}
+
+hipError_t launch_step(const StepArgs &a, hipStream_t st)
+{
+    MAC_DISPATCH_TD(step_go, a, st);
+    return hipGetLastError();
+}
+
 template <class T, int D, bool W>
 static void merge_go_w(const StepArgs &a, hipStream_t st)
 {
@@ -1204,7 +1530,9 @@ hipError_t launch_ring_reset(const Shape &s, void *q_ring, float *o_ring,
                              float *lse_ring, int32_t *pos_ring, const WsPtrs &w,
                              hipStream_t st)
 {
-    const int64_t n_keys = (int64_t)s.B * s.Hq;
+    const int64_t n_keys = 2 * (int64_t)s.B * s.Hq;  // both key buffers
+    const int64_t n_sync = kSyncWords;
+    const int64_t n_gs = (int64_t)s.B * s.Hkv * kGrpStride;
     const int64_t n_q = (int64_t)s.B * s.Hq * s.K * s.D;
     const int64_t n_l = (int64_t)s.B * s.Hq * s.K;
     const int64_t n_p = (int64_t)s.B * s.K;
@@ -1214,11 +1542,11 @@ hipError_t launch_ring_reset(const Shape &s, void *q_ring, float *o_ring,
     if (s.dtype == MAC_DTYPE_BF16)
         hipLaunchKernelGGL(ring_reset_kernel<uint16_t>, dim3((int)blocks), dim3(256), 0, st,
                            n_q, (uint16_t *)q_ring, o_ring, n_l, lse_ring, n_p, pos_ring, w.ctrl,
-                           n_keys, w.keys);
+                           n_keys, w.keys, n_sync, w.sync, n_gs, w.grp_sync);
     else
         hipLaunchKernelGGL(ring_reset_kernel<float>, dim3((int)blocks), dim3(256), 0, st, n_q,
                            (float *)q_ring, o_ring, n_l, lse_ring, n_p, pos_ring, w.ctrl, n_keys,
-                           w.keys);
+                           w.keys, n_sync, w.sync, n_gs, w.grp_sync);
     return hipGetLastError();
 }
 

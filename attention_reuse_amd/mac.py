@@ -21,11 +21,14 @@ MAC_DTYPE_BF16 = 1
 MAC_THRESH_ONE_MINUS_TAU = 0
 MAC_THRESH_TAU = 1
 MAC_DEV_BAD_POSITION = 1
+MAC_DEV_SYNC_TIMEOUT = 2
 MAC_FLAG_FUSED_APPEND = 1
+MAC_FLAG_SPLIT_STAGES = 2
+MAC_FLAG_SINGLE_LAUNCH = 4
 STATUS = {0: "MAC_OK", -1: "MAC_ERR_INVALID_ARG", -2: "MAC_ERR_UNSUPPORTED",
           -3: "MAC_ERR_HIP", -4: "MAC_ERR_WORKSPACE_TOO_SMALL",
           -5: "MAC_ERR_MISALIGNED"}
-STAGES = ("match", "attend", "merge", "append")
+STAGES = ("match", "attend", "merge", "append", "step")
 
 
 class MacError(RuntimeError):
@@ -185,7 +188,7 @@ def mac_profile_start(handle, n_steps):
 
 def mac_profile_read(handle):
     """Summed milliseconds per stage (dict) and the number of steps."""
-    ms = (ctypes.c_double * 4)()
+    ms = (ctypes.c_double * len(STAGES))()
     n = ctypes.c_int32()
     _check("mac_profile_read", load().mac_profile_read(handle, ms, ctypes.byref(n)))
     return dict(zip(STAGES, list(ms))), n.value

@@ -26,9 +26,9 @@ sys.path.insert(0, ROOT)
 from attention_reuse_amd import workload as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-STAGES = ("match", "attend", "merge", "append")
+STAGES = ("match", "attend", "merge", "append", "step")
 KERNEL_NAMES = {"match": "match_kernel", "attend": "attend_kernel",
-                "merge": "merge_kernel", "append": "append_kernel"}
+                "merge": "merge_kernel", "append": "append_kernel", "step": "step_kernel"}
 
 
 def parse():
@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--mode", choices=("mac", "full"), default="mac")
     ap.add_argument("--append", choices=("aux", "fused"), default="fused",
                     help="rectify-append on the auxiliary stream or fused into the merge")
+    ap.add_argument("--launch", choices=("auto", "single", "split"), default="auto",
+                    help="decode step as one launch, as match / attend / merge kernels, "
+                         "or the library's choice for the shape")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--no-profile", action="store_true")
@@ -193,7 +196,9 @@ def main():
     pos = to_dev(pos_np)
     p = mac.make_params(B, H, Hkv, d, mac.MAC_DTYPE_F32 if cfg.dtype == "f32" else mac.MAC_DTYPE_BF16,
                         R, cfg.band_r, cfg.capacity, cfg.tau,
-                        flags=mac.MAC_FLAG_FUSED_APPEND if args.append == "fused" else 0)
+                        flags=(mac.MAC_FLAG_FUSED_APPEND if args.append == "fused" else 0)
+                        | {"auto": 0, "single": mac.MAC_FLAG_SINGLE_LAUNCH,
+                           "split": mac.MAC_FLAG_SPLIT_STAGES}[args.launch])
     wsb = mac.mac_workspace_bytes(p)
     stream = torch.cuda.current_stream()
     st = stream.cuda_stream
@@ -297,8 +302,18 @@ def main():
         stage_ms = {k: tot[k] / max(cnt, 1) for k in STAGES}
 
     roofline = None
+    launched = None
     if stage_ms:
+        launched = "single" if stage_ms["step"] > 0 else "split"
+    if stage_ms and launched == "single":
+        # One kernel moves the match, attention and merge bytes (and the ring
+        # append when fused).
+        dom = "step"
+        per_launch["step"] = sum(per_launch[k] for k in ("match", "attend", "merge")) + (
+            per_launch["append"] if args.append == "fused" else 0.0)
+    elif stage_ms:
         dom = max(("match", "attend"), key=lambda k: stage_ms[k])
+    if stage_ms:
         ach = per_launch[dom] / (stage_ms[dom] * 1e-3) / 1e9
         roofline = dict(bound="hbm", kernel=KERNEL_NAMES[dom], achieved=round(ach, 1),
                         peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4),
@@ -326,7 +341,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded N(0,1) K/V, prototype+noise query stream)",
-        "config": {"workload": cfg.name, "mode": args.mode, "append": args.append,
+        "config": {"workload": cfg.name, "mode": args.mode,
+                   "launch": launched or args.launch,
+                   "append": args.append,
                    "layers": NL, "kv_dtype": cfg.dtype,
                    "batch": B, "q_heads": H, "kv_heads": Hkv, "head_dim": d,
                    "context": cfg.ctx, "ring_k": R, "band_r": cfg.band_r, "tau": cfg.tau,

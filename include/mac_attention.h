@@ -63,12 +63,26 @@ enum { MAC_DTYPE_F32 = 0, MAC_DTYPE_BF16 = 1 };
 enum { MAC_THRESH_ONE_MINUS_TAU = 0, MAC_THRESH_TAU = 1 };
 
 /* mac_params.flags bits.
- *   MAC_FLAG_FUSED_APPEND: the rectify-append is done by the merge inside the
- *   attention kernel instead of a separate kernel on the auxiliary stream. */
-enum { MAC_FLAG_FUSED_APPEND = 1 };
+ *   MAC_FLAG_FUSED_APPEND: the rectify-append is done by the merge instead
+ *   of a separate kernel on the auxiliary stream.
+ *   MAC_FLAG_SPLIT_STAGES: mac_decode_step always runs match, plan +
+ *   attention and merge as three kernels.
+ *   MAC_FLAG_SINGLE_LAUNCH: mac_decode_step always runs the step as one
+ *   launch.
+ * With neither of the last two, the step is one launch when a layer has at
+ * most 16 KV groups (batch * n_kv_heads), where the step is bound by
+ * latency, and three kernels otherwise, where it is bound by bandwidth.
+ * Both forms give the same results bit for bit. */
+enum { MAC_FLAG_FUSED_APPEND = 1, MAC_FLAG_SPLIT_STAGES = 2, MAC_FLAG_SINGLE_LAUNCH = 4 };
 
 /* Device status flags latched in the workspace. */
-enum { MAC_DEV_BAD_POSITION = 1 /* some m outside [0, kv_capacity) */ };
+enum {
+    MAC_DEV_BAD_POSITION = 1, /* some m outside [0, kv_capacity)            */
+    MAC_DEV_SYNC_TIMEOUT = 2  /* a single-launch step gave up waiting for
+                                 workgroups that never became resident: its
+                                 outputs are not valid, and the handle must
+                                 be re-initialised with mac_init_rings      */
+};
 
 typedef struct mac_params {
     int32_t batch;        /* B requests                                      */
@@ -144,14 +158,25 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
  *   match_p [B, Hq] int32 or NULL  matched position, -1 on a miss
  *   match_d2[B, Hq] fp32 or NULL   squared distance of the nearest candidate
  *                                  (+inf when the window is empty)
- * Match, amend and complete run on main_stream as three kernels (match,
- * plan + attention, merge).  The rectify-append of the rings runs as a third
+ * Match, amend and complete run on main_stream as one kernel launch whose
+ * workgroups are all resident at once (they meet at a grid barrier after
+ * the match), or as three kernels (match, plan + attention, merge); see
+ * MAC_FLAG_SPLIT_STAGES for the choice.  Other work that holds compute units while the
+ * launch waits for residency only delays it; a launch that cannot get all
+ * its workgroups resident within about a second stops waiting and latches
+ * MAC_DEV_SYNC_TIMEOUT.  The rectify-append of the rings runs as another
  * kernel on aux_stream (main_stream if NULL or equal), ordered after the
  * merge by an event; the next call on the same handle waits for it.  With
  * MAC_FLAG_FUSED_APPEND the merge writes the rings itself and aux_stream is
- * unused.  Returns without a host synchronisation, so a steady-state step
+ * unused.  The append reads qtilde: when it runs on aux_stream, work that
+ * overwrites qtilde must be ordered after mac_join_aux (or after a later
+ * mac_decode_step on the handle) on the stream that does it; the other
+ * inputs are read on main_stream only.  Returns without a host
+ * synchronisation, so a steady-state step
  * can be captured into a HIP graph (join aux_stream back with mac_join_aux
- * first).  Calls on one handle must not overlap; handles are independent.
+ * first).  Calls on one handle must not overlap; handles are independent,
+ * and each owns its workspace (the single launch keeps synchronisation
+ * counters there between calls).
  */
 mac_status mac_decode_step(mac_handle *h, const void *qtilde, const float *q,
                            const void *k_cache, const void *v_cache,
@@ -175,17 +200,21 @@ mac_status mac_full_decode(const mac_params *p, const float *q,
                            void *workspace, size_t ws_bytes, void *stream);
 
 /* Read (with a synchronisation of `stream`) and clear the device status
- * flags (MAC_DEV_*) of the latest call on a workspace laid out for p. */
+ * flags (MAC_DEV_*) of a workspace laid out for p: MAC_DEV_BAD_POSITION of
+ * the latest call, MAC_DEV_SYNC_TIMEOUT of any call since the last read. */
 mac_status mac_read_device_status(const mac_params *p, void *workspace,
                                   void *stream, int32_t *flags);
 
 /* Per-kernel timing with HIP events (diagnostics).  mac_profile_start arms
  * recording for the next `n_steps` decode steps of the handle; stages are
- * 0 match, 1 plan + attention, 2 merge, 3 rectify-append (0 when fused).
- * mac_profile_read synchronises, returns the summed milliseconds per stage
- * in ms[4] and the number of recorded steps in *n, and disarms. */
+ * 0 match, 1 plan + attention, 2 merge (these three 0 for the single
+ * launch), 3 rectify-append (0 when fused), 4 the single launch (0 with
+ * MAC_FLAG_SPLIT_STAGES).  mac_profile_read synchronises, returns the
+ * summed milliseconds per stage in ms[5] and the number of recorded steps
+ * in *n, and disarms. */
+enum { MAC_PROFILE_STAGES = 5 };
 mac_status mac_profile_start(mac_handle *h, int32_t n_steps);
-mac_status mac_profile_read(mac_handle *h, double ms[4], int32_t *n);
+mac_status mac_profile_read(mac_handle *h, double ms[MAC_PROFILE_STAGES], int32_t *n);
 
 /* Free the handle and its events (not the caller's buffers). */
 mac_status mac_release(mac_handle *h);

@@ -31,13 +31,17 @@ def _sample_heads(cfg, sig):
     return sorted(set(cand))
 
 
-@pytest.mark.parametrize("cfg_id,append", [(2, "aux"), (3, "fused"), (4, "aux"), (5, "fused")])
-def test_fullsize_config(oracle_lib, cfg_id, append):
+@pytest.mark.parametrize("cfg_id,append,launch", [
+    (2, "aux", "single"), (2, "fused", "split"), (3, "fused", "single"), (4, "aux", "single"),
+    (5, "fused", "single"), (5, "aux", "split")])
+def test_fullsize_config(oracle_lib, cfg_id, append, launch):
     cfg = wl.WORKLOADS[cfg_id]
-    print("full-size parity: config %d (%s), append=%s" % (cfg_id, cfg.name, append), flush=True)
+    print("full-size parity: config %d (%s), append=%s, launch=%s"
+          % (cfg_id, cfg.name, append, launch), flush=True)
     K, V = wl.gen_kv(cfg)
     qt, q, _, sig = wl.gen_queries(cfg)
-    flags = mac.MAC_FLAG_FUSED_APPEND if append == "fused" else 0
+    flags = (mac.MAC_FLAG_FUSED_APPEND if append == "fused" else 0) | (
+        mac.MAC_FLAG_SPLIT_STAGES if launch == "split" else mac.MAC_FLAG_SINGLE_LAUNCH)
     p = params_for(cfg, flags=flags)
     layer = Layer(cfg, K, V, qt, q, params=p).init()
     gpu = run_steps(layer, cfg.steps, aux=torch.cuda.Stream() if append == "aux" else None)
@@ -77,6 +81,7 @@ def test_fullsize_config(oracle_lib, cfg_id, append):
         print("  step %d: MAC vs full relative L2 median %.3g max %.3g"
               % (s, float(np.median(err)), float(err.max())), flush=True)
     print("  miss heads bitwise equal to full decode: %d" % n_miss, flush=True)
+    assert mac.mac_read_device_status(p, layer.ws) == 0
 
     # Sampled streams against the oracle in lock step.
     heads = _sample_heads(cfg, sig)

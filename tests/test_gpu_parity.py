@@ -159,15 +159,19 @@ def test_forced_miss_is_bitwise_full_decode():
         assert np.array_equal(out.cpu().numpy(), gpu["out"][s]), s
 
 
-def test_run_to_run_deterministic_and_append_mode_invariant():
-    """Outputs and rings are bitwise identical run to run, with the
-    rectify-append on an auxiliary stream, on the main stream, or fused into
-    the merge."""
+def test_run_to_run_deterministic_and_launch_and_append_mode_invariant():
+    """Outputs and rings are bitwise identical run to run, as one launch or
+    three kernels, with the rectify-append on an auxiliary stream, on the
+    main stream, or fused into the merge."""
     cfg = _cfg(steps=12, sigma=(0.02, 0.5))
     K, V, qt, q = _inputs(cfg)
     runs = []
-    for flags, aux in ((0, torch.cuda.Stream()), (0, None),
-                       (mac.MAC_FLAG_FUSED_APPEND, torch.cuda.Stream()), (0, torch.cuda.Stream())):
+    split, fused = mac.MAC_FLAG_SPLIT_STAGES, mac.MAC_FLAG_FUSED_APPEND
+    single = mac.MAC_FLAG_SINGLE_LAUNCH
+    for flags, aux in ((single, torch.cuda.Stream()), (single, None),
+                       (single | fused, torch.cuda.Stream()), (0, torch.cuda.Stream()),
+                       (split, torch.cuda.Stream()), (split | fused, None), (split, None)):
+        print("  flags %d, aux stream %s" % (flags, aux is not None), flush=True)
         layer = Layer(cfg, K, V, qt, q, params=params_for(cfg, flags=flags))
         res = run_steps(layer.init(), cfg.steps, aux=aux)
         res["rings"] = [t.cpu().float().numpy() for t in
@@ -179,6 +183,37 @@ def test_run_to_run_deterministic_and_append_mode_invariant():
             assert np.array_equal(runs[0][k], r[k]), k
         for x, y in zip(runs[0]["rings"], r["rings"]):
             assert np.array_equal(x, y)
+
+
+def test_lockstep_split_stages(oracle_lib):
+    """The three-kernel form of the step against the oracle (the other
+    lockstep tests have at most 16 KV groups, so they run one launch)."""
+    cfg = _cfg(batch=2, ctx=1800, steps=24, ring_k=128, band_r=48, sigma=(0.02, 0.5), seed=7)
+    K, V, qt, q = _inputs(cfg)
+    layer = Layer(cfg, K, V, qt, q, params=params_for(cfg, flags=mac.MAC_FLAG_SPLIT_STAGES))
+    _lockstep(oracle_lib, cfg, layer=layer)
+
+
+def test_interleaved_handles_one_stream():
+    """Several layers' single-launch steps interleaved on one stream (as in
+    a model): each layer's results equal those of that layer run alone."""
+    cfg = _cfg(batch=1, steps=8, sigma=(0.02, 0.5))
+    K, V, qt, q = _inputs(cfg)
+    alone = run_steps(Layer(cfg, K, V, qt, q).init(), cfg.steps)
+    layers = [Layer(cfg, K, V, qt, q).init() for _ in range(3)]
+    B, H, d = cfg.batch, cfg.n_q_heads, cfg.head_dim
+    outs = [torch.empty((cfg.steps, B, H, d), device=DEV) for _ in layers]
+    pos = torch.from_numpy(wl.decode_positions(cfg)).to(DEV)
+    ms = torch.cuda.current_stream().cuda_stream
+    for s in range(cfg.steps):
+        for L, o in zip(layers, outs):
+            mac.mac_decode_step(L.handle, L.dec_qt[s], L.dec_q[s], L.K, L.V, pos[s], o[s],
+                                None, None, None, ms, None)
+    torch.cuda.synchronize()
+    for L, o in zip(layers, outs):
+        assert np.array_equal(o.cpu().numpy(), alone["out"])
+        assert mac.mac_read_device_status(L.p, L.ws) == 0
+        L.release()
 
 
 def test_lockstep_fused_append(oracle_lib):
