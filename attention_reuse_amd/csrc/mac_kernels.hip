@@ -612,37 +612,31 @@ __device__ inline void fold_items(const StepArgs &a, int64_t begin, int i0, int 
     }
 }
 
-// Merge of group grp by the NT threads of the calling workgroup: cnt items
-// from item index `begin`, the group's range starting at gstart.  Outputs
-// are handled in pair tasks (two adjacent dims of one head), the same for
-// every NT.  The partials are read device-coherently when kWT.  The matched
-// slot of each head comes from the planner's per-head codes (codes !=
-// nullptr) or from the published plan.  lds holds MergeShape::kFloats
-// floats.
-template <class T, int D, int G, int NT, bool kWT>
-__device__ void merge_group(const StepArgs &a, int grp, int cnt, int64_t begin, int gstart,
-                            float *lds, const int32_t *codes)
-{
-    using M = MergeShape<T, D, G>;
-    constexpr int P = M::P, DPT = M::DPT, TPS = M::TPS, SEG = M::SEG, NTASK = M::NTASK;
-    constexpr int NPAIR = G * D / 2;                  // pair tasks
-    constexpr int NPK = (NPAIR + NT - 1) / NT;        // pair tasks per thread
-    using S = typename T::S;
-    const Shape &s = a.s;
-    const int tid = threadIdx.x;
-    const int b = grp / s.Hkv, g = grp - b * s.Hkv;
-    const int e = end_of(a, b);
-    const int r_split = (a.mode == kPlanInit) ? 0 : s.r;
-    const int nA = RangeSplit(gstart, e, r_split).n_before_split();
+// Pair tasks of the merge: two adjacent dims of one head, the same split for
+// every thread count NT.
+template <int D, int G, int NT>
+struct MergePairs {
+    static constexpr int NPAIR = G * D / 2;            // pair tasks
+    static constexpr int NPK = (NPAIR + NT - 1) / NT;  // pair tasks per thread
+};
 
-    // The cached summary C of each pair, requested before the partials.
-    float c_l[NPK], c_o[NPK][2];
+// Cached summary C of each of this thread's pairs of group grp (empty on a
+// miss): from the planner's per-head codes (codes != nullptr) or from the
+// published plan.
+template <class T, int D, int G, int NT>
+__device__ inline void load_cached(const StepArgs &a, int grp, const int32_t *codes,
+                                   float (&c_l)[MergePairs<D, G, NT>::NPK],
+                                   float (&c_o)[MergePairs<D, G, NT>::NPK][2])
+{
+    using MP = MergePairs<D, G, NT>;
+    const Shape &s = a.s;
+    const int b = grp / s.Hkv, g = grp - b * s.Hkv;
 #pragma unroll
-    for (int k = 0; k < NPK; ++k) {
-        const int pt = tid + k * NT;
+    for (int k = 0; k < MP::NPK; ++k) {
+        const int pt = threadIdx.x + k * NT;
         c_l[k] = -INFINITY;
         c_o[k][0] = c_o[k][1] = 0.f;
-        if (pt < NPAIR) {
+        if (pt < MP::NPAIR) {
             const int jj = 2 * pt / D, dim = 2 * pt - jj * D;
             const int bh = b * s.Hq + g * G + jj;
             const int slot = codes ? code_slot(codes[bh], s.r, s.K) : a.w.dec_slot[bh];
@@ -655,6 +649,29 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int64_t begin, 
             }
         }
     }
+}
+
+// Merge of group grp by the NT threads of the calling workgroup: cnt items
+// from item index `begin`, the group's range starting at gstart, with the
+// cached summaries (c_l, c_o) from load_cached.  Outputs are handled in pair
+// tasks, so the fold is the same for every NT.  The partials are read
+// device-coherently when kWT.  lds holds MergeShape::kFloats floats.
+template <class T, int D, int G, int NT, bool kWT>
+__device__ void merge_group(const StepArgs &a, int grp, int cnt, int64_t begin, int gstart,
+                            float *lds, const float (&c_l)[MergePairs<D, G, NT>::NPK],
+                            const float (&c_o)[MergePairs<D, G, NT>::NPK][2])
+{
+    using M = MergeShape<T, D, G>;
+    constexpr int P = M::P, DPT = M::DPT, TPS = M::TPS, SEG = M::SEG, NTASK = M::NTASK;
+    constexpr int NPAIR = MergePairs<D, G, NT>::NPAIR;
+    constexpr int NPK = MergePairs<D, G, NT>::NPK;
+    using S = typename T::S;
+    const Shape &s = a.s;
+    const int tid = threadIdx.x;
+    const int b = grp / s.Hkv, g = grp - b * s.Hkv;
+    const int e = end_of(a, b);
+    const int r_split = (a.mode == kPlanInit) ? 0 : s.r;
+    const int nA = RangeSplit(gstart, e, r_split).n_before_split();
 
     // list 0 = A (items [0, nA)), list 1 = Bt (items [nA, cnt)); each pair
     // folds into res[list][k].
@@ -809,8 +826,10 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(StepArgs a)
     const int cnt = a.w.grp_count[grp];
     if (cnt == 0)
         return;  // the planner wrote this group's outputs
+    float c_l[MergePairs<D, G, kMergeBlock>::NPK], c_o[MergePairs<D, G, kMergeBlock>::NPK][2];
+    load_cached<T, D, G, kMergeBlock>(a, grp, nullptr, c_l, c_o);
     merge_group<T, D, G, kMergeBlock, false>(a, grp, cnt, a.w.grp_begin[grp],
-                                             a.w.grp_start[grp], lds, nullptr);
+                                             a.w.grp_start[grp], lds, c_l, c_o);
 }
 
 // ---------------------------------------------------------------------------
@@ -993,9 +1012,11 @@ __device__ inline int group_of(const PlanTables &pt, int it, int NG)
 // Attention of work item `it` (of group grp) by the whole workgroup, ending
 // with its partial (o, log2-lse) per head in the workspace (written
 // device-coherently when kWT).  lds holds AttendShape::kFloats floats.
-template <class T, int D, int G, bool kWT>
+// after_issue() runs once the item's first K/V and query loads are in
+// flight (extra requests whose latency should hide behind them).
+template <class T, int D, int G, bool kWT, class AfterIssue>
 __device__ inline void run_item(const StepArgs &a, const PlanTables &pt, int it, int grp,
-                                float *lds)
+                                float *lds, AfterIssue &&after_issue)
 {
     using L = AttendShape<T, D, G>;
     constexpr int EPL = L::EPL, LPR = L::LPR, RPB = L::RPB, NB = L::NB;
@@ -1033,6 +1054,8 @@ __device__ inline void run_item(const StepArgs &a, const PlanTables &pt, int it,
         }
         st[j] = __builtin_amdgcn_readfirstlane(code_start(pt.code[b * s.Hq + g * G + j]));
     }
+
+    after_issue();
 
     float mrun[G], lrun[G], acc[G][EPL];
 #pragma unroll
@@ -1155,7 +1178,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
     const PlanTables pt = plan_tables<false>(a, plan_lds, blockIdx.x == 0, a.w.keys);
     const int NG = a.s.B * a.s.Hkv;
     for (int it = blockIdx.x; it < pt.total; it += gridDim.x) {
-        run_item<T, D, G, false>(a, pt, it, group_of(pt, it, NG), lds);
+        run_item<T, D, G, false>(a, pt, it, group_of(pt, it, NG), lds, [] {});
         __syncthreads();
     }
 }
@@ -1240,9 +1263,14 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
         st_wt(&sync[kSyncEpoch], epoch + 1);  // every workgroup read the epoch before arriving
 
     const PlanTables pt = plan_tables<true>(a, plan_lds, blockIdx.x == 0, keys);
+    using MP = MergePairs<D, G, kBlock>;
     for (int it = blockIdx.x; it < pt.total; it += gridDim.x) {
         const int grp = group_of(pt, it, NG);
-        run_item<T, D, G, true>(a, pt, it, grp, lds);
+        // The cached summaries are requested with the item's first loads, in
+        // case this workgroup completes the group and merges it.
+        float c_l[MP::NPK], c_o[MP::NPK][2];
+        run_item<T, D, G, true>(a, pt, it, grp, lds,
+                                [&] { load_cached<T, D, G, kBlock>(a, grp, pt.code, c_l, c_o); });
         wait_vmem();  // this wave's partial stores have completed
         __syncthreads();
         if (threadIdx.x == 0)
@@ -1251,7 +1279,7 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
         __syncthreads();
         if (s_last) {
             merge_group<T, D, G, kBlock, true>(a, grp, pt.gcount[grp], pt.gbegin[grp],
-                                               pt.gstart[grp], lds, pt.code);
+                                               pt.gstart[grp], lds, c_l, c_o);
             if (threadIdx.x == 0)
                 st_wt(&a.w.grp_sync[(int64_t)grp * kGrpStride], 0u);
         }
