@@ -14,7 +14,23 @@ namespace mac {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-WsLayout ws_layout(int B, int Hq, int Hkv, int D, int K, int T)
+static int elem_bytes(int32_t dtype) { return dtype == MAC_DTYPE_F32 ? 4 : 2; }
+
+// Fewest splits per head of the single launch's match (largest units).
+static int single_min_nsplit(int K, int dtype, int D)
+{
+    const int slots = single_slots(elem_bytes(dtype), D);
+    return (K + slots - 1) / slots;
+}
+
+// 64-bit words of the single launch's tagged key region (key words per
+// group are at most kMaxSingleUnits).
+static int64_t single_tag_words(int B, int Hkv)
+{
+    return (int64_t)kKeyReps * B * Hkv * kMaxSingleUnits;
+}
+
+WsLayout ws_layout(int B, int Hq, int Hkv, int D, int K, int T, int dtype, bool single)
 {
     WsLayout L;
     const int G = Hq / Hkv;
@@ -27,7 +43,7 @@ WsLayout ws_layout(int B, int Hq, int Hkv, int D, int K, int T)
         return o;
     };
     const size_t BH = (size_t)B * Hq, BG = (size_t)B * Hkv;
-    L.keys = take(2 * BH * kKeyStride * sizeof(unsigned long long));
+    L.keys = take(BH * kKeyStride * sizeof(unsigned long long));
     L.ctx = take((size_t)B * 4);
     L.dec_slot = take(BH * 4);
     L.grp_begin = take(BG * 4);
@@ -35,11 +51,17 @@ WsLayout ws_layout(int B, int Hq, int Hkv, int D, int K, int T)
     L.grp_start = take(BG * 4);
     L.ctrl = take(64);
     L.sync = take((size_t)kSyncWords * sizeof(unsigned long long));
-    L.grp_sync = take(BG * kGrpStride * sizeof(uint32_t));
     L.part_o = take((size_t)L.max_items * G * D * 4);
     L.part_l = take((size_t)L.max_items * G * 4);
     L.rect_o = take(BH * D * 4);
     L.rect_l = take(BH * 4);
+    // The single-launch regions come last, so the layout without them is a
+    // prefix of the layout with them.
+    L.skeys = L.grp_sync = 0;
+    if (single) {
+        L.skeys = take(single_tag_words(B, Hkv) * sizeof(unsigned long long));
+        L.grp_sync = take(BG * kGrpStride * sizeof(uint32_t));
+    }
     L.total = off;
     return L;
 }
@@ -56,11 +78,12 @@ WsPtrs ws_ptrs(void *base, const WsLayout &L)
     w.grp_start = (int32_t *)(c + L.grp_start);
     w.ctrl = (int32_t *)(c + L.ctrl);
     w.sync = (unsigned long long *)(c + L.sync);
-    w.grp_sync = (uint32_t *)(c + L.grp_sync);
     w.part_o = (float *)(c + L.part_o);
     w.part_l = (float *)(c + L.part_l);
     w.rect_o = (float *)(c + L.rect_o);
     w.rect_l = (float *)(c + L.rect_l);
+    w.skeys = L.skeys ? (unsigned long long *)(c + L.skeys) : nullptr;
+    w.grp_sync = L.grp_sync ? (uint32_t *)(c + L.grp_sync) : nullptr;
     return w;
 }
 
@@ -80,6 +103,7 @@ struct mac_handle {
     mac_rings rings;
     bool fused_append;
     bool split_stages;
+    int32_t wpg, upg, nkw, done_shift, unit_slots, nsplit;  // single-launch geometry
     hipEvent_t ev_main = nullptr, ev_aux = nullptr;
     // Per-stage timing events: prof[(step * kStages + stage) * 2 + {0,1}].
     std::vector<hipEvent_t> prof;
@@ -87,8 +111,6 @@ struct mac_handle {
 };
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
-
-static int elem_bytes(int32_t dtype) { return dtype == MAC_DTYPE_F32 ? 4 : 2; }
 
 // Host-side validation of the parameter block; fills the kernel shape.
 static mac_status check_params(const mac_params *p, Shape *s)
@@ -153,6 +175,29 @@ static mac_status check_params(const mac_params *p, Shape *s)
     return MAC_OK;
 }
 
+// Shapes the single launch handles: positions that the tagged keys encode,
+// match units that its LDS holds.
+static bool single_launch_supported(const Shape &s)
+{
+    return s.T <= kSingleMaxPositions &&
+           s.G * single_min_nsplit(s.K, s.dtype, s.D) <= kMaxSingleUnits;
+}
+
+// Whether a handle for p may run the single launch: not forced to three
+// kernels, at most kSingleLaunchMaxGroups KV groups unless forced, and
+// positions that the tagged keys encode.
+static bool single_launch_form(const mac_params *p, const Shape &s)
+{
+    if (p->flags & MAC_FLAG_SPLIT_STAGES || !single_launch_supported(s))
+        return false;
+    return (p->flags & MAC_FLAG_SINGLE_LAUNCH) || s.B * s.Hkv <= kSingleLaunchMaxGroups;
+}
+
+static WsLayout layout_for(const mac_params *p, const Shape &s)
+{
+    return ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T, s.dtype, single_launch_form(p, s));
+}
+
 extern "C" {
 
 size_t mac_workspace_bytes(const mac_params *p)
@@ -160,7 +205,7 @@ size_t mac_workspace_bytes(const mac_params *p)
     Shape s;
     if (check_params(p, &s) != MAC_OK)
         return 0;
-    return ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T).total;
+    return layout_for(p, s).total;
 }
 
 mac_status mac_ring_bytes(const mac_params *p, size_t out[4])
@@ -175,7 +220,7 @@ mac_status mac_ring_bytes(const mac_params *p, size_t out[4])
     out[0] = n * s.D * elem_bytes(s.dtype);
     out[1] = n * s.D * 4;
     out[2] = n * 4;
-    out[3] = (size_t)s.B * s.K * 4;
+    out[3] = (size_t)s.B * s.Hkv * s.K * 4;
     return MAC_OK;
 }
 
@@ -246,9 +291,11 @@ mac_status mac_full_decode(const mac_params *p, const float *q,
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
         !aligned16(workspace))
         return MAC_ERR_MISALIGNED;
-    const WsLayout L = ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T);
-    if (ws_bytes < L.total)
+    // The documented size is required; full decode uses only the regions
+    // that precede the single-launch ones.
+    if (ws_bytes < layout_for(p, s).total)
         return MAC_ERR_WORKSPACE_TOO_SMALL;
+    const WsLayout L = ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T, s.dtype, false);
     StepArgs a = base_args(s, L, ws_ptrs(workspace, L));
     a.mode = kPlanFull;
     a.pos = pos;
@@ -282,7 +329,9 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
     if (!aligned16(rings->q_ring) || !aligned16(rings->o_ring) ||
         !aligned16(workspace))
         return MAC_ERR_MISALIGNED;
-    const WsLayout L = ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T);
+    if ((p->flags & MAC_FLAG_SINGLE_LAUNCH) && !single_launch_supported(s))
+        return MAC_ERR_UNSUPPORTED;
+    const WsLayout L = layout_for(p, s);
     if (ws_bytes < L.total)
         return MAC_ERR_WORKSPACE_TOO_SMALL;
     if (n_warm < 0 || n_warm > s.K)
@@ -310,16 +359,44 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
     h->ws = workspace;
     h->rings = *rings;
     h->fused_append = (p->flags & MAC_FLAG_FUSED_APPEND) != 0;
-    h->split_stages = (p->flags & MAC_FLAG_SPLIT_STAGES) != 0 ||
-                      ((p->flags & MAC_FLAG_SINGLE_LAUNCH) == 0 &&
-                       s.B * s.Hkv > kSingleLaunchMaxGroups);
+    h->split_stages = !single_launch_form(p, s);
+    if (!h->split_stages) {
+        // wpg workgroups per KV group, all resident at once, each with at
+        // least one key word to store.
+        const int NG = s.B * s.Hkv;
+        const int resident = step_resident_workgroups(s);
+        h->wpg = resident / NG < kGroupWorkgroups ? resident / NG : kGroupWorkgroups;
+        // Match units: about one per workgroup, whole row loads, at most
+        // single_slots slots each.
+        const int rpl = match_rows_per_load(elem_bytes(s.dtype), s.D);
+        const int64_t want = h->wpg > 0 ? ((int64_t)s.G * s.K + h->wpg - 1) / h->wpg : 1;
+        int64_t us = (want + rpl - 1) / rpl * rpl;
+        const int smax = single_slots(elem_bytes(s.dtype), s.D);
+        us = us > smax ? smax : us;
+        h->unit_slots = (int)us;
+        h->nsplit = (s.K + h->unit_slots - 1) / h->unit_slots;
+        h->upg = s.G * h->nsplit;
+        h->nkw = h->upg > h->wpg ? h->upg : h->wpg;
+        int sh = 0;
+        while ((1 << sh) < NG)
+            ++sh;
+        h->done_shift = sh;
+        if (h->wpg < 1) {
+            if (p->flags & MAC_FLAG_SINGLE_LAUNCH) {
+                delete h;
+                return MAC_ERR_UNSUPPORTED;
+            }
+            h->split_stages = true;
+        }
+    }
     if (hipEventCreateWithFlags(&h->ev_main, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&h->ev_aux, hipEventDisableTiming) != hipSuccess) {
         mac_release(h);
         return MAC_ERR_HIP;
     }
+    const int64_t n_tag = L.skeys ? single_tag_words(s.B, s.Hkv) : 0;
     if (launch_ring_reset(s, rings->q_ring, rings->o_ring, rings->lse_ring,
-                          rings->pos_ring, w, st) != hipSuccess) {
+                          rings->pos_ring, w, n_tag, st) != hipSuccess) {
         mac_release(h);
         return MAC_ERR_HIP;
     }
@@ -402,6 +479,12 @@ mac_status mac_decode_step(mac_handle *h, const void *qtilde, const float *q,
     a.lse_ring = h->rings.lse_ring;
     a.pos_ring = h->rings.pos_ring;
     a.append_fused = h->fused_append ? 1 : 0;
+    a.wpg = h->wpg;
+    a.upg = h->upg;
+    a.nkw = h->nkw;
+    a.done_shift = h->done_shift;
+    a.nsplit = h->split_stages ? h->L.nsplit : h->nsplit;
+    a.unit_slots = h->unit_slots;
 
     const bool prof = h->prof_n < h->prof_cap;
     hipEvent_t *pe = prof ? &h->prof[(size_t)h->prof_n * kStages * 2] : nullptr;
@@ -457,7 +540,7 @@ mac_status mac_read_device_status(const mac_params *p, void *workspace,
         return rc;
     if (!workspace || !flags)
         return MAC_ERR_INVALID_ARG;
-    const WsLayout L = ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T);
+    const WsLayout L = ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T, s.dtype, false);
     const WsPtrs w = ws_ptrs(workspace, L);
     hipStream_t st = (hipStream_t)stream;
     int32_t v = 0;

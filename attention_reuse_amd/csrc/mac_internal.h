@@ -19,29 +19,67 @@ constexpr int kSlotsPerSplit = 64;
 // Workgroup size of the match and attention kernels.
 constexpr int kBlock = 256;
 
-// Single-launch step: cross-workgroup synchronisation words in the
-// workspace, 64-bit, one 128-byte line (kLineU64 words) each:
-//   line 0: [0] launch epoch, [1] kSyncMagic once the rings were
-//           initialised on the workspace, [2] latched time-outs;
-//   lines 1..kBarLines: grid-barrier arrival counters;
-//   line 1 + kBarLines: count of completed arrival lines;
-//   the kRelLines lines after it: the barrier's release word.
-// The per-group arrival counters are 32-bit, kGrpStride words apart.
-constexpr int kBarLines = 16;
-constexpr int kRelLines = 32;
-constexpr int kLineU64 = 16;
-constexpr int kSyncWords = kLineU64 * (2 + kBarLines + kRelLines);
+// Items of one KV group never exceed this (grid cells plus the two range
+// ends around the rectify split).
+constexpr int kItemsPerGroupMax = kMaxItemsPerGroup + 2;
+
+// Single-launch step.  Each KV group has its own run of workgroups, and data
+// crosses workgroups only inside a group:
+//   split keys [kKeyReps][groups][key words]: per match unit the key
+//       d2_bits << 32 | (0xffffffff - p) with bits 31..24 replaced by the
+//       low byte of the launch's tag (positions < 2^24); each workgroup
+//       polls the words of its group until all carry the tag.  kKeyReps
+//       copies spread the pollers of a group over several lines;
+//   partials: the split-KV partial arrays, item i of group grp at index
+//       grp * kItemsPerGroupMax + i, handed to the workgroup that completes
+//       the group's per-group counter.
+// The tag of a launch is 1 + its epoch; the epoch is floor(done / 2^s)
+// where `done` grows by exactly 2^s per launch (the merger of group 0 adds
+// 2^s - groups + 1, every other group's merger 1), so it is constant during
+// a launch until its last group completes, and every workgroup reads it
+// before its own group can complete.
+constexpr int kKeyReps = 4;
+// Ring rows one 256-thread workgroup loads per instruction (one row per
+// 16-byte lane group), and the largest match unit of the single launch: 16
+// such loads per lane, at most 256 slots.  The host sizes the units so that
+// a group's ring rows spread over its workgroups.
+__host__ __device__ constexpr int match_rows_per_load(int elem_bytes, int D)
+{
+    return 4096 / (elem_bytes * D);
+}
+__host__ __device__ constexpr int single_slots(int elem_bytes, int D)
+{
+    return 16 * match_rows_per_load(elem_bytes, D) < 256 ? 16 * match_rows_per_load(elem_bytes, D)
+                                                         : 256;
+}
+// Match units per group of the single launch are at most this many (the
+// host falls back to three kernels beyond).
+constexpr int kMaxSingleUnits = 256;
+// Workgroups per group of the single launch (fewer when the device does
+// not hold that many resident); those without a match unit store a tagged
+// dummy word, so that every workgroup's tag read precedes its group's
+// completion.
+constexpr int kGroupWorkgroups = 64;
+// Per-group arrival counters of the single launch, kGrpStride words apart.
 constexpr int kGrpStride = 16;
+// Largest position the tagged keys encode.
+constexpr int32_t kSingleMaxPositions = 1 << 24;
+// Synchronisation line of the workspace (64-bit words).
+constexpr int kLineU64 = 16;
+constexpr int kSyncWords = kLineU64;
 // Default form of the decode step: one launch for at most this many KV
 // groups per layer (latency-bound steps), three kernels above (measured on
 // MI355X: one launch is ahead at 8 groups, behind at 64 and 128).
 constexpr int kSingleLaunchMaxGroups = 16;
-// Match keys are kKeyStride words apart (one 128-byte line per head): the
-// atomic minima of a head's splits serialise per line, so heads must not
-// share one.
+// Match keys of the three-kernel step are kKeyStride words apart (one
+// 128-byte line per head): the atomic minima of a head's splits serialise
+// per line, so heads must not share one.
 constexpr int kKeyStride = 16;
 constexpr unsigned long long kSyncMagic = 0x4d41432d53594e43ull;
-enum { kSyncEpoch = 0, kSyncMagicWord = 1, kSyncSticky = 2 };
+enum { kSyncDone = 0, kSyncMagicWord = 1, kSyncSticky = 2 };
+
+// Key words per group of the single launch: one per match unit, at least
+// one per workgroup, never more than kMaxSingleUnits.
 
 // Plan: work-item partition of one group's token range [s, e].
 // Boundaries: s, the multiples of C in (s, e], the rectify split
@@ -107,7 +145,7 @@ struct RangeSplit {
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WsLayout {
     size_t keys, ctx, dec_slot, grp_begin, grp_count, grp_start, ctrl, sync,
-        grp_sync, part_o, part_l, rect_o, rect_l, total;
+        part_o, part_l, rect_o, rect_l, skeys, grp_sync, total;
     int64_t max_items;
     int32_t nsplit;
 };
@@ -131,14 +169,16 @@ struct Shape {
 
 // Device pointers into the workspace.
 struct WsPtrs {
-    // [2][B*Hq * kKeyStride] per-head match keys; the three-kernel step
-    // uses the first half, the single-launch step alternates by epoch.
+    // [B*Hq * kKeyStride] per-head match keys of the three-kernel step
     unsigned long long *keys;
     int32_t *ctx;  // [B] prompt lengths during the warm-up
     int32_t *dec_slot, *grp_begin, *grp_count, *grp_start, *ctrl;
-    unsigned long long *sync;  // epoch + kBarLines arrival lines
-    uint32_t *grp_sync;        // [B*Hkv * kGrpStride] per-group arrivals
+    unsigned long long *sync;  // done counter, magic, latched time-outs
     float *part_o, *part_l, *rect_o, *rect_l;
+    // single launch only (null otherwise): tagged split keys, per-group
+    // arrival counters
+    unsigned long long *skeys;
+    uint32_t *grp_sync;
 };
 
 // Everything the kernels of one call read or write.
@@ -165,12 +205,17 @@ struct StepArgs {
     float *o_ring, *lse_ring;
     int32_t *pos_ring;
     int32_t append_fused;
+    // single launch: workgroups per group, match units per group (G *
+    // nsplit), key words per group, log2 of the done increment per launch,
+    // ring slots per match unit
+    int32_t wpg, upg, nkw, done_shift, unit_slots;
 };
 
 // Bytes of dynamic LDS the planner needs.
 size_t plan_lds_bytes(int B, int Hq, int Hkv);
 
-WsLayout ws_layout(int B, int Hq, int Hkv, int D, int K, int T);
+// single: include the single-launch regions.
+WsLayout ws_layout(int B, int Hq, int Hkv, int D, int K, int T, int dtype, bool single);
 WsPtrs ws_ptrs(void *base, const WsLayout &L);
 
 // Kernel launchers (mac_kernels.hip); each returns its launch status.
@@ -183,14 +228,19 @@ hipError_t launch_attend(const StepArgs &a, hipStream_t st);
 hipError_t launch_merge(const StepArgs &a, hipStream_t st);
 // The whole decode step (match, plan, attention, merge and, with
 // append_fused, the ring append) as one launch of a grid that is resident
-// at once.
+// at once: a.wpg workgroups per KV group.
 hipError_t launch_step(const StepArgs &a, hipStream_t st);
+// Workgroups of the single-launch kernel for this shape that the device
+// holds resident at once (0 if unknown).
+int step_resident_workgroups(const Shape &s);
 // Rectify-append from the workspace staging into the rings; the position of
 // request b is pos[b] + pos_offset.
 hipError_t launch_append(const StepArgs &a, int32_t pos_offset, hipStream_t st);
+// Empties the rings, resets the synchronisation words and clears the first
+// n_tag words of each single-launch tagged region present in w.
 hipError_t launch_ring_reset(const Shape &s, void *q_ring, float *o_ring,
                              float *lse_ring, int32_t *pos_ring, const WsPtrs &w,
-                             hipStream_t st);
+                             int64_t n_tag, hipStream_t st);
 int device_cu_count();
 
 }  // namespace mac

@@ -213,9 +213,11 @@ __device__ inline void merge_into(float &l, float *o, float lb, const float *ob)
     const float M = fmaxf(l, lb);
     const float ln = M + lg2(ex2(l - M) + ex2(lb - M));
     const float wa = ex2(l - ln), wb = ex2(lb - ln);
+    // One explicit contraction, so every inlining of the merge rounds alike
+    // (the kernel forms must agree bit for bit).
 #pragma unroll
     for (int i = 0; i < N; ++i)
-        o[i] = wa * o[i] + wb * ob[i];
+        o[i] = fmaf(wa, o[i], wb * ob[i]);
     l = ln;
 }
 
@@ -254,27 +256,26 @@ __device__ inline unsigned long long ld_wt(const unsigned long long *p)
                              __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Plain or device-coherent load of one float / four floats.
-template <bool kWT>
-__device__ inline float ld_f(const float *p)
+// Workgroup-wide AND / OR of a predicate over the kBlock threads: a wave
+// vote, then the kBlock / 64 votes through LDS.  The library's
+// __syncthreads_and/_or obtain the workgroup size from the dispatch packet,
+// which lives in host memory: one uncached read per workgroup, serialised
+// across the grid (measured: microseconds per launch).
+__device__ inline bool block_and(bool p)
 {
-    if constexpr (kWT)
-        return ld_wt(p);
-    else
-        return *p;
+    __shared__ int votes[kBlock / 64];
+    const bool w = __all(p);
+    __syncthreads();  // the previous call's readers are done
+    if ((threadIdx.x & 63) == 0)
+        votes[threadIdx.x >> 6] = w;
+    __syncthreads();
+    bool r = true;
+#pragma unroll
+    for (int i = 0; i < kBlock / 64; ++i)
+        r = r && votes[i] != 0;
+    return r;
 }
-template <bool kWT>
-__device__ inline float4 ld_f4(const float *p)
-{
-    if constexpr (kWT) {
-        const unsigned long long lo = ld_wt(reinterpret_cast<const unsigned long long *>(p));
-        const unsigned long long hi = ld_wt(reinterpret_cast<const unsigned long long *>(p) + 1);
-        return make_float4(__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
-                           __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32)));
-    } else {
-        return *reinterpret_cast<const float4 *>(p);
-    }
-}
+__device__ inline bool block_or(bool p) { return !block_and(!p); }
 
 // s_waitcnt vmcnt(0): this wave's loads and stores have completed (a
 // write-through store is then visible to every XCD).  Encoding (gfx9):
@@ -323,14 +324,10 @@ struct PlanTables {
     int total;
 };
 
-// keys: the per-head match keys to decide from (read device-coherently
-// when kWT: they were written by atomics of the same launch).
-template <bool kWT>
-__device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish,
-                                  const unsigned long long *keys)
+__device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
 {
     const Shape &s = a.s;
-    const int tid = threadIdx.x, nt = blockDim.x;
+    const int tid = threadIdx.x, nt = kBlock;
     const int lane = tid & 63, wave = tid >> 6;
     const int BH = s.B * s.Hq, NG = s.B * s.Hkv;
     const int r_split = (a.mode == kPlanInit) ? 0 : s.r;
@@ -350,8 +347,7 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish,
         bad |= !ok;
         int32_t code = kMissCode, slot = -1;
         if (a.mode == kPlanMatch) {
-            const unsigned long long *kp = &keys[bh * kKeyStride];
-            const Decision dc = decide(a, kWT ? ld_wt(kp) : *kp, ok);
+            const Decision dc = decide(a, a.w.keys[bh * kKeyStride], ok);
             code = dc.hit ? dc.p - s.r + 1 : kMissCode;
             slot = dc.slot;
             if (publish && a.match_p)
@@ -363,7 +359,7 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish,
         if (publish)
             a.w.dec_slot[bh] = slot;
     }
-    bad = __syncthreads_or(bad);
+    bad = block_or(bad);
 
     // Token range and item count per (b, g): a contiguous run of groups per
     // thread, so the scan below needs one pass over the runs.
@@ -454,37 +450,37 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish,
 }
 
 // ---------------------------------------------------------------------------
-// Match of one unit: ring slots [split * kSlotsPerSplit, +kSlotsPerSplit) of
-// head bh.  Each LPR-lane row of a wave computes the squared distance of one
+// Match of one unit: ring slots [split * slots, +slots) of head bh, slots a
+// multiple of the rows per workgroup and at most UMAX rows per lane; m is
+// the current position.  Each LPR-lane row of a wave computes the squared distance of one
 // slot; the workgroup keeps the smallest
 //   key = float_bits(D) << 32 | (0xffffffff - p)
 // (non-negative floats order like their bits; equal D prefers larger p).
 // The result is valid in thread 0; sm holds kBlock/64 words of LDS.
-template <class T, int D>
-__device__ inline unsigned long long match_unit(const StepArgs &a, int split, int bh,
-                                                unsigned long long *sm)
+template <class T, int D, int UMAX>
+__device__ inline unsigned long long match_unit(const StepArgs &a, int split, int slots, int bh,
+                                                int m, unsigned long long *sm)
 {
     constexpr int EPL = T::EPL, LPR = D / EPL, RPB = kBlock / LPR;
-    constexpr int U = kSlotsPerSplit / RPB;
-    static_assert(U >= 1 && U * RPB == kSlotsPerSplit, "split shape");
+    constexpr int U = UMAX;
+    const int urt = slots / RPB;
     using S = typename T::S;
     const Shape &s = a.s;
     const int b = bh / s.Hq, h = bh - b * s.Hq;
     const int lane = threadIdx.x % LPR, row = threadIdx.x / LPR;
-    const int m = a.pos[b];
     const bool m_ok = m >= 0 && m < s.T;
 
     float qv[EPL];
     unpack<T>(load16((const S *)a.qtilde + b * a.qt_sb + h * a.qt_sh + lane * EPL), qv);
     const S *ring = (const S *)a.q_ring + (int64_t)bh * s.K * D + lane * EPL;
-    const int32_t *pr = a.pos_ring + (int64_t)b * s.K;
+    const int32_t *pr = a.pos_ring + ((int64_t)b * s.Hkv + h / s.G) * s.K;
 
     uint4 raw[U];
     int p[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int k = split * kSlotsPerSplit + u * RPB + row;
-        if (k < s.K) {
+        const int k = split * slots + u * RPB + row;
+        if (u < urt && k < s.K) {
             raw[u] = load16(ring + (int64_t)k * D);
             p[u] = pr[k];
         } else {
@@ -495,23 +491,25 @@ __device__ inline unsigned long long match_unit(const StepArgs &a, int split, in
     unsigned long long best = ~0ull;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        float rv[EPL];
-        unpack<T>(raw[u], rv);
-        float acc = 0.f;
+        if (u < urt) {  // uniform: rows past the unit are not computed
+            float rv[EPL];
+            unpack<T>(raw[u], rv);
+            float acc = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const float df = qv[e] - rv[e];
-            acc = fmaf(df, df, acc);
+            for (int e = 0; e < EPL; ++e) {
+                const float df = qv[e] - rv[e];
+                acc = fmaf(df, df, acc);
+            }
+            acc = row_sum<LPR>(acc);
+            const int pu = p[u];
+            const bool valid = m_ok && pu >= 0 && pu >= m - s.K && pu <= m - 1;
+            uint32_t bits = __float_as_uint(acc);
+            if (acc != acc)
+                bits = 0x7f800000u;  // NaN distance counts as +inf
+            const unsigned long long key =
+                ((unsigned long long)bits << 32) | (0xffffffffu - (uint32_t)pu);
+            best = umin64(best, valid ? key : ~0ull);
         }
-        acc = row_sum<LPR>(acc);
-        const int pu = p[u];
-        const bool valid = m_ok && pu >= 0 && pu >= m - s.K && pu <= m - 1;
-        uint32_t bits = __float_as_uint(acc);
-        if (acc != acc)
-            bits = 0x7f800000u;  // NaN distance counts as +inf
-        const unsigned long long key =
-            ((unsigned long long)bits << 32) | (0xffffffffu - (uint32_t)pu);
-        best = umin64(best, valid ? key : ~0ull);
     }
 #pragma unroll
     for (int off = LPR; off < 64; off <<= 1)
@@ -535,7 +533,10 @@ __global__ __launch_bounds__(kBlock) void match_kernel(StepArgs a)
 {
     __shared__ unsigned long long sm[kBlock / 64];
     const int bh = blockIdx.y;
-    const unsigned long long best = match_unit<T, D>(a, blockIdx.x, bh, sm);
+    constexpr int RPB = kBlock / (D / T::EPL);
+    const unsigned long long best =
+        match_unit<T, D, kSlotsPerSplit / RPB>(a, blockIdx.x, kSlotsPerSplit, bh,
+                                               a.pos[bh / a.s.Hq], sm);
     if (threadIdx.x == 0 && best != ~0ull)
         atomicMin(&a.w.keys[bh * kKeyStride], best);
 }
@@ -544,14 +545,14 @@ __global__ __launch_bounds__(kBlock) void match_kernel(StepArgs a)
 // Merge of one KV group.  The fold has a fixed shape, so a head's result
 // depends only on its own item list (not on the thread count that runs it):
 // the list is cut into A = items before the rectify split and Bt = the
-// rest; with more than kMergeDirect items each list is cut into at most P
-// equal segments folded left to right, then the segments in order.
+// rest; with more than MergeDirect<G>::N items each list is cut into at most
+// P equal segments folded left to right, then the segments in order.
 // R = C (+) A with C the cached summary of the matched slot (empty on a
 // miss); out = R (+) Bt.
 constexpr int kMergeBlock = 1024;
-// Groups with at most this many items are folded directly, one task per
-// (head, dim) output; larger groups use the segmented fold.
-constexpr int kMergeDirect = 16;
+// Bounded spin of a wait on another workgroup (polls of about a
+// microsecond each).
+constexpr int kSpinLimit = 1 << 18;
 
 template <class T, int D, int G>
 struct MergeShape {
@@ -564,11 +565,80 @@ struct MergeShape {
     static_assert(NTASK == 1024, "merge shape");
 };
 
+// Groups with at most N items are folded directly, one task per pair of
+// output dims with every load issued up front; larger groups use the
+// segmented fold.
+template <int G>
+struct MergeDirect {
+    static constexpr int N = G >= 8 ? 8 : 16;
+};
+
+// Partials of one KV group as the merge reads them.
+// PlainParts: the three-kernel arrays, item i of the group at global index
+// begin + i; every load is valid.
+template <int D, int G>
+struct PlainParts {
+    const float *o, *l;
+    int64_t begin;
+    __device__ bool lse(int i, int j, float &v) const
+    {
+        v = l[(begin + i) * G + j];
+        return true;
+    }
+    // N consecutive dims from d0 (N = 2 or a multiple of 4)
+    template <int N>
+    __device__ bool vec(int i, int j, int d0, float *v) const
+    {
+        const float *src = o + ((begin + i) * G + j) * D + d0;
+        if constexpr (N == 2) {
+            const float2 x = *reinterpret_cast<const float2 *>(src);
+            v[0] = x.x;
+            v[1] = x.y;
+        } else {
+#pragma unroll
+            for (int k = 0; k < N; k += 4) {
+                const float4 x = *reinterpret_cast<const float4 *>(src + k);
+                v[k] = x.x;
+                v[k + 1] = x.y;
+                v[k + 2] = x.z;
+                v[k + 3] = x.w;
+            }
+        }
+        return true;
+    }
+};
+
+// CoherentParts: the single launch's partials of the group (item i at
+// index i), written by other workgroups of the same launch and therefore
+// read device-coherently.
+template <int D, int G>
+struct CoherentParts {
+    const float *o, *l;
+    __device__ bool lse(int i, int j, float &v) const
+    {
+        v = ld_wt(l + (int64_t)i * G + j);
+        return true;
+    }
+    template <int N>
+    __device__ bool vec(int i, int j, int d0, float *v) const
+    {
+        const unsigned long long *src =
+            reinterpret_cast<const unsigned long long *>(o + ((int64_t)i * G + j) * D + d0);
+#pragma unroll
+        for (int k = 0; k < N; k += 2) {
+            const unsigned long long w = ld_wt(src + k / 2);
+            v[k] = __uint_as_float((uint32_t)w);
+            v[k + 1] = __uint_as_float((uint32_t)(w >> 32));
+        }
+        return true;
+    }
+};
+
 // Fold items [i0, i1) of head j into (l, o) for dims [d0, d0 + DPT), with
 // the loads of the next batch of four items in flight during each merge.
-template <int D, int G, int DPT, bool kWT>
-__device__ inline void fold_items(const StepArgs &a, int64_t begin, int i0, int i1, int j,
-                                  int d0, float &l, float *o)
+template <int D, int G, int DPT, class Src>
+__device__ inline void fold_items(const Src &src, int i0, int i1, int j, int d0, float &l,
+                                  float *o)
 {
     constexpr int NBUF = 4;
     // Two register buffers with compile-time indices (no scratch).
@@ -579,17 +649,8 @@ __device__ inline void fold_items(const StepArgs &a, int64_t begin, int i0, int 
             const int i = base + u;
             lb[u] = -INFINITY;
             if (i < i1) {
-                const int64_t ix = begin + i;
-                lb[u] = ld_f<kWT>(a.w.part_l + ix * G + j);
-                const float *src = a.w.part_o + (ix * G + j) * D + d0;
-#pragma unroll
-                for (int k = 0; k < DPT; k += 4) {
-                    const float4 v = ld_f4<kWT>(src + k);
-                    ob[u][k] = v.x;
-                    ob[u][k + 1] = v.y;
-                    ob[u][k + 2] = v.z;
-                    ob[u][k + 3] = v.w;
-                }
+                src.lse(i, j, lb[u]);
+                src.template vec<DPT>(i, j, d0, ob[u]);
             }
         }
     };
@@ -621,10 +682,9 @@ struct MergePairs {
 };
 
 // Cached summary C of each of this thread's pairs of group grp (empty on a
-// miss): from the planner's per-head codes (codes != nullptr) or from the
-// published plan.
-template <class T, int D, int G, int NT>
-__device__ inline void load_cached(const StepArgs &a, int grp, const int32_t *codes,
+// miss); slot_of(jj) is the matched ring slot of the group's head jj, or -1.
+template <class T, int D, int G, int NT, class SlotOf>
+__device__ inline void load_cached(const StepArgs &a, int grp, SlotOf &&slot_of,
                                    float (&c_l)[MergePairs<D, G, NT>::NPK],
                                    float (&c_o)[MergePairs<D, G, NT>::NPK][2])
 {
@@ -639,7 +699,7 @@ __device__ inline void load_cached(const StepArgs &a, int grp, const int32_t *co
         if (pt < MP::NPAIR) {
             const int jj = 2 * pt / D, dim = 2 * pt - jj * D;
             const int bh = b * s.Hq + g * G + jj;
-            const int slot = codes ? code_slot(codes[bh], s.r, s.K) : a.w.dec_slot[bh];
+            const int slot = slot_of(jj);
             if (slot >= 0) {
                 c_l[k] = a.lse_ring[(int64_t)bh * s.K + slot] * kLog2e;
                 const float2 v = *reinterpret_cast<const float2 *>(
@@ -652,12 +712,12 @@ __device__ inline void load_cached(const StepArgs &a, int grp, const int32_t *co
 }
 
 // Merge of group grp by the NT threads of the calling workgroup: cnt items
-// from item index `begin`, the group's range starting at gstart, with the
-// cached summaries (c_l, c_o) from load_cached.  Outputs are handled in pair
-// tasks, so the fold is the same for every NT.  The partials are read
-// device-coherently when kWT.  lds holds MergeShape::kFloats floats.
-template <class T, int D, int G, int NT, bool kWT>
-__device__ void merge_group(const StepArgs &a, int grp, int cnt, int64_t begin, int gstart,
+// read from src, the group's range starting at gstart, with the cached
+// summaries (c_l, c_o) from load_cached.  Outputs are handled in pair tasks,
+// so the fold is the same for every NT and every source.  lds holds
+// MergeShape::kFloats floats.
+template <class T, int D, int G, int NT, class Src>
+__device__ void merge_group(const StepArgs &a, int grp, int cnt, int gstart, const Src &src,
                             float *lds, const float (&c_l)[MergePairs<D, G, NT>::NPK],
                             const float (&c_o)[MergePairs<D, G, NT>::NPK][2])
 {
@@ -665,6 +725,7 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int64_t begin, 
     constexpr int P = M::P, DPT = M::DPT, TPS = M::TPS, SEG = M::SEG, NTASK = M::NTASK;
     constexpr int NPAIR = MergePairs<D, G, NT>::NPAIR;
     constexpr int NPK = MergePairs<D, G, NT>::NPK;
+    constexpr int MD = MergeDirect<G>::N;
     using S = typename T::S;
     const Shape &s = a.s;
     const int tid = threadIdx.x;
@@ -676,32 +737,21 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int64_t begin, 
     // list 0 = A (items [0, nA)), list 1 = Bt (items [nA, cnt)); each pair
     // folds into res[list][k].
     float res_l[2][NPK], res_o[2][NPK][2];
-    if (cnt <= kMergeDirect) {
+    if (cnt <= MD) {
         // Few items: each pair is folded over the items in order, with every
         // load issued before the first merge.
-        float li[NPK][kMergeDirect], oi[NPK][kMergeDirect][2];
+        float li[NPK][MD], oi[NPK][MD][2];
 #pragma unroll
         for (int k = 0; k < NPK; ++k) {
             const int pt = tid + k * NT;
             const int jj = 2 * pt / D, dim = 2 * pt - jj * D;
 #pragma unroll
-            for (int i = 0; i < kMergeDirect; ++i) {
+            for (int i = 0; i < MD; ++i) {
                 li[k][i] = -INFINITY;
                 oi[k][i][0] = oi[k][i][1] = 0.f;
                 if (pt < NPAIR && i < cnt) {
-                    const int64_t ix = begin + i;
-                    li[k][i] = ld_f<kWT>(a.w.part_l + ix * G + jj);
-                    const float *src = a.w.part_o + (ix * G + jj) * D + dim;
-                    if constexpr (kWT) {
-                        const unsigned long long w =
-                            ld_wt(reinterpret_cast<const unsigned long long *>(src));
-                        oi[k][i][0] = __uint_as_float((uint32_t)w);
-                        oi[k][i][1] = __uint_as_float((uint32_t)(w >> 32));
-                    } else {
-                        const float2 v = *reinterpret_cast<const float2 *>(src);
-                        oi[k][i][0] = v.x;
-                        oi[k][i][1] = v.y;
-                    }
+                    src.lse(i, jj, li[k][i]);
+                    src.template vec<2>(i, jj, dim, oi[k][i]);
                 }
             }
         }
@@ -709,7 +759,7 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int64_t begin, 
         for (int k = 0; k < NPK; ++k) {
             float la = -INFINITY, oa[2] = {0.f, 0.f}, lb = -INFINITY, ob[2] = {0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < kMergeDirect; ++i) {
+            for (int i = 0; i < MD; ++i) {
                 if (i < nA)
                     merge_into<2>(la, oa, li[k][i], oi[k][i]);
                 else if (i < cnt)
@@ -735,8 +785,8 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int64_t begin, 
                 for (int i = 0; i < DPT; ++i)
                     o[i] = 0.f;
                 if (seg < Pe)
-                    fold_items<D, G, DPT, kWT>(a, begin, l0 + seg * L / Pe,
-                                               l0 + (seg + 1) * L / Pe, j, d0, l, o);
+                    fold_items<D, G, DPT>(src, l0 + seg * L / Pe, l0 + (seg + 1) * L / Pe, j, d0,
+                                          l, o);
                 float *rec = lds + (j * P + seg) * SEG;
                 if ((task % TPS) == 0)
                     rec[D] = l;
@@ -803,8 +853,8 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int64_t begin, 
             *reinterpret_cast<float2 *>(a.o_ring + ri) = make_float2(rec_o[k][0], rec_o[k][1]);
             if (dim == 0)
                 a.lse_ring[(int64_t)bh * s.K + slot] = rec_l[k] * kLn2;
-            if (h == 0 && dim == 0)
-                a.pos_ring[(int64_t)b * s.K + slot] = e;
+            if (jj == 0 && dim == 0)
+                a.pos_ring[((int64_t)b * s.Hkv + g) * s.K + slot] = e;
         } else {
             *reinterpret_cast<float2 *>(a.w.rect_o + (int64_t)bh * D + dim) =
                 make_float2(rec_o[k][0], rec_o[k][1]);
@@ -827,9 +877,10 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(StepArgs a)
     if (cnt == 0)
         return;  // the planner wrote this group's outputs
     float c_l[MergePairs<D, G, kMergeBlock>::NPK], c_o[MergePairs<D, G, kMergeBlock>::NPK][2];
-    load_cached<T, D, G, kMergeBlock>(a, grp, nullptr, c_l, c_o);
-    merge_group<T, D, G, kMergeBlock, false>(a, grp, cnt, a.w.grp_begin[grp],
-                                             a.w.grp_start[grp], lds, c_l, c_o);
+    const int32_t *dec = a.w.dec_slot + (int64_t)grp * G;
+    load_cached<T, D, G, kMergeBlock>(a, grp, [&](int jj) { return dec[jj]; }, c_l, c_o);
+    const PlainParts<D, G> src{a.w.part_o, a.w.part_l, (int64_t)a.w.grp_begin[grp]};
+    merge_group<T, D, G, kMergeBlock>(a, grp, cnt, a.w.grp_start[grp], src, lds, c_l, c_o);
 }
 
 // ---------------------------------------------------------------------------
@@ -1009,51 +1060,62 @@ __device__ inline int group_of(const PlanTables &pt, int it, int NG)
     return __builtin_amdgcn_readfirstlane(lo - 1);
 }
 
-// Attention of work item `it` (of group grp) by the whole workgroup, ending
-// with its partial (o, log2-lse) per head in the workspace (written
-// device-coherently when kWT).  lds holds AttendShape::kFloats floats.
-// after_issue() runs once the item's first K/V and query loads are in
-// flight (extra requests whose latency should hide behind them).
-template <class T, int D, int G, bool kWT, class AfterIssue>
-__device__ inline void run_item(const StepArgs &a, const PlanTables &pt, int it, int grp,
-                                float *lds, AfterIssue &&after_issue)
+// Per-(request, KV group) state of the attention items: this lane's K/V
+// row pointers and its slice of the group's post-RoPE queries (pre-scaled
+// by scale * log2 e).  Built once per group, before the items are known.
+template <class T, int D, int G>
+struct ItemCtx {
+    using S = typename T::S;
+    static constexpr int EPL = T::EPL;
+    const S *kb, *vb;
+    float qr[G][EPL];
+    __device__ ItemCtx(const StepArgs &a, int b, int g)
+    {
+        const Shape &s = a.s;
+        const int lane = threadIdx.x % (D / EPL);
+        kb = (const S *)a.k + b * s.kv_sb + g * s.kv_sh + lane * EPL;
+        vb = (const S *)a.v + b * s.kv_sb + g * s.kv_sh + lane * EPL;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const float *qp = a.q + b * a.q_sb + (int64_t)(g * G + j) * a.q_sh + lane * EPL;
+#pragma unroll
+            for (int e4 = 0; e4 < EPL; e4 += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(qp + e4);
+                qr[j][e4 + 0] = v.x * s.qscale;
+                qr[j][e4 + 1] = v.y * s.qscale;
+                qr[j][e4 + 2] = v.z * s.qscale;
+                qr[j][e4 + 3] = v.w * s.qscale;
+            }
+        }
+    }
+};
+
+// Attention of one work item, tokens [t0, t1) of the group of ctx, head j
+// of the group attending from st[j], by the whole workgroup.  The partial
+// (o, log2-lse) of each head goes to sink(j, dim, o, lse) for every dim (lse
+// meaningful at dim 0).  lds holds AttendShape::kFloats floats.
+// after_issue() runs once the item's first K/V loads are in flight (extra
+// requests whose latency should hide behind them).
+template <class T, int D, int G, class Sink, class AfterIssue>
+__device__ inline void run_item(const StepArgs &a, const ItemCtx<T, D, G> &ctx, int t0, int t1,
+                                const int (&st)[G], float *lds, Sink &&sink,
+                                AfterIssue &&after_issue)
 {
     using L = AttendShape<T, D, G>;
     constexpr int EPL = L::EPL, LPR = L::LPR, RPB = L::RPB, NB = L::NB;
     constexpr int TPB = RPB * NB;  // tokens per block
-    using S = typename T::S;
     float *sm_m = lds;                  // [RPB][G]
     float *sm_l = lds + RPB * G;        // [RPB][G]
     float *sm_acc = lds + 2 * RPB * G;  // [RPB][G][D]
     const Shape &s = a.s;
     const int lane = threadIdx.x % LPR, row = threadIdx.x / LPR;
-    const int r_split = (a.mode == kPlanInit) ? 0 : s.r;
-    const int b = grp / s.Hkv, g = grp - b * s.Hkv;
-    int t0, t1;
-    RangeSplit(pt.gstart[grp], pt.gend[grp], r_split).item(it - pt.gbegin[grp], t0, t1);
     t0 = __builtin_amdgcn_readfirstlane(t0);
     t1 = __builtin_amdgcn_readfirstlane(t1);
-    const S *kb = (const S *)a.k + b * s.kv_sb + g * s.kv_sh + lane * EPL;
-    const S *vb = (const S *)a.v + b * s.kv_sb + g * s.kv_sh + lane * EPL;
+    const auto *kb = ctx.kb, *vb = ctx.vb;
+    const auto &qr = ctx.qr;
 
     KvBlock<T, G, EPL, NB> bufA, bufB;
     load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, t0, t1, row);
-
-    float qr[G][EPL];
-    int st[G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-        const float *qp = a.q + b * a.q_sb + (int64_t)(g * G + j) * a.q_sh + lane * EPL;
-#pragma unroll
-        for (int e4 = 0; e4 < EPL; e4 += 4) {
-            const float4 v = *reinterpret_cast<const float4 *>(qp + e4);
-            qr[j][e4 + 0] = v.x * s.qscale;
-            qr[j][e4 + 1] = v.y * s.qscale;
-            qr[j][e4 + 2] = v.z * s.qscale;
-            qr[j][e4 + 3] = v.w * s.qscale;
-        }
-        st[j] = __builtin_amdgcn_readfirstlane(code_start(pt.code[b * s.Hq + g * G + j]));
-    }
 
     after_issue();
 
@@ -1069,10 +1131,10 @@ __device__ inline void run_item(const StepArgs &a, const PlanTables &pt, int it,
     if constexpr (L::kScatter) {
         // Lane k keeps the running max / sum of head k % G in mrun[0],
         // lrun[0]; its token-start bound is that head's.
-        int my_st = st[0];
+        int my_st = __builtin_amdgcn_readfirstlane(st[0]);
 #pragma unroll
         for (int j = 1; j < G; ++j)
-            my_st = (lane % G == j) ? st[j] : my_st;
+            my_st = (lane % G == j) ? __builtin_amdgcn_readfirstlane(st[j]) : my_st;
         for (int base = t0; base < t1; base += 2 * TPB) {
             if (base + TPB < t1)
                 load_block<T, D, G, LPR, RPB, NB>(bufB, kb, vb, s.kv_st, base + TPB, t1, row);
@@ -1156,15 +1218,7 @@ __device__ inline void run_item(const StepArgs &a, const PlanTables &pt, int it,
             o = os / ls;
             Lg = sm_l[(RPB - 1) * G + j] + lg2(ls);
         }
-        if constexpr (kWT) {
-            st_wt(a.w.part_o + ((int64_t)it * G + j) * D + dim, o);
-            if (dim == 0)
-                st_wt(a.w.part_l + (int64_t)it * G + j, Lg);
-        } else {
-            a.w.part_o[((int64_t)it * G + j) * D + dim] = o;
-            if (dim == 0)
-                a.w.part_l[(int64_t)it * G + j] = Lg;
-        }
+        sink(j, dim, o, Lg);
     }
 }
 
@@ -1175,116 +1229,249 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
 {
     __shared__ float lds[AttendShape<T, D, G>::kFloats];
     extern __shared__ int32_t plan_lds[];
-    const PlanTables pt = plan_tables<false>(a, plan_lds, blockIdx.x == 0, a.w.keys);
-    const int NG = a.s.B * a.s.Hkv;
+    const PlanTables pt = plan_tables(a, plan_lds, blockIdx.x == 0);
+    const Shape &s = a.s;
+    const int NG = s.B * s.Hkv;
+    const int r_split = (a.mode == kPlanInit) ? 0 : s.r;
     for (int it = blockIdx.x; it < pt.total; it += gridDim.x) {
-        run_item<T, D, G, false>(a, pt, it, group_of(pt, it, NG), lds, [] {});
+        const int grp = group_of(pt, it, NG);
+        const int b = grp / s.Hkv, g = grp - b * s.Hkv;
+        int t0, t1, st[G];
+        RangeSplit(pt.gstart[grp], pt.gend[grp], r_split).item(it - pt.gbegin[grp], t0, t1);
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            st[j] = code_start(pt.code[b * s.Hq + g * G + j]);
+        float *po = a.w.part_o + (int64_t)it * G * D;
+        float *pl = a.w.part_l + (int64_t)it * G;
+        const ItemCtx<T, D, G> ctx(a, b, g);
+        run_item<T, D, G>(
+            a, ctx, t0, t1, st, lds,
+            [&](int j, int dim, float o, float lg) {
+                po[j * D + dim] = o;
+                if (dim == 0)
+                    pl[j] = lg;
+            },
+            [] {});
         __syncthreads();
     }
 }
 
-// Bounded spin of the grid barrier (polls of about a microsecond each).
-constexpr int kSpinLimit = 1 << 18;
-
-// Grid barrier of one single-launch step, in two levels so that no line is
-// both counted on and polled by many workgroups (same-line accesses
-// serialise at the memory side).  Workgroup i arrives on line
-// i mod kBarLines with a returning atomic; the counters only grow, so the
-// arrival that brings line c to (epoch + 1) times its workgroup count is the
-// line's last, and counts the line as complete.  The arrival that completes
-// the last line writes epoch + 1 to every release line; each workgroup
-// polls release line i mod kRelLines.  Returns false (in every thread) if
-// the wait timed out.
-__device__ inline bool grid_barrier(unsigned long long *sync, unsigned long long epoch)
+// Single-launch key words (see mac_internal.h): bits 31..24 of the low word
+// carry the tag's low byte instead of 0xff (positions are below 2^24).
+__device__ inline unsigned long long key_tagged(unsigned long long key, uint32_t tag8)
 {
-    int ok = 1;
-    if (threadIdx.x == 0) {
-        wait_vmem();  // this workgroup's match atomics have completed
-        const unsigned c = blockIdx.x % kBarLines;
-        const unsigned per = gridDim.x / kBarLines + (c < gridDim.x % kBarLines ? 1u : 0u);
-        const unsigned lines = gridDim.x < (unsigned)kBarLines ? gridDim.x : kBarLines;
-        const unsigned long long old = atomicAdd(&sync[kLineU64 * (1 + c)], 1ull);
-        if (old + 1 == (epoch + 1) * per) {
-            const unsigned long long done = atomicAdd(&sync[kLineU64 * (1 + kBarLines)], 1ull);
-            if (done + 1 == (epoch + 1) * lines)
-                for (int i = 0; i < kRelLines; ++i)
-                    st_wt(&sync[kLineU64 * (2 + kBarLines + i)], epoch + 1);
-        }
-        const unsigned long long *rel = &sync[kLineU64 * (2 + kBarLines + blockIdx.x % kRelLines)];
-        int it = 0;
-        while (ld_wt(rel) < epoch + 1 && ++it < kSpinLimit)
-            __builtin_amdgcn_s_sleep(1);
-        ok = it < kSpinLimit;
-    }
-    return __syncthreads_and(ok);
+    return (key & ~0xff000000ull) | ((unsigned long long)tag8 << 24);
 }
 
-// The whole decode step in one launch; the grid must be resident at once.
-//   1. match units (split, head) strided over the grid, atomic-min into the
-//      key buffer of this launch's epoch; the other buffer is reset for the
-//      next launch;
-//   2. grid barrier; workgroup 0 advances the epoch;
-//   3. every workgroup plans from the keys; items strided over the grid;
-//   4. after its item's partials have completed, a workgroup counts the
-//      item on its group; the one that completes the group merges it (with
-//      the fused append) and resets the group's counter.
+// Wave 0 of a workgroup polls the nkw key words of its group until all hold
+// tag8, leaving the untagged keys of the match units in s_keys[upg].
+// Returns false if the wait gave up.
+__device__ inline bool poll_keys(const StepArgs &a, const unsigned long long *kw, uint32_t tag8,
+                                 unsigned long long *s_keys)
+{
+    const int lane = threadIdx.x & 63;
+    for (int spin = 0;; ++spin) {
+        bool fresh = true;
+        for (int u = lane; u < a.nkw; u += 64) {
+            const unsigned long long w = ld_wt(kw + u);
+            fresh &= ((uint32_t)(w >> 24) & 0xffu) == tag8;
+            if (u < a.upg)
+                s_keys[u] = w | 0xff000000ull;
+        }
+        if (__all(fresh))
+            return true;
+        if (spin >= kSpinLimit)
+            return false;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// Key of single-launch match unit u of the group whose first head is bh0
+// (~0 for a dummy word u >= upg); valid in thread 0.
+template <class T, int D>
+__device__ __forceinline__ unsigned long long single_unit_key(const StepArgs &a, int u, int bh0,
+                                                              int m, unsigned long long *sm)
+{
+    if (u >= a.upg)
+        return ~0ull;
+    const int j = u / a.nsplit, split = u - j * a.nsplit;
+    constexpr int RPB = kBlock / (D / T::EPL);
+    return match_unit<T, D, single_slots(sizeof(typename T::S), D) / RPB>(
+        a, split, a.unit_slots, bh0 + j, m, sm);
+}
+
+// Thread 0's key, tagged, to word u of the group's kKeyReps copies; then a
+// workgroup barrier (the match's LDS is reused).
+__device__ __forceinline__ void store_unit_key(unsigned long long *kw, int64_t rep_stride, int u,
+                                               unsigned long long key, uint32_t tag8)
+{
+    if (threadIdx.x < 64) {
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)key);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(key >> 32));
+        key = ((unsigned long long)hi << 32) | lo;
+        if (threadIdx.x < kKeyReps)
+            st_wt(kw + threadIdx.x * rep_stride + u, key_tagged(key, tag8));
+    }
+    __syncthreads();
+}
+
+// The whole decode step in one launch of a.wpg workgroups per KV group, all
+// resident at once.  Workgroup `loc` of group grp:
+//   1. reads the done counter (the launch's epoch and key tag);
+//   2. runs match units loc, loc + wpg, ... of the group (unit u: head
+//      u / nsplit, unit_slots ring slots of split u mod nsplit)
+//      and stores each key, tagged, in kKeyReps copies; words past the units
+//      are tagged dummies;
+//   3. polls the group's key words (copy loc mod kKeyReps) until all carry
+//      the tag, and plans the group: decisions, range [s_g, m], items;
+//   4. runs items loc, loc + wpg, ...: stores the partials, waits for the
+//      stores to complete and counts the item on the group's counter; the
+//      workgroup that completes the group merges it (with the fused append),
+//      resets the counter and counts the group on the done counter.
 template <class T, int D, int G>
 __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
 {
     using AS = AttendShape<T, D, G>;
     using MS = MergeShape<T, D, G>;
+    using MP = MergePairs<D, G, kBlock>;
     constexpr int kFloats = AS::kFloats > MS::kFloats ? AS::kFloats : MS::kFloats;
     __shared__ float lds[kFloats];
+    __shared__ unsigned long long s_keys[kMaxSingleUnits];
+    __shared__ int s_code[G];
     __shared__ int s_last;
-    extern __shared__ int32_t plan_lds[];
     const Shape &s = a.s;
-    const int BH = s.B * s.Hq, NG = s.B * s.Hkv;
+    const int NG = s.B * s.Hkv;
+    const int grp = blockIdx.x / a.wpg, loc = blockIdx.x - grp * a.wpg;
+    const int b = grp / s.Hkv, g = grp - b * s.Hkv;
     unsigned long long *sync = a.w.sync;
-    const unsigned long long epoch = ld_wt(&sync[kSyncEpoch]);
-    unsigned long long *keys = a.w.keys + (epoch & 1) * BH * kKeyStride;
-    unsigned long long *keys_next = a.w.keys + ((epoch + 1) & 1) * BH * kKeyStride;
+    // Read before any store of the launch, so both are scalar loads.  The
+    // done counter is read with a plain load: its value from earlier
+    // launches is visible at kernel start, and the increments of this
+    // launch's groups leave floor(done / 2^s) unchanged until this
+    // workgroup's own group completes.
+    const int e = a.pos[b];
+    const unsigned long long done = sync[kSyncDone];
+    const int64_t rep_stride = (int64_t)NG * a.nkw;
+    unsigned long long *kw = a.w.skeys + (int64_t)grp * a.nkw;
 
-    const int units = a.nsplit * BH;
-    for (int u = blockIdx.x; u < units; u += gridDim.x) {
-        const int bh = u / a.nsplit, split = u - bh * a.nsplit;
-        const unsigned long long best =
-            match_unit<T, D>(a, split, bh, reinterpret_cast<unsigned long long *>(lds));
-        if (threadIdx.x == 0) {
-            if (best != ~0ull)
-                atomicMin(&keys[bh * kKeyStride], best);
-            if (split == 0)
-                keys_next[bh * kKeyStride] = ~0ull;
+    // Match units loc, loc + wpg, ... (loc < wpg <= nkw: the first exists).
+    const int bh0 = b * s.Hq + g * G;
+    unsigned long long *klds = reinterpret_cast<unsigned long long *>(lds);
+    const unsigned long long key0 = single_unit_key<T, D>(a, loc, bh0, e, klds);
+    const uint32_t tag8 = (uint32_t)((done >> a.done_shift) + 1) & 0xffu;
+    store_unit_key(kw, rep_stride, loc, key0, tag8);
+    for (int u = loc + a.wpg; u < a.nkw; u += a.wpg)
+        store_unit_key(kw, rep_stride, u, single_unit_key<T, D>(a, u, bh0, e, klds), tag8);
+
+    // The group's query slice and K/V row pointers do not depend on the
+    // plan: their loads are in flight during the poll.
+    const ItemCtx<T, D, G> ctx(a, b, g);
+    bool ok = true;
+    if (threadIdx.x < 64)
+        ok = poll_keys(a, kw + (loc % kKeyReps) * rep_stride, tag8, s_keys);
+    ok = block_and(ok);
+
+    // Plan of the group.  Head j's key is the minimum over its units (exact
+    // in any order), taken by the 64 / G lanes j * 64 / G, ... of wave 0;
+    // the first of them decides head j.  Every thread then reads the codes
+    // from LDS.
+    const bool e_ok = e >= 0 && e < s.T;
+    if (threadIdx.x < 64) {
+        constexpr int LPH = 64 / G;
+        const int j = threadIdx.x / LPH, sub = threadIdx.x % LPH;
+        unsigned long long key = ~0ull;
+        for (int u = sub; u < a.nsplit; u += LPH)
+            key = umin64(key, s_keys[j * a.nsplit + u]);
+#pragma unroll
+        for (int off = 1; off < LPH; off <<= 1)
+            key = umin64(key, shfl_xor_u64(key, off));
+        if (sub == 0) {
+            const Decision dc = decide(a, key, e_ok);
+            s_code[j] = dc.hit ? dc.p - s.r + 1 : kMissCode;
+            if (loc == 0) {
+                const int bh = b * s.Hq + g * G + j;
+                if (a.match_p)
+                    a.match_p[bh] = dc.hit ? dc.p : -1;
+                if (a.match_d2)
+                    a.match_d2[bh] = dc.d2;
+            }
         }
-        __syncthreads();
     }
-    if (!grid_barrier(sync, epoch) && threadIdx.x == 0)
-        atomicOr(&sync[kSyncSticky], (unsigned long long)MAC_DEV_SYNC_TIMEOUT);
-    if (blockIdx.x == 0 && threadIdx.x == 0)
-        st_wt(&sync[kSyncEpoch], epoch + 1);  // every workgroup read the epoch before arriving
+    __syncthreads();
+    int st[G];
+    int sg = e;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        st[j] = code_start(s_code[j]);
+        sg = st[j] < sg ? st[j] : sg;
+    }
+    if (grp == 0 && loc == 0 && threadIdx.x == 0) {
+        int bad = 0;
+        for (int bb = 0; bb < s.B; ++bb) {
+            const int eb = a.pos[bb];
+            bad |= !(eb >= 0 && eb < s.T);
+        }
+        a.w.ctrl[kCtrlStatus] = bad ? MAC_DEV_BAD_POSITION : 0;
+    }
+    const RangeSplit rs(e_ok ? sg : 0, e_ok ? e : 0, s.r);
+    const int n = e_ok ? rs.n : 0;
+    const unsigned long long done_add =
+        grp == 0 ? (1ull << a.done_shift) - (unsigned long long)NG + 1ull : 1ull;
 
-    const PlanTables pt = plan_tables<true>(a, plan_lds, blockIdx.x == 0, keys);
-    using MP = MergePairs<D, G, kBlock>;
-    for (int it = blockIdx.x; it < pt.total; it += gridDim.x) {
-        const int grp = group_of(pt, it, NG);
+    float *gpo = a.w.part_o + (int64_t)grp * kItemsPerGroupMax * G * D;
+    float *gpl = a.w.part_l + (int64_t)grp * kItemsPerGroupMax * G;
+    uint32_t *counter = a.w.grp_sync + (int64_t)grp * kGrpStride;
+    for (int it = loc; it < n; it += a.wpg) {
+        int t0, t1;
+        rs.item(it, t0, t1);
+        float *po = gpo + (int64_t)it * G * D, *pl = gpl + (int64_t)it * G;
         // The cached summaries are requested with the item's first loads, in
         // case this workgroup completes the group and merges it.
         float c_l[MP::NPK], c_o[MP::NPK][2];
-        run_item<T, D, G, true>(a, pt, it, grp, lds,
-                                [&] { load_cached<T, D, G, kBlock>(a, grp, pt.code, c_l, c_o); });
+        run_item<T, D, G>(
+            a, ctx, t0, t1, st, lds,
+            [&](int j, int dim, float o, float lg) {
+                st_wt(po + j * D + dim, o);
+                if (dim == 0)
+                    st_wt(pl + j, lg);
+            },
+            [&] {
+                load_cached<T, D, G, kBlock>(
+                    a, grp, [&](int jj) { return code_slot(s_code[jj], s.r, s.K); }, c_l, c_o);
+            });
         wait_vmem();  // this wave's partial stores have completed
         __syncthreads();
         if (threadIdx.x == 0)
-            s_last = atomicAdd(&a.w.grp_sync[(int64_t)grp * kGrpStride], 1u) ==
-                     (uint32_t)(pt.gcount[grp] - 1);
+            s_last = atomicAdd(counter, 1u) == (uint32_t)(n - 1);
         __syncthreads();
         if (s_last) {
-            merge_group<T, D, G, kBlock, true>(a, grp, pt.gcount[grp], pt.gbegin[grp],
-                                               pt.gstart[grp], lds, c_l, c_o);
-            if (threadIdx.x == 0)
-                st_wt(&a.w.grp_sync[(int64_t)grp * kGrpStride], 0u);
+            const CoherentParts<D, G> src{gpo, gpl};
+            merge_group<T, D, G, kBlock>(a, grp, n, sg, src, lds, c_l, c_o);
+            if (threadIdx.x == 0) {
+                st_wt(counter, 0u);
+                atomicAdd(&sync[kSyncDone], done_add);
+            }
         }
         __syncthreads();
     }
+    if (n == 0 && loc == 0) {
+        // Position out of range: NaN outputs, nothing appended.
+        for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
+            const int bh = b * s.Hq + g * G + idx / D;
+            if (a.out)
+                a.out[(int64_t)bh * D + idx % D] = NAN;
+            a.w.rect_o[(int64_t)bh * D + idx % D] = 0.f;
+            if (idx % D == 0) {
+                if (a.out_lse)
+                    a.out_lse[bh] = NAN;
+                a.w.rect_l[bh] = -INFINITY;
+            }
+        }
+        if (threadIdx.x == 0)
+            atomicAdd(&sync[kSyncDone], done_add);
+    }
+    if (!ok && threadIdx.x == 0)
+        atomicOr(&sync[kSyncSticky], (unsigned long long)MAC_DEV_SYNC_TIMEOUT);
 }
 
 // ---------------------------------------------------------------------------
@@ -1306,8 +1493,8 @@ __global__ __launch_bounds__(D) void append_kernel(StepArgs a, int32_t pos_offse
     a.o_ring[ri] = a.w.rect_o[(int64_t)bh * D + dim];
     if (dim == 0)
         a.lse_ring[(int64_t)bh * s.K + slot] = a.w.rect_l[bh] * kLn2;
-    if (h == 0 && dim == 0)
-        a.pos_ring[(int64_t)b * s.K + slot] = t;
+    if (h % s.G == 0 && dim == 0)
+        a.pos_ring[((int64_t)b * s.Hkv + h / s.G) * s.K + slot] = t;
 }
 
 template <class S>
@@ -1317,7 +1504,8 @@ __global__ void ring_reset_kernel(int64_t n_q, S *__restrict__ q_ring,
                                   int32_t *__restrict__ pos_ring,
                                   int32_t *__restrict__ ctrl, int64_t n_keys,
                                   unsigned long long *__restrict__ keys, int64_t n_sync,
-                                  unsigned long long *__restrict__ sync, int64_t n_gs,
+                                  unsigned long long *__restrict__ sync, int64_t n_tag,
+                                  unsigned long long *__restrict__ skeys, int64_t n_gs,
                                   uint32_t *__restrict__ grp_sync)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -1334,6 +1522,9 @@ __global__ void ring_reset_kernel(int64_t n_q, S *__restrict__ q_ring,
         keys[i * kKeyStride] = ~0ull;
     for (int64_t i = i0; i < n_sync; i += stride)
         sync[i] = i == kSyncMagicWord ? kSyncMagic : 0ull;
+    // Tagged words: no stale word may hold a tag of the restarted epochs.
+    for (int64_t i = i0; i < n_tag; i += stride)
+        skeys[i] = 0;
     for (int64_t i = i0; i < n_gs; i += stride)
         grp_sync[i] = 0;
     if (i0 < 16)
@@ -1461,20 +1652,13 @@ hipError_t launch_attend(const StepArgs &a, hipStream_t st)
     return hipGetLastError();
 }
 
-// Grid of the single-launch step: the workgroups resident at once (the
-// grid barrier needs all of them running), never more than the larger of
-// the match units and the item bound.
+// Grid of the single-launch step: a.wpg workgroups per KV group (the host
+// sized wpg to what is resident at once).
 template <class T, int D, int G>
 static void step_go_g(const StepArgs &a, hipStream_t st)
 {
-    const size_t lds = plan_lds_bytes(a.s.B, a.s.Hq, a.s.Hkv);
-    const void *fn = (const void *)step_kernel<T, D, G>;
-    int64_t grid = (int64_t)device_cu_count() * resident_per_cu(fn, lds);
-    const int64_t units = (int64_t)a.nsplit * a.s.B * a.s.Hq;
-    const int64_t need = units > a.max_items ? units : a.max_items;
-    if (grid > need)
-        grid = need;
-    hipLaunchKernelGGL((step_kernel<T, D, G>), dim3((int)grid), dim3(kBlock), lds, st, a);
+    const int grid = a.wpg * a.s.B * a.s.Hkv;
+    hipLaunchKernelGGL((step_kernel<T, D, G>), dim3(grid), dim3(kBlock), 0, st, a);
 }
 
 template <class T, int D>
@@ -1494,6 +1678,30 @@ static void step_go(const StepArgs &a, hipStream_t st)
         step_go_g<T, D, 8>(a, st);
         break;
     }
+}
+
+template <class T, int D>
+static void step_resident_go(const Shape &s, int *n)
+{
+    const void *fn = s.G == 1   ? (const void *)step_kernel<T, D, 1>
+                     : s.G == 2 ? (const void *)step_kernel<T, D, 2>
+                     : s.G == 4 ? (const void *)step_kernel<T, D, 4>
+                                : (const void *)step_kernel<T, D, 8>;
+    *n = device_cu_count() * resident_per_cu(fn, 0);
+}
+
+int step_resident_workgroups(const Shape &s)
+{
+    int n = 0;
+    if (s.dtype == MAC_DTYPE_BF16 && s.D == 128)
+        step_resident_go<BF16, 128>(s, &n);
+    else if (s.dtype == MAC_DTYPE_BF16 && s.D == 64)
+        step_resident_go<BF16, 64>(s, &n);
+    else if (s.dtype == MAC_DTYPE_F32 && s.D == 128)
+        step_resident_go<F32, 128>(s, &n);
+    else
+        step_resident_go<F32, 64>(s, &n);
+    return n;
 }
 
 hipError_t launch_step(const StepArgs &a, hipStream_t st)
@@ -1556,25 +1764,26 @@ hipError_t launch_append(const StepArgs &a, int32_t pos_offset, hipStream_t st)
 
 hipError_t launch_ring_reset(const Shape &s, void *q_ring, float *o_ring,
                              float *lse_ring, int32_t *pos_ring, const WsPtrs &w,
-                             hipStream_t st)
+                             int64_t n_tag, hipStream_t st)
 {
-    const int64_t n_keys = 2 * (int64_t)s.B * s.Hq;  // both key buffers
+    const int64_t n_keys = (int64_t)s.B * s.Hq;
     const int64_t n_sync = kSyncWords;
-    const int64_t n_gs = (int64_t)s.B * s.Hkv * kGrpStride;
     const int64_t n_q = (int64_t)s.B * s.Hq * s.K * s.D;
     const int64_t n_l = (int64_t)s.B * s.Hq * s.K;
-    const int64_t n_p = (int64_t)s.B * s.K;
-    int64_t blocks = (n_q + 255) / 256;
+    const int64_t n_p = (int64_t)s.B * s.Hkv * s.K;
+    const int64_t n_gs = w.grp_sync ? (int64_t)s.B * s.Hkv * kGrpStride : 0;
+    const int64_t n_max = n_q > n_tag ? n_q : n_tag;
+    int64_t blocks = (n_max + 255) / 256;
     if (blocks > 4096)
         blocks = 4096;
     if (s.dtype == MAC_DTYPE_BF16)
         hipLaunchKernelGGL(ring_reset_kernel<uint16_t>, dim3((int)blocks), dim3(256), 0, st,
                            n_q, (uint16_t *)q_ring, o_ring, n_l, lse_ring, n_p, pos_ring, w.ctrl,
-                           n_keys, w.keys, n_sync, w.sync, n_gs, w.grp_sync);
+                           n_keys, w.keys, n_sync, w.sync, n_tag, w.skeys, n_gs, w.grp_sync);
     else
         hipLaunchKernelGGL(ring_reset_kernel<float>, dim3((int)blocks), dim3(256), 0, st, n_q,
                            (float *)q_ring, o_ring, n_l, lse_ring, n_p, pos_ring, w.ctrl, n_keys,
-                           w.keys, n_sync, w.sync, n_gs, w.grp_sync);
+                           w.keys, n_sync, w.sync, n_tag, w.skeys, n_gs, w.grp_sync);
     return hipGetLastError();
 }
 

@@ -94,7 +94,7 @@ def algorithmic_bytes(cfg, match_p, m):
     B, H, Hkv, G, d = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.group, cfg.head_dim
     e = cfg.elem_bytes
     K_valid = min(cfg.ring_k, cfg.ctx)
-    match = B * H * K_valid * d * e + B * K_valid * 4 + B * H * d * e
+    match = B * H * K_valid * d * e + B * Hkv * K_valid * 4 + B * H * d * e
     start = np.where(match_p >= 0, np.maximum(0, match_p - cfg.band_r + 1), 0)
     s_g = start.reshape(B, Hkv, G).min(axis=2)
     span = (m[:, None] - s_g + 1).astype(np.int64)
@@ -104,7 +104,7 @@ def algorithmic_bytes(cfg, match_p, m):
     # The merge reads the cached summary of every hit head and writes the
     # output and its lse (split-KV partials are overhead, not credited).
     merge = hits * (d + 1) * 4 + B * H * (d + 1) * 4
-    append = B * H * (d * e + (d + 1) * 4) + B * 4
+    append = B * H * (d * e + (d + 1) * 4) + B * Hkv * 4
     full_kv = int((m + 1).sum()) * Hkv * d * e * 2
     return dict(match=match, plan=0, attend=attend, merge=merge, append=append, kv=kv,
                 full_kv=full_kv,
@@ -210,7 +210,7 @@ def main():
                  q_ring=torch.zeros((B, H, R, d), dtype=K0.dtype, device=dev),
                  o_ring=torch.zeros((B, H, R, d), device=dev),
                  lse_ring=torch.zeros((B, H, R), device=dev),
-                 pos_ring=torch.zeros((B, R), dtype=torch.int32, device=dev),
+                 pos_ring=torch.zeros((B, cfg.n_kv_heads, R), dtype=torch.int32, device=dev),
                  ws=torch.empty(wsb, dtype=torch.uint8, device=dev),
                  out=torch.empty((B, H, d), device=dev))
         layers.append(L)

@@ -68,10 +68,14 @@ enum { MAC_THRESH_ONE_MINUS_TAU = 0, MAC_THRESH_TAU = 1 };
  *   MAC_FLAG_SPLIT_STAGES: mac_decode_step always runs match, plan +
  *   attention and merge as three kernels.
  *   MAC_FLAG_SINGLE_LAUNCH: mac_decode_step always runs the step as one
- *   launch.
+ *   launch (MAC_ERR_UNSUPPORTED from mac_init_rings when kv_capacity exceeds
+ *   2^24, when a KV group's ring match needs more than 256 units of up to
+ *   256 slots, or when the device cannot hold one workgroup per KV group
+ *   resident).
  * With neither of the last two, the step is one launch when a layer has at
- * most 16 KV groups (batch * n_kv_heads), where the step is bound by
- * latency, and three kernels otherwise, where it is bound by bandwidth.
+ * most 16 KV groups (batch * n_kv_heads) and the shape is one the single
+ * launch handles, where the step is bound by latency, and three kernels
+ * otherwise, where it is bound by bandwidth.
  * Both forms give the same results bit for bit. */
 enum { MAC_FLAG_FUSED_APPEND = 1, MAC_FLAG_SPLIT_STAGES = 2, MAC_FLAG_SINGLE_LAUNCH = 4 };
 
@@ -107,8 +111,11 @@ typedef struct mac_params {
  *   q_ring   [B, Hq, K, d] kv_dtype  pre-RoPE queries of the last K positions
  *   o_ring   [B, Hq, K, d] fp32      rectified summaries: normalised output
  *   lse_ring [B, Hq, K]    fp32      rectified summaries: ln Z (-inf = empty)
- *   pos_ring [B, K]        int32     position held by each slot (-1 = empty)
- * Slot of position t is t mod K.  Sizes: mac_ring_bytes(). */
+ *   pos_ring [B, Hkv, K]   int32     position held by each slot of the rings
+ *                                   of KV group g's query heads (-1 = empty)
+ * Slot of position t is t mod K.  The position ring is kept per KV group
+ * so that each group's rings are written only by that group's work.
+ * Sizes: mac_ring_bytes(). */
 typedef struct mac_rings {
     void *q_ring;
     float *o_ring;
@@ -159,12 +166,13 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
  *   match_d2[B, Hq] fp32 or NULL   squared distance of the nearest candidate
  *                                  (+inf when the window is empty)
  * Match, amend and complete run on main_stream as one kernel launch whose
- * workgroups are all resident at once (they meet at a grid barrier after
- * the match), or as three kernels (match, plan + attention, merge); see
- * MAC_FLAG_SPLIT_STAGES for the choice.  Other work that holds compute units while the
- * launch waits for residency only delays it; a launch that cannot get all
- * its workgroups resident within about a second stops waiting and latches
- * MAC_DEV_SYNC_TIMEOUT.  The rectify-append of the rings runs as another
+ * workgroups are all resident at once (the workgroups of each KV group hand
+ * match keys and partial summaries to each other inside the launch), or as
+ * three kernels (match, plan + attention, merge); see MAC_FLAG_SPLIT_STAGES
+ * for the choice.  The single launch needs kv_capacity <= 2^24.  Other work
+ * that holds compute units while the launch waits for residency only delays
+ * it; a launch that cannot get all its workgroups resident within about a
+ * second stops waiting and latches MAC_DEV_SYNC_TIMEOUT.  The rectify-append of the rings runs as another
  * kernel on aux_stream (main_stream if NULL or equal), ordered after the
  * merge by an event; the next call on the same handle waits for it.  With
  * MAC_FLAG_FUSED_APPEND the merge writes the rings itself and aux_stream is

@@ -43,7 +43,7 @@ class Layer:
         self.q_ring = torch.zeros((B, H, R, d), dtype=st, device=DEV)
         self.o_ring = torch.zeros((B, H, R, d), dtype=torch.float32, device=DEV)
         self.lse_ring = torch.zeros((B, H, R), dtype=torch.float32, device=DEV)
-        self.pos_ring = torch.zeros((B, R), dtype=torch.int32, device=DEV)
+        self.pos_ring = torch.zeros((B, cfg.n_kv_heads, R), dtype=torch.int32, device=DEV)
         self.ws_bytes = mac.mac_workspace_bytes(self.p)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=DEV)
         self.qt = qt

@@ -56,7 +56,7 @@ def test_workspace_and_ring_sizes(lib):
     assert ws > 0
     # 2 x 32 heads x 1024 slots x 128 dims: bf16 query ring, fp32 summaries.
     assert mac.mac_ring_bytes(p) == (2 * 32 * 1024 * 128 * 2, 2 * 32 * 1024 * 128 * 4,
-                                     2 * 32 * 1024 * 4, 2 * 1024 * 4)
+                                     2 * 32 * 1024 * 4, 2 * 8 * 1024 * 4)
     # The split-KV partials are bounded per KV group, so the workspace does
     # not grow with the KV capacity.
     assert mac.mac_workspace_bytes(_params(kv_capacity=65536)) == ws

@@ -95,7 +95,7 @@ def _lockstep(oracle_lib, cfg, layer=None, heads=None, n_warm=None, want_ring=Tr
             stats["diverged"] += 1
             continue
         if want_ring:
-            assert np.array_equal(pr[b], o["ring_pos"]), (b, h)
+            assert np.array_equal(pr[b, h // cfg.group], o["ring_pos"]), (b, h)
             np.testing.assert_array_equal(qr[b, h], o["ring_q"])
             fin = np.isfinite(o["ring_lse"])
             assert np.array_equal(np.isfinite(lr[b, h]), fin)
