@@ -366,14 +366,12 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
         const int NG = s.B * s.Hkv;
         const int resident = step_resident_workgroups(s);
         h->wpg = resident / NG < kGroupWorkgroups ? resident / NG : kGroupWorkgroups;
-        // Match units: about one per workgroup, whole row loads, at most
-        // single_slots slots each.
-        const int rpl = match_rows_per_load(elem_bytes(s.dtype), s.D);
+        // Match units: the small size when one unit per workgroup covers
+        // the group's ring rows with it, the large size otherwise.
+        const int eb = elem_bytes(s.dtype);
         const int64_t want = h->wpg > 0 ? ((int64_t)s.G * s.K + h->wpg - 1) / h->wpg : 1;
-        int64_t us = (want + rpl - 1) / rpl * rpl;
-        const int smax = single_slots(elem_bytes(s.dtype), s.D);
-        us = us > smax ? smax : us;
-        h->unit_slots = (int)us;
+        h->unit_slots = want <= step_unit_slots(eb, s.D, false) ? step_unit_slots(eb, s.D, false)
+                                                                 : step_unit_slots(eb, s.D, true);
         h->nsplit = (s.K + h->unit_slots - 1) / h->unit_slots;
         h->upg = s.G * h->nsplit;
         h->nkw = h->upg > h->wpg ? h->upg : h->wpg;

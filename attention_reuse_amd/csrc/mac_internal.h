@@ -11,11 +11,16 @@ namespace mac {
 // C tokens, C = kChunkMin * 2^k the smallest such that the range spans at
 // most kMaxItemsPerGroup grid cells.  C depends only on the group's own
 // range, so a head that misses sees exactly the items of a full decode.
-constexpr int kChunkMinShift = 7;
+constexpr int kChunkMinShift = 6;
 constexpr int kChunkMin = 1 << kChunkMinShift;
 constexpr int kMaxItemsPerGroup = 128;
 // Ring slots scanned by one match workgroup.
 constexpr int kSlotsPerSplit = 64;
+// Single launch: workgroups 0 .. kSpecMax-1 of a group may request the K/V
+// of their item before the match has decided the group's range: the item
+// they would run if the range kept the span it had at the group's previous
+// step, so that the data is in flight during the match.
+constexpr int kSpecMax = 24;
 // Workgroup size of the match and attention kernels.
 constexpr int kBlock = 256;
 
@@ -40,17 +45,28 @@ constexpr int kItemsPerGroupMax = kMaxItemsPerGroup + 2;
 // before its own group can complete.
 constexpr int kKeyReps = 4;
 // Ring rows one 256-thread workgroup loads per instruction (one row per
-// 16-byte lane group), and the largest match unit of the single launch: 16
-// such loads per lane, at most 256 slots.  The host sizes the units so that
-// a group's ring rows spread over its workgroups.
+// 16-byte lane group).
 __host__ __device__ constexpr int match_rows_per_load(int elem_bytes, int D)
 {
     return 4096 / (elem_bytes * D);
 }
+// Match units of the single launch come in two sizes: `large` ones of 16
+// loads per lane (at most 256 slots) and small ones of 4 (at most 64
+// slots).  Each size is its own kernel instantiation, so every load of a
+// unit is issued without a branch.
+__host__ __device__ constexpr int step_rows(int elem_bytes, int D, bool large)
+{
+    return (large ? 16 : 4) * match_rows_per_load(elem_bytes, D) <= (large ? 256 : 64)
+               ? (large ? 16 : 4)
+               : (large ? 256 : 64) / match_rows_per_load(elem_bytes, D);
+}
+__host__ __device__ constexpr int step_unit_slots(int elem_bytes, int D, bool large)
+{
+    return step_rows(elem_bytes, D, large) * match_rows_per_load(elem_bytes, D);
+}
 __host__ __device__ constexpr int single_slots(int elem_bytes, int D)
 {
-    return 16 * match_rows_per_load(elem_bytes, D) < 256 ? 16 * match_rows_per_load(elem_bytes, D)
-                                                         : 256;
+    return step_unit_slots(elem_bytes, D, true);
 }
 // Match units per group of the single launch are at most this many (the
 // host falls back to three kernels beyond).
@@ -60,8 +76,11 @@ constexpr int kMaxSingleUnits = 256;
 // dummy word, so that every workgroup's tag read precedes its group's
 // completion.
 constexpr int kGroupWorkgroups = 64;
-// Per-group arrival counters of the single launch, kGrpStride words apart.
+// Per-group line of the single launch, kGrpStride words apart: word 0 the
+// arrival counter, word kGrpSpan the span of the group's range at its last
+// step (0 = none yet).
 constexpr int kGrpStride = 16;
+constexpr int kGrpSpan = 1;
 // Largest position the tagged keys encode.
 constexpr int32_t kSingleMaxPositions = 1 << 24;
 // Synchronisation line of the workspace (64-bit words).
@@ -96,11 +115,14 @@ struct RangeSplit {
         return cs + kChunkMinShift;
     }
     __host__ __device__ static int chunk_for(int s_, int e_) { return 1 << chunk_shift_for(s_, e_); }
-    __host__ __device__ RangeSplit(int s_, int e_, int r)
+    __host__ __device__ RangeSplit(int s_, int e_, int r) { init(s_, e_, r, chunk_shift_for(s_, e_)); }
+    // The same cuts with the chunk C = 1 << cs_ given.
+    __host__ __device__ RangeSplit(int s_, int e_, int r, int cs_) { init(s_, e_, r, cs_); }
+    __host__ __device__ void init(int s_, int e_, int r, int cs_)
     {
         s = s_;
         e = e_;
-        cs = chunk_shift_for(s_, e_);
+        cs = cs_;
         c_first = (s >> cs) + 1;
         const int c_last = e >> cs;
         n_grid = c_last - c_first + 1;

@@ -277,6 +277,10 @@ __device__ inline bool block_and(bool p)
 }
 __device__ inline bool block_or(bool p) { return !block_and(!p); }
 
+// Cache-policy operand of the buffer-load builtins selecting sc1 (device
+// coherence, as the agent-scope atomic accesses above use).
+constexpr int kCacheSc1 = 16;
+
 // s_waitcnt vmcnt(0): this wave's loads and stores have completed (a
 // write-through store is then visible to every XCD).  Encoding (gfx9):
 // vmcnt bits [3:0] and [15:14] = 0, expcnt [6:4] = 7, lgkmcnt [11:8] = 15.
@@ -450,66 +454,74 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
 }
 
 // ---------------------------------------------------------------------------
-// Match of one unit: ring slots [split * slots, +slots) of head bh, slots a
-// multiple of the rows per workgroup and at most UMAX rows per lane; m is
-// the current position.  Each LPR-lane row of a wave computes the squared distance of one
-// slot; the workgroup keeps the smallest
+// Match of one unit: U ring rows per lane of head bh, starting at slot
+// `first`; each LPR-lane row of a wave computes the squared distance of one
+// slot, and the workgroup keeps the smallest
 //   key = float_bits(D) << 32 | (0xffffffff - p)
 // (non-negative floats order like their bits; equal D prefers larger p).
-// The result is valid in thread 0; sm holds kBlock/64 words of LDS.
-template <class T, int D, int UMAX>
-__device__ inline unsigned long long match_unit(const StepArgs &a, int split, int slots, int bh,
-                                                int m, unsigned long long *sm)
+// The loads are issued unconditionally: rows past the ring repeat its last
+// slot, and rows past the unit belong to the head's next unit.  Either way
+// they are slots of the same head, so the minimum is unchanged.  Splitting
+// issue from finish lets the caller request other data before the rows are
+// needed.
+template <class T, int D, int U>
+struct MatchLoads {
+    uint4 q, raw[U];
+    int p[U];
+};
+
+template <class T, int D, int U>
+__device__ inline void match_issue(const StepArgs &a, int first, int bh, MatchLoads<T, D, U> &ml)
 {
     constexpr int EPL = T::EPL, LPR = D / EPL, RPB = kBlock / LPR;
-    constexpr int U = UMAX;
-    const int urt = slots / RPB;
     using S = typename T::S;
     const Shape &s = a.s;
     const int b = bh / s.Hq, h = bh - b * s.Hq;
     const int lane = threadIdx.x % LPR, row = threadIdx.x / LPR;
-    const bool m_ok = m >= 0 && m < s.T;
-
-    float qv[EPL];
-    unpack<T>(load16((const S *)a.qtilde + b * a.qt_sb + h * a.qt_sh + lane * EPL), qv);
+    ml.q = load16((const S *)a.qtilde + b * a.qt_sb + h * a.qt_sh + lane * EPL);
     const S *ring = (const S *)a.q_ring + (int64_t)bh * s.K * D + lane * EPL;
     const int32_t *pr = a.pos_ring + ((int64_t)b * s.Hkv + h / s.G) * s.K;
-
-    uint4 raw[U];
-    int p[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int k = split * slots + u * RPB + row;
-        if (u < urt && k < s.K) {
-            raw[u] = load16(ring + (int64_t)k * D);
-            p[u] = pr[k];
-        } else {
-            raw[u] = make_uint4(0, 0, 0, 0);
-            p[u] = -1;
-        }
+        int k = first + u * RPB + row;
+        k = k < s.K ? k : s.K - 1;
+        ml.raw[u] = load16(ring + (int64_t)k * D);
+        ml.p[u] = pr[k];
     }
+}
+
+// Key of the unit issued by match_issue at position m; valid in thread 0.
+// sm holds kBlock/64 words of LDS.
+template <class T, int D, int U>
+__device__ inline unsigned long long match_finish(const StepArgs &a, int m,
+                                                  const MatchLoads<T, D, U> &ml,
+                                                  unsigned long long *sm)
+{
+    constexpr int EPL = T::EPL, LPR = D / EPL;
+    const Shape &s = a.s;
+    const bool m_ok = m >= 0 && m < s.T;
+    float qv[EPL];
+    unpack<T>(ml.q, qv);
     unsigned long long best = ~0ull;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        if (u < urt) {  // uniform: rows past the unit are not computed
-            float rv[EPL];
-            unpack<T>(raw[u], rv);
-            float acc = 0.f;
+        float rv[EPL];
+        unpack<T>(ml.raw[u], rv);
+        float acc = 0.f;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                const float df = qv[e] - rv[e];
-                acc = fmaf(df, df, acc);
-            }
-            acc = row_sum<LPR>(acc);
-            const int pu = p[u];
-            const bool valid = m_ok && pu >= 0 && pu >= m - s.K && pu <= m - 1;
-            uint32_t bits = __float_as_uint(acc);
-            if (acc != acc)
-                bits = 0x7f800000u;  // NaN distance counts as +inf
-            const unsigned long long key =
-                ((unsigned long long)bits << 32) | (0xffffffffu - (uint32_t)pu);
-            best = umin64(best, valid ? key : ~0ull);
+        for (int e = 0; e < EPL; ++e) {
+            const float df = qv[e] - rv[e];
+            acc = fmaf(df, df, acc);
         }
+        acc = row_sum<LPR>(acc);
+        const int pu = ml.p[u];
+        const bool valid = m_ok && pu >= 0 && pu >= m - s.K && pu <= m - 1;
+        uint32_t bits = __float_as_uint(acc);
+        if (acc != acc)
+            bits = 0x7f800000u;  // NaN distance counts as +inf
+        const unsigned long long key =
+            ((unsigned long long)bits << 32) | (0xffffffffu - (uint32_t)pu);
+        best = umin64(best, valid ? key : ~0ull);
     }
 #pragma unroll
     for (int off = LPR; off < 64; off <<= 1)
@@ -532,11 +544,11 @@ template <class T, int D>
 __global__ __launch_bounds__(kBlock) void match_kernel(StepArgs a)
 {
     __shared__ unsigned long long sm[kBlock / 64];
+    constexpr int U = kSlotsPerSplit / (kBlock / (D / T::EPL));
     const int bh = blockIdx.y;
-    constexpr int RPB = kBlock / (D / T::EPL);
-    const unsigned long long best =
-        match_unit<T, D, kSlotsPerSplit / RPB>(a, blockIdx.x, kSlotsPerSplit, bh,
-                                               a.pos[bh / a.s.Hq], sm);
+    MatchLoads<T, D, U> ml;
+    match_issue<T, D, U>(a, blockIdx.x * kSlotsPerSplit, bh, ml);
+    const unsigned long long best = match_finish<T, D, U>(a, a.pos[bh / a.s.Hq], ml, sm);
     if (threadIdx.x == 0 && best != ~0ull)
         atomicMin(&a.w.keys[bh * kKeyStride], best);
 }
@@ -550,6 +562,12 @@ __global__ __launch_bounds__(kBlock) void match_kernel(StepArgs a)
 // R = C (+) A with C the cached summary of the matched slot (empty on a
 // miss); out = R (+) Bt.
 constexpr int kMergeBlock = 1024;
+// Groups with at most N items take the merge's direct path (all of a
+// wave's loads in registers at once).
+template <int G>
+struct MergeDirect {
+    static constexpr int N = G >= 8 ? 12 : 24;
+};
 // Bounded spin of a wait on another workgroup (polls of about a
 // microsecond each).
 constexpr int kSpinLimit = 1 << 18;
@@ -560,18 +578,52 @@ struct MergeShape {
     static constexpr int DPT = D / 16;                 // dims per task
     static constexpr int TPS = 16;                     // tasks per (head, segment)
     static constexpr int SEG = D + 1;                  // floats per segment record
-    static constexpr int kFloats = G * P * SEG;
+    // direct path: weights, list results, and the four waves' sums per list
+    static constexpr int kDirect = 2 * G * MergeDirect<G>::N + 4 * G + 8 * G * D;
+    static constexpr int kFloats = G * P * SEG > kDirect ? G * P * SEG : kDirect;
     static constexpr int NTASK = G * P * TPS;
     static_assert(NTASK == 1024, "merge shape");
 };
 
-// Groups with at most N items are folded directly, one task per pair of
-// output dims with every load issued up front; larger groups use the
-// segmented fold.
-template <int G>
-struct MergeDirect {
-    static constexpr int N = G >= 8 ? 8 : 16;
-};
+// Direct fold of a group's items [0, cnt), cnt <= MD, list A = items
+// [0, nA), list Bt = the rest.  Per head and list, one lane sums the item
+// weights w_i = 2^(l_i - M) in item order against the list maximum M and
+// leaves them in LDS with the list's log2-lse M + log2(S) and 1 / S; every
+// pair of output dims is then sum_i w_i o_i (item order) times 1 / S.  An
+// empty list gives the empty summary.  lds: 2 * G * MD + 4 * G floats.
+template <int MD, int G, class Src>
+__device__ inline void fold_weights(const Src &src, int cnt, int nA, float *lds)
+{
+    float *s_l = lds, *s_w = lds + G * MD, *s_hl = s_w + G * MD, *s_inv = s_hl + 2 * G;
+    const int tid = threadIdx.x;
+    if (tid < G * MD) {
+        const int j = tid / MD, i = tid - j * MD;
+        float v = -INFINITY;
+        if (i < cnt)
+            src.lse(i, j, v);
+        s_l[tid] = v;
+        s_w[tid] = 0.f;
+    }
+    __syncthreads();
+    if (tid < 2 * G) {
+        const int j = tid >> 1, L = tid & 1;
+        const int i0 = L ? nA : 0, i1 = L ? cnt : nA;
+        const float *l = s_l + j * MD;
+        float M = -INFINITY;
+        for (int i = i0; i < i1; ++i)
+            M = fmaxf(M, l[i]);
+        float S = 0.f;
+        if (M != -INFINITY)
+            for (int i = i0; i < i1; ++i) {
+                const float w = l[i] == -INFINITY ? 0.f : ex2(l[i] - M);
+                s_w[j * MD + i] = w;
+                S += w;
+            }
+        s_hl[tid] = M != -INFINITY ? M + lg2(S) : -INFINITY;
+        s_inv[tid] = M != -INFINITY ? 1.f / S : 0.f;
+    }
+    __syncthreads();
+}
 
 // Partials of one KV group as the merge reads them.
 // PlainParts: the three-kernel arrays, item i of the group at global index
@@ -580,6 +632,20 @@ template <int D, int G>
 struct PlainParts {
     const float *o, *l;
     int64_t begin;
+    // N floats (a multiple of 4) of item i from float f of its G * D.
+    template <int N>
+    __device__ void span(int i, int f, float *v) const
+    {
+        const float *src = o + (begin + i) * G * D + f;
+#pragma unroll
+        for (int k = 0; k < N; k += 4) {
+            const float4 x = *reinterpret_cast<const float4 *>(src + k);
+            v[k] = x.x;
+            v[k + 1] = x.y;
+            v[k + 2] = x.z;
+            v[k + 3] = x.w;
+        }
+    }
     __device__ bool lse(int i, int j, float &v) const
     {
         v = l[(begin + i) * G + j];
@@ -614,6 +680,23 @@ struct PlainParts {
 template <int D, int G>
 struct CoherentParts {
     const float *o, *l;
+    // As PlainParts::span, with 16-byte loads that carry the same
+    // device-coherence bit (sc1) as the agent-scope atomic loads.
+    template <int N>
+    __device__ void span(int i, int f, float *v) const
+    {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(o), (short)0, kItemsPerGroupMax * G * D * 4, 0x00020000);
+#pragma unroll
+        for (int k = 0; k < N; k += 4) {
+            const float4 x = __builtin_bit_cast(
+                float4, __builtin_amdgcn_raw_buffer_load_b128(r, (i * G * D + f + k) * 4, 0, kCacheSc1));
+            v[k] = x.x;
+            v[k + 1] = x.y;
+            v[k + 2] = x.z;
+            v[k + 3] = x.w;
+        }
+    }
     __device__ bool lse(int i, int j, float &v) const
     {
         v = ld_wt(l + (int64_t)i * G + j);
@@ -683,6 +766,8 @@ struct MergePairs {
 
 // Cached summary C of each of this thread's pairs of group grp (empty on a
 // miss); slot_of(jj) is the matched ring slot of the group's head jj, or -1.
+// The lse is kept as loaded (natural log) so that no instruction waits for
+// these loads before the merge uses them.
 template <class T, int D, int G, int NT, class SlotOf>
 __device__ inline void load_cached(const StepArgs &a, int grp, SlotOf &&slot_of,
                                    float (&c_l)[MergePairs<D, G, NT>::NPK],
@@ -701,7 +786,7 @@ __device__ inline void load_cached(const StepArgs &a, int grp, SlotOf &&slot_of,
             const int bh = b * s.Hq + g * G + jj;
             const int slot = slot_of(jj);
             if (slot >= 0) {
-                c_l[k] = a.lse_ring[(int64_t)bh * s.K + slot] * kLog2e;
+                c_l[k] = a.lse_ring[(int64_t)bh * s.K + slot];
                 const float2 v = *reinterpret_cast<const float2 *>(
                     a.o_ring + ((int64_t)bh * s.K + slot) * D + dim);
                 c_o[k][0] = v.x;
@@ -733,45 +818,90 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int gstart, con
     const int e = end_of(a, b);
     const int r_split = (a.mode == kPlanInit) ? 0 : s.r;
     const int nA = RangeSplit(gstart, e, r_split).n_before_split();
+    // The pre-RoPE queries of the fused append are requested first.
+    S qa[NPK][2];
+    if (a.append_fused) {
+#pragma unroll
+        for (int k = 0; k < NPK; ++k) {
+            const int pt = tid + k * NT;
+            const int f = pt < NPAIR ? 2 * pt : 0, jj = f / D, dim = f - jj * D;
+            const S *qs = (const S *)a.qtilde + b * a.qt_sb + (g * G + jj) * a.qt_sh + dim;
+            qa[k][0] = qs[0];
+            qa[k][1] = qs[1];
+        }
+    }
 
     // list 0 = A (items [0, nA)), list 1 = Bt (items [nA, cnt)); each pair
     // folds into res[list][k].
     float res_l[2][NPK], res_o[2][NPK][2];
     if (cnt <= MD) {
-        // Few items: each pair is folded over the items in order, with every
-        // load issued before the first merge.
-        float li[NPK][MD], oi[NPK][MD][2];
+        // Few items: waves 0..3 each load every float of items w, w + 4, ...
+        // (16-byte loads, issued before the weights are formed), sum them
+        // per list with the weights of fold_weights, and the four wave sums
+        // are added in wave order.  The result does not depend on NT.
+        constexpr int FPL = G * D / 64 < 4 ? 4 : G * D / 64;  // floats per lane
+        constexpr int LANES = G * D / FPL;
+        constexpr int IPW = (MD + 3) / 4;
+        const int wave = tid >> 6, lane = tid & 63;
+        const bool loader = wave < 4 && lane < LANES;
+        const int f0 = lane * FPL, jl = (loader ? f0 : 0) / D;
+        float ov[IPW][FPL];
+#pragma unroll
+        for (int u = 0; u < IPW; ++u) {
+            const int i = wave + 4 * u;
+#pragma unroll
+            for (int e = 0; e < FPL; ++e)
+                ov[u][e] = 0.f;
+            if (loader)
+                src.template span<FPL>(i < cnt ? i : cnt - 1, f0, ov[u]);
+        }
+        fold_weights<MD, G>(src, cnt, nA, lds);
+        const float *s_w = lds + G * MD, *s_hl = s_w + G * MD, *s_inv = s_hl + 2 * G;
+        float *s_sum = lds + 2 * G * MD + 4 * G;  // [4 waves][2 lists][G * D]
+        if (loader) {
+            float acc[2][FPL];
+#pragma unroll
+            for (int e = 0; e < FPL; ++e)
+                acc[0][e] = acc[1][e] = 0.f;
+#pragma unroll
+            for (int u = 0; u < IPW; ++u) {
+                const int i = wave + 4 * u;
+                const float w = i < cnt ? s_w[jl * MD + i] : 0.f;
+                const float wa = i < nA ? w : 0.f, wb = i < nA ? 0.f : w;
+#pragma unroll
+                for (int e = 0; e < FPL; ++e) {
+                    acc[0][e] = fmaf(wa, ov[u][e], acc[0][e]);
+                    acc[1][e] = fmaf(wb, ov[u][e], acc[1][e]);
+                }
+            }
+#pragma unroll
+            for (int L = 0; L < 2; ++L)
+#pragma unroll
+                for (int e = 0; e < FPL; e += 4)
+                    *reinterpret_cast<float4 *>(s_sum + (wave * 2 + L) * G * D + f0 + e) =
+                        make_float4(acc[L][e], acc[L][e + 1], acc[L][e + 2], acc[L][e + 3]);
+        }
+        __syncthreads();
 #pragma unroll
         for (int k = 0; k < NPK; ++k) {
             const int pt = tid + k * NT;
-            const int jj = 2 * pt / D, dim = 2 * pt - jj * D;
+            const int f = pt < NPAIR ? 2 * pt : 0, jj = f / D;
 #pragma unroll
-            for (int i = 0; i < MD; ++i) {
-                li[k][i] = -INFINITY;
-                oi[k][i][0] = oi[k][i][1] = 0.f;
-                if (pt < NPAIR && i < cnt) {
-                    src.lse(i, jj, li[k][i]);
-                    src.template vec<2>(i, jj, dim, oi[k][i]);
+            for (int L = 0; L < 2; ++L) {
+                float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float2 x =
+                        *reinterpret_cast<const float2 *>(s_sum + (w * 2 + L) * G * D + f);
+                    o0 += x.x;
+                    o1 += x.y;
                 }
+                res_l[L][k] = s_hl[2 * jj + L];
+                res_o[L][k][0] = o0 * s_inv[2 * jj + L];
+                res_o[L][k][1] = o1 * s_inv[2 * jj + L];
             }
         }
-#pragma unroll
-        for (int k = 0; k < NPK; ++k) {
-            float la = -INFINITY, oa[2] = {0.f, 0.f}, lb = -INFINITY, ob[2] = {0.f, 0.f};
-#pragma unroll
-            for (int i = 0; i < MD; ++i) {
-                if (i < nA)
-                    merge_into<2>(la, oa, li[k][i], oi[k][i]);
-                else if (i < cnt)
-                    merge_into<2>(lb, ob, li[k][i], oi[k][i]);
-            }
-            res_l[0][k] = la;
-            res_o[0][k][0] = oa[0];
-            res_o[0][k][1] = oa[1];
-            res_l[1][k] = lb;
-            res_o[1][k][0] = ob[0];
-            res_o[1][k][1] = ob[1];
-        }
+        __syncthreads();  // lds is reused below
     } else {
 #pragma unroll
         for (int list = 0; list < 2; ++list) {
@@ -819,7 +949,7 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int gstart, con
     float out_l[NPK], out_o[NPK][2], rec_l[NPK], rec_o[NPK][2];
 #pragma unroll
     for (int k = 0; k < NPK; ++k) {
-        float lr = c_l[k], orr[2] = {c_o[k][0], c_o[k][1]};
+        float lr = c_l[k] * kLog2e, orr[2] = {c_o[k][0], c_o[k][1]};
         merge_into<2>(lr, orr, res_l[0][k], res_o[0][k]);
         float lo = lr, oo[2] = {orr[0], orr[1]};
         merge_into<2>(lo, oo, res_l[1][k], res_o[1][k]);
@@ -847,9 +977,8 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int gstart, con
             // Rectify-append into slot m mod K of this head's rings.
             const int slot = e % s.K;
             const int64_t ri = ((int64_t)bh * s.K + slot) * D + dim;
-            const S *qs = (const S *)a.qtilde + b * a.qt_sb + h * a.qt_sh + dim;
-            ((S *)a.q_ring)[ri] = qs[0];
-            ((S *)a.q_ring)[ri + 1] = qs[1];
+            ((S *)a.q_ring)[ri] = qa[k][0];
+            ((S *)a.q_ring)[ri + 1] = qa[k][1];
             *reinterpret_cast<float2 *>(a.o_ring + ri) = make_float2(rec_o[k][0], rec_o[k][1]);
             if (dim == 0)
                 a.lse_ring[(int64_t)bh * s.K + slot] = rec_l[k] * kLn2;
@@ -905,6 +1034,10 @@ struct KvBlock {
     int base;  // token of row 0, i = 0
 };
 
+// K/V rows of one block.  Every lane loads: a token at or past t1 reads row
+// t1 - 1 of the item instead, which the block computation masks (its logit
+// is -inf, its probability exactly 0).  No branch separates the loads, so
+// the compiler can wait for each block on its own.
 template <class T, int D, int G, int LPR, int RPB, int NB>
 __device__ inline void load_block(KvBlock<T, G, T::EPL, NB> &kv, const typename T::S *kb,
                                   const typename T::S *vb, int64_t kv_st, int base, int t1,
@@ -913,14 +1046,10 @@ __device__ inline void load_block(KvBlock<T, G, T::EPL, NB> &kv, const typename 
     kv.base = base;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-        const int t = base + i * RPB + row;
-        if (t < t1) {
-            kv.k[i] = load16(kb + (int64_t)t * kv_st);
-            kv.v[i] = load16(vb + (int64_t)t * kv_st);
-        } else {
-            kv.k[i] = make_uint4(0, 0, 0, 0);
-            kv.v[i] = make_uint4(0, 0, 0, 0);
-        }
+        int t = base + i * RPB + row;
+        t = t < t1 ? t : t1 - 1;
+        kv.k[i] = load16(kb + (int64_t)t * kv_st);
+        kv.v[i] = load16(vb + (int64_t)t * kv_st);
     }
 }
 
@@ -1069,6 +1198,31 @@ struct ItemCtx {
     static constexpr int EPL = T::EPL;
     const S *kb, *vb;
     float qr[G][EPL];
+    // K/V row pointers only; the queries come from queries_from_lds.
+    __device__ ItemCtx(const StepArgs &a, int b, int g, bool)
+    {
+        const Shape &s = a.s;
+        const int lane = threadIdx.x % (D / EPL);
+        kb = (const S *)a.k + b * s.kv_sb + g * s.kv_sh + lane * EPL;
+        vb = (const S *)a.v + b * s.kv_sb + g * s.kv_sh + lane * EPL;
+    }
+    // This lane's slice of the group's queries from LDS ([G][D] floats, as
+    // stored by stage_queries), scaled as the global-memory constructor
+    // scales them.
+    __device__ void queries_from_lds(const float *s_q, float qscale)
+    {
+        const int lane = threadIdx.x % (D / EPL);
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+            for (int e4 = 0; e4 < EPL; e4 += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(s_q + j * D + lane * EPL + e4);
+                qr[j][e4 + 0] = v.x * qscale;
+                qr[j][e4 + 1] = v.y * qscale;
+                qr[j][e4 + 2] = v.z * qscale;
+                qr[j][e4 + 3] = v.w * qscale;
+            }
+    }
     __device__ ItemCtx(const StepArgs &a, int b, int g)
     {
         const Shape &s = a.s;
@@ -1090,16 +1244,68 @@ struct ItemCtx {
     }
 };
 
-// Attention of one work item, tokens [t0, t1) of the group of ctx, head j
-// of the group attending from st[j], by the whole workgroup.  The partial
-// (o, log2-lse) of each head goes to sink(j, dim, o, lse) for every dim (lse
-// meaningful at dim 0).  lds holds AttendShape::kFloats floats.
-// after_issue() runs once the item's first K/V loads are in flight (extra
-// requests whose latency should hide behind them).
-template <class T, int D, int G, class Sink, class AfterIssue>
-__device__ inline void run_item(const StepArgs &a, const ItemCtx<T, D, G> &ctx, int t0, int t1,
-                                const int (&st)[G], float *lds, Sink &&sink,
-                                AfterIssue &&after_issue)
+// The group's post-RoPE queries, G * D floats, read once per workgroup (one
+// float2 per thread) instead of once per 16-lane row: request, then store
+// to LDS (s_q[G][D]) once the values are needed.
+template <int D, int G>
+struct QueryStage {
+    static constexpr int kPairs = G * D / 2;
+    static constexpr int kPer = (kPairs + kBlock - 1) / kBlock;
+    float2 v[kPer];
+    __device__ void request(const StepArgs &a, int b, int g)
+    {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            int i = threadIdx.x + k * kBlock;
+            i = i < kPairs ? i : kPairs - 1;
+            const int j = i / (D / 2), dim = 2 * (i - j * (D / 2));
+            v[k] = *reinterpret_cast<const float2 *>(a.q + b * a.q_sb +
+                                                     (int64_t)(g * G + j) * a.q_sh + dim);
+        }
+    }
+    __device__ void store(float *s_q) const
+    {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int i = threadIdx.x + k * kBlock;
+            if (i < kPairs)
+                *reinterpret_cast<float2 *>(s_q + 2 * i) = v[k];
+        }
+    }
+};
+
+// The first two K/V blocks of a work item (tokens [t0, t1) of the group of
+// ctx), requested without waiting.  t0 < t1.
+template <class T, int D, int G>
+struct ItemBufs {
+    using L = AttendShape<T, D, G>;
+    KvBlock<T, G, T::EPL, L::NB> a, b;
+};
+
+template <class T, int D, int G>
+__device__ inline void item_issue(const StepArgs &a, const ItemCtx<T, D, G> &ctx, int t0, int t1,
+                                  ItemBufs<T, D, G> &bufs, bool both)
+{
+    using L = AttendShape<T, D, G>;
+    constexpr int LPR = L::LPR, RPB = L::RPB, NB = L::NB, TPB = RPB * NB;
+    const int row = threadIdx.x / LPR;
+    load_block<T, D, G, LPR, RPB, NB>(bufs.a, ctx.kb, ctx.vb, a.s.kv_st, t0, t1, row);
+    // both: the second block is requested without a branch (all its rows
+    // clamp to t1 - 1 when the item has one block).
+    if (both || t0 + TPB < t1)
+        load_block<T, D, G, LPR, RPB, NB>(bufs.b, ctx.kb, ctx.vb, a.s.kv_st, t0 + TPB, t1, row);
+}
+
+// Attention of one work item whose first two blocks item_issue requested,
+// by the whole workgroup; head j of the group attends from st[j].  Each
+// block's successor two blocks ahead is requested as soon as the block has
+// been consumed.  The partial (o, log2-lse) of each head goes to
+// sink(j, dim, o, lse) for every dim (lse meaningful at dim 0).  lds holds
+// AttendShape::kFloats floats.
+template <class T, int D, int G, class Sink>
+__device__ inline void item_finish(const StepArgs &a, const ItemCtx<T, D, G> &ctx, int t0, int t1,
+                                   const int (&st)[G], float *lds, ItemBufs<T, D, G> &bufs,
+                                   Sink &&sink)
 {
     using L = AttendShape<T, D, G>;
     constexpr int EPL = L::EPL, LPR = L::LPR, RPB = L::RPB, NB = L::NB;
@@ -1113,11 +1319,8 @@ __device__ inline void run_item(const StepArgs &a, const ItemCtx<T, D, G> &ctx, 
     t1 = __builtin_amdgcn_readfirstlane(t1);
     const auto *kb = ctx.kb, *vb = ctx.vb;
     const auto &qr = ctx.qr;
-
-    KvBlock<T, G, EPL, NB> bufA, bufB;
-    load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, t0, t1, row);
-
-    after_issue();
+    auto &bufA = bufs.a;
+    auto &bufB = bufs.b;
 
     float mrun[G], lrun[G], acc[G][EPL];
 #pragma unroll
@@ -1136,16 +1339,17 @@ __device__ inline void run_item(const StepArgs &a, const ItemCtx<T, D, G> &ctx, 
         for (int j = 1; j < G; ++j)
             my_st = (lane % G == j) ? __builtin_amdgcn_readfirstlane(st[j]) : my_st;
         for (int base = t0; base < t1; base += 2 * TPB) {
-            if (base + TPB < t1)
-                load_block<T, D, G, LPR, RPB, NB>(bufB, kb, vb, s.kv_st, base + TPB, t1, row);
             compute_block_rs<T, G, RPB, NB>(bufA, row, lane, qr, my_st, t1, mrun[0], lrun[0],
                                             acc);
+            if (base + 2 * TPB < t1)
+                load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, base + 2 * TPB, t1,
+                                                  row);
             if (base + TPB < t1) {
-                if (base + 2 * TPB < t1)
-                    load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, base + 2 * TPB,
-                                                      t1, row);
                 compute_block_rs<T, G, RPB, NB>(bufB, row, lane, qr, my_st, t1, mrun[0],
                                                 lrun[0], acc);
+                if (base + 3 * TPB < t1)
+                    load_block<T, D, G, LPR, RPB, NB>(bufB, kb, vb, s.kv_st, base + 3 * TPB,
+                                                      t1, row);
             }
         }
         if (lane < G) {
@@ -1153,17 +1357,17 @@ __device__ inline void run_item(const StepArgs &a, const ItemCtx<T, D, G> &ctx, 
             sm_l[row * G + lane] = lrun[0];
         }
     } else {
-        // Blocks alternate between the two buffers; the next block is
-        // always requested before the current one is consumed.
+        // Blocks alternate between the two buffers.
         for (int base = t0; base < t1; base += 2 * TPB) {
-            if (base + TPB < t1)
-                load_block<T, D, G, LPR, RPB, NB>(bufB, kb, vb, s.kv_st, base + TPB, t1, row);
             compute_block<T, D, G, LPR, RPB, NB>(bufA, row, qr, st, t1, mrun, lrun, acc);
+            if (base + 2 * TPB < t1)
+                load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, base + 2 * TPB, t1,
+                                                  row);
             if (base + TPB < t1) {
-                if (base + 2 * TPB < t1)
-                    load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, base + 2 * TPB,
-                                                      t1, row);
                 compute_block<T, D, G, LPR, RPB, NB>(bufB, row, qr, st, t1, mrun, lrun, acc);
+                if (base + 3 * TPB < t1)
+                    load_block<T, D, G, LPR, RPB, NB>(bufB, kb, vb, s.kv_st, base + 3 * TPB,
+                                                      t1, row);
             }
         }
         if (lane == 0) {
@@ -1244,14 +1448,13 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
         float *po = a.w.part_o + (int64_t)it * G * D;
         float *pl = a.w.part_l + (int64_t)it * G;
         const ItemCtx<T, D, G> ctx(a, b, g);
-        run_item<T, D, G>(
-            a, ctx, t0, t1, st, lds,
-            [&](int j, int dim, float o, float lg) {
-                po[j * D + dim] = o;
-                if (dim == 0)
-                    pl[j] = lg;
-            },
-            [] {});
+        ItemBufs<T, D, G> bufs;
+        item_issue<T, D, G>(a, ctx, t0, t1, bufs, false);
+        item_finish<T, D, G>(a, ctx, t0, t1, st, lds, bufs, [&](int j, int dim, float o, float lg) {
+            po[j * D + dim] = o;
+            if (dim == 0)
+                pl[j] = lg;
+        });
         __syncthreads();
     }
 }
@@ -1286,18 +1489,59 @@ __device__ inline bool poll_keys(const StepArgs &a, const unsigned long long *kw
     }
 }
 
-// Key of single-launch match unit u of the group whose first head is bh0
-// (~0 for a dummy word u >= upg); valid in thread 0.
-template <class T, int D>
-__device__ __forceinline__ unsigned long long single_unit_key(const StepArgs &a, int u, int bh0,
-                                                              int m, unsigned long long *sm)
+// Single-launch match unit u of a group: head u / nsplit of the group,
+// slots from (u mod nsplit) * unit_slots.  Key words u >= upg carry a copy
+// of the last unit (only their tag is read).
+__device__ inline void single_unit(const StepArgs &a, int u, int &j, int &first)
 {
-    if (u >= a.upg)
-        return ~0ull;
-    const int j = u / a.nsplit, split = u - j * a.nsplit;
-    constexpr int RPB = kBlock / (D / T::EPL);
-    return match_unit<T, D, single_slots(sizeof(typename T::S), D) / RPB>(
-        a, split, a.unit_slots, bh0 + j, m, sm);
+    u = u < a.upg ? u : a.upg - 1;
+    j = u / a.nsplit;
+    first = (u - j * a.nsplit) * a.unit_slots;
+}
+
+// Minimum of a 64-bit key over aligned groups of W lanes (8 <= W <= 64).
+template <int CTRL>
+__device__ inline unsigned long long dpp64(unsigned long long v)
+{
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf, 0xf, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, true);
+    return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+template <int W>
+__device__ inline unsigned long long lanes_min64(unsigned long long v)
+{
+    static_assert(W == 8 || W == 16 || W == 32 || W == 64, "lane group");
+    v = umin64(v, dpp64<kDppQuadXor1>(v));
+    v = umin64(v, dpp64<kDppQuadXor2>(v));
+    v = umin64(v, dpp64<kDppHalfMirror>(v));
+    if constexpr (W >= 16)
+        v = umin64(v, dpp64<kDppRowMirror>(v));
+    if constexpr (W >= 32)
+        v = umin64(v, shfl_xor_u64(v, 16));
+    if constexpr (W >= 64)
+        v = umin64(v, shfl_xor_u64(v, 32));
+    return v;
+}
+
+// Speculative item of workgroup loc of a group at position e: the loc-th
+// item from the end of the range [e - span + 1, e], span being the group's
+// span at its previous step (a range keeps its span while every head keeps
+// matching the previous position).  A hit range spans at most K + r tokens,
+// so its chunk is kChunkMin; every item but the first is then fixed by e
+// and r alone.  False if loc has no such item.
+__device__ inline bool spec_item(const StepArgs &a, int e, int loc, int span, int &t0, int &t1)
+{
+    if (loc >= kSpecMax || e < 0 || e >= a.s.T)
+        return false;
+    const int hit_span = a.s.K + a.s.r;
+    span = (span <= 0 || span > hit_span) ? hit_span : span;
+    const int s0 = e - span + 1;
+    const RangeSplit rs(s0 > 0 ? s0 : 0, e, a.s.r, kChunkMinShift);
+    const int it = rs.n - 1 - loc;
+    if (it < 0)
+        return false;
+    rs.item(it, t0, t1);
+    return true;
 }
 
 // Thread 0's key, tagged, to word u of the group's kKeyReps copies; then a
@@ -1316,19 +1560,23 @@ __device__ __forceinline__ void store_unit_key(unsigned long long *kw, int64_t r
 }
 
 // The whole decode step in one launch of a.wpg workgroups per KV group, all
-// resident at once.  Workgroup `loc` of group grp:
-//   1. reads the done counter (the launch's epoch and key tag);
-//   2. runs match units loc, loc + wpg, ... of the group (unit u: head
-//      u / nsplit, unit_slots ring slots of split u mod nsplit)
-//      and stores each key, tagged, in kKeyReps copies; words past the units
-//      are tagged dummies;
+// resident at once; U ring rows per lane per match unit.  Workgroup `loc`
+// of group grp:
+//   1. requests the position and the done counter (the launch's epoch and
+//      key tag), its first match unit's ring rows and the group's queries;
+//   2. finishes its match units (unit loc, loc + wpg, ...: unit u is head
+//      u / nsplit, unit_slots ring slots from split u mod nsplit) and stores
+//      each key, tagged, in kKeyReps copies; then requests the K/V of its
+//      speculative item, if it has one;
 //   3. polls the group's key words (copy loc mod kKeyReps) until all carry
 //      the tag, and plans the group: decisions, range [s_g, m], items;
-//   4. runs items loc, loc + wpg, ...: stores the partials, waits for the
-//      stores to complete and counts the item on the group's counter; the
-//      workgroup that completes the group merges it (with the fused append),
-//      resets the counter and counts the group on the done counter.
-template <class T, int D, int G>
+//   4. runs the items n-1-loc, n-1-loc-wpg, ... (from the end of the range,
+//      so the speculative loads usually are the first item's data): stores
+//      the partials, waits for the stores to complete and counts the item on
+//      the group's counter; the workgroup that completes the group merges it
+//      (with the fused append), resets the counter and counts the group on
+//      the done counter.
+template <class T, int D, int G, int U>
 __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
 {
     using AS = AttendShape<T, D, G>;
@@ -1339,33 +1587,51 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
     __shared__ unsigned long long s_keys[kMaxSingleUnits];
     __shared__ int s_code[G];
     __shared__ int s_last;
+    __shared__ float s_q[G * D];
     const Shape &s = a.s;
     const int NG = s.B * s.Hkv;
     const int grp = blockIdx.x / a.wpg, loc = blockIdx.x - grp * a.wpg;
     const int b = grp / s.Hkv, g = grp - b * s.Hkv;
+    const int bh0 = b * s.Hq + g * G;
     unsigned long long *sync = a.w.sync;
-    // Read before any store of the launch, so both are scalar loads.  The
+    // Requested first, so that waiting for them waits for nothing else.  The
     // done counter is read with a plain load: its value from earlier
     // launches is visible at kernel start, and the increments of this
     // launch's groups leave floor(done / 2^s) unchanged until this
     // workgroup's own group completes.
     const int e = a.pos[b];
     const unsigned long long done = sync[kSyncDone];
+    uint32_t *counter = a.w.grp_sync + (int64_t)grp * kGrpStride;
+    const int span_prev = (int)counter[kGrpSpan];
+    int uj, ufirst;
+    single_unit(a, loc, uj, ufirst);
+    MatchLoads<T, D, U> ml;
+    match_issue<T, D, U>(a, ufirst, bh0 + uj, ml);
+    // The group's queries and K/V row pointers do not depend on the plan.
+    QueryStage<D, G> qs;
+    qs.request(a, b, g);
+    ItemCtx<T, D, G> ctx(a, b, g, true);
+
+    unsigned long long *klds = reinterpret_cast<unsigned long long *>(lds);
     const int64_t rep_stride = (int64_t)NG * a.nkw;
     unsigned long long *kw = a.w.skeys + (int64_t)grp * a.nkw;
-
-    // Match units loc, loc + wpg, ... (loc < wpg <= nkw: the first exists).
-    const int bh0 = b * s.Hq + g * G;
-    unsigned long long *klds = reinterpret_cast<unsigned long long *>(lds);
-    const unsigned long long key0 = single_unit_key<T, D>(a, loc, bh0, e, klds);
     const uint32_t tag8 = (uint32_t)((done >> a.done_shift) + 1) & 0xffu;
-    store_unit_key(kw, rep_stride, loc, key0, tag8);
-    for (int u = loc + a.wpg; u < a.nkw; u += a.wpg)
-        store_unit_key(kw, rep_stride, u, single_unit_key<T, D>(a, u, bh0, e, klds), tag8);
+    store_unit_key(kw, rep_stride, loc, match_finish<T, D, U>(a, e, ml, klds), tag8);
+    qs.store(s_q);  // read after the barriers of the poll and the plan
+    for (int u = loc + a.wpg; u < a.nkw; u += a.wpg) {
+        single_unit(a, u, uj, ufirst);
+        match_issue<T, D, U>(a, ufirst, bh0 + uj, ml);
+        store_unit_key(kw, rep_stride, u, match_finish<T, D, U>(a, e, ml, klds), tag8);
+    }
+    // Speculative K/V, requested once the keys are out: loads complete in
+    // order, so requests made earlier would hold back the match.  They are
+    // in flight while the other units' keys arrive.
+    int sp_t0 = 0, sp_t1 = 0;
+    const bool spec = spec_item(a, e, loc, span_prev, sp_t0, sp_t1);
+    ItemBufs<T, D, G> bufs;
+    if (spec)
+        item_issue<T, D, G>(a, ctx, sp_t0, sp_t1, bufs, false);
 
-    // The group's query slice and K/V row pointers do not depend on the
-    // plan: their loads are in flight during the poll.
-    const ItemCtx<T, D, G> ctx(a, b, g);
     bool ok = true;
     if (threadIdx.x < 64)
         ok = poll_keys(a, kw + (loc % kKeyReps) * rep_stride, tag8, s_keys);
@@ -1382,14 +1648,12 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
         unsigned long long key = ~0ull;
         for (int u = sub; u < a.nsplit; u += LPH)
             key = umin64(key, s_keys[j * a.nsplit + u]);
-#pragma unroll
-        for (int off = 1; off < LPH; off <<= 1)
-            key = umin64(key, shfl_xor_u64(key, off));
+        key = lanes_min64<LPH>(key);
         if (sub == 0) {
             const Decision dc = decide(a, key, e_ok);
             s_code[j] = dc.hit ? dc.p - s.r + 1 : kMissCode;
             if (loc == 0) {
-                const int bh = b * s.Hq + g * G + j;
+                const int bh = bh0 + j;
                 if (a.match_p)
                     a.match_p[bh] = dc.hit ? dc.p : -1;
                 if (a.match_d2)
@@ -1415,49 +1679,55 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
     }
     const RangeSplit rs(e_ok ? sg : 0, e_ok ? e : 0, s.r);
     const int n = e_ok ? rs.n : 0;
+    ctx.queries_from_lds(s_q, s.qscale);
     const unsigned long long done_add =
         grp == 0 ? (1ull << a.done_shift) - (unsigned long long)NG + 1ull : 1ull;
 
     float *gpo = a.w.part_o + (int64_t)grp * kItemsPerGroupMax * G * D;
     float *gpl = a.w.part_l + (int64_t)grp * kItemsPerGroupMax * G;
-    uint32_t *counter = a.w.grp_sync + (int64_t)grp * kGrpStride;
-    for (int it = loc; it < n; it += a.wpg) {
+    // The cached summaries are requested now, in case this workgroup
+    // completes the group and merges it.
+    float c_l[MP::NPK], c_o[MP::NPK][2];
+    if (n > 0)
+        load_cached<T, D, G, kBlock>(
+            a, grp, [&](int j) { return code_slot(s_code[j], s.r, s.K); }, c_l, c_o);
+    bool merger = false;
+    for (int jj = loc; jj < n; jj += a.wpg) {
+        const int it = n - 1 - jj;
         int t0, t1;
         rs.item(it, t0, t1);
+        // The speculative loads hold exactly this item's rows when its
+        // bounds are the speculated ones.
+        if (!(jj == loc && spec && t0 == sp_t0 && t1 == sp_t1))
+            item_issue<T, D, G>(a, ctx, t0, t1, bufs, false);
         float *po = gpo + (int64_t)it * G * D, *pl = gpl + (int64_t)it * G;
-        // The cached summaries are requested with the item's first loads, in
-        // case this workgroup completes the group and merges it.
-        float c_l[MP::NPK], c_o[MP::NPK][2];
-        run_item<T, D, G>(
-            a, ctx, t0, t1, st, lds,
-            [&](int j, int dim, float o, float lg) {
-                st_wt(po + j * D + dim, o);
-                if (dim == 0)
-                    st_wt(pl + j, lg);
-            },
-            [&] {
-                load_cached<T, D, G, kBlock>(
-                    a, grp, [&](int jj) { return code_slot(s_code[jj], s.r, s.K); }, c_l, c_o);
-            });
+        item_finish<T, D, G>(a, ctx, t0, t1, st, lds, bufs, [&](int j, int dim, float o, float lg) {
+            st_wt(po + j * D + dim, o);
+            if (dim == 0)
+                st_wt(pl + j, lg);
+        });
         wait_vmem();  // this wave's partial stores have completed
         __syncthreads();
         if (threadIdx.x == 0)
             s_last = atomicAdd(counter, 1u) == (uint32_t)(n - 1);
         __syncthreads();
-        if (s_last) {
-            const CoherentParts<D, G> src{gpo, gpl};
-            merge_group<T, D, G, kBlock>(a, grp, n, sg, src, lds, c_l, c_o);
-            if (threadIdx.x == 0) {
-                st_wt(counter, 0u);
-                atomicAdd(&sync[kSyncDone], done_add);
-            }
+        // The count that completes the group is the last one of the group,
+        // so a workgroup merges at most once, after its items.
+        merger = merger || s_last;
+    }
+    if (merger) {
+        const CoherentParts<D, G> src{gpo, gpl};
+        merge_group<T, D, G, kBlock>(a, grp, n, sg, src, lds, c_l, c_o);
+        if (threadIdx.x == 0) {
+            st_wt(counter, 0u);
+            st_wt(counter + kGrpSpan, (uint32_t)(e - sg + 1));
+            atomicAdd(&sync[kSyncDone], done_add);
         }
-        __syncthreads();
     }
     if (n == 0 && loc == 0) {
         // Position out of range: NaN outputs, nothing appended.
         for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
-            const int bh = b * s.Hq + g * G + idx / D;
+            const int bh = bh0 + idx / D;
             if (a.out)
                 a.out[(int64_t)bh * D + idx % D] = NAN;
             a.w.rect_o[(int64_t)bh * D + idx % D] = 0.f;
@@ -1658,7 +1928,13 @@ template <class T, int D, int G>
 static void step_go_g(const StepArgs &a, hipStream_t st)
 {
     const int grid = a.wpg * a.s.B * a.s.Hkv;
-    hipLaunchKernelGGL((step_kernel<T, D, G>), dim3(grid), dim3(kBlock), 0, st, a);
+    constexpr int eb = sizeof(typename T::S);
+    if (a.unit_slots == step_unit_slots(eb, D, false))
+        hipLaunchKernelGGL((step_kernel<T, D, G, step_rows(eb, D, false)>), dim3(grid), dim3(kBlock),
+                           0, st, a);
+    else
+        hipLaunchKernelGGL((step_kernel<T, D, G, step_rows(eb, D, true)>), dim3(grid), dim3(kBlock),
+                           0, st, a);
 }
 
 template <class T, int D>
@@ -1680,14 +1956,23 @@ static void step_go(const StepArgs &a, hipStream_t st)
     }
 }
 
+// Resident workgroups of both unit sizes' kernels (the smaller count).
+template <class T, int D, int U>
+static int step_resident_u(const Shape &s)
+{
+    const void *fn = s.G == 1   ? (const void *)step_kernel<T, D, 1, U>
+                     : s.G == 2 ? (const void *)step_kernel<T, D, 2, U>
+                     : s.G == 4 ? (const void *)step_kernel<T, D, 4, U>
+                                : (const void *)step_kernel<T, D, 8, U>;
+    return device_cu_count() * resident_per_cu(fn, 0);
+}
 template <class T, int D>
 static void step_resident_go(const Shape &s, int *n)
 {
-    const void *fn = s.G == 1   ? (const void *)step_kernel<T, D, 1>
-                     : s.G == 2 ? (const void *)step_kernel<T, D, 2>
-                     : s.G == 4 ? (const void *)step_kernel<T, D, 4>
-                                : (const void *)step_kernel<T, D, 8>;
-    *n = device_cu_count() * resident_per_cu(fn, 0);
+    constexpr int eb = sizeof(typename T::S);
+    const int a = step_resident_u<T, D, step_rows(eb, D, false)>(s);
+    const int b = step_resident_u<T, D, step_rows(eb, D, true)>(s);
+    *n = a < b ? a : b;
 }
 
 int step_resident_workgroups(const Shape &s)

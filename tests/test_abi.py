@@ -41,7 +41,9 @@ def test_struct_layout_matches_header():
 def test_status_strings_and_chunk(lib):
     assert mac.mac_status_string(0) == "ok"
     assert "workspace" in mac.mac_status_string(-4)
-    assert mac.mac_chunk_tokens(0, 63) == 128
+    assert mac.mac_chunk_tokens(0, 63) == 64
+    assert mac.mac_chunk_tokens(0, 64 * 128 - 1) == 64
+    assert mac.mac_chunk_tokens(0, 64 * 128) == 128
     assert mac.mac_chunk_tokens(0, 128 * 128 - 1) == 128
     assert mac.mac_chunk_tokens(0, 128 * 128) == 256
     assert mac.mac_chunk_tokens(0, 65536) == 1024
