@@ -139,6 +139,11 @@ static mac_status check_params(const mac_params *p, Shape *s)
     if ((int64_t)p->batch * p->n_q_heads > 8192 ||
         plan_lds_bytes(p->batch, p->n_q_heads, p->n_kv_heads) > 48 * 1024)
         return MAC_ERR_UNSUPPORTED;
+    // The planner's work offsets (tokens plus a per-item cost, summed over
+    // the KV groups of a step) are 32-bit.
+    if ((int64_t)p->batch * p->n_kv_heads * ((int64_t)p->kv_capacity + (int64_t)kItemCost * (kMaxItemsPerGroup + 2)) >=
+        ((int64_t)1 << 31))
+        return MAC_ERR_UNSUPPORTED;
     int64_t st = p->kv_stride_t, sh = p->kv_stride_h, sb = p->kv_stride_b;
     if (st == 0 && sh == 0 && sb == 0) {
         st = p->head_dim;

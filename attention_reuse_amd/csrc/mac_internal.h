@@ -13,6 +13,9 @@ namespace mac {
 // range, so a head that misses sees exactly the items of a full decode.
 constexpr int kChunkMinShift = 6;
 constexpr int kChunkMin = 1 << kChunkMinShift;
+// Work of an item in the attention kernel's balanced split: its tokens plus
+// this many (the per-item cost of combining rows and storing the partial).
+constexpr int kItemCost = 64;
 constexpr int kMaxItemsPerGroup = 128;
 // Ring slots scanned by one match workgroup.
 constexpr int kSlotsPerSplit = 64;

@@ -9,9 +9,10 @@
 //       folded into a per-head (distance, position) key by an atomic min.
 //   plan + attend -- every workgroup plans from the match keys (final
 //       decision per head, threshold, token range [s_g, m] per (request, KV
-//       group); every range is cut into items on an absolute 128-token grid
-//       plus the rectify split m-r+1: the span-proportional allocator of
-//       "K2"), then runs persistent split-KV attention over the items.  A K/V
+//       group); every range is cut into items on an absolute 64-token grid
+//       (coarser for long ranges) plus the rectify split m-r+1: the
+//       span-proportional allocator of "K2"), takes an equal contiguous share
+//       of the items' work and streams its split-KV attention.  A K/V
 //       row is loaded once (16 B per lane, one 16-lane DPP row per row) and
 //       serves the G query heads of the group from registers; each item
 //       leaves one partial (o, lse) per head.
@@ -23,10 +24,11 @@
 //       an auxiliary stream.
 //
 // The stages run either as one launch (step_kernel) or as one kernel each.
-// The separate kernels hand over at kernel boundaries.  Inside the single
-// launch, match -> plan is a grid barrier (the grid is sized to be resident
-// at once; the wait is bounded) and attention -> merge is a hand-off to the
-// workgroup that completes a group's last item.  The eight XCDs of MI355X
+// The separate kernels hand over at kernel boundaries.  The single launch
+// gives each KV group its own run of workgroups, all resident at once:
+// match -> plan is a hand-off of tagged match keys that every workgroup of
+// the group polls (the wait is bounded), and attention -> merge a hand-off to
+// the workgroup that completes the group's last item.  The eight XCDs of MI355X
 // have private L2 caches that are not coherent with each other, and a
 // device-scope release fence writes a whole L2 back, which costs tens of
 // microseconds under load.  Data that crosses workgroups inside the launch
@@ -320,12 +322,13 @@ __device__ inline int code_slot(int32_t c, int r, int K)
 // ---------------------------------------------------------------------------
 // Planner, run redundantly by every attention workgroup from the match keys
 // (a few KiB, L2-resident): decision per (b, h), token range [s_g, e] and
-// item count per (b, g), and an exclusive scan of the counts, all in LDS.
-// Workgroup 0 also publishes what the merge kernel and the caller need.
-// LDS: ints [BH + 4*NG + 1 + nt/64].
+// item count per (b, g), and exclusive scans of the counts and of the
+// groups' work (tokens plus kItemCost per item), all in LDS.  Workgroup 0
+// also publishes what the merge kernel and the caller need.
+// LDS: ints [BH + 5*NG + 2 + 2*nt/64].
 struct PlanTables {
-    const int32_t *code, *gstart, *gend, *gcount, *gbegin;
-    int total;
+    const int32_t *code, *gstart, *gend, *gcount, *gbegin, *gwork;
+    int total, work;
 };
 
 __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
@@ -340,7 +343,8 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
     int32_t *s_gend = s_gstart + NG;
     int32_t *s_gcount = s_gend + NG;
     int32_t *s_gbegin = s_gcount + NG;  // NG + 1
-    int32_t *s_wave = s_gbegin + NG + 1;  // one per wave
+    int32_t *s_gwork = s_gbegin + NG + 1;  // NG + 1
+    int32_t *s_wave = s_gwork + NG + 1;  // two per wave
 
     // Decisions per (b, h).
     int bad = 0;
@@ -369,7 +373,7 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
     // thread, so the scan below needs one pass over the runs.
     const int per = (NG + nt - 1) / nt;
     const int lo = tid * per, hi = lo + per < NG ? lo + per : NG;
-    int run = 0;
+    int run = 0, runw = 0;
     for (int grp = lo; grp < hi; ++grp) {
         const int b = grp / s.Hkv, g = grp - b * s.Hkv;
         const int e = end_of(a, b);
@@ -386,32 +390,43 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
         s_gend[grp] = e;
         s_gcount[grp] = cnt;
         run += cnt;
+        runw += cnt > 0 ? e - st + 1 + kItemCost * cnt : 0;
     }
-    // Exclusive scan of the counts: inclusive scan of the run totals within
-    // each wave, then across the waves.
-    int x = run;
+    // Exclusive scans of the counts and the work: inclusive scans of the run
+    // totals within each wave, then across the waves.
+    int x = run, xw = runw;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o)
+        const int y = __shfl_up(x, o, 64), yw = __shfl_up(xw, o, 64);
+        if (lane >= o) {
             x += y;
+            xw += yw;
+        }
     }
-    if (lane == 63)
+    if (lane == 63) {
         s_wave[wave] = x;
+        s_wave[(nt >> 6) + wave] = xw;
+    }
     __syncthreads();
-    int before = 0, total = 0;
+    int before = 0, total = 0, beforew = 0, totalw = 0;
     for (int w = 0; w < (nt >> 6); ++w) {
-        const int v = s_wave[w];
+        const int v = s_wave[w], vw = s_wave[(nt >> 6) + w];
         before += w < wave ? v : 0;
         total += v;
+        beforew += w < wave ? vw : 0;
+        totalw += vw;
     }
-    int acc = before + x - run;
+    int acc = before + x - run, accw = beforew + xw - runw;
     for (int grp = lo; grp < hi; ++grp) {
         s_gbegin[grp] = acc;
         acc += s_gcount[grp];
+        s_gwork[grp] = accw;
+        accw += s_gcount[grp] > 0 ? s_gend[grp] - s_gstart[grp] + 1 + kItemCost * s_gcount[grp] : 0;
     }
-    if (tid == 0)
+    if (tid == 0) {
         s_gbegin[NG] = total;
+        s_gwork[NG] = totalw;
+    }
     __syncthreads();
     if (total > a.max_items)
         total = (int)a.max_items;
@@ -449,7 +464,9 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
     t.gend = s_gend;
     t.gcount = s_gcount;
     t.gbegin = s_gbegin;
+    t.gwork = s_gwork;
     t.total = total;
+    t.work = totalw;
     return t;
 }
 
@@ -1025,7 +1042,8 @@ struct AttendShape {
     // lane); other row widths all-reduce every logit.
     static constexpr bool kScatter = LPR == 16;
     static constexpr int NB = kScatter ? (16 / G < 4 ? 16 / G : 4) : 4;  // tokens per row per block
-    static constexpr int kFloats = RPB * G * (D + 2);
+    // m, l, acc per row; row weights; per-head sum and maximum
+    static constexpr int kFloats = RPB * G * (D + 3) + 2 * G;
 };
 
 template <class T, int G, int EPL, int NB>
@@ -1174,21 +1192,6 @@ __device__ inline void compute_block_rs(const KvBlock<T, G, T::EPL, NB> &kv, int
     });
 }
 
-// Group of work item `it`: the last group whose first item is <= it,
-// moved to a scalar register (workgroup-uniform).
-__device__ inline int group_of(const PlanTables &pt, int it, int NG)
-{
-    int lo = 0, hi = NG;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (pt.gbegin[mid] <= it)
-            lo = mid + 1;
-        else
-            hi = mid;
-    }
-    return __builtin_amdgcn_readfirstlane(lo - 1);
-}
-
 // Per-(request, KV group) state of the attention items: this lane's K/V
 // row pointers and its slice of the group's post-RoPE queries (pre-scaled
 // by scale * log2 e).  Built once per group, before the items are known.
@@ -1296,85 +1299,69 @@ __device__ inline void item_issue(const StepArgs &a, const ItemCtx<T, D, G> &ctx
         load_block<T, D, G, LPR, RPB, NB>(bufs.b, ctx.kb, ctx.vb, a.s.kv_st, t0 + TPB, t1, row);
 }
 
-// Attention of one work item whose first two blocks item_issue requested,
-// by the whole workgroup; head j of the group attends from st[j].  Each
-// block's successor two blocks ahead is requested as soon as the block has
-// been consumed.  The partial (o, log2-lse) of each head goes to
-// sink(j, dim, o, lse) for every dim (lse meaningful at dim 0).  lds holds
-// AttendShape::kFloats floats.
-template <class T, int D, int G, class Sink>
-__device__ inline void item_finish(const StepArgs &a, const ItemCtx<T, D, G> &ctx, int t0, int t1,
-                                   const int (&st)[G], float *lds, ItemBufs<T, D, G> &bufs,
-                                   Sink &&sink)
-{
-    using L = AttendShape<T, D, G>;
-    constexpr int EPL = L::EPL, LPR = L::LPR, RPB = L::RPB, NB = L::NB;
-    constexpr int TPB = RPB * NB;  // tokens per block
-    float *sm_m = lds;                  // [RPB][G]
-    float *sm_l = lds + RPB * G;        // [RPB][G]
-    float *sm_acc = lds + 2 * RPB * G;  // [RPB][G][D]
-    const Shape &s = a.s;
-    const int lane = threadIdx.x % LPR, row = threadIdx.x / LPR;
-    t0 = __builtin_amdgcn_readfirstlane(t0);
-    t1 = __builtin_amdgcn_readfirstlane(t1);
-    const auto *kb = ctx.kb, *vb = ctx.vb;
-    const auto &qr = ctx.qr;
-    auto &bufA = bufs.a;
-    auto &bufB = bufs.b;
-
-    float mrun[G], lrun[G], acc[G][EPL];
+// Running state of one work item's attention: per-row online softmax in
+// log2 units (with 16-lane rows, lane k keeps the running max / sum of head
+// k % G in mrun[0], lrun[0], and my_st is that head's token-start bound).
+template <class T, int D, int G>
+struct ItemAcc {
+    float mrun[G], lrun[G], acc[G][T::EPL];
+    int my_st;
+    __device__ void reset(const int (&st)[G], int lane)
+    {
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-        mrun[j] = -INFINITY;
-        lrun[j] = 0.f;
+        for (int j = 0; j < G; ++j) {
+            mrun[j] = -INFINITY;
+            lrun[j] = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e)
-            acc[j][e] = 0.f;
-    }
-    if constexpr (L::kScatter) {
-        // Lane k keeps the running max / sum of head k % G in mrun[0],
-        // lrun[0]; its token-start bound is that head's.
-        int my_st = __builtin_amdgcn_readfirstlane(st[0]);
+            for (int e = 0; e < T::EPL; ++e)
+                acc[j][e] = 0.f;
+        }
+        my_st = __builtin_amdgcn_readfirstlane(st[0]);
 #pragma unroll
         for (int j = 1; j < G; ++j)
             my_st = (lane % G == j) ? __builtin_amdgcn_readfirstlane(st[j]) : my_st;
-        for (int base = t0; base < t1; base += 2 * TPB) {
-            compute_block_rs<T, G, RPB, NB>(bufA, row, lane, qr, my_st, t1, mrun[0], lrun[0],
-                                            acc);
-            if (base + 2 * TPB < t1)
-                load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, base + 2 * TPB, t1,
-                                                  row);
-            if (base + TPB < t1) {
-                compute_block_rs<T, G, RPB, NB>(bufB, row, lane, qr, my_st, t1, mrun[0],
-                                                lrun[0], acc);
-                if (base + 3 * TPB < t1)
-                    load_block<T, D, G, LPR, RPB, NB>(bufB, kb, vb, s.kv_st, base + 3 * TPB,
-                                                      t1, row);
-            }
-        }
+    }
+};
+
+// One block of an item (tokens < t1; head j attends from st[j]).
+template <class T, int D, int G>
+__device__ inline void item_block(const KvBlock<T, G, T::EPL, AttendShape<T, D, G>::NB> &buf,
+                                  int row, int lane, const float (&qr)[G][T::EPL],
+                                  const int (&st)[G], int t1, ItemAcc<T, D, G> &ia)
+{
+    using L = AttendShape<T, D, G>;
+    if constexpr (L::kScatter)
+        compute_block_rs<T, G, L::RPB, L::NB>(buf, row, lane, qr, ia.my_st, t1, ia.mrun[0],
+                                              ia.lrun[0], ia.acc);
+    else
+        compute_block<T, D, G, L::LPR, L::RPB, L::NB>(buf, row, qr, st, t1, ia.mrun, ia.lrun,
+                                                      ia.acc);
+}
+
+// The RPB row states of an item are combined in LDS in a fixed order into
+// one partial (o, log2-lse) per head, handed to sink(j, dim, o, lse) for
+// every dim (lse meaningful at dim 0).  lds holds AttendShape::kFloats
+// floats; the call starts and ends with the workgroup in step.
+template <class T, int D, int G, class Sink>
+__device__ inline void item_combine(const ItemAcc<T, D, G> &ia, float *lds, int row, int lane,
+                                    Sink &&sink)
+{
+    using L = AttendShape<T, D, G>;
+    constexpr int EPL = L::EPL, RPB = L::RPB;
+    float *sm_m = lds;                  // [RPB][G]
+    float *sm_l = lds + RPB * G;        // [RPB][G]
+    float *sm_acc = lds + 2 * RPB * G;  // [RPB][G][D]
+    if constexpr (L::kScatter) {
         if (lane < G) {
-            sm_m[row * G + lane] = mrun[0];
-            sm_l[row * G + lane] = lrun[0];
+            sm_m[row * G + lane] = ia.mrun[0];
+            sm_l[row * G + lane] = ia.lrun[0];
         }
     } else {
-        // Blocks alternate between the two buffers.
-        for (int base = t0; base < t1; base += 2 * TPB) {
-            compute_block<T, D, G, LPR, RPB, NB>(bufA, row, qr, st, t1, mrun, lrun, acc);
-            if (base + 2 * TPB < t1)
-                load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, base + 2 * TPB, t1,
-                                                  row);
-            if (base + TPB < t1) {
-                compute_block<T, D, G, LPR, RPB, NB>(bufB, row, qr, st, t1, mrun, lrun, acc);
-                if (base + 3 * TPB < t1)
-                    load_block<T, D, G, LPR, RPB, NB>(bufB, kb, vb, s.kv_st, base + 3 * TPB,
-                                                      t1, row);
-            }
-        }
         if (lane == 0) {
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                sm_m[row * G + j] = mrun[j];
-                sm_l[row * G + j] = lrun[j];
+                sm_m[row * G + j] = ia.mrun[j];
+                sm_l[row * G + j] = ia.lrun[j];
             }
         }
     }
@@ -1382,49 +1369,146 @@ __device__ inline void item_finish(const StepArgs &a, const ItemCtx<T, D, G> &ct
     for (int j = 0; j < G; ++j)
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
-            sm_acc[(row * G + j) * D + lane * EPL + e] = acc[j][e];
+            sm_acc[(row * G + j) * D + lane * EPL + e] = ia.acc[j][e];
     __syncthreads();
-    // Row weights: c[rr][j] = 2^(m[rr][j] - M_j) replaces m in LDS;
-    // sm_l[0][j] becomes head j's total sum and sm_l[RPB-1][j] its M.
-    float cw = 0.f, Ls = 0.f, Mj = -INFINITY;
+    // Row weights c[rr][j] = 2^(m[rr][j] - M_j), one per thread; then head
+    // j's total sum L_j = sum_rr c[rr][j] * l[rr][j] in row order.
+    float *sm_c = sm_acc + RPB * G * D;  // [RPB][G]
+    float *sm_hd = sm_c + RPB * G;       // [G]: L_j, then [G]: M_j
     const int wr = threadIdx.x / G, wj = threadIdx.x - wr * G;
     if (threadIdx.x < RPB * G) {
-#pragma unroll 8
+        float Mj = -INFINITY;
+#pragma unroll
         for (int q = 0; q < RPB; ++q)
             Mj = fmaxf(Mj, sm_m[q * G + wj]);
-        if (Mj != -INFINITY) {
-            cw = ex2(sm_m[wr * G + wj] - Mj);
-            if (wr == 0) {
-#pragma unroll 8
-                for (int q = 0; q < RPB; ++q)
-                    Ls = fmaf(ex2(sm_m[q * G + wj] - Mj), sm_l[q * G + wj], Ls);
-            }
-        }
+        sm_c[wr * G + wj] = Mj != -INFINITY ? ex2(sm_m[wr * G + wj] - Mj) : 0.f;
+        if (wr == 0)
+            sm_hd[G + wj] = Mj;
     }
     __syncthreads();
-    if (threadIdx.x < RPB * G) {
-        sm_m[wr * G + wj] = cw;
-        if (wr == 0) {
-            sm_l[wj] = Ls;
-            sm_l[(RPB - 1) * G + wj] = Mj;
+    if (threadIdx.x < G) {
+        float Ls = 0.f;
+        if (sm_hd[G + threadIdx.x] != -INFINITY) {
+#pragma unroll
+            for (int q = 0; q < RPB; ++q)
+                Ls = fmaf(sm_c[q * G + threadIdx.x], sm_l[q * G + threadIdx.x], Ls);
         }
+        sm_hd[threadIdx.x] = Ls;
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
         const int j = idx / D, dim = idx - j * D;
-        const float ls = sm_l[j];
+        const float ls = sm_hd[j];
         float o = 0.f, Lg = -INFINITY;
         if (ls > 0.f) {
             float os = 0.f;
-#pragma unroll 8
+#pragma unroll
             for (int rr = 0; rr < RPB; ++rr)
-                os = fmaf(sm_m[rr * G + j], sm_acc[(rr * G + j) * D + dim], os);
+                os = fmaf(sm_c[rr * G + j], sm_acc[(rr * G + j) * D + dim], os);
             o = os / ls;
-            Lg = sm_l[(RPB - 1) * G + j] + lg2(ls);
+            Lg = sm_hd[G + j] + lg2(ls);
         }
         sink(j, dim, o, Lg);
     }
+    __syncthreads();  // lds is free again
 }
+
+// Attention of one work item whose first two blocks item_issue requested,
+// by the whole workgroup; head j of the group attends from st[j].  Each
+// block's successor two blocks ahead is requested as soon as the block has
+// been consumed.  The partial goes to sink as in item_combine.
+template <class T, int D, int G, class Sink>
+__device__ inline void item_finish(const StepArgs &a, const ItemCtx<T, D, G> &ctx, int t0, int t1,
+                                   const int (&st)[G], float *lds, ItemBufs<T, D, G> &bufs,
+                                   Sink &&sink)
+{
+    using L = AttendShape<T, D, G>;
+    constexpr int LPR = L::LPR, RPB = L::RPB, NB = L::NB;
+    constexpr int TPB = RPB * NB;  // tokens per block
+    const Shape &s = a.s;
+    const int lane = threadIdx.x % LPR, row = threadIdx.x / LPR;
+    t0 = __builtin_amdgcn_readfirstlane(t0);
+    t1 = __builtin_amdgcn_readfirstlane(t1);
+    const auto *kb = ctx.kb, *vb = ctx.vb;
+    auto &bufA = bufs.a;
+    auto &bufB = bufs.b;
+    ItemAcc<T, D, G> ia;
+    ia.reset(st, lane);
+    for (int base = t0; base < t1; base += 2 * TPB) {
+        item_block<T, D, G>(bufA, row, lane, ctx.qr, st, t1, ia);
+        if (base + 2 * TPB < t1)
+            load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, base + 2 * TPB, t1, row);
+        if (base + TPB < t1) {
+            item_block<T, D, G>(bufB, row, lane, ctx.qr, st, t1, ia);
+            if (base + 3 * TPB < t1)
+                load_block<T, D, G, LPR, RPB, NB>(bufB, kb, vb, s.kv_st, base + 3 * TPB, t1, row);
+        }
+    }
+    item_combine<T, D, G>(ia, lds, row, lane, sink);
+}
+
+// This workgroup's share of the work list (see attend_kernel): the items
+// in order, skipping empty groups; `valid` is false past the share.
+struct ShareIter {
+    const PlanTables *pt;
+    int NG, r_split, hi;
+    int grp, i, t0, t1;
+    bool valid;
+    RangeSplit rs;
+    __device__ ShareIter(const PlanTables &p, int ng, int rsplit, int lo, int hi_)
+        : pt(&p), NG(ng), r_split(rsplit), hi(hi_), grp(0), i(0), t0(0), t1(0), valid(false),
+          rs(0, 0, 0)
+    {
+        int l = 0, h = NG;  // last group with work offset <= lo
+        while (l < h) {
+            const int mid = (l + h) >> 1;
+            if (pt->gwork[mid] <= lo)
+                l = mid + 1;
+            else
+                h = mid;
+        }
+        grp = l - 1 < 0 ? 0 : l - 1;
+        rs = RangeSplit(pt->gstart[grp], pt->gend[grp], r_split);
+        l = 0;
+        h = pt->gcount[grp];  // first item with offset >= lo
+        while (l < h) {
+            const int mid = (l + h) >> 1;
+            if (offset(mid) < lo)
+                l = mid + 1;
+            else
+                h = mid;
+        }
+        i = l;
+        settle();
+    }
+    __device__ int offset(int ii) const
+    {
+        int a0, a1;
+        rs.item(ii, a0, a1);
+        return pt->gwork[grp] + (a0 - pt->gstart[grp]) + kItemCost * ii;
+    }
+    __device__ void settle()
+    {
+        while (grp < NG && i >= pt->gcount[grp]) {
+            ++grp;
+            i = 0;
+            if (grp < NG)
+                rs = RangeSplit(pt->gstart[grp], pt->gend[grp], r_split);
+        }
+        valid = grp < NG && offset(i) < hi;
+        if (valid)
+            rs.item(i, t0, t1);
+        grp = __builtin_amdgcn_readfirstlane(grp);
+        t0 = __builtin_amdgcn_readfirstlane(t0);
+        t1 = __builtin_amdgcn_readfirstlane(t1);
+    }
+    __device__ void next()
+    {
+        ++i;
+        settle();
+    }
+    __device__ int item_index() const { return pt->gbegin[grp] + i; }
+};
 
 // Plan + attention kernel.  kWarm only renames the instantiation used by
 // the ring warm-up, so kernel profiles separate it from decode steps.
@@ -1437,25 +1521,82 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
     const Shape &s = a.s;
     const int NG = s.B * s.Hkv;
     const int r_split = (a.mode == kPlanInit) ? 0 : s.r;
-    for (int it = blockIdx.x; it < pt.total; it += gridDim.x) {
-        const int grp = group_of(pt, it, NG);
-        const int b = grp / s.Hkv, g = grp - b * s.Hkv;
-        int t0, t1, st[G];
-        RangeSplit(pt.gstart[grp], pt.gend[grp], r_split).item(it - pt.gbegin[grp], t0, t1);
+    using L = AttendShape<T, D, G>;
+    constexpr int LPR = L::LPR, RPB = L::RPB, NB = L::NB, TPB = RPB * NB;
+    using S = typename T::S;
+    const int lane = threadIdx.x % LPR, row = threadIdx.x / LPR;
+    // Balanced contiguous share: this workgroup runs the items whose work
+    // offset (the group's offset + tokens before the item + kItemCost per
+    // earlier item of the group) lies in [lo, hi), the grid splitting the
+    // total work evenly.  Which workgroup runs an item does not change the
+    // results: partials are stored by item index.
+    const int lo = (int)((int64_t)pt.work * blockIdx.x / gridDim.x);
+    const int hi = (int)((int64_t)pt.work * (blockIdx.x + 1) / gridDim.x);
+    ShareIter cur(pt, NG, r_split, lo, hi);
+    if (!cur.valid)
+        return;
+    // The share's blocks stream through two buffers, two blocks ahead of the
+    // computation, across item and group boundaries.
+    ShareIter ld = cur;
+    int ld_base = ld.t0;
+    auto issue = [&](KvBlock<T, G, T::EPL, NB> &buf) {
+        if (!ld.valid)
+            return;
+        const int lb = ld.grp / s.Hkv, lg = ld.grp - lb * s.Hkv;
+        const S *kb = (const S *)a.k + lb * s.kv_sb + lg * s.kv_sh + lane * T::EPL;
+        const S *vb = (const S *)a.v + lb * s.kv_sb + lg * s.kv_sh + lane * T::EPL;
+        load_block<T, D, G, LPR, RPB, NB>(buf, kb, vb, s.kv_st, ld_base, ld.t1, row);
+        ld_base += TPB;
+        if (ld_base >= ld.t1) {
+            ld.next();
+            ld_base = ld.t0;
+        }
+    };
+    KvBlock<T, G, T::EPL, NB> bufA, bufB;
+    issue(bufA);
+    issue(bufB);
+
+    int qgrp = cur.grp;
+    ItemCtx<T, D, G> ctx(a, qgrp / s.Hkv, qgrp % s.Hkv);
+    int st[G];
+    ItemAcc<T, D, G> ia;
+    auto begin_item = [&] {
+        const int b = cur.grp / s.Hkv, g = cur.grp - b * s.Hkv;
 #pragma unroll
         for (int j = 0; j < G; ++j)
             st[j] = code_start(pt.code[b * s.Hq + g * G + j]);
+        if (cur.grp != qgrp) {
+            qgrp = cur.grp;
+            ctx = ItemCtx<T, D, G>(a, b, g);
+        }
+        ia.reset(st, lane);
+    };
+    begin_item();
+    int cb = cur.t0;  // first token of the block being consumed
+    // Consumes the block in buf, refills buf two blocks ahead, and closes the
+    // item after its last block; false once the share is done.
+    auto consume = [&](KvBlock<T, G, T::EPL, NB> &buf) {
+        item_block<T, D, G>(buf, row, lane, ctx.qr, st, cur.t1, ia);
+        issue(buf);
+        cb += TPB;
+        if (cb < cur.t1)
+            return true;
+        const int it = cur.item_index();
         float *po = a.w.part_o + (int64_t)it * G * D;
         float *pl = a.w.part_l + (int64_t)it * G;
-        const ItemCtx<T, D, G> ctx(a, b, g);
-        ItemBufs<T, D, G> bufs;
-        item_issue<T, D, G>(a, ctx, t0, t1, bufs, false);
-        item_finish<T, D, G>(a, ctx, t0, t1, st, lds, bufs, [&](int j, int dim, float o, float lg) {
+        item_combine<T, D, G>(ia, lds, row, lane, [&](int j, int dim, float o, float lgv) {
             po[j * D + dim] = o;
             if (dim == 0)
-                pl[j] = lg;
+                pl[j] = lgv;
         });
-        __syncthreads();
+        cur.next();
+        if (!cur.valid)
+            return false;
+        cb = cur.t0;
+        begin_item();
+        return true;
+    };
+    while (consume(bufA) && consume(bufB)) {
     }
 }
 
@@ -1809,7 +1950,7 @@ __global__ void ring_reset_kernel(int64_t n_q, S *__restrict__ q_ring,
 size_t plan_lds_bytes(int B, int Hq, int Hkv)
 {
     const size_t BH = (size_t)B * Hq, NG = (size_t)B * Hkv;
-    return 4 * (BH + 4 * NG + 1 + kBlock / 64);
+    return 4 * (BH + 5 * NG + 2 + 2 * (kBlock / 64));
 }
 
 int device_cu_count()
