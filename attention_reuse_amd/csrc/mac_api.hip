@@ -279,6 +279,7 @@ static StepArgs base_args(const Shape &s, const WsLayout &L, const WsPtrs &w)
     a.w = w;
     a.max_items = L.max_items;
     a.nsplit = L.nsplit;
+    a.dyn_pool = 1;
     return a;
 }
 
@@ -303,6 +304,9 @@ mac_status mac_full_decode(const mac_params *p, const float *q,
     const WsLayout L = ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T, s.dtype, false);
     StepArgs a = base_args(s, L, ws_ptrs(workspace, L));
     a.mode = kPlanFull;
+    // A caller's workspace may be fresh: full decode splits its (regular)
+    // work statically and claims nothing.
+    a.dyn_pool = 0;
     a.pos = pos;
     a.q = q;
     a.q_sh = s.D;

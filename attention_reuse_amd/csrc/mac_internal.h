@@ -16,6 +16,11 @@ constexpr int kChunkMin = 1 << kChunkMinShift;
 // Work of an item in the attention kernel's balanced split: its tokens plus
 // this many (the per-item cost of combining rows and storing the partial).
 constexpr int kItemCost = 64;
+// The attention kernel splits the first kStaticPct percent of the work
+// statically; workgroups that finish their share claim the rest item by item.
+constexpr int kStaticPct = 70;
+// ... when the plan has at least this many items per workgroup.
+constexpr int kPoolItems = 4;
 constexpr int kMaxItemsPerGroup = 128;
 // Ring slots scanned by one match workgroup.
 constexpr int kSlotsPerSplit = 64;
@@ -182,8 +187,10 @@ enum PlanMode : int32_t {
     kPlanInit = 2,   // full, end = pos[b] + end_offset, a negative end is empty
 };
 
-// ctrl words: [0] work items of the latest call, [1] its status flags.
-enum { kCtrlItems = 0, kCtrlStatus = 1 };
+// ctrl words: [0] work items of the latest call, [1] its status flags, [2]
+// the attention kernel's claim counter of its dynamic items (reset to 0 by
+// the merge kernel that follows every attention launch).
+enum { kCtrlItems = 0, kCtrlStatus = 1, kCtrlClaim = 2 };
 
 struct Shape {
     int32_t B, Hq, Hkv, G, D, dtype, K, r, T;
@@ -234,6 +241,11 @@ struct StepArgs {
     // nsplit), key words per group, log2 of the done increment per launch,
     // ring slots per match unit
     int32_t wpg, upg, nkw, done_shift, unit_slots;
+    // attention kernel: 1 = the last (100 - kStaticPct)% of the work is a pool
+    // claimed through ctrl[kCtrlClaim], which must then read 0 at the launch
+    // (the ring reset and every merge kernel leave it so); 0 = all of the
+    // work is split statically and the counter is not touched
+    int32_t dyn_pool;
 };
 
 // Bytes of dynamic LDS the planner needs.

@@ -63,6 +63,26 @@ struct BF16 {
     static constexpr int EPL = 8;
 };
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ inline uint32_t bf16_bits(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// x * scale rounded to bf16 (hi) and the remainder rounded to bf16 (lo).
+// No contraction: every caller rounds the product and the difference alike.
+__device__ inline void split_bf16(float x, float scale, uint32_t &hi, uint32_t &lo)
+{
+#pragma clang fp contract(off)
+    const float xs = x * scale;
+    hi = bf16_bits(xs);
+    lo = bf16_bits(xs - __uint_as_float(hi << 16));
+}
+
 template <class T>
 __device__ inline void unpack(const uint4 &v, float *f);
 
@@ -138,6 +158,7 @@ __device__ inline void static_for(F &&f)
 }
 
 constexpr int kDppRowRor = 0x120;       // + n: lane i <- lane (i - n) mod 16
+constexpr int kDppRowShr = 0x110;       // + n: lane i <- lane i - n (0 below n)
 constexpr int kDppRowNewBcast = 0x150;  // + n: every lane <- lane n of its row
 
 // Reduce-scatter of 16 values over the 16 lanes of a row: lane L returns
@@ -1019,6 +1040,8 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(StepArgs a)
     const int grp = blockIdx.x;
     if (threadIdx.x < G)  // ready for the next step's match
         a.w.keys[((int64_t)grp * G + threadIdx.x) * kKeyStride] = ~0ull;
+    if (grp == 0 && threadIdx.x == 0)  // ready for the next attention launch
+        a.w.ctrl[kCtrlClaim] = 0;
     const int cnt = a.w.grp_count[grp];
     if (cnt == 0)
         return;  // the planner wrote this group's outputs
@@ -1042,6 +1065,11 @@ struct AttendShape {
     // lane); other row widths all-reduce every logit.
     static constexpr bool kScatter = LPR == 16;
     static constexpr int NB = kScatter ? (16 / G < 4 ? 16 / G : 4) : 4;  // tokens per row per block
+    // bf16 K with d = 128 and 4 heads per KV head: the logits of a wave's 16
+    // tokens come from 4 MFMAs (16 tokens x 32 dims x 16 columns: the 4
+    // heads' queries split into bf16 high and low parts, 8 columns unused)
+    // instead of VALU dot products and a row reduce-scatter.
+    static constexpr bool kMfma = kScatter && T::EPL == 8 && D == 128 && G == 4;
     // m, l, acc per row; row weights; per-head sum and maximum
     static constexpr int kFloats = RPB * G * (D + 3) + 2 * G;
 };
@@ -1051,6 +1079,19 @@ struct KvBlock {
     uint4 k[NB], v[NB];
     int base;  // token of row 0, i = 0
 };
+
+// Per-lane element offset into a K row.  On the MFMA path lane l of a wave
+// holds dims 8 * (l / 16) + 32 * kk of its token for MFMA kk (the A-operand
+// layout of v_mfma_f32_16x16x32_bf16: row l % 16, 8 consecutive k per 16
+// lanes); otherwise lane l % 16 of a row holds dims 8 * (l % 16).
+template <class T, int D, int G>
+__device__ inline int k_lane_offset()
+{
+    if constexpr (AttendShape<T, D, G>::kMfma)
+        return 8 * ((threadIdx.x & 63) >> 4);
+    else
+        return (threadIdx.x % (D / T::EPL)) * T::EPL;
+}
 
 // K/V rows of one block.  Every lane loads: a token at or past t1 reads row
 // t1 - 1 of the item instead, which the block computation masks (its logit
@@ -1062,14 +1103,87 @@ __device__ inline void load_block(KvBlock<T, G, T::EPL, NB> &kv, const typename 
                                   int row)
 {
     kv.base = base;
+    if constexpr (AttendShape<T, D, G>::kMfma) {
+        // K in the MFMA A layout: lane l (m = l % 16) loads token
+        // base + 16 * (m % 4) + 4 * wave + m / 4, i.e. slot m % 4 of row
+        // 4 * wave + m / 4, so that logit row 4 * r + v of the product is
+        // slot v of the wave's row r; kb carries the lane's dim offset.
+        const int m = threadIdx.x & 15;
+        int tk = base + 16 * (m & 3) + 4 * (threadIdx.x >> 6) + (m >> 2);
+        tk = tk < t1 ? tk : t1 - 1;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        int t = base + i * RPB + row;
-        t = t < t1 ? t : t1 - 1;
-        kv.k[i] = load16(kb + (int64_t)t * kv_st);
-        kv.v[i] = load16(vb + (int64_t)t * kv_st);
+        for (int kk = 0; kk < NB; ++kk)
+            kv.k[kk] = load16(kb + (int64_t)tk * kv_st + 32 * kk);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            int t = base + i * RPB + row;
+            t = t < t1 ? t : t1 - 1;
+            kv.v[i] = load16(vb + (int64_t)t * kv_st);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            int t = base + i * RPB + row;
+            t = t < t1 ? t : t1 - 1;
+            kv.k[i] = load16(kb + (int64_t)t * kv_st);
+            kv.v[i] = load16(vb + (int64_t)t * kv_st);
+        }
     }
 }
+
+// The group's post-RoPE queries in the form the logit computation takes,
+// scaled by scale * log2 e: this lane's fp32 slices for the VALU dot
+// products, or, on the MFMA path, the B operands of the 4 MFMAs.  B operand
+// kk of lane l holds column n = l % 16, dims 32 * kk + 8 * ((l / 16) % 4) + e:
+// head n's query rounded to bf16 for n < 4, what that rounding lost (again in
+// bf16) for 4 <= n < 8 (the sum of the two columns' logits carries the query
+// to about 16 significant bits), zero above.
+template <class T, int D, int G>
+struct QRegs {
+    static constexpr bool kMfma = AttendShape<T, D, G>::kMfma;
+    float qr[kMfma ? 1 : G][T::EPL];
+    uint4 qb[4];
+    // src(j, d0, x): the 4 floats of head j's query from dim d0 into x.
+    template <class Src>
+    __device__ void fill(Src &&src, float qscale)
+    {
+        if constexpr (kMfma) {
+            const int n = threadIdx.x & 15, kg = (threadIdx.x >> 4) & 3;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    x[e] = 0.f;
+                if (n < 8) {
+                    src(n & 3, 32 * kk + 8 * kg, x);
+                    src(n & 3, 32 * kk + 8 * kg + 4, x + 4);
+                }
+                uint32_t bb[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    uint32_t hb, lb;
+                    split_bf16(x[e], qscale, hb, lb);
+                    bb[e] = n < 4 ? hb : n < 8 ? lb : 0u;
+                }
+                qb[kk] = make_uint4(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16),
+                                    bb[4] | (bb[5] << 16), bb[6] | (bb[7] << 16));
+            }
+        } else {
+            const int lane = threadIdx.x % (D / T::EPL);
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+#pragma unroll
+                for (int e4 = 0; e4 < T::EPL; e4 += 4) {
+                    float x[4];
+                    src(j, lane * T::EPL + e4, x);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        qr[j][e4 + e] = x[e] * qscale;
+                }
+        }
+    }
+};
 
 template <class T, int D, int G, int LPR, int RPB, int NB>
 __device__ inline void compute_block(const KvBlock<T, G, T::EPL, NB> &kv, int row,
@@ -1140,31 +1254,59 @@ __device__ inline void compute_block(const KvBlock<T, G, T::EPL, NB> &kv, int ro
 // exponentials per lane.  The per-head running max and sum live in the
 // lanes of that head; probabilities and rescale factors reach the P*V
 // products through row broadcasts.
-template <class T, int G, int RPB, int NB>
+template <class T, int D, int G, int RPB, int NB>
 __device__ inline void compute_block_rs(const KvBlock<T, G, T::EPL, NB> &kv, int row, int lane,
-                                        const float (&qr)[G][T::EPL], int my_st, int t1,
+                                        const QRegs<T, D, G> &q, int my_st, int t1,
                                         float &mrun, float &lrun, float (&acc)[G][T::EPL])
 {
+    constexpr bool kMfma = QRegs<T, D, G>::kMfma;
+    const auto &qr = q.qr;
+    const auto &qb = q.qb;
     constexpr int EPL = T::EPL;
     static_assert(NB * G <= 16, "values per row");
-    float v[16];
+    float sv;
+    if constexpr (kMfma) {
+        // qb[kk]: this lane's B operand of MFMA kk (see ItemCtx).  Product
+        // row 4 * r + v, column n sits in lane 16 * r + n, element v: the
+        // logit of slot v of row r against column n.  Column n + 4 holds the
+        // low part of head n's query.
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
-        v[k] = 0.f;
+        for (int kk = 0; kk < 4; ++kk)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv.k[kk]),
+                                                        __builtin_bit_cast(bf16x8, qb[kk]), c, 0,
+                                                        0, 0);
+        float sh[4];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        float kf[EPL];
-        unpack<T>(kv.k[i], kf);
+        for (int v = 0; v < 4; ++v)
+            sh[v] = c[v] + dpp<kDppRowRor + 12>(c[v]);
+        // Lane 4 * v + h of the row takes lane h's value v: the layout of
+        // the reduce-scatter below (lane k: slot k / 4, head k % 4).
+        const float s1 = dpp<kDppRowShr + 4>(sh[1]);
+        const float s2 = dpp<kDppRowShr + 8>(sh[2]);
+        const float s3 = dpp<kDppRowShr + 12>(sh[3]);
+        const int qd = lane >> 2;
+        sv = qd == 0 ? sh[0] : qd == 1 ? s1 : qd == 2 ? s2 : s3;
+    } else {
+        float v[16];
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            float x = 0.f;
+        for (int k = 0; k < 16; ++k)
+            v[k] = 0.f;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e)
-                x = fmaf(qr[j][e], kf[e], x);
-            v[i * G + j] = x;
+        for (int i = 0; i < NB; ++i) {
+            float kf[EPL];
+            unpack<T>(kv.k[i], kf);
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                float x = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e)
+                    x = fmaf(qr[j][e], kf[e], x);
+                v[i * G + j] = x;
+            }
         }
+        sv = row_reduce_scatter16(v, lane);
     }
-    float sv = row_reduce_scatter16(v, lane);
     const int t = kv.base + (lane / G) * RPB + row;
     sv = (lane < NB * G && t < t1 && t >= my_st) ? sv : -INFINITY;
     const float bm = row_mod_reduce<G, true>(sv);
@@ -1200,50 +1342,49 @@ struct ItemCtx {
     using S = typename T::S;
     static constexpr int EPL = T::EPL;
     const S *kb, *vb;
-    float qr[G][EPL];
+    QRegs<T, D, G> q;
     // K/V row pointers only; the queries come from queries_from_lds.
     __device__ ItemCtx(const StepArgs &a, int b, int g, bool)
     {
         const Shape &s = a.s;
         const int lane = threadIdx.x % (D / EPL);
-        kb = (const S *)a.k + b * s.kv_sb + g * s.kv_sh + lane * EPL;
+        kb = (const S *)a.k + b * s.kv_sb + g * s.kv_sh + k_lane_offset<T, D, G>();
         vb = (const S *)a.v + b * s.kv_sb + g * s.kv_sh + lane * EPL;
     }
-    // This lane's slice of the group's queries from LDS ([G][D] floats, as
-    // stored by stage_queries), scaled as the global-memory constructor
-    // scales them.
-    __device__ void queries_from_lds(const float *s_q, float qscale)
+    // This lane's queries from LDS ([G][D] floats, as QueryStage stores
+    // them, and on the MFMA path the B operands QueryStage::store_b forms),
+    // scaled as the global-memory constructor scales them.
+    __device__ void queries_from_lds(const float *s_q, const uint4 *s_qb, float qscale)
     {
-        const int lane = threadIdx.x % (D / EPL);
+        if constexpr (QRegs<T, D, G>::kMfma) {
 #pragma unroll
-        for (int j = 0; j < G; ++j)
-#pragma unroll
-            for (int e4 = 0; e4 < EPL; e4 += 4) {
-                const float4 v = *reinterpret_cast<const float4 *>(s_q + j * D + lane * EPL + e4);
-                qr[j][e4 + 0] = v.x * qscale;
-                qr[j][e4 + 1] = v.y * qscale;
-                qr[j][e4 + 2] = v.z * qscale;
-                qr[j][e4 + 3] = v.w * qscale;
-            }
-    }
-    __device__ ItemCtx(const StepArgs &a, int b, int g)
-    {
-        const Shape &s = a.s;
-        const int lane = threadIdx.x % (D / EPL);
-        kb = (const S *)a.k + b * s.kv_sb + g * s.kv_sh + lane * EPL;
-        vb = (const S *)a.v + b * s.kv_sb + g * s.kv_sh + lane * EPL;
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const float *qp = a.q + b * a.q_sb + (int64_t)(g * G + j) * a.q_sh + lane * EPL;
-#pragma unroll
-            for (int e4 = 0; e4 < EPL; e4 += 4) {
-                const float4 v = *reinterpret_cast<const float4 *>(qp + e4);
-                qr[j][e4 + 0] = v.x * s.qscale;
-                qr[j][e4 + 1] = v.y * s.qscale;
-                qr[j][e4 + 2] = v.z * s.qscale;
-                qr[j][e4 + 3] = v.w * s.qscale;
-            }
+            for (int kk = 0; kk < 4; ++kk)
+                q.qb[kk] = s_qb[kk * 64 + (threadIdx.x & 63)];
+            return;
         }
+        q.fill(
+            [&](int j, int d0, float *x) {
+                const float4 v = *reinterpret_cast<const float4 *>(s_q + j * D + d0);
+                x[0] = v.x;
+                x[1] = v.y;
+                x[2] = v.z;
+                x[3] = v.w;
+            },
+            qscale);
+    }
+    __device__ ItemCtx(const StepArgs &a, int b, int g) : ItemCtx(a, b, g, true)
+    {
+        const float *qp = a.q + b * a.q_sb + (int64_t)(g * G) * a.q_sh;
+        const int64_t qsh = a.q_sh;
+        q.fill(
+            [&](int j, int d0, float *x) {
+                const float4 v = *reinterpret_cast<const float4 *>(qp + j * qsh + d0);
+                x[0] = v.x;
+                x[1] = v.y;
+                x[2] = v.z;
+                x[3] = v.w;
+            },
+            a.s.qscale);
     }
 };
 
@@ -1273,6 +1414,28 @@ struct QueryStage {
             const int i = threadIdx.x + k * kBlock;
             if (i < kPairs)
                 *reinterpret_cast<float2 *>(s_q + 2 * i) = v[k];
+        }
+    }
+    // The MFMA B operands of QRegs (D = 128, G = 4), formed once per
+    // workgroup: s_qb[kk * 64 + l] is lane l's operand of MFMA kk.  Each
+    // thread rounds its pair (high and low bf16 parts, as QRegs::fill does)
+    // into the two columns of its head; the threads below 128 clear the
+    // unused columns 8..15.
+    __device__ void store_b(uint4 *s_qb, float qscale) const
+    {
+        static_assert(D == 128 && G == 4 && kPer == 1, "MFMA operand shape");
+        uint32_t *w = reinterpret_cast<uint32_t *>(s_qb);
+        const int i = threadIdx.x;  // pair: head j, dims d, d + 1
+        const int j = i / (D / 2), d = 2 * (i - j * (D / 2));
+        const int kk = d / 32, kg = (d % 32) / 8, e = d % 8;
+        uint32_t h0, h1, l0, l1;
+        split_bf16(v[0].x, qscale, h0, l0);
+        split_bf16(v[0].y, qscale, h1, l1);
+        w[(kk * 64 + 16 * kg + j) * 4 + e / 2] = h0 | (h1 << 16);
+        w[(kk * 64 + 16 * kg + j + 4) * 4 + e / 2] = l0 | (l1 << 16);
+        if (threadIdx.x < 128) {
+            const int zk = threadIdx.x / 32, z = threadIdx.x % 32;
+            s_qb[zk * 64 + 16 * (z / 8) + 8 + z % 8] = make_uint4(0, 0, 0, 0);
         }
     }
 };
@@ -1326,16 +1489,16 @@ struct ItemAcc {
 // One block of an item (tokens < t1; head j attends from st[j]).
 template <class T, int D, int G>
 __device__ inline void item_block(const KvBlock<T, G, T::EPL, AttendShape<T, D, G>::NB> &buf,
-                                  int row, int lane, const float (&qr)[G][T::EPL],
+                                  int row, int lane, const QRegs<T, D, G> &q,
                                   const int (&st)[G], int t1, ItemAcc<T, D, G> &ia)
 {
     using L = AttendShape<T, D, G>;
     if constexpr (L::kScatter)
-        compute_block_rs<T, G, L::RPB, L::NB>(buf, row, lane, qr, ia.my_st, t1, ia.mrun[0],
-                                              ia.lrun[0], ia.acc);
+        compute_block_rs<T, D, G, L::RPB, L::NB>(buf, row, lane, q, ia.my_st, t1, ia.mrun[0],
+                                                 ia.lrun[0], ia.acc);
     else
-        compute_block<T, D, G, L::LPR, L::RPB, L::NB>(buf, row, qr, st, t1, ia.mrun, ia.lrun,
-                                                      ia.acc);
+        compute_block<T, D, G, L::LPR, L::RPB, L::NB>(buf, row, q.qr, st, t1, ia.mrun,
+                                                      ia.lrun, ia.acc);
 }
 
 // The RPB row states of an item are combined in LDS in a fixed order into
@@ -1435,11 +1598,11 @@ __device__ inline void item_finish(const StepArgs &a, const ItemCtx<T, D, G> &ct
     ItemAcc<T, D, G> ia;
     ia.reset(st, lane);
     for (int base = t0; base < t1; base += 2 * TPB) {
-        item_block<T, D, G>(bufA, row, lane, ctx.qr, st, t1, ia);
+        item_block<T, D, G>(bufA, row, lane, ctx.q, st, t1, ia);
         if (base + 2 * TPB < t1)
             load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, base + 2 * TPB, t1, row);
         if (base + TPB < t1) {
-            item_block<T, D, G>(bufB, row, lane, ctx.qr, st, t1, ia);
+            item_block<T, D, G>(bufB, row, lane, ctx.q, st, t1, ia);
             if (base + 3 * TPB < t1)
                 load_block<T, D, G, LPR, RPB, NB>(bufB, kb, vb, s.kv_st, base + 3 * TPB, t1, row);
         }
@@ -1525,32 +1688,104 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
     constexpr int LPR = L::LPR, RPB = L::RPB, NB = L::NB, TPB = RPB * NB;
     using S = typename T::S;
     const int lane = threadIdx.x % LPR, row = threadIdx.x / LPR;
-    // Balanced contiguous share: this workgroup runs the items whose work
-    // offset (the group's offset + tokens before the item + kItemCost per
-    // earlier item of the group) lies in [lo, hi), the grid splitting the
-    // total work evenly.  Which workgroup runs an item does not change the
-    // results: partials are stored by item index.
-    const int lo = (int)((int64_t)pt.work * blockIdx.x / gridDim.x);
-    const int hi = (int)((int64_t)pt.work * (blockIdx.x + 1) / gridDim.x);
+    // Work split: the items whose work offset (the group's offset + tokens
+    // before the item + kItemCost per earlier item of the group) lies below
+    // kStaticPct percent of the total are shared statically, workgroup w
+    // running those in [w * Ws / grid, (w + 1) * Ws / grid): a contiguous run
+    // of near-equal work.  The remaining items form a pool that workgroups
+    // claim one at a time, with an atomic counter, once their share is done,
+    // so faster workgroups take more of it.  Which workgroup runs an item
+    // does not change the results: partials are stored by item index.
+    // The pool pays for its claims (an atomic round trip and a barrier each)
+    // only when workgroups have several items to run: at least kPoolItems
+    // per workgroup on average.
+    const bool pooled = a.dyn_pool && pt.total >= kPoolItems * (int)gridDim.x;
+    const int Ws = pooled ? (int)((int64_t)pt.work * kStaticPct / 100) : pt.work;
+    const int lo = (int)((int64_t)Ws * blockIdx.x / gridDim.x);
+    const int hi = (int)((int64_t)Ws * (blockIdx.x + 1) / gridDim.x);
+    __shared__ int s_claim[4];
+    int dyn_first;
+    {
+        const ShareIter pool(pt, NG, r_split, Ws, INT_MAX);
+        dyn_first = pool.valid ? pool.item_index() : pt.total;
+    }
+    // Claims the next pool item for the whole workgroup (one atomic, handed
+    // to the other waves through LDS); pt.total when the pool is empty.  A
+    // count outside the pool ends the claims.
+    int n_claims = 0;
+    auto claim = [&]() {
+        if (threadIdx.x == 0) {
+            const uint32_t pool = (uint32_t)(pt.total - dyn_first);
+            const uint32_t c =
+                pooled ? atomicAdd((uint32_t *)&a.w.ctrl[kCtrlClaim], 1u) : pool;
+            s_claim[n_claims & 3] = c < pool ? dyn_first + (int)c : pt.total;
+        }
+        __syncthreads();
+        const int it = s_claim[n_claims & 3];
+        ++n_claims;
+        return it < pt.total ? it : pt.total;
+    };
     ShareIter cur(pt, NG, r_split, lo, hi);
-    if (!cur.valid)
-        return;
     // The share's blocks stream through two buffers, two blocks ahead of the
-    // computation, across item and group boundaries.
+    // computation, across item and group boundaries; the loader also makes
+    // the claims, and the computation follows its sequence of items.
     ShareIter ld = cur;
+    bool ld_valid = cur.valid;
     int ld_base = ld.t0;
+    int n_seen = 0;  // pool items the computation has taken over
+    auto pool_item = [&](ShareIter &itr, int it) {
+        // Position itr on pool item it (< pt.total).
+        int l = 0, h = NG;
+        while (l < h) {
+            const int mid = (l + h) >> 1;
+            if (pt.gbegin[mid] <= it)
+                l = mid + 1;
+            else
+                h = mid;
+        }
+        itr.grp = __builtin_amdgcn_readfirstlane(l - 1);
+        itr.i = it - pt.gbegin[itr.grp];
+        itr.rs = RangeSplit(pt.gstart[itr.grp], pt.gend[itr.grp], r_split);
+        itr.rs.item(itr.i, itr.t0, itr.t1);
+        itr.t0 = __builtin_amdgcn_readfirstlane(itr.t0);
+        itr.t1 = __builtin_amdgcn_readfirstlane(itr.t1);
+        itr.valid = true;
+    };
+    if (!ld_valid) {
+        const int it = claim();
+        ld_valid = it < pt.total;
+        if (ld_valid) {
+            pool_item(ld, it);
+            cur = ld;
+            ++n_seen;
+        }
+        ld_base = ld.t0;
+    }
+    if (!ld_valid)
+        return;
     auto issue = [&](KvBlock<T, G, T::EPL, NB> &buf) {
-        if (!ld.valid)
+        if (!ld_valid)
             return;
         const int lb = ld.grp / s.Hkv, lg = ld.grp - lb * s.Hkv;
-        const S *kb = (const S *)a.k + lb * s.kv_sb + lg * s.kv_sh + lane * T::EPL;
+        const S *kb = (const S *)a.k + lb * s.kv_sb + lg * s.kv_sh + k_lane_offset<T, D, G>();
         const S *vb = (const S *)a.v + lb * s.kv_sb + lg * s.kv_sh + lane * T::EPL;
         load_block<T, D, G, LPR, RPB, NB>(buf, kb, vb, s.kv_st, ld_base, ld.t1, row);
         ld_base += TPB;
-        if (ld_base >= ld.t1) {
-            ld.next();
-            ld_base = ld.t0;
+        if (ld_base < ld.t1)
+            return;
+        if (ld.valid && ld.hi != INT_MAX)
+            ld.next();  // the static share's next item, if any
+        else
+            ld.valid = false;
+        if (!ld.valid) {
+            const int it = claim();
+            if (it < pt.total) {
+                pool_item(ld, it);
+                ld.hi = INT_MAX;  // marks a pool item
+            }
         }
+        ld_valid = ld.valid;
+        ld_base = ld.t0;
     };
     KvBlock<T, G, T::EPL, NB> bufA, bufB;
     issue(bufA);
@@ -1574,9 +1809,9 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
     begin_item();
     int cb = cur.t0;  // first token of the block being consumed
     // Consumes the block in buf, refills buf two blocks ahead, and closes the
-    // item after its last block; false once the share is done.
+    // item after its last block; false once the work is done.
     auto consume = [&](KvBlock<T, G, T::EPL, NB> &buf) {
-        item_block<T, D, G>(buf, row, lane, ctx.qr, st, cur.t1, ia);
+        item_block<T, D, G>(buf, row, lane, ctx.q, st, cur.t1, ia);
         issue(buf);
         cb += TPB;
         if (cb < cur.t1)
@@ -1589,9 +1824,22 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
             if (dim == 0)
                 pl[j] = lgv;
         });
-        cur.next();
-        if (!cur.valid)
-            return false;
+        // The next item: the static share's, else the pool item the loader
+        // claimed next (claims complete before their item is consumed).
+        if (cur.valid && cur.hi != INT_MAX)
+            cur.next();
+        else
+            cur.valid = false;
+        if (!cur.valid) {
+            if (n_seen >= n_claims)
+                return false;
+            const int pit = s_claim[n_seen & 3];
+            ++n_seen;
+            if (pit >= pt.total)
+                return false;
+            pool_item(cur, pit);
+            cur.hi = INT_MAX;
+        }
         cb = cur.t0;
         begin_item();
         return true;
@@ -1729,6 +1977,7 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
     __shared__ int s_code[G];
     __shared__ int s_last;
     __shared__ float s_q[G * D];
+    __shared__ uint4 s_qb[AS::kMfma ? 4 * 64 : 1];
     const Shape &s = a.s;
     const int NG = s.B * s.Hkv;
     const int grp = blockIdx.x / a.wpg, loc = blockIdx.x - grp * a.wpg;
@@ -1759,6 +2008,8 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
     const uint32_t tag8 = (uint32_t)((done >> a.done_shift) + 1) & 0xffu;
     store_unit_key(kw, rep_stride, loc, match_finish<T, D, U>(a, e, ml, klds), tag8);
     qs.store(s_q);  // read after the barriers of the poll and the plan
+    if constexpr (AS::kMfma)
+        qs.store_b(s_qb, s.qscale);
     for (int u = loc + a.wpg; u < a.nkw; u += a.wpg) {
         single_unit(a, u, uj, ufirst);
         match_issue<T, D, U>(a, ufirst, bh0 + uj, ml);
@@ -1820,7 +2071,7 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
     }
     const RangeSplit rs(e_ok ? sg : 0, e_ok ? e : 0, s.r);
     const int n = e_ok ? rs.n : 0;
-    ctx.queries_from_lds(s_q, s.qscale);
+    ctx.queries_from_lds(s_q, s_qb, s.qscale);
     const unsigned long long done_add =
         grp == 0 ? (1ull << a.done_shift) - (unsigned long long)NG + 1ull : 1ull;
 
