@@ -39,8 +39,10 @@
 // Both forms run the same device functions in the same order, so their
 // results are bitwise identical.
 //
-// The path is HBM-bound (about 4 flop per KV byte for G = 4), so attention
-// and match run on VALU; MFMA tiles would be 3/4 padding at G = 4.
+// The path is HBM-bound (about 4 flop per KV byte for G = 4).  The match,
+// the softmax and P*V run on VALU; for bf16 K with d = 128 and G = 4 the
+// logits come from MFMAs (the queries' bf16 high and low parts as 8 of the
+// 16 columns), which removes most of the VALU work per token.
 #include <math.h>
 
 #include <utility>
