@@ -188,6 +188,22 @@ void mac_oracle_unmerge(int d, const double *ow, double lw, const double *op,
  *  Rectify-append ([MAC] "Paper version", K3): the merged summary minus the
  *          last r tokens' contribution gives AS_{0:m-r}; it is written with
  *          qt_m and pos = m into slot m mod K.
+ *
+ * Attention-sink isolation ([MAC] "Production version: one fused persistent
+ * BF16 kernel", its front-sink item): with F = front_sink > 0 the
+ * first F positions never enter a reusable summary.  Every ring summary
+ * covers [F, t-r] instead of [0, t-r] (warm ones included); a hit adds the
+ * sink [0, min(F, m+1)) computed exactly with q_m to the cached summary and
+ * the fresh range, which starts at max(F, p-r+1); a miss is full attention
+ * as before; the rectified summary is the merged one minus the sink and
+ * minus the band, i.e. it covers [F, m-r] (empty when m-r < F).  F = 0 is
+ * the plain method.
+ *
+ * Ready/epoch gating ([MAC], same section, its graph-safe readiness
+ * item): restart[s] != 0 marks a ring that is not ready or was invalidated
+ * before step s.  Its contents are dropped (every slot empty), so the step
+ * finds no candidate and is exact full attention, and its rectify-append
+ * starts the ring anew.  restart may be NULL.
  */
 typedef struct {
     int d, ring_k, band_r, dtype;
@@ -197,6 +213,7 @@ typedef struct {
     double scale;    /* logit scale, 1/sqrt(d) */
     double thresh2;  /* squared-distance threshold T2 (the fp32 value) */
     double exempt;   /* decision-exemption band on distances (1e-4) */
+    long front_sink; /* F: leading positions kept out of every summary */
 } mac_oracle_cfg;
 
 /*
@@ -214,7 +231,8 @@ int mac_oracle_stream(const mac_oracle_cfg *c, const void *K, const void *V,
                       const float *q_dec, double *out, double *lse, int *hit,
                       long *p_out, double *dist, double *dist2, int *exempt,
                       long *ring_pos, double *ring_q, double *ring_o,
-                      double *ring_lse, double *warm_seconds)
+                      double *ring_lse, double *warm_seconds,
+                      const int *restart)
 {
     const int d = c->d, Kr = c->ring_k, r = c->band_r;
     long *pos = (long *)malloc(sizeof(long) * Kr);
@@ -229,9 +247,11 @@ int mac_oracle_stream(const mac_oracle_cfg *c, const void *K, const void *V,
     double *mo = (double *)malloc(sizeof(double) * d);
     double *bo = (double *)malloc(sizeof(double) * d);
     double *ro = (double *)malloc(sizeof(double) * d);
+    double *ko = (double *)malloc(sizeof(double) * d);
+    const long F = c->front_sink;
     double warm_t = 0.0;
     if (!pos || !lazy || !qr || !so || !sl || !qv || !qw || !qt || !fo || !mo ||
-        !bo || !ro)
+        !bo || !ro || !ko)
         return -1;
 
     for (int k = 0; k < Kr; ++k) {
@@ -261,7 +281,7 @@ int mac_oracle_stream(const mac_oracle_cfg *c, const void *K, const void *V,
                 qw[i] = (double)q_warm[(long)w_ * d + i];                    \
             double l_;                                                       \
             mac_oracle_summary(d, qw, c->scale, K, V, c->dtype, row_stride, \
-                               0, pos[k_] - r, fo, &l_);                     \
+                               F, pos[k_] - r, fo, &l_);                     \
             for (int i = 0; i < d; ++i)                                      \
                 so[(k_) * d + i] = round_to_f32(fo[i]);                      \
             sl[k_] = round_to_f32(l_);                                       \
@@ -275,6 +295,13 @@ int mac_oracle_stream(const mac_oracle_cfg *c, const void *K, const void *V,
         for (int i = 0; i < d; ++i) {
             qt[i] = elem(qt_dec, c->dtype, (long)s * d + i);
             qv[i] = (double)q_dec[(long)s * d + i];
+        }
+        if (restart && restart[s]) {
+            /* Ring not ready for this step: every slot is dropped. */
+            for (int k = 0; k < Kr; ++k) {
+                pos[k] = -1;
+                lazy[k] = 0;
+            }
         }
 
         /* Match: nearest pre-RoPE query among the last K positions. */
@@ -310,14 +337,20 @@ int mac_oracle_stream(const mac_oracle_cfg *c, const void *K, const void *V,
         hit[s] = h;
         p_out[s] = h ? pb : -1;
 
-        double ml;
+        double ml, kl = -INFINITY;
+        if (F > 0) /* the sink [0, min(F, m+1)), exact with q_m */
+            mac_oracle_summary(d, qv, c->scale, K, V, c->dtype, row_stride, 0,
+                               F - 1 < m ? F - 1 : m, ko, &kl);
         if (h) {
-            /* Amend + Complete: cached AS_{0:p-r} (+) fresh [p-r+1, m]. */
+            /* Amend + Complete: cached AS_{F:p-r} (+) fresh [max(F, p-r+1),
+             * m] (+) the sink. */
             OR_FILL_WARM(kb);
             double fl;
             mac_oracle_summary(d, qv, c->scale, K, V, c->dtype, row_stride,
-                               pb - r + 1, m, fo, &fl);
+                               pb - r + 1 > F ? pb - r + 1 : F, m, fo, &fl);
             mac_oracle_merge(d, so + (long)kb * d, sl[kb], fo, fl, mo, &ml);
+            if (F > 0)
+                mac_oracle_merge(d, mo, ml, ko, kl, mo, &ml);
         } else {
             /* Miss: full attention over [0, m]. */
             mac_oracle_summary(d, qv, c->scale, K, V, c->dtype, row_stride, 0,
@@ -327,9 +360,10 @@ int mac_oracle_stream(const mac_oracle_cfg *c, const void *K, const void *V,
             out[(long)s * d + i] = mo[i];
         lse[s] = ml;
 
-        /* Rectify: merged minus the last r tokens' contribution. */
+        /* Rectify: merged minus the last r tokens' contribution and minus
+         * the sink, leaving [F, m-r]. */
         double rl;
-        if (m - r < 0) {
+        if (m - r < F) {
             for (int i = 0; i < d; ++i)
                 ro[i] = 0.0;
             rl = -INFINITY;
@@ -338,6 +372,8 @@ int mac_oracle_stream(const mac_oracle_cfg *c, const void *K, const void *V,
             mac_oracle_summary(d, qv, c->scale, K, V, c->dtype, row_stride,
                                m - r + 1, m, bo, &bl);
             mac_oracle_unmerge(d, mo, ml, bo, bl, ro, &rl);
+            if (F > 0)
+                mac_oracle_unmerge(d, ro, rl, ko, kl, ro, &rl);
         }
         /* Append into slot m mod K (the slot's old entry is overwritten). */
         int ks = (int)(m % Kr);
@@ -379,5 +415,6 @@ int mac_oracle_stream(const mac_oracle_cfg *c, const void *K, const void *V,
     free(mo);
     free(bo);
     free(ro);
+    free(ko);
     return 0;
 }

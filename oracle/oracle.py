@@ -37,6 +37,7 @@ class _Cfg(ctypes.Structure):
         ("scale", ctypes.c_double),
         ("thresh2", ctypes.c_double),
         ("exempt", ctypes.c_double),
+        ("front_sink", ctypes.c_long),
     ]
 
 
@@ -71,7 +72,7 @@ def load():
         lib.mac_oracle_unmerge.restype = None
         lib.mac_oracle_stream.argtypes = [
             ctypes.POINTER(_Cfg), _vp, _vp, ctypes.c_long, _vp, _vp, _vp, _vp,
-            _dp, _dp, _ip, _lp, _dp, _dp, _ip, _lp, _dp, _dp, _dp, _dp]
+            _dp, _dp, _ip, _lp, _dp, _dp, _ip, _lp, _dp, _dp, _dp, _dp, _ip]
         lib.mac_oracle_stream.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -153,13 +154,15 @@ def unmerge(ow, lw, op, lp):
 def run_stream(K, V, qt_warm, q_warm, qt_dec, q_dec, *, ctx_len: int,
                ring_k: int, band_r: int, thresh2: float, n_steps: int | None = None,
                scale: float | None = None, exempt: float = 1e-4,
-               want_ring: bool = False):
+               want_ring: bool = False, front_sink: int = 0, restart=None):
     """Run MAC decode steps for one (request, query head) stream.
 
     K, V: [T, d] of the head's KV group.  qt_warm: [W, d] pre-RoPE warm
     queries for positions [ctx_len-W, ctx_len-1] (same dtype as K);
     q_warm: [W, d] float32 post-RoPE.  qt_dec / q_dec: [S, d] for decode
-    positions ctx_len + s.
+    positions ctx_len + s.  front_sink: F leading positions kept out of
+    every summary.  restart: optional [S] flags, nonzero where the ring is
+    dropped before that step (not ready / invalidated).
     """
     lib = load()
     d = K.shape[1]
@@ -175,7 +178,12 @@ def run_stream(K, V, qt_warm, q_warm, qt_dec, q_dec, *, ctx_len: int,
     S = qt_dec.shape[0] if n_steps is None else int(n_steps)
     cfg = _Cfg(d, ring_k, band_r, dt, int(ctx_len), W, S,
                (1.0 / math.sqrt(d)) if scale is None else scale,
-               float(thresh2), exempt)
+               float(thresh2), exempt, int(front_sink))
+    rst = None
+    if restart is not None:
+        rst = np.ascontiguousarray(restart, np.int32)
+        if rst.shape[0] < S:
+            raise ValueError("restart needs one flag per step")
     out = np.zeros((S, d), np.float64)
     lse = np.zeros(S, np.float64)
     hit = np.zeros(S, np.int32)
@@ -195,7 +203,7 @@ def run_stream(K, V, qt_warm, q_warm, qt_dec, q_dec, *, ctx_len: int,
         qt_warm.ctypes.data, q_warm.ctypes.data, qt_dec.ctypes.data,
         q_dec.ctypes.data, _ptr(out), _ptr(lse), _ptr(hit, _ip), _ptr(p, _lp),
         _ptr(dist), _ptr(dist2), _ptr(ex, _ip), _ptr(rp, _lp), _ptr(rq),
-        _ptr(ro), _ptr(rl), ctypes.byref(ws))
+        _ptr(ro), _ptr(rl), ctypes.byref(ws), _ptr(rst, _ip))
     if rc != 0:
         raise MemoryError("oracle stream allocation failed")
     res = dict(out=out, lse=lse, hit=hit.astype(bool), p=p, dist=dist,
@@ -207,11 +215,13 @@ def run_stream(K, V, qt_warm, q_warm, qt_dec, q_dec, *, ctx_len: int,
 
 def run_streams(K, V, qt, q, heads, *, ctx_len: int, n_warm: int, ring_k: int,
                 band_r: int, thresh2: float, n_steps: int | None = None,
-                threads: int | None = None, want_ring: bool = False):
+                threads: int | None = None, want_ring: bool = False,
+                front_sink: int = 0, restart=None):
     """Run many (b, h) streams in parallel threads (ctypes drops the GIL).
 
     K, V: [B, Hkv, T, d]; qt, q: [B, Hq, W+S, d] (warm part first).
-    heads: iterable of (b, h).  Returns {(b, h): result}.
+    heads: iterable of (b, h).  restart: optional [B, S] flags (see
+    run_stream).  Returns {(b, h): result}.
     """
     Hq, Hkv = qt.shape[1], K.shape[1]
     G = Hq // Hkv
@@ -223,7 +233,8 @@ def run_streams(K, V, qt, q, heads, *, ctx_len: int, n_warm: int, ring_k: int,
         return bh, run_stream(
             K[b, g], V[b, g], qt[b, h, :W], q[b, h, :W], qt[b, h, W:],
             q[b, h, W:], ctx_len=ctx_len, ring_k=ring_k, band_r=band_r,
-            thresh2=thresh2, n_steps=n_steps, want_ring=want_ring)
+            thresh2=thresh2, n_steps=n_steps, want_ring=want_ring,
+            front_sink=front_sink, restart=None if restart is None else restart[b])
 
     heads = list(heads)
     nt = threads or min(len(heads), os.cpu_count() or 1, 16)
