@@ -35,7 +35,7 @@ WsLayout ws_layout(int B, int Hq, int Hkv, int D, int K, int T, int dtype, bool 
     WsLayout L;
     const int G = Hq / Hkv;
     L.nsplit = (K + kSlotsPerSplit - 1) / kSlotsPerSplit;
-    L.max_items = (int64_t)B * Hkv * (kMaxItemsPerGroup + 2);
+    L.max_items = (int64_t)B * Hkv * kItemsPerGroupMax;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -55,6 +55,8 @@ WsLayout ws_layout(int B, int Hq, int Hkv, int D, int K, int T, int dtype, bool 
     L.part_l = take((size_t)L.max_items * G * 4);
     L.rect_o = take(BH * D * 4);
     L.rect_l = take(BH * 4);
+    L.ring_epoch = take(BG * 4);
+    L.restart = take(BG * 4);
     // The single-launch regions come last, so the layout without them is a
     // prefix of the layout with them.
     L.skeys = L.grp_sync = 0;
@@ -82,6 +84,8 @@ WsPtrs ws_ptrs(void *base, const WsLayout &L)
     w.part_l = (float *)(c + L.part_l);
     w.rect_o = (float *)(c + L.rect_o);
     w.rect_l = (float *)(c + L.rect_l);
+    w.ring_epoch = (int32_t *)(c + L.ring_epoch);
+    w.restart = (int32_t *)(c + L.restart);
     w.skeys = L.skeys ? (unsigned long long *)(c + L.skeys) : nullptr;
     w.grp_sync = L.grp_sync ? (uint32_t *)(c + L.grp_sync) : nullptr;
     return w;
@@ -104,6 +108,7 @@ struct mac_handle {
     bool fused_append;
     bool split_stages;
     int32_t wpg, upg, nkw, done_shift, unit_slots, nsplit;  // single-launch geometry
+    const int32_t *epoch = nullptr;  // bound by mac_bind_epochs
     hipEvent_t ev_main = nullptr, ev_aux = nullptr;
     // Per-stage timing events: prof[(step * kStages + stage) * 2 + {0,1}].
     std::vector<hipEvent_t> prof;
@@ -124,6 +129,7 @@ static mac_status check_params(const mac_params *p, Shape *s)
                       MAC_FLAG_SINGLE_LAUNCH)) != 0 ||
         (p->flags & MAC_FLAG_SPLIT_STAGES && p->flags & MAC_FLAG_SINGLE_LAUNCH) ||
         !isfinite(p->tau) || !isfinite(p->sm_scale) || p->sm_scale < 0.f ||
+        p->front_sink < 0 || p->front_sink > kMaxFrontSink ||
         (p->thresh_mode != MAC_THRESH_ONE_MINUS_TAU &&
          p->thresh_mode != MAC_THRESH_TAU))
         return MAC_ERR_INVALID_ARG;
@@ -141,7 +147,7 @@ static mac_status check_params(const mac_params *p, Shape *s)
         return MAC_ERR_UNSUPPORTED;
     // The planner's work offsets (tokens plus a per-item cost, summed over
     // the KV groups of a step) are 32-bit.
-    if ((int64_t)p->batch * p->n_kv_heads * ((int64_t)p->kv_capacity + (int64_t)kItemCost * (kMaxItemsPerGroup + 2)) >=
+    if ((int64_t)p->batch * p->n_kv_heads * ((int64_t)p->kv_capacity + (int64_t)kItemCost * kItemsPerGroupMax) >=
         ((int64_t)1 << 31))
         return MAC_ERR_UNSUPPORTED;
     int64_t st = p->kv_stride_t, sh = p->kv_stride_h, sb = p->kv_stride_b;
@@ -171,6 +177,7 @@ static mac_status check_params(const mac_params *p, Shape *s)
         s->K = p->ring_k;
         s->r = p->band_r;
         s->T = p->kv_capacity;
+        s->F = p->front_sink;
         s->kv_sb = sb;
         s->kv_sh = sh;
         s->kv_st = st;
@@ -486,6 +493,7 @@ mac_status mac_decode_step(mac_handle *h, const void *qtilde, const float *q,
     a.lse_ring = h->rings.lse_ring;
     a.pos_ring = h->rings.pos_ring;
     a.append_fused = h->fused_append ? 1 : 0;
+    a.epoch = h->epoch;
     a.wpg = h->wpg;
     a.upg = h->upg;
     a.nkw = h->nkw;
@@ -527,6 +535,14 @@ mac_status mac_decode_step(mac_handle *h, const void *qtilde, const float *q,
 #undef MAC_STAGE
     if (prof)
         ++h->prof_n;
+    return MAC_OK;
+}
+
+mac_status mac_bind_epochs(mac_handle *h, const int32_t *epoch)
+{
+    if (!h || (epoch && ((uintptr_t)epoch & 3u)))
+        return MAC_ERR_INVALID_ARG;
+    h->epoch = epoch;
     return MAC_OK;
 }
 

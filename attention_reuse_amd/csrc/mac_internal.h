@@ -32,9 +32,12 @@ constexpr int kSpecMax = 24;
 // Workgroup size of the match and attention kernels.
 constexpr int kBlock = 256;
 
-// Items of one KV group never exceed this (grid cells plus the two range
-// ends around the rectify split).
-constexpr int kItemsPerGroupMax = kMaxItemsPerGroup + 2;
+// Items of one KV group never exceed this (grid cells, the two range ends
+// around the rectify split, and the attention-sink item).
+constexpr int kItemsPerGroupMax = kMaxItemsPerGroup + 3;
+// Largest front sink (tokens that stay out of every reusable summary and
+// are attended exactly on every step); the sink is one work item.
+constexpr int kMaxFrontSink = 4096;
 
 // Single-launch step.  Each KV group has its own run of workgroups, and data
 // crosses workgroups only inside a group:
@@ -172,10 +175,63 @@ struct RangeSplit {
     }
 };
 
+// Work items of one KV group at end position e whose heads attend from s
+// (the smallest start over the group's heads).  First the main items: the
+// range [max(s, F), e] cut by RangeSplit (none when e < F).  Then, when
+// `sink` is set and F > 0, one item [0, min(F, e + 1)) that every head of
+// the group attends in full whatever its match: the attention sink, kept
+// out of every reusable summary.  The sink item comes after the rectify
+// split, so it counts in the output but not in the rectified summary.
+// With F = 0 the items are exactly RangeSplit(s, e, r)'s.
+struct GroupItems {
+    RangeSplit rs;
+    int ms, n_main, sink_end, n;
+    __host__ __device__ GroupItems() : rs(0, 0, 0), ms(0), n_main(0), sink_end(0), n(0) {}
+    // cs >= 0 forces the grid (1 << cs), as RangeSplit's second constructor.
+    __host__ __device__ GroupItems(int s, int e, int r, int F, bool sink, int cs = -1) : rs(0, 0, 0)
+    {
+        ms = s > F ? s : F;
+        n_main = 0;
+        if (ms <= e) {
+            if (cs < 0)
+                rs.init(ms, e, r, RangeSplit::chunk_shift_for(ms, e));
+            else
+                rs.init(ms, e, r, cs);
+            n_main = rs.n;
+        }
+        sink_end = (sink && F > 0) ? (F < e + 1 ? F : e + 1) : 0;
+        n = n_main + (sink_end > 0 ? 1 : 0);
+    }
+    __host__ __device__ bool is_sink(int i) const { return i >= n_main; }
+    __host__ __device__ void item(int i, int &t0, int &t1) const
+    {
+        if (i < n_main) {
+            rs.item(i, t0, t1);
+        } else {
+            t0 = 0;
+            t1 = sink_end;
+        }
+    }
+    // Leading items before the rectify split (the sink is never among them).
+    __host__ __device__ int n_before_split() const { return n_main > 0 ? rs.n_before_split() : 0; }
+    __host__ __device__ int main_tokens() const { return n_main > 0 ? rs.e - ms + 1 : 0; }
+    // Work of the group in the attention kernel's balanced split: tokens plus
+    // kItemCost per item.
+    __host__ __device__ int work() const { return main_tokens() + sink_end + kItemCost * n; }
+    // Work before item i.
+    __host__ __device__ int offset(int i) const
+    {
+        int t0 = 0, t1 = 0;
+        if (i < n_main)
+            rs.item(i, t0, t1);
+        return (i < n_main ? t0 - ms : main_tokens()) + kItemCost * i;
+    }
+};
+
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WsLayout {
     size_t keys, ctx, dec_slot, grp_begin, grp_count, grp_start, ctrl, sync,
-        part_o, part_l, rect_o, rect_l, skeys, grp_sync, total;
+        part_o, part_l, rect_o, rect_l, ring_epoch, restart, skeys, grp_sync, total;
     int64_t max_items;
     int32_t nsplit;
 };
@@ -194,6 +250,7 @@ enum { kCtrlItems = 0, kCtrlStatus = 1, kCtrlClaim = 2 };
 
 struct Shape {
     int32_t B, Hq, Hkv, G, D, dtype, K, r, T;
+    int32_t F;                    // front sink: leading positions never reused
     int64_t kv_sb, kv_sh, kv_st;  // elements
     float qscale;                 // sm_scale * log2(e)
     float thresh2;
@@ -207,6 +264,12 @@ struct WsPtrs {
     int32_t *dec_slot, *grp_begin, *grp_count, *grp_start, *ctrl;
     unsigned long long *sync;  // done counter, magic, latched time-outs
     float *part_o, *part_l, *rect_o, *rect_l;
+    // [B * Hkv] the epoch each KV group's rings were built for (see
+    // StepArgs::epoch); reset to 0 with the rings
+    int32_t *ring_epoch;
+    // [B * Hkv] 1 where the latest step's merge found the group not ready:
+    // the separate append kernel then restarts the group's position ring
+    int32_t *restart;
     // single launch only (null otherwise): tagged split keys, per-group
     // arrival counters
     unsigned long long *skeys;
@@ -237,6 +300,13 @@ struct StepArgs {
     float *o_ring, *lse_ring;
     int32_t *pos_ring;
     int32_t append_fused;
+    // [B] device, or null: the caller's epoch of each request, read by the
+    // match, plan and merge of the step only.  A KV group whose ring_epoch
+    // differs, or whose request epoch is negative, is not ready: its match
+    // sees no candidate (exact attention), its merge records the epoch, and
+    // its append empties the group's position ring before adding the
+    // step's entry.
+    const int32_t *epoch;
     // single launch: workgroups per group, match units per group (G *
     // nsplit), key words per group, log2 of the done increment per launch,
     // ring slots per match unit

@@ -256,6 +256,37 @@ __device__ inline bool end_ok(const StepArgs &a, int e)
     return e < a.s.T && (a.mode == kPlanInit || e >= 0);
 }
 
+// Whether KV group grp (of request b) may reuse its rings: always when the
+// caller binds no epochs, else when the request's epoch is non-negative and
+// equals the one the group's rings were built for.  A group that is not
+// ready matches nothing, so every head of it is exact attention; its merge
+// adopts the request's epoch, and its append restarts the position ring
+// (see ring_append_pos).
+__device__ inline bool group_ready(const StepArgs &a, int b, int grp)
+{
+    if (!a.epoch)
+        return true;
+    const int32_t ep = a.epoch[b];
+    return ep >= 0 && a.w.ring_epoch[grp] == ep;
+}
+
+// Position-ring update of the rectify-append of KV group grp at position e,
+// run by n threads (thread index i): slot e mod K receives e; on a restart
+// every other slot is emptied.
+__device__ inline void ring_append_pos(const StepArgs &a, int grp, int e, bool restart, int i,
+                                       int n)
+{
+    int32_t *row = a.pos_ring + (int64_t)grp * a.s.K;
+    const int slot = e % a.s.K;
+    if (!restart) {
+        if (i == 0)
+            row[slot] = e;
+        return;
+    }
+    for (int k = i; k < a.s.K; k += n)
+        row[k] = k == slot ? e : -1;
+}
+
 // Device-coherent accesses for data handed between workgroups of one
 // launch: relaxed agent-scope atomics, which gfx950 issues with the sc1
 // bit (write-through on stores, L2 bypass on loads).
@@ -400,20 +431,23 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
     for (int grp = lo; grp < hi; ++grp) {
         const int b = grp / s.Hkv, g = grp - b * s.Hkv;
         const int e = end_of(a, b);
-        int st = 0, cnt = 0;
+        int st = 0, cnt = 0, wk = 0;
         if (e >= 0 && e < s.T) {
             st = e;
             for (int j = 0; j < s.G; ++j) {
                 const int v = code_start(s_code[b * s.Hq + g * s.G + j]);
                 st = v < st ? v : st;
             }
-            cnt = RangeSplit(st, e, r_split).n;
+            const GroupItems gi(st, e, r_split, s.F, a.mode != kPlanInit);
+            cnt = gi.n;
+            wk = gi.work();
         }
         s_gstart[grp] = st;
         s_gend[grp] = e;
         s_gcount[grp] = cnt;
+        s_gwork[grp] = wk;  // the group's own work until the scan below
         run += cnt;
-        runw += cnt > 0 ? e - st + 1 + kItemCost * cnt : 0;
+        runw += wk;
     }
     // Exclusive scans of the counts and the work: inclusive scans of the run
     // totals within each wave, then across the waves.
@@ -443,8 +477,9 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
     for (int grp = lo; grp < hi; ++grp) {
         s_gbegin[grp] = acc;
         acc += s_gcount[grp];
+        const int wk = s_gwork[grp];
         s_gwork[grp] = accw;
-        accw += s_gcount[grp] > 0 ? s_gend[grp] - s_gstart[grp] + 1 + kItemCost * s_gcount[grp] : 0;
+        accw += wk;
     }
     if (tid == 0) {
         s_gbegin[NG] = total;
@@ -531,15 +566,16 @@ __device__ inline void match_issue(const StepArgs &a, int first, int bh, MatchLo
 }
 
 // Key of the unit issued by match_issue at position m; valid in thread 0.
-// sm holds kBlock/64 words of LDS.
+// A group that is not ready has no candidate.  sm holds kBlock/64 words of
+// LDS.
 template <class T, int D, int U>
-__device__ inline unsigned long long match_finish(const StepArgs &a, int m,
+__device__ inline unsigned long long match_finish(const StepArgs &a, int m, bool ready,
                                                   const MatchLoads<T, D, U> &ml,
                                                   unsigned long long *sm)
 {
     constexpr int EPL = T::EPL, LPR = D / EPL;
     const Shape &s = a.s;
-    const bool m_ok = m >= 0 && m < s.T;
+    const bool m_ok = ready && m >= 0 && m < s.T;
     float qv[EPL];
     unpack<T>(ml.q, qv);
     unsigned long long best = ~0ull;
@@ -585,10 +621,11 @@ __global__ __launch_bounds__(kBlock) void match_kernel(StepArgs a)
 {
     __shared__ unsigned long long sm[kBlock / 64];
     constexpr int U = kSlotsPerSplit / (kBlock / (D / T::EPL));
-    const int bh = blockIdx.y;
+    const int bh = blockIdx.y, b = bh / a.s.Hq;
+    const bool ready = group_ready(a, b, b * a.s.Hkv + (bh - b * a.s.Hq) / a.s.G);
     MatchLoads<T, D, U> ml;
     match_issue<T, D, U>(a, blockIdx.x * kSlotsPerSplit, bh, ml);
-    const unsigned long long best = match_finish<T, D, U>(a, a.pos[bh / a.s.Hq], ml, sm);
+    const unsigned long long best = match_finish<T, D, U>(a, a.pos[b], ready, ml, sm);
     if (threadIdx.x == 0 && best != ~0ull)
         atomicMin(&a.w.keys[bh * kKeyStride], best);
 }
@@ -857,7 +894,10 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int gstart, con
     const int b = grp / s.Hkv, g = grp - b * s.Hkv;
     const int e = end_of(a, b);
     const int r_split = (a.mode == kPlanInit) ? 0 : s.r;
-    const int nA = RangeSplit(gstart, e, r_split).n_before_split();
+    const int nA = GroupItems(gstart, e, r_split, s.F, a.mode != kPlanInit).n_before_split();
+    // Read by every thread before the barrier below; thread 0 rewrites the
+    // group's epoch after it.
+    const bool ready = group_ready(a, b, grp);
     // The pre-RoPE queries of the fused append are requested first.
     S qa[NPK][2];
     if (a.append_fused) {
@@ -871,8 +911,8 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int gstart, con
         }
     }
 
-    // list 0 = A (items [0, nA)), list 1 = Bt (items [nA, cnt)); each pair
-    // folds into res[list][k].
+    // list 0 = A (items [0, nA)), list 1 = Bt (items [nA, cnt), the sink item
+    // last); each pair folds into res[list][k].
     float res_l[2][NPK], res_o[2][NPK][2];
     if (cnt <= MD) {
         // Few items: waves 0..3 each load every float of items w, w + 4, ...
@@ -985,7 +1025,8 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int gstart, con
     }
 
     // R = C (+) A, out = R (+) Bt.  Results are held until every thread has
-    // read its cached summary, since the fused append may overwrite it.
+    // read its cached summary (and the group's epoch), since the fused
+    // append may overwrite them.
     float out_l[NPK], out_o[NPK][2], rec_l[NPK], rec_o[NPK][2];
 #pragma unroll
     for (int k = 0; k < NPK; ++k) {
@@ -1022,8 +1063,6 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int gstart, con
             *reinterpret_cast<float2 *>(a.o_ring + ri) = make_float2(rec_o[k][0], rec_o[k][1]);
             if (dim == 0)
                 a.lse_ring[(int64_t)bh * s.K + slot] = rec_l[k] * kLn2;
-            if (jj == 0 && dim == 0)
-                a.pos_ring[((int64_t)b * s.Hkv + g) * s.K + slot] = e;
         } else {
             *reinterpret_cast<float2 *>(a.w.rect_o + (int64_t)bh * D + dim) =
                 make_float2(rec_o[k][0], rec_o[k][1]);
@@ -1031,6 +1070,14 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int gstart, con
                 a.w.rect_l[bh] = rec_l[k];
         }
     }
+    // A group that was not ready adopts the request's epoch; its ring
+    // restarts with this step's entry, here or in the append kernel.
+    if (!ready && tid == 0)
+        a.w.ring_epoch[grp] = a.epoch[b];
+    if (a.append_fused)
+        ring_append_pos(a, grp, e, !ready, tid, NT);
+    else if (tid == 0)
+        a.w.restart[grp] = ready ? 0 : 1;
 }
 
 // Merge kernel: one workgroup of kMergeBlock threads per KV group, from the
@@ -1616,13 +1663,14 @@ __device__ inline void item_finish(const StepArgs &a, const ItemCtx<T, D, G> &ct
 // in order, skipping empty groups; `valid` is false past the share.
 struct ShareIter {
     const PlanTables *pt;
-    int NG, r_split, hi;
+    int NG, r_split, F, hi;
+    bool sink;
     int grp, i, t0, t1;
     bool valid;
-    RangeSplit rs;
-    __device__ ShareIter(const PlanTables &p, int ng, int rsplit, int lo, int hi_)
-        : pt(&p), NG(ng), r_split(rsplit), hi(hi_), grp(0), i(0), t0(0), t1(0), valid(false),
-          rs(0, 0, 0)
+    GroupItems gi;
+    __device__ ShareIter(const PlanTables &p, int ng, int rsplit, int f, bool snk, int lo, int hi_)
+        : pt(&p), NG(ng), r_split(rsplit), F(f), hi(hi_), sink(snk), grp(0), i(0), t0(0), t1(0),
+          valid(false)
     {
         int l = 0, h = NG;  // last group with work offset <= lo
         while (l < h) {
@@ -1633,7 +1681,7 @@ struct ShareIter {
                 h = mid;
         }
         grp = l - 1 < 0 ? 0 : l - 1;
-        rs = RangeSplit(pt->gstart[grp], pt->gend[grp], r_split);
+        gi = items(grp);
         l = 0;
         h = pt->gcount[grp];  // first item with offset >= lo
         while (l < h) {
@@ -1646,23 +1694,22 @@ struct ShareIter {
         i = l;
         settle();
     }
-    __device__ int offset(int ii) const
+    __device__ GroupItems items(int gr) const
     {
-        int a0, a1;
-        rs.item(ii, a0, a1);
-        return pt->gwork[grp] + (a0 - pt->gstart[grp]) + kItemCost * ii;
+        return GroupItems(pt->gstart[gr], pt->gend[gr], r_split, F, sink);
     }
+    __device__ int offset(int ii) const { return pt->gwork[grp] + gi.offset(ii); }
     __device__ void settle()
     {
         while (grp < NG && i >= pt->gcount[grp]) {
             ++grp;
             i = 0;
             if (grp < NG)
-                rs = RangeSplit(pt->gstart[grp], pt->gend[grp], r_split);
+                gi = items(grp);
         }
         valid = grp < NG && offset(i) < hi;
         if (valid)
-            rs.item(i, t0, t1);
+            gi.item(i, t0, t1);
         grp = __builtin_amdgcn_readfirstlane(grp);
         t0 = __builtin_amdgcn_readfirstlane(t0);
         t1 = __builtin_amdgcn_readfirstlane(t1);
@@ -1707,8 +1754,9 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
     const int hi = (int)((int64_t)Ws * (blockIdx.x + 1) / gridDim.x);
     __shared__ int s_claim[4];
     int dyn_first;
+    const bool with_sink = a.mode != kPlanInit;
     {
-        const ShareIter pool(pt, NG, r_split, Ws, INT_MAX);
+        const ShareIter pool(pt, NG, r_split, s.F, with_sink, Ws, INT_MAX);
         dyn_first = pool.valid ? pool.item_index() : pt.total;
     }
     // Claims the next pool item for the whole workgroup (one atomic, handed
@@ -1727,7 +1775,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
         ++n_claims;
         return it < pt.total ? it : pt.total;
     };
-    ShareIter cur(pt, NG, r_split, lo, hi);
+    ShareIter cur(pt, NG, r_split, s.F, with_sink, lo, hi);
     // The share's blocks stream through two buffers, two blocks ahead of the
     // computation, across item and group boundaries; the loader also makes
     // the claims, and the computation follows its sequence of items.
@@ -1747,8 +1795,8 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
         }
         itr.grp = __builtin_amdgcn_readfirstlane(l - 1);
         itr.i = it - pt.gbegin[itr.grp];
-        itr.rs = RangeSplit(pt.gstart[itr.grp], pt.gend[itr.grp], r_split);
-        itr.rs.item(itr.i, itr.t0, itr.t1);
+        itr.gi = itr.items(itr.grp);
+        itr.gi.item(itr.i, itr.t0, itr.t1);
         itr.t0 = __builtin_amdgcn_readfirstlane(itr.t0);
         itr.t1 = __builtin_amdgcn_readfirstlane(itr.t1);
         itr.valid = true;
@@ -1799,9 +1847,10 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
     ItemAcc<T, D, G> ia;
     auto begin_item = [&] {
         const int b = cur.grp / s.Hkv, g = cur.grp - b * s.Hkv;
+        const bool sink_item = cur.gi.is_sink(cur.i);  // every head attends the sink
 #pragma unroll
         for (int j = 0; j < G; ++j)
-            st[j] = code_start(pt.code[b * s.Hq + g * G + j]);
+            st[j] = sink_item ? 0 : code_start(pt.code[b * s.Hq + g * G + j]);
         if (cur.grp != qgrp) {
             qgrp = cur.grp;
             ctx = ItemCtx<T, D, G>(a, b, g);
@@ -1915,11 +1964,12 @@ __device__ inline unsigned long long lanes_min64(unsigned long long v)
 }
 
 // Speculative item of workgroup loc of a group at position e: the loc-th
-// item from the end of the range [e - span + 1, e], span being the group's
-// span at its previous step (a range keeps its span while every head keeps
-// matching the previous position).  A hit range spans at most K + r tokens,
-// so its chunk is kChunkMin; every item but the first is then fixed by e
-// and r alone.  False if loc has no such item.
+// item from the end of the group's items for the range [e - span + 1, e],
+// span being the group's span at its previous step (a range keeps its span
+// while every head keeps matching the previous position).  A hit range
+// spans at most K + r tokens, so its chunk is kChunkMin; every main item
+// but the first is then fixed by e and r alone, and the sink item by e.
+// False if loc has no such item.
 __device__ inline bool spec_item(const StepArgs &a, int e, int loc, int span, int &t0, int &t1)
 {
     if (loc >= kSpecMax || e < 0 || e >= a.s.T)
@@ -1927,11 +1977,11 @@ __device__ inline bool spec_item(const StepArgs &a, int e, int loc, int span, in
     const int hit_span = a.s.K + a.s.r;
     span = (span <= 0 || span > hit_span) ? hit_span : span;
     const int s0 = e - span + 1;
-    const RangeSplit rs(s0 > 0 ? s0 : 0, e, a.s.r, kChunkMinShift);
-    const int it = rs.n - 1 - loc;
+    const GroupItems gi(s0 > 0 ? s0 : 0, e, a.s.r, a.s.F, true, kChunkMinShift);
+    const int it = gi.n - 1 - loc;
     if (it < 0)
         return false;
-    rs.item(it, t0, t1);
+    gi.item(it, t0, t1);
     return true;
 }
 
@@ -1992,6 +2042,9 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
     // launch's groups leave floor(done / 2^s) unchanged until this
     // workgroup's own group completes.
     const int e = a.pos[b];
+    // Read before this workgroup's keys are stored (they depend on it), so
+    // before the group can complete and its merge restart the rings.
+    const bool ready = group_ready(a, b, grp);
     const unsigned long long done = sync[kSyncDone];
     uint32_t *counter = a.w.grp_sync + (int64_t)grp * kGrpStride;
     const int span_prev = (int)counter[kGrpSpan];
@@ -2008,14 +2061,14 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
     const int64_t rep_stride = (int64_t)NG * a.nkw;
     unsigned long long *kw = a.w.skeys + (int64_t)grp * a.nkw;
     const uint32_t tag8 = (uint32_t)((done >> a.done_shift) + 1) & 0xffu;
-    store_unit_key(kw, rep_stride, loc, match_finish<T, D, U>(a, e, ml, klds), tag8);
+    store_unit_key(kw, rep_stride, loc, match_finish<T, D, U>(a, e, ready, ml, klds), tag8);
     qs.store(s_q);  // read after the barriers of the poll and the plan
     if constexpr (AS::kMfma)
         qs.store_b(s_qb, s.qscale);
     for (int u = loc + a.wpg; u < a.nkw; u += a.wpg) {
         single_unit(a, u, uj, ufirst);
         match_issue<T, D, U>(a, ufirst, bh0 + uj, ml);
-        store_unit_key(kw, rep_stride, u, match_finish<T, D, U>(a, e, ml, klds), tag8);
+        store_unit_key(kw, rep_stride, u, match_finish<T, D, U>(a, e, ready, ml, klds), tag8);
     }
     // Speculative K/V, requested once the keys are out: loads complete in
     // order, so requests made earlier would hold back the match.  They are
@@ -2071,8 +2124,12 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
         }
         a.w.ctrl[kCtrlStatus] = bad ? MAC_DEV_BAD_POSITION : 0;
     }
-    const RangeSplit rs(e_ok ? sg : 0, e_ok ? e : 0, s.r);
-    const int n = e_ok ? rs.n : 0;
+    const GroupItems gi(e_ok ? sg : 0, e_ok ? e : 0, s.r, s.F, true);
+    const int n = e_ok ? gi.n : 0;
+    int st0[G];  // the sink item: every head attends all of it
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+        st0[j] = 0;
     ctx.queries_from_lds(s_q, s_qb, s.qscale);
     const unsigned long long done_add =
         grp == 0 ? (1ull << a.done_shift) - (unsigned long long)NG + 1ull : 1ull;
@@ -2089,13 +2146,14 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
     for (int jj = loc; jj < n; jj += a.wpg) {
         const int it = n - 1 - jj;
         int t0, t1;
-        rs.item(it, t0, t1);
+        gi.item(it, t0, t1);
+        const int(&sti)[G] = gi.is_sink(it) ? st0 : st;
         // The speculative loads hold exactly this item's rows when its
         // bounds are the speculated ones.
         if (!(jj == loc && spec && t0 == sp_t0 && t1 == sp_t1))
             item_issue<T, D, G>(a, ctx, t0, t1, bufs, false);
         float *po = gpo + (int64_t)it * G * D, *pl = gpl + (int64_t)it * G;
-        item_finish<T, D, G>(a, ctx, t0, t1, st, lds, bufs, [&](int j, int dim, float o, float lg) {
+        item_finish<T, D, G>(a, ctx, t0, t1, sti, lds, bufs, [&](int j, int dim, float o, float lg) {
             st_wt(po + j * D + dim, o);
             if (dim == 0)
                 st_wt(pl + j, lg);
@@ -2157,8 +2215,11 @@ __global__ __launch_bounds__(D) void append_kernel(StepArgs a, int32_t pos_offse
     a.o_ring[ri] = a.w.rect_o[(int64_t)bh * D + dim];
     if (dim == 0)
         a.lse_ring[(int64_t)bh * s.K + slot] = a.w.rect_l[bh] * kLn2;
-    if (h % s.G == 0 && dim == 0)
-        a.pos_ring[((int64_t)b * s.Hkv + h / s.G) * s.K + slot] = t;
+    if (h % s.G == 0) {
+        // The merge of the step recorded whether the group restarts.
+        const int grp = b * s.Hkv + h / s.G;
+        ring_append_pos(a, grp, t, !kWarm && a.w.restart[grp] != 0, dim, D);
+    }
 }
 
 template <class S>
@@ -2170,7 +2231,8 @@ __global__ void ring_reset_kernel(int64_t n_q, S *__restrict__ q_ring,
                                   unsigned long long *__restrict__ keys, int64_t n_sync,
                                   unsigned long long *__restrict__ sync, int64_t n_tag,
                                   unsigned long long *__restrict__ skeys, int64_t n_gs,
-                                  uint32_t *__restrict__ grp_sync)
+                                  uint32_t *__restrict__ grp_sync, int64_t n_ep,
+                                  int32_t *__restrict__ ring_epoch)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -2191,6 +2253,8 @@ __global__ void ring_reset_kernel(int64_t n_q, S *__restrict__ q_ring,
         skeys[i] = 0;
     for (int64_t i = i0; i < n_gs; i += stride)
         grp_sync[i] = 0;
+    for (int64_t i = i0; i < n_ep; i += stride)
+        ring_epoch[i] = 0;
     if (i0 < 16)
         ctrl[i0] = 0;
 }
@@ -2458,11 +2522,13 @@ hipError_t launch_ring_reset(const Shape &s, void *q_ring, float *o_ring,
     if (s.dtype == MAC_DTYPE_BF16)
         hipLaunchKernelGGL(ring_reset_kernel<uint16_t>, dim3((int)blocks), dim3(256), 0, st,
                            n_q, (uint16_t *)q_ring, o_ring, n_l, lse_ring, n_p, pos_ring, w.ctrl,
-                           n_keys, w.keys, n_sync, w.sync, n_tag, w.skeys, n_gs, w.grp_sync);
+                           n_keys, w.keys, n_sync, w.sync, n_tag, w.skeys, n_gs, w.grp_sync, n_p / s.K,
+                           w.ring_epoch);
     else
         hipLaunchKernelGGL(ring_reset_kernel<float>, dim3((int)blocks), dim3(256), 0, st, n_q,
                            (float *)q_ring, o_ring, n_l, lse_ring, n_p, pos_ring, w.ctrl, n_keys,
-                           w.keys, n_sync, w.sync, n_tag, w.skeys, n_gs, w.grp_sync);
+                           w.keys, n_sync, w.sync, n_tag, w.skeys, n_gs, w.grp_sync, n_p / s.K,
+                           w.ring_epoch);
     return hipGetLastError();
 }
 

@@ -46,7 +46,7 @@ class mac_params(ctypes.Structure):
         ("tau", ctypes.c_float), ("thresh_mode", ctypes.c_int32),
         ("sm_scale", ctypes.c_float), ("flags", ctypes.c_int32),
         ("kv_stride_b", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64),
-        ("kv_stride_t", ctypes.c_int64),
+        ("kv_stride_t", ctypes.c_int64), ("front_sink", ctypes.c_int32),
     ]
 
 
@@ -79,6 +79,7 @@ def load():
         "mac_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                            _vp, _vp, _vp, _vp]),
         "mac_join_aux": (ctypes.c_int, [_vp, _vp]),
+        "mac_bind_epochs": (ctypes.c_int, [_vp, _vp]),
         "mac_full_decode": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                            ctypes.c_size_t, _vp]),
         "mac_read_device_status": (ctypes.c_int, [_P, _vp, _vp,
@@ -125,10 +126,10 @@ def _check(fn, rc):
 
 def make_params(batch, n_q_heads, n_kv_heads, head_dim, kv_dtype, ring_k,
                 band_r, kv_capacity, tau, thresh_mode=MAC_THRESH_ONE_MINUS_TAU,
-                sm_scale=0.0, strides=(0, 0, 0), flags=0) -> mac_params:
+                sm_scale=0.0, strides=(0, 0, 0), flags=0, front_sink=0) -> mac_params:
     return mac_params(batch, n_q_heads, n_kv_heads, head_dim, kv_dtype, ring_k,
                       band_r, kv_capacity, tau, thresh_mode, sm_scale, flags,
-                      *strides)
+                      *strides, front_sink)
 
 
 def mac_workspace_bytes(p: mac_params) -> int:
@@ -162,6 +163,11 @@ def mac_decode_step(handle, qtilde, q, k_cache, v_cache, pos, out, out_lse=None,
         handle, _ptr(qtilde), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(pos),
         _ptr(out), _ptr(out_lse), _ptr(match_p), _ptr(match_d2), main_stream,
         aux_stream))
+
+
+def mac_bind_epochs(handle, epoch):
+    """Bind a [B] int32 device array of request epochs (None unbinds)."""
+    _check("mac_bind_epochs", load().mac_bind_epochs(handle, _ptr(epoch)))
 
 
 def mac_join_aux(handle, stream=None):

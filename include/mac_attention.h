@@ -12,8 +12,10 @@
  * less KV reading in long-context decoding (MLSys 2026)" (blog post),
  * sections "Decomposable representation of attention", "Reuse", "Match
  * (1)-(3)", "Amend", "Complete" and "Paper version: the K1/K2/K3
- * micro-pipeline"; "Attention Cache and Sequence Parallelism", section "MHA:
- * per-token K/V" for the baseline decode semantics.
+ * micro-pipeline", and "Production version: one fused persistent BF16
+ * kernel" for the attention-sink isolation and the ready/epoch gating;
+ * "Attention Cache and Sequence Parallelism", section "MHA: per-token K/V"
+ * for the baseline decode semantics.
  *
  * Conventions for every entry point:
  *  - All buffers are DEVICE pointers owned by the caller, unless noted.  The
@@ -105,6 +107,12 @@ typedef struct mac_params {
      * Row t of (b, g) starts at b*kv_stride_b + g*kv_stride_h + t*kv_stride_t
      * and must be 16-byte aligned. */
     int64_t kv_stride_b, kv_stride_h, kv_stride_t;
+    /* F in [0, 4096]: attention-sink isolation (blog, "Production version:
+     * one fused persistent BF16 kernel").  The first F positions never enter
+     * a reusable summary: ring summaries cover [F, t-r] instead of
+     * [0, t-r], and every step attends [0, min(F, m+1)) exactly with its own
+     * query, hit or miss.  0 (the default) is the plain method. */
+    int32_t front_sink;
 } mac_params;
 
 /* Ring buffers of one attention layer, caller-allocated device memory:
@@ -134,11 +142,13 @@ mac_status mac_ring_bytes(const mac_params *p, size_t out[4]);
 /*
  * mac_init_rings -- reset one layer's rings and bind them to a handle.
  *
- * Every slot is emptied (pos -1, lse -inf).  With n_warm = W > 0 the last W
- * prompt positions t = ctx_len[b] - W + w (w = 0..W-1) are pre-filled: slot
- * t mod K receives the pre-RoPE query warm_qtilde[b, h, w, :], the summary of
- * full attention of the post-RoPE query warm_q[b, h, w, :] over [0, t-r]
- * (empty when t < r) and pos t.  W must not exceed K, and ctx_len[b] >= W.
+ * Every slot is emptied (pos -1, lse -inf) and the rings' epochs are set to
+ * 0 (see mac_bind_epochs).  With n_warm = W > 0 the last W prompt positions
+ * t = ctx_len[b] - W + w (w = 0..W-1) are pre-filled: slot t mod K receives
+ * the pre-RoPE query warm_qtilde[b, h, w, :], the summary of attention of
+ * the post-RoPE query warm_q[b, h, w, :] over [F, t-r] (empty when
+ * t - r < F; F = front_sink) and pos t.  W must not exceed K, and
+ * ctx_len[b] >= W.
  *   warm_qtilde [B, Hq, W, d] kv_dtype   (device; ignored when W = 0)
  *   warm_q      [B, Hq, W, d] fp32       (device; ignored when W = 0)
  *   ctx_len     [B] int32 on the HOST: the prompt length of each request.
@@ -165,6 +175,10 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
  *   match_p [B, Hq] int32 or NULL  matched position, -1 on a miss
  *   match_d2[B, Hq] fp32 or NULL   squared distance of the nearest candidate
  *                                  (+inf when the window is empty)
+ * With front_sink F > 0 a hit at p merges the cached summary of [F, p-r],
+ * the sink [0, min(F, m+1)) and fresh attention over [max(F, p-r+1), m],
+ * and the appended summary covers [F, m-r].  Requests whose rings are not
+ * ready (mac_bind_epochs) are computed as misses.
  * Match, amend and complete run on main_stream as one kernel launch whose
  * workgroups are all resident at once (the workgroups of each KV group hand
  * match keys and partial summaries to each other inside the launch), or as
@@ -192,13 +206,32 @@ mac_status mac_decode_step(mac_handle *h, const void *qtilde, const float *q,
                            int32_t *match_p, float *match_d2,
                            void *main_stream, void *aux_stream);
 
+/*
+ * mac_bind_epochs -- device ready/epoch gating (blog, "Production version:
+ * one fused persistent BF16 kernel", the graph-safe readiness item).
+ *   epoch [B] int32 (device, 4-byte aligned), or NULL to unbind.
+ * Binds the caller's per-request epoch array to the handle; later
+ * mac_decode_step calls read it on the device.  The rings of each KV group
+ * remember the epoch they were built for (0 after mac_init_rings).  At a
+ * step where epoch[b] differs from that, or is negative, request b's rings
+ * are not ready: its match finds no candidate, so every head of b is exact
+ * full attention (match_p -1, match_d2 +inf), and the step's rectify-append
+ * empties b's position ring before adding its own entry and adopts
+ * epoch[b] (a negative epoch is never adopted as ready).  Bumping epoch[b]
+ * on the device -- inside a captured graph too -- thus invalidates and
+ * restarts request b's rings without a host call.  The array is read on
+ * main_stream and must stay valid while steps that read it run.
+ */
+mac_status mac_bind_epochs(mac_handle *h, const int32_t *epoch);
+
 /* Make `stream` wait for the last rectify-append enqueued on the handle. */
 mac_status mac_join_aux(mac_handle *h, void *stream);
 
 /*
  * mac_full_decode -- exact split-KV decode attention over [0, pos[b]] for
  * every (request, query head); the miss path of mac_decode_step runs the
- * same kernels on the same partition, so a forced miss gives bitwise the
+ * same kernels on the same partition (with front_sink F > 0 the positions
+ * [0, F) are their own item in both), so a forced miss gives bitwise the
  * same output.  Arguments as in mac_decode_step; needs a workspace of
  * mac_workspace_bytes(p) (not shared with a concurrently running handle).
  */
@@ -230,7 +263,7 @@ mac_status mac_release(mac_handle *h);
 const char *mac_status_string(mac_status s);
 
 /* Grid of the split-KV partition for a KV group attending [s, e]: the
- * smallest C = 128 * 2^k with at most 128 grid cells over the range (-1 on
+ * smallest C = 64 * 2^k with at most 128 grid cells over the range (-1 on
  * bad input). */
 int32_t mac_chunk_tokens(int32_t s, int32_t e);
 
@@ -238,6 +271,8 @@ int32_t mac_chunk_tokens(int32_t s, int32_t e);
  * [s, e] with band r (host mirror of the device planner): item i covers
  * [t0[i], t1[i]); boundaries are s, the multiples of mac_chunk_tokens(s, e)
  * in (s, e], the rectify split e - r + 1 when inside (s, e], and e + 1.
+ * With front_sink F > 0 the planner applies this to [max(s, F), e] and
+ * adds the sink [0, min(F, e + 1)) as one more item.
  * Writes min(n, cap) items (host arrays) and returns n, or -1 on bad input. */
 int32_t mac_partition(int32_t s, int32_t e, int32_t r, int32_t *t0,
                       int32_t *t1, int32_t cap);

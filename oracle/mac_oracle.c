@@ -301,6 +301,9 @@ int mac_oracle_stream(const mac_oracle_cfg *c, const void *K, const void *V,
             for (int k = 0; k < Kr; ++k) {
                 pos[k] = -1;
                 lazy[k] = 0;
+                sl[k] = -INFINITY;
+                for (int i = 0; i < d; ++i)
+                    qr[k * d + i] = so[k * d + i] = 0.0;
             }
         }
 

@@ -33,9 +33,16 @@ def test_exports_every_declared_function(lib):
 
 
 def test_struct_layout_matches_header():
-    assert ctypes.sizeof(mac.mac_params) == 72
+    assert ctypes.sizeof(mac.mac_params) == 80
     assert mac.mac_params.kv_stride_b.offset == 48
+    assert mac.mac_params.front_sink.offset == 72
     assert ctypes.sizeof(mac.mac_rings) == 32
+
+
+def test_front_sink_bounds(lib):
+    assert mac.mac_workspace_bytes(_params(front_sink=4096)) > 0
+    assert mac.mac_workspace_bytes(_params(front_sink=4097)) == 0
+    assert mac.mac_workspace_bytes(_params(front_sink=-1)) == 0
 
 
 def test_status_strings_and_chunk(lib):
