@@ -126,7 +126,7 @@ static mac_status check_params(const mac_params *p, Shape *s)
         p->n_q_heads % p->n_kv_heads != 0 || p->ring_k < 1 ||
         p->band_r < 0 || p->kv_capacity < 1 ||
         (p->flags & ~(MAC_FLAG_FUSED_APPEND | MAC_FLAG_SPLIT_STAGES |
-                      MAC_FLAG_SINGLE_LAUNCH)) != 0 ||
+                      MAC_FLAG_SINGLE_LAUNCH | MAC_FLAG_MATCH_FILTER)) != 0 ||
         (p->flags & MAC_FLAG_SPLIT_STAGES && p->flags & MAC_FLAG_SINGLE_LAUNCH) ||
         !isfinite(p->tau) || !isfinite(p->sm_scale) || p->sm_scale < 0.f ||
         p->front_sink < 0 || p->front_sink > kMaxFrontSink ||
@@ -142,6 +142,9 @@ static mac_status check_params(const mac_params *p, Shape *s)
     // planner keeps its per-head and per-group tables in LDS.
     if ((int64_t)p->kv_capacity > (1 << 30) || p->ring_k > (1 << 24))
         return MAC_ERR_INVALID_ARG;
+    // One head's query ring is addressed with 32-bit byte offsets.
+    if ((int64_t)p->ring_k * p->head_dim * elem_bytes(p->kv_dtype) >= ((int64_t)1 << 31))
+        return MAC_ERR_UNSUPPORTED;
     if ((int64_t)p->batch * p->n_q_heads > 8192 ||
         plan_lds_bytes(p->batch, p->n_q_heads, p->n_kv_heads) > 48 * 1024)
         return MAC_ERR_UNSUPPORTED;
@@ -494,6 +497,7 @@ mac_status mac_decode_step(mac_handle *h, const void *qtilde, const float *q,
     a.pos_ring = h->rings.pos_ring;
     a.append_fused = h->fused_append ? 1 : 0;
     a.epoch = h->epoch;
+    a.match_filter = (h->p.flags & MAC_FLAG_MATCH_FILTER) ? 1 : 0;
     a.wpg = h->wpg;
     a.upg = h->upg;
     a.nkw = h->nkw;

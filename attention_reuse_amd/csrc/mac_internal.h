@@ -316,6 +316,9 @@ struct StepArgs {
     // (the ring reset and every merge kernel leave it so); 0 = all of the
     // work is split statically and the counter is not touched
     int32_t dyn_pool;
+    // match: read the second half of a ring row only when the first half's
+    // squared distance is below the threshold (exact lower-bound filter)
+    int32_t match_filter;
 };
 
 // Bytes of dynamic LDS the planner needs.

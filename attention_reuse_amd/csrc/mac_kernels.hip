@@ -543,7 +543,21 @@ template <class T, int D, int U>
 struct MatchLoads {
     uint4 q, raw[U];
     int p[U];
+    // The head's query ring as a buffer: a load at offset `oob` (its size)
+    // returns zeros without touching memory, so reads are skipped per lane
+    // without a branch.
+    __amdgpu_buffer_rsrc_t ring;
+    uint32_t oob;
+    int first;
 };
+
+// Ring slot of load u of this lane's row.
+template <int U>
+__device__ inline int match_slot(const StepArgs &a, int first, int u, int rpb, int row)
+{
+    const int k = first + u * rpb + row;
+    return k < a.s.K ? k : a.s.K - 1;
+}
 
 template <class T, int D, int U>
 __device__ inline void match_issue(const StepArgs &a, int first, int bh, MatchLoads<T, D, U> &ml)
@@ -554,16 +568,28 @@ __device__ inline void match_issue(const StepArgs &a, int first, int bh, MatchLo
     const int b = bh / s.Hq, h = bh - b * s.Hq;
     const int lane = threadIdx.x % LPR, row = threadIdx.x / LPR;
     ml.q = load16((const S *)a.qtilde + b * a.qt_sb + h * a.qt_sh + lane * EPL);
-    const S *ring = (const S *)a.q_ring + (int64_t)bh * s.K * D + lane * EPL;
+    ml.oob = (uint32_t)s.K * D * sizeof(S);
+    ml.ring = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<S *>((const S *)a.q_ring + (int64_t)bh * s.K * D), (short)0, (int)ml.oob,
+        0x00020000);
+    ml.first = first;
     const int32_t *pr = a.pos_ring + ((int64_t)b * s.Hkv + h / s.G) * s.K;
+    // With the match filter only the first half of each row is read here.
+    const bool first_half = !a.match_filter || lane < LPR / 2;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        int k = first + u * RPB + row;
-        k = k < s.K ? k : s.K - 1;
-        ml.raw[u] = load16(ring + (int64_t)k * D);
+        const int k = match_slot<U>(a, first, u, RPB, row);
+        const uint32_t off = first_half ? (uint32_t)(k * D + lane * EPL) * sizeof(S) : ml.oob;
+        ml.raw[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ml.ring, off, 0, 0));
         ml.p[u] = pr[k];
     }
 }
+
+// Lower bound of the filter: a row whose first-half squared distance is at
+// least thresh2 * kFilterMargin has a full distance above the threshold
+// whatever the fp32 rounding of either sum (both are sums of the same
+// non-negative per-lane terms, so they differ by far less than the margin).
+constexpr float kFilterMargin = 1.0f + 1.0f / 1024.0f;
 
 // Key of the unit issued by match_issue at position m; valid in thread 0.
 // A group that is not ready has no candidate.  sm holds kBlock/64 words of
@@ -573,25 +599,59 @@ __device__ inline unsigned long long match_finish(const StepArgs &a, int m, bool
                                                   const MatchLoads<T, D, U> &ml,
                                                   unsigned long long *sm)
 {
-    constexpr int EPL = T::EPL, LPR = D / EPL;
+    constexpr int EPL = T::EPL, LPR = D / EPL, RPB = kBlock / LPR;
     const Shape &s = a.s;
     const bool m_ok = ready && m >= 0 && m < s.T;
     float qv[EPL];
     unpack<T>(ml.q, qv);
-    unsigned long long best = ~0ull;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
+    // This lane's share of each row's squared distance.
+    auto lane_d2 = [&](const uint4 &raw) {
         float rv[EPL];
-        unpack<T>(ml.raw[u], rv);
+        unpack<T>(raw, rv);
         float acc = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
             const float df = qv[e] - rv[e];
             acc = fmaf(df, df, acc);
         }
-        acc = row_sum<LPR>(acc);
+        return acc;
+    };
+    float part[U];
+    bool keep[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        part[u] = lane_d2(ml.raw[u]);
+        keep[u] = true;
+    }
+    if (a.match_filter) {
+        // Exact lower-bound filter: the second half of a row is read only
+        // when its first half leaves the row able to hit.  The full sum of
+        // a kept row is formed below exactly as without the filter.
+        const int lane = threadIdx.x % LPR, row = threadIdx.x / LPR;
+        const bool upper = lane >= LPR / 2;
+        const float lb_max = s.thresh2 * kFilterMargin;
+        uint4 raw2[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float lb = row_sum<LPR>(upper ? 0.f : part[u]);
+            const int pu = ml.p[u];
+            keep[u] = lb < lb_max && m_ok && pu >= 0 && pu >= m - s.K && pu <= m - 1;
+            const int k = match_slot<U>(a, ml.first, u, RPB, row);
+            const uint32_t off =
+                upper && keep[u] ? (uint32_t)(k * D + lane * EPL) * sizeof(typename T::S) : ml.oob;
+            raw2[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ml.ring, off, 0, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (upper)
+                part[u] = lane_d2(raw2[u]);
+    }
+    unsigned long long best = ~0ull;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const float acc = row_sum<LPR>(part[u]);
         const int pu = ml.p[u];
-        const bool valid = m_ok && pu >= 0 && pu >= m - s.K && pu <= m - 1;
+        const bool valid = keep[u] && m_ok && pu >= 0 && pu >= m - s.K && pu <= m - 1;
         uint32_t bits = __float_as_uint(acc);
         if (acc != acc)
             bits = 0x7f800000u;  // NaN distance counts as +inf

@@ -25,6 +25,7 @@ MAC_DEV_SYNC_TIMEOUT = 2
 MAC_FLAG_FUSED_APPEND = 1
 MAC_FLAG_SPLIT_STAGES = 2
 MAC_FLAG_SINGLE_LAUNCH = 4
+MAC_FLAG_MATCH_FILTER = 8
 STATUS = {0: "MAC_OK", -1: "MAC_ERR_INVALID_ARG", -2: "MAC_ERR_UNSUPPORTED",
           -3: "MAC_ERR_HIP", -4: "MAC_ERR_WORKSPACE_TOO_SMALL",
           -5: "MAC_ERR_MISALIGNED"}

@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--launch", choices=("auto", "single", "split"), default="auto",
                     help="decode step as one launch, as match / attend / merge kernels, "
                          "or the library's choice for the shape")
+    ap.add_argument("--match-filter", action="store_true",
+                    help="exact lower-bound filter of the match (second halves of ring "
+                         "rows read only where a hit is still possible)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--no-profile", action="store_true")
@@ -87,14 +90,30 @@ def read_traffic(workload_name, kernel):
     return None
 
 
-def algorithmic_bytes(cfg, match_p, m):
+def filter_second_halves(cfg, qt, s):
+    """Ring rows whose second half the match filter reads at decode step s:
+    candidates whose first-half squared distance (fp32) is below the
+    threshold times the filter margin.  qt: [B, Hq, W+S, d] storage."""
+    W, K, d = cfg.n_warm, min(cfg.ring_k, cfg.ctx), cfg.head_dim
+    cur = wl.from_storage(qt[:, :, W + s, : d // 2]).astype(np.float32)
+    ring = wl.from_storage(qt[:, :, W + s - K:W + s, : d // 2]).astype(np.float32)
+    lb = ((ring - cur[:, :, None, :]) ** 2).sum(-1, dtype=np.float32)
+    t2 = np.float32(2.0 * d * (1.0 - float(np.float32(cfg.tau))) ** 2)
+    return int((lb < t2 * np.float32(1.0 + 1.0 / 1024.0)).sum())
+
+
+def algorithmic_bytes(cfg, match_p, m, second_halves=None):
     """Bytes the method must move per layer-step, by stage.
 
-    match_p: [B, Hq] matched position (-1 miss); m: [B] positions."""
+    match_p: [B, Hq] matched position (-1 miss); m: [B] positions;
+    second_halves: with the match filter, the ring rows read in full."""
     B, H, Hkv, G, d = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.group, cfg.head_dim
     e = cfg.elem_bytes
     K_valid = min(cfg.ring_k, cfg.ctx)
-    match = B * H * K_valid * d * e + B * Hkv * K_valid * 4 + B * H * d * e
+    rows = B * H * K_valid * d * e
+    if second_halves is not None:
+        rows = rows // 2 + second_halves * (d * e // 2)
+    match = rows + B * Hkv * K_valid * 4 + B * H * d * e
     start = np.where(match_p >= 0, np.maximum(0, match_p - cfg.band_r + 1), 0)
     s_g = start.reshape(B, Hkv, G).min(axis=2)
     span = (m[:, None] - s_g + 1).astype(np.int64)
@@ -197,6 +216,7 @@ def main():
     p = mac.make_params(B, H, Hkv, d, mac.MAC_DTYPE_F32 if cfg.dtype == "f32" else mac.MAC_DTYPE_BF16,
                         R, cfg.band_r, cfg.capacity, cfg.tau,
                         flags=(mac.MAC_FLAG_FUSED_APPEND if args.append == "fused" else 0)
+                        | (mac.MAC_FLAG_MATCH_FILTER if args.match_filter else 0)
                         | {"auto": 0, "single": mac.MAC_FLAG_SINGLE_LAUNCH,
                            "split": mac.MAC_FLAG_SPLIT_STAGES}[args.launch])
     wsb = mac.mac_workspace_bytes(p)
@@ -271,9 +291,11 @@ def main():
                             "hits", "group_miss")}
     timed = range(args.warmup, args.warmup + args.steps)
     for s in timed:
+        halves = (filter_second_halves(cfg, qt, s)
+                  if args.mode == "mac" and args.match_filter else None)
         for li in range(NL):
             mp = mrec[s, li] if args.mode == "mac" else np.full((B, H), -1, np.int32)
-            ab = algorithmic_bytes(cfg, mp, pos_np[s].astype(np.int64))
+            ab = algorithmic_bytes(cfg, mp, pos_np[s].astype(np.int64), halves)
             for k in per:
                 per[k] += ab[k]
     n_ls = args.steps * NL
@@ -344,6 +366,7 @@ def main():
         "config": {"workload": cfg.name, "mode": args.mode,
                    "launch": launched or args.launch,
                    "append": args.append,
+                   "match_filter": bool(args.match_filter),
                    "layers": NL, "kv_dtype": cfg.dtype,
                    "batch": B, "q_heads": H, "kv_heads": Hkv, "head_dim": d,
                    "context": cfg.ctx, "ring_k": R, "band_r": cfg.band_r, "tau": cfg.tau,

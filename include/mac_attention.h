@@ -78,8 +78,24 @@ enum { MAC_THRESH_ONE_MINUS_TAU = 0, MAC_THRESH_TAU = 1 };
  * most 16 KV groups (batch * n_kv_heads) and the shape is one the single
  * launch handles, where the step is bound by latency, and three kernels
  * otherwise, where it is bound by bandwidth.
- * Both forms give the same results bit for bit. */
-enum { MAC_FLAG_FUSED_APPEND = 1, MAC_FLAG_SPLIT_STAGES = 2, MAC_FLAG_SINGLE_LAUNCH = 4 };
+ * Both forms give the same results bit for bit.
+ *   MAC_FLAG_MATCH_FILTER: exact lower-bound filter of the match (blog,
+ *   "Production version: one fused persistent BF16 kernel", the match-scan
+ *   item).  The first half of every candidate row is read; the second half
+ *   only when the first half's squared distance is below the threshold
+ *   (times 1 + 2^-10, a margin that covers fp32 rounding).  A row cut there
+ *   cannot hit, so the decisions, matched positions, outputs and rings are
+ *   bit for bit those of the full scan; match_d2 is unchanged for hits, and
+ *   for a miss is the smallest distance among the rows read in full (+inf
+ *   if none), always at least the threshold.  It pays where the match is
+ *   bound by bandwidth (many KV groups, three kernels) and ring rows are
+ *   128-byte aligned; it adds a dependent read to a latency-bound step. */
+enum {
+    MAC_FLAG_FUSED_APPEND = 1,
+    MAC_FLAG_SPLIT_STAGES = 2,
+    MAC_FLAG_SINGLE_LAUNCH = 4,
+    MAC_FLAG_MATCH_FILTER = 8
+};
 
 /* Device status flags latched in the workspace. */
 enum {

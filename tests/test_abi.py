@@ -75,7 +75,7 @@ def test_workspace_and_ring_sizes(lib):
     (dict(head_dim=96), -2), (dict(kv_dtype=7), -2), (dict(n_q_heads=48, n_kv_heads=3), -2),
     (dict(n_q_heads=30), -1), (dict(ring_k=0), -1), (dict(band_r=-1), -1),
     (dict(batch=0), -1), (dict(kv_capacity=0), -1), (dict(tau=float("nan")), -1),
-    (dict(thresh_mode=2), -1), (dict(strides=(0, 0, 100)), -1), (dict(flags=8), -1),
+    (dict(thresh_mode=2), -1), (dict(strides=(0, 0, 100)), -1), (dict(flags=16), -1),
     (dict(flags=6), -1), (dict(flags=1), 0), (dict(flags=3), 0), (dict(flags=5), 0),
     (dict(batch=300), -2),
     (dict(strides=(1 << 20, 4096 * 136, 136)), 0), (dict(strides=(1 << 20, 4096 * 132, 132)), -5),
