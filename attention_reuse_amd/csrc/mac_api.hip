@@ -153,10 +153,27 @@ static mac_status check_params(const mac_params *p, Shape *s)
     if ((int64_t)p->batch * p->n_kv_heads * ((int64_t)p->kv_capacity + (int64_t)kItemCost * kItemsPerGroupMax) >=
         ((int64_t)1 << 31))
         return MAC_ERR_UNSUPPORTED;
+    // Paged K/V: a power-of-two page size of at least 16 tokens, a page
+    // table whose rows cover kv_capacity.
+    const bool paged = p->page_size != 0;
+    int shift = 0;
+    if (paged) {
+        while (shift < 30 && (1 << shift) < p->page_size)
+            ++shift;
+        if (p->page_size < 16 || p->page_size > (1 << 20) || (1 << shift) != p->page_size ||
+            p->max_pages < 1 || !p->page_table || ((uintptr_t)p->page_table & 3u) ||
+            (int64_t)p->max_pages * p->page_size < p->kv_capacity ||
+            (int64_t)p->batch * p->max_pages >= ((int64_t)1 << 31))
+            return MAC_ERR_INVALID_ARG;
+    } else if (p->max_pages != 0 || p->page_table) {
+        return MAC_ERR_INVALID_ARG;
+    }
     int64_t st = p->kv_stride_t, sh = p->kv_stride_h, sb = p->kv_stride_b;
     if (st == 0 && sh == 0 && sb == 0) {
+        // Dense [B, Hkv, T, d]; paged [pages, Hkv, page_size, d].
+        const int64_t rows = paged ? p->page_size : p->kv_capacity;
         st = p->head_dim;
-        sh = st * p->kv_capacity;
+        sh = st * rows;
         sb = sh * p->n_kv_heads;
     }
     if (st < p->head_dim || sh < 0 || sb < 0)
@@ -181,6 +198,9 @@ static mac_status check_params(const mac_params *p, Shape *s)
         s->r = p->band_r;
         s->T = p->kv_capacity;
         s->F = p->front_sink;
+        s->page_shift = paged ? shift : 0;
+        s->max_pages = paged ? p->max_pages : 0;
+        s->page_table = paged ? p->page_table : nullptr;
         s->kv_sb = sb;
         s->kv_sh = sh;
         s->kv_st = st;
@@ -539,6 +559,26 @@ mac_status mac_decode_step(mac_handle *h, const void *qtilde, const float *q,
 #undef MAC_STAGE
     if (prof)
         ++h->prof_n;
+    return MAC_OK;
+}
+
+mac_status mac_append_kv(const mac_params *p, const void *k_new, const void *v_new,
+                         const void *q_tilde, float *q_out, const int32_t *pos, double rope_base,
+                         void *k_cache, void *v_cache, void *stream)
+{
+    Shape s;
+    mac_status rc = check_params(p, &s);
+    if (rc != MAC_OK)
+        return rc;
+    if (!k_new || !v_new || !pos || !k_cache || !v_cache || (!q_tilde) != (!q_out) ||
+        !(rope_base >= 0.0) || !isfinite(rope_base))
+        return MAC_ERR_INVALID_ARG;
+    const int eb = elem_bytes(s.dtype);
+    if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)q_tilde | (uintptr_t)k_cache |
+         (uintptr_t)v_cache) % eb || ((uintptr_t)q_out & 3u))
+        return MAC_ERR_MISALIGNED;
+    MAC_HIP(launch_append_kv(s, k_new, v_new, q_tilde, q_out, pos, rope_base, k_cache, v_cache,
+                             (hipStream_t)stream));
     return MAC_OK;
 }
 

@@ -251,6 +251,11 @@ enum { kCtrlItems = 0, kCtrlStatus = 1, kCtrlClaim = 2 };
 struct Shape {
     int32_t B, Hq, Hkv, G, D, dtype, K, r, T;
     int32_t F;                    // front sink: leading positions never reused
+    // Paged K/V (page_table non-null): row t of request b, KV head g at
+    // b's page page_table[b * max_pages + (t >> page_shift)], element
+    // offset page * kv_sb + g * kv_sh + (t mod page size) * kv_st.
+    int32_t page_shift, max_pages;
+    const int32_t *page_table;
     int64_t kv_sb, kv_sh, kv_st;  // elements
     float qscale;                 // sm_scale * log2(e)
     float thresh2;
@@ -352,5 +357,10 @@ hipError_t launch_ring_reset(const Shape &s, void *q_ring, float *o_ring,
                              float *lse_ring, int32_t *pos_ring, const WsPtrs &w,
                              int64_t n_tag, hipStream_t st);
 int device_cu_count();
+// K and V of position pos[b] into the cache, K rotated by RoPE (base > 0),
+// and q_out = RoPE(q_tilde) when q_out is non-null.
+hipError_t launch_append_kv(const Shape &s, const void *k_new, const void *v_new,
+                            const void *q_tilde, float *q_out, const int32_t *pos, double base,
+                            void *k_cache, void *v_cache, hipStream_t st);
 
 }  // namespace mac

@@ -1179,6 +1179,9 @@ struct AttendShape {
     // heads' queries split into bf16 high and low parts, 8 columns unused)
     // instead of VALU dot products and a row reduce-scatter.
     static constexpr bool kMfma = kScatter && T::EPL == 8 && D == 128 && G == 4;
+    // The MFMA path fits two waves per SIMD (256 registers) when the
+    // register allocator is told to; the other shapes are left to it.
+    static constexpr int kWavesPerEu = kMfma ? 2 : 1;
     // m, l, acc per row; row weights; per-head sum and maximum
     static constexpr int kFloats = RPB * G * (D + 3) + 2 * G;
 };
@@ -1202,15 +1205,75 @@ __device__ inline int k_lane_offset()
         return (threadIdx.x % (D / T::EPL)) * T::EPL;
 }
 
-// K/V rows of one block.  Every lane loads: a token at or past t1 reads row
-// t1 - 1 of the item instead, which the block computation masks (its logit
-// is -inf, its probability exactly 0).  No branch separates the loads, so
-// the compiler can wait for each block on its own.
-template <class T, int D, int G, int LPR, int RPB, int NB>
-__device__ inline void load_block(KvBlock<T, G, T::EPL, NB> &kv, const typename T::S *kb,
-                                  const typename T::S *vb, int64_t kv_st, int base, int t1,
-                                  int row)
+// Where one KV group's rows live, as seen by one lane.  Dense: row t at
+// k + t * kv_st (k at the request and group).  Paged: row t of the request
+// at k + table[t >> page_shift] * kv_sb + (t mod page size) * kv_st (k at
+// the group only; table is the request's row of the page table).
+template <class T>
+struct KvRows {
+    const typename T::S *k, *v;
+    const int32_t *table;  // null when dense
+};
+
+template <class T, int D, int G, bool kPaged>
+__device__ inline KvRows<T> kv_rows(const StepArgs &a, int b, int g)
 {
+    using S = typename T::S;
+    const Shape &s = a.s;
+    const int64_t gb = (kPaged ? 0 : b * s.kv_sb) + g * s.kv_sh;
+    KvRows<T> r;
+    r.k = (const S *)a.k + gb + k_lane_offset<T, D, G>();
+    r.v = (const S *)a.v + gb + (threadIdx.x % (D / T::EPL)) * T::EPL;
+    r.table = kPaged ? s.page_table + (int64_t)b * s.max_pages : nullptr;
+    return r;
+}
+
+// Element offsets of the rows of a paged block: the block's page numbers
+// come through scalar loads (the table is read-only during the launch, and
+// scalar loads do not queue behind the vector loads in flight), then each
+// lane picks its token's page.  A block of TPB tokens spans at most
+// TPB / kMinPage + 1 pages.
+constexpr int kMinPage = 16;
+template <int TPB>
+struct BlockPages {
+    static constexpr int N = TPB / kMinPage + 1;
+    int pg[N];
+    int p0, shift;
+    __device__ BlockPages() {}
+    __device__ BlockPages(const Shape &s, const int32_t *table, int base, int t1)
+    {
+        base = __builtin_amdgcn_readfirstlane(base);
+        t1 = __builtin_amdgcn_readfirstlane(t1);
+        shift = s.page_shift;
+        const int last = (base + TPB < t1 ? base + TPB : t1) - 1;
+        p0 = base >> shift;
+        const int pl = last >> shift;
+        const __attribute__((address_space(4))) int32_t *ct =
+            (const __attribute__((address_space(4))) int32_t *)table;
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+            pg[j] = ct[p0 + j < pl ? p0 + j : pl];
+    }
+    // The page of token t as pg[0] plus the steps pg[k] - pg[k-1] for
+    // k <= j: a sum over the few scalars rather than an indexed read, which
+    // the compiler would place in scratch memory.
+    __device__ int64_t offset(const Shape &s, int t) const
+    {
+        const int j = (t >> shift) - p0;
+        int page = pg[0];
+#pragma unroll
+        for (int k = 1; k < N; ++k)
+            page += (j >= k) ? pg[k] - pg[k - 1] : 0;
+        return (int64_t)page * s.kv_sb + (int64_t)(t & ((1 << shift) - 1)) * s.kv_st;
+    }
+};
+
+// load_block with row t at element offset off(t) from the lane's column.
+template <class T, int D, int G, int LPR, int RPB, int NB, class Off>
+__device__ inline void load_block_at(KvBlock<T, G, T::EPL, NB> &kv, const KvRows<T> &rows,
+                                     int base, int t1, int row, Off &&off)
+{
+    const typename T::S *kb = rows.k, *vb = rows.v;
     kv.base = base;
     if constexpr (AttendShape<T, D, G>::kMfma) {
         // K in the MFMA A layout: lane l (m = l % 16) loads token
@@ -1220,23 +1283,44 @@ __device__ inline void load_block(KvBlock<T, G, T::EPL, NB> &kv, const typename 
         const int m = threadIdx.x & 15;
         int tk = base + 16 * (m & 3) + 4 * (threadIdx.x >> 6) + (m >> 2);
         tk = tk < t1 ? tk : t1 - 1;
+        const int64_t ok = off(tk);
 #pragma unroll
         for (int kk = 0; kk < NB; ++kk)
-            kv.k[kk] = load16(kb + (int64_t)tk * kv_st + 32 * kk);
+            kv.k[kk] = load16(kb + ok + 32 * kk);
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             int t = base + i * RPB + row;
             t = t < t1 ? t : t1 - 1;
-            kv.v[i] = load16(vb + (int64_t)t * kv_st);
+            kv.v[i] = load16(vb + off(t));
         }
     } else {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             int t = base + i * RPB + row;
             t = t < t1 ? t : t1 - 1;
-            kv.k[i] = load16(kb + (int64_t)t * kv_st);
-            kv.v[i] = load16(vb + (int64_t)t * kv_st);
+            const int64_t o = off(t);
+            kv.k[i] = load16(kb + o);
+            kv.v[i] = load16(vb + o);
         }
+    }
+}
+
+// K/V rows of one block.  Every lane loads: a token at or past t1 reads row
+// t1 - 1 of the item instead, which the block computation masks (its logit
+// is -inf, its probability exactly 0).  No branch separates the loads, so
+// the compiler can wait for each block on its own.
+template <class T, int D, int G, int LPR, int RPB, int NB, bool kPaged>
+__device__ inline void load_block(KvBlock<T, G, T::EPL, NB> &kv, const KvRows<T> &rows,
+                                  const Shape &s, int base, int t1, int row)
+{
+    if constexpr (kPaged) {
+        const BlockPages<RPB * NB> bp(s, rows.table, base, t1);
+        load_block_at<T, D, G, LPR, RPB, NB>(kv, rows, base, t1, row,
+                                             [&](int t) { return bp.offset(s, t); });
+    } else {
+        const int64_t st = s.kv_st;
+        load_block_at<T, D, G, LPR, RPB, NB>(kv, rows, base, t1, row,
+                                             [&](int t) { return (int64_t)t * st; });
     }
 }
 
@@ -1446,20 +1530,14 @@ __device__ inline void compute_block_rs(const KvBlock<T, G, T::EPL, NB> &kv, int
 // Per-(request, KV group) state of the attention items: this lane's K/V
 // row pointers and its slice of the group's post-RoPE queries (pre-scaled
 // by scale * log2 e).  Built once per group, before the items are known.
-template <class T, int D, int G>
+template <class T, int D, int G, bool kPaged = false>
 struct ItemCtx {
     using S = typename T::S;
     static constexpr int EPL = T::EPL;
-    const S *kb, *vb;
+    KvRows<T> rows;
     QRegs<T, D, G> q;
-    // K/V row pointers only; the queries come from queries_from_lds.
-    __device__ ItemCtx(const StepArgs &a, int b, int g, bool)
-    {
-        const Shape &s = a.s;
-        const int lane = threadIdx.x % (D / EPL);
-        kb = (const S *)a.k + b * s.kv_sb + g * s.kv_sh + k_lane_offset<T, D, G>();
-        vb = (const S *)a.v + b * s.kv_sb + g * s.kv_sh + lane * EPL;
-    }
+    // K/V rows only; the queries come from queries_from_lds.
+    __device__ ItemCtx(const StepArgs &a, int b, int g, bool) : rows(kv_rows<T, D, G, kPaged>(a, b, g)) {}
     // This lane's queries from LDS ([G][D] floats, as QueryStage stores
     // them, and on the MFMA path the B operands QueryStage::store_b forms),
     // scaled as the global-memory constructor scales them.
@@ -1557,18 +1635,18 @@ struct ItemBufs {
     KvBlock<T, G, T::EPL, L::NB> a, b;
 };
 
-template <class T, int D, int G>
-__device__ inline void item_issue(const StepArgs &a, const ItemCtx<T, D, G> &ctx, int t0, int t1,
+template <class T, int D, int G, bool kPaged>
+__device__ inline void item_issue(const StepArgs &a, const ItemCtx<T, D, G, kPaged> &ctx, int t0, int t1,
                                   ItemBufs<T, D, G> &bufs, bool both)
 {
     using L = AttendShape<T, D, G>;
     constexpr int LPR = L::LPR, RPB = L::RPB, NB = L::NB, TPB = RPB * NB;
     const int row = threadIdx.x / LPR;
-    load_block<T, D, G, LPR, RPB, NB>(bufs.a, ctx.kb, ctx.vb, a.s.kv_st, t0, t1, row);
+    load_block<T, D, G, LPR, RPB, NB, kPaged>(bufs.a, ctx.rows, a.s, t0, t1, row);
     // both: the second block is requested without a branch (all its rows
     // clamp to t1 - 1 when the item has one block).
     if (both || t0 + TPB < t1)
-        load_block<T, D, G, LPR, RPB, NB>(bufs.b, ctx.kb, ctx.vb, a.s.kv_st, t0 + TPB, t1, row);
+        load_block<T, D, G, LPR, RPB, NB, kPaged>(bufs.b, ctx.rows, a.s, t0 + TPB, t1, row);
 }
 
 // Running state of one work item's attention: per-row online softmax in
@@ -1689,8 +1767,8 @@ __device__ inline void item_combine(const ItemAcc<T, D, G> &ia, float *lds, int 
 // by the whole workgroup; head j of the group attends from st[j].  Each
 // block's successor two blocks ahead is requested as soon as the block has
 // been consumed.  The partial goes to sink as in item_combine.
-template <class T, int D, int G, class Sink>
-__device__ inline void item_finish(const StepArgs &a, const ItemCtx<T, D, G> &ctx, int t0, int t1,
+template <class T, int D, int G, bool kPaged, class Sink>
+__device__ inline void item_finish(const StepArgs &a, const ItemCtx<T, D, G, kPaged> &ctx, int t0, int t1,
                                    const int (&st)[G], float *lds, ItemBufs<T, D, G> &bufs,
                                    Sink &&sink)
 {
@@ -1701,7 +1779,6 @@ __device__ inline void item_finish(const StepArgs &a, const ItemCtx<T, D, G> &ct
     const int lane = threadIdx.x % LPR, row = threadIdx.x / LPR;
     t0 = __builtin_amdgcn_readfirstlane(t0);
     t1 = __builtin_amdgcn_readfirstlane(t1);
-    const auto *kb = ctx.kb, *vb = ctx.vb;
     auto &bufA = bufs.a;
     auto &bufB = bufs.b;
     ItemAcc<T, D, G> ia;
@@ -1709,11 +1786,11 @@ __device__ inline void item_finish(const StepArgs &a, const ItemCtx<T, D, G> &ct
     for (int base = t0; base < t1; base += 2 * TPB) {
         item_block<T, D, G>(bufA, row, lane, ctx.q, st, t1, ia);
         if (base + 2 * TPB < t1)
-            load_block<T, D, G, LPR, RPB, NB>(bufA, kb, vb, s.kv_st, base + 2 * TPB, t1, row);
+            load_block<T, D, G, LPR, RPB, NB, kPaged>(bufA, ctx.rows, s, base + 2 * TPB, t1, row);
         if (base + TPB < t1) {
             item_block<T, D, G>(bufB, row, lane, ctx.q, st, t1, ia);
             if (base + 3 * TPB < t1)
-                load_block<T, D, G, LPR, RPB, NB>(bufB, kb, vb, s.kv_st, base + 3 * TPB, t1, row);
+                load_block<T, D, G, LPR, RPB, NB, kPaged>(bufB, ctx.rows, s, base + 3 * TPB, t1, row);
         }
     }
     item_combine<T, D, G>(ia, lds, row, lane, sink);
@@ -1784,8 +1861,8 @@ struct ShareIter {
 
 // Plan + attention kernel.  kWarm only renames the instantiation used by
 // the ring warm-up, so kernel profiles separate it from decode steps.
-template <class T, int D, int G, bool kWarm>
-__global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
+template <class T, int D, int G, bool kWarm, bool kPaged>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(AttendShape<T, D, G>::kWavesPerEu))) void attend_kernel(StepArgs a)
 {
     __shared__ float lds[AttendShape<T, D, G>::kFloats];
     extern __shared__ int32_t plan_lds[];
@@ -1873,36 +1950,52 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
     }
     if (!ld_valid)
         return;
+    // Paged K/V: the page numbers of the block `issue` requests next are
+    // fetched (scalar loads) one block ahead, so no request waits for them.
+    BlockPages<TPB> pages;
+    auto fetch_pages = [&] {
+        if constexpr (kPaged) {
+            if (ld_valid)
+                pages = BlockPages<TPB>(s, s.page_table + (int64_t)(ld.grp / s.Hkv) * s.max_pages,
+                                        ld_base, ld.t1);
+        }
+    };
     auto issue = [&](KvBlock<T, G, T::EPL, NB> &buf) {
         if (!ld_valid)
             return;
         const int lb = ld.grp / s.Hkv, lg = ld.grp - lb * s.Hkv;
-        const S *kb = (const S *)a.k + lb * s.kv_sb + lg * s.kv_sh + k_lane_offset<T, D, G>();
-        const S *vb = (const S *)a.v + lb * s.kv_sb + lg * s.kv_sh + lane * T::EPL;
-        load_block<T, D, G, LPR, RPB, NB>(buf, kb, vb, s.kv_st, ld_base, ld.t1, row);
-        ld_base += TPB;
-        if (ld_base < ld.t1)
-            return;
-        if (ld.valid && ld.hi != INT_MAX)
-            ld.next();  // the static share's next item, if any
+        if constexpr (kPaged)
+            load_block_at<T, D, G, LPR, RPB, NB>(buf, kv_rows<T, D, G, true>(a, lb, lg), ld_base,
+                                                 ld.t1, row,
+                                                 [&](int t) { return pages.offset(s, t); });
         else
-            ld.valid = false;
-        if (!ld.valid) {
-            const int it = claim();
-            if (it < pt.total) {
-                pool_item(ld, it);
-                ld.hi = INT_MAX;  // marks a pool item
+            load_block<T, D, G, LPR, RPB, NB, false>(buf, kv_rows<T, D, G, false>(a, lb, lg), s,
+                                                     ld_base, ld.t1, row);
+        ld_base += TPB;
+        if (ld_base >= ld.t1) {
+            if (ld.valid && ld.hi != INT_MAX)
+                ld.next();  // the static share's next item, if any
+            else
+                ld.valid = false;
+            if (!ld.valid) {
+                const int it = claim();
+                if (it < pt.total) {
+                    pool_item(ld, it);
+                    ld.hi = INT_MAX;  // marks a pool item
+                }
             }
+            ld_valid = ld.valid;
+            ld_base = ld.t0;
         }
-        ld_valid = ld.valid;
-        ld_base = ld.t0;
+        fetch_pages();
     };
+    fetch_pages();
     KvBlock<T, G, T::EPL, NB> bufA, bufB;
     issue(bufA);
     issue(bufB);
 
     int qgrp = cur.grp;
-    ItemCtx<T, D, G> ctx(a, qgrp / s.Hkv, qgrp % s.Hkv);
+    ItemCtx<T, D, G, kPaged> ctx(a, qgrp / s.Hkv, qgrp % s.Hkv);
     int st[G];
     ItemAcc<T, D, G> ia;
     auto begin_item = [&] {
@@ -1913,7 +2006,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(StepArgs a)
             st[j] = sink_item ? 0 : code_start(pt.code[b * s.Hq + g * G + j]);
         if (cur.grp != qgrp) {
             qgrp = cur.grp;
-            ctx = ItemCtx<T, D, G>(a, b, g);
+            ctx = ItemCtx<T, D, G, kPaged>(a, b, g);
         }
         ia.reset(st, lane);
     };
@@ -2077,7 +2170,7 @@ __device__ __forceinline__ void store_unit_key(unsigned long long *kw, int64_t r
 //      the group's counter; the workgroup that completes the group merges it
 //      (with the fused append), resets the counter and counts the group on
 //      the done counter.
-template <class T, int D, int G, int U>
+template <class T, int D, int G, int U, bool kPaged>
 __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
 {
     using AS = AttendShape<T, D, G>;
@@ -2115,7 +2208,7 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
     // The group's queries and K/V row pointers do not depend on the plan.
     QueryStage<D, G> qs;
     qs.request(a, b, g);
-    ItemCtx<T, D, G> ctx(a, b, g, true);
+    ItemCtx<T, D, G, kPaged> ctx(a, b, g, true);
 
     unsigned long long *klds = reinterpret_cast<unsigned long long *>(lds);
     const int64_t rep_stride = (int64_t)NG * a.nkw;
@@ -2137,7 +2230,7 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
     const bool spec = spec_item(a, e, loc, span_prev, sp_t0, sp_t1);
     ItemBufs<T, D, G> bufs;
     if (spec)
-        item_issue<T, D, G>(a, ctx, sp_t0, sp_t1, bufs, false);
+        item_issue<T, D, G, kPaged>(a, ctx, sp_t0, sp_t1, bufs, false);
 
     bool ok = true;
     if (threadIdx.x < 64)
@@ -2211,9 +2304,9 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
         // The speculative loads hold exactly this item's rows when its
         // bounds are the speculated ones.
         if (!(jj == loc && spec && t0 == sp_t0 && t1 == sp_t1))
-            item_issue<T, D, G>(a, ctx, t0, t1, bufs, false);
+            item_issue<T, D, G, kPaged>(a, ctx, t0, t1, bufs, false);
         float *po = gpo + (int64_t)it * G * D, *pl = gpl + (int64_t)it * G;
-        item_finish<T, D, G>(a, ctx, t0, t1, sti, lds, bufs, [&](int j, int dim, float o, float lg) {
+        item_finish<T, D, G, kPaged>(a, ctx, t0, t1, sti, lds, bufs, [&](int j, int dim, float o, float lg) {
             st_wt(po + j * D + dim, o);
             if (dim == 0)
                 st_wt(pl + j, lg);
@@ -2280,6 +2373,75 @@ __global__ __launch_bounds__(D) void append_kernel(StepArgs a, int32_t pos_offse
         const int grp = b * s.Hkv + h / s.G;
         ring_append_pos(a, grp, t, !kWarm && a.w.restart[grp] != 0, dim, D);
     }
+}
+
+// Rounding of an fp64 value to the K/V element type, once: fp32 directly;
+// bf16 through fp32 rounded to odd, which then rounds to nearest even
+// exactly as the fp64 value would.
+__device__ inline float kv_round(double x, F32) { return (float)x; }
+__device__ inline uint16_t kv_round(double x, BF16)
+{
+    float f = __double2float_rz(x);
+    uint32_t u = __float_as_uint(f);
+    if ((double)f != x)
+        u |= 1u;  // round to odd
+    return (uint16_t)(bf16_bits(__uint_as_float(u)) & 0xffffu);
+}
+__device__ inline double kv_value(float x) { return (double)x; }
+__device__ inline double kv_value(uint16_t x) { return (double)__uint_as_float((uint32_t)x << 16); }
+
+// New token's K and V into the cache with RoPE applied to K on the way,
+// and optionally the post-RoPE query: workgroup (b, x) with x < Hkv a KV
+// head, x >= Hkv query head x - Hkv; thread j rotates pair (2j, 2j + 1) by
+// pos[b] * base^(-2j/d), in fp64, rounded once ("Match (1)" of the blog
+// describes the rotation as independent 2x2 rotations of such pairs).
+template <class T, int D>
+__global__ __launch_bounds__(D / 2) void append_kv_kernel(Shape s, const void *k_new,
+                                                          const void *v_new, const void *q_tilde,
+                                                          float *q_out, const int32_t *pos,
+                                                          double base, void *k_cache,
+                                                          void *v_cache)
+{
+#pragma clang fp contract(off)
+    using S = typename T::S;
+    const int nh = s.Hkv + (q_out ? s.Hq : 0);
+    const int b = blockIdx.x / nh, x = blockIdx.x - b * nh;
+    const int j = threadIdx.x;
+    const int m = pos[b];
+    if (m < 0 || m >= s.T)
+        return;
+    double c = 1.0, sn = 0.0;
+    if (base > 0.0) {
+        const double ang = (double)m * pow(base, -2.0 * j / D);
+        sincos(ang, &sn, &c);
+    }
+    const bool kv = x < s.Hkv;
+    const int h = kv ? x : x - s.Hkv;
+    const S *src = kv ? (const S *)k_new + ((int64_t)b * s.Hkv + h) * D
+                      : (const S *)q_tilde + ((int64_t)b * s.Hq + h) * D;
+    const double x0 = kv_value(src[2 * j]), x1 = kv_value(src[2 * j + 1]);
+    const double y0 = x0 * c - x1 * sn, y1 = x0 * sn + x1 * c;
+    if (!kv) {
+        float *qo = q_out + ((int64_t)b * s.Hq + h) * D;
+        qo[2 * j] = (float)y0;
+        qo[2 * j + 1] = (float)y1;
+        return;
+    }
+    int64_t row;
+    if (s.page_table) {
+        const int page = s.page_table[(int64_t)b * s.max_pages + (m >> s.page_shift)];
+        row = (int64_t)page * s.kv_sb + (int64_t)(m & ((1 << s.page_shift) - 1)) * s.kv_st;
+    } else {
+        row = (int64_t)b * s.kv_sb + (int64_t)m * s.kv_st;
+    }
+    row += (int64_t)h * s.kv_sh;
+    S *kd = (S *)k_cache + row;
+    kd[2 * j] = kv_round(y0, T());
+    kd[2 * j + 1] = kv_round(y1, T());
+    const S *vs = (const S *)v_new + ((int64_t)b * s.Hkv + h) * D;
+    S *vd = (S *)v_cache + row;
+    vd[2 * j] = vs[2 * j];
+    vd[2 * j + 1] = vs[2 * j + 1];
 }
 
 template <class S>
@@ -2394,28 +2556,28 @@ static int resident_per_cu(const void *fn, size_t lds)
     return n;
 }
 
-template <class T, int D>
-static void attend_go(const StepArgs &a, hipStream_t st)
+template <class T, int D, bool P>
+static void attend_go_p(const StepArgs &a, hipStream_t st)
 {
     const size_t lds = plan_lds_bytes(a.s.B, a.s.Hq, a.s.Hkv);
     // Persistent grid: exactly the workgroups that are resident at once, so
     // no workgroup waits for a slot only to find no work; never more than
     // the item bound.
-    const void *fn = a.s.G == 1   ? (const void *)attend_kernel<T, D, 1, false>
-                     : a.s.G == 2 ? (const void *)attend_kernel<T, D, 2, false>
-                     : a.s.G == 4 ? (const void *)attend_kernel<T, D, 4, false>
-                                  : (const void *)attend_kernel<T, D, 8, false>;
+    const void *fn = a.s.G == 1   ? (const void *)attend_kernel<T, D, 1, false, P>
+                     : a.s.G == 2 ? (const void *)attend_kernel<T, D, 2, false, P>
+                     : a.s.G == 4 ? (const void *)attend_kernel<T, D, 4, false, P>
+                                  : (const void *)attend_kernel<T, D, 8, false, P>;
     int64_t grid = (int64_t)device_cu_count() * resident_per_cu(fn, lds);
     if (grid > a.max_items)
         grid = a.max_items > 0 ? a.max_items : 1;
 #define MAC_ATT(GG)                                                                       \
     do {                                                                                  \
         if (a.mode == kPlanInit)                                                          \
-            hipLaunchKernelGGL((attend_kernel<T, D, GG, true>), dim3((int)grid), dim3(kBlock), \
-                               lds, st, a);                                               \
+            hipLaunchKernelGGL((attend_kernel<T, D, GG, true, P>), dim3((int)grid),        \
+                               dim3(kBlock), lds, st, a);                                 \
         else                                                                              \
-            hipLaunchKernelGGL((attend_kernel<T, D, GG, false>), dim3((int)grid), dim3(kBlock), \
-                               lds, st, a);                                               \
+            hipLaunchKernelGGL((attend_kernel<T, D, GG, false, P>), dim3((int)grid),       \
+                               dim3(kBlock), lds, st, a);                                 \
     } while (0)
     switch (a.s.G) {
     case 1:
@@ -2434,6 +2596,15 @@ static void attend_go(const StepArgs &a, hipStream_t st)
 #undef MAC_ATT
 }
 
+template <class T, int D>
+static void attend_go(const StepArgs &a, hipStream_t st)
+{
+    if (a.s.page_table)
+        attend_go_p<T, D, true>(a, st);
+    else
+        attend_go_p<T, D, false>(a, st);
+}
+
 hipError_t launch_attend(const StepArgs &a, hipStream_t st)
 {
     MAC_DISPATCH_TD(attend_go, a, st);
@@ -2442,17 +2613,25 @@ hipError_t launch_attend(const StepArgs &a, hipStream_t st)
 
 // Grid of the single-launch step: a.wpg workgroups per KV group (the host
 // sized wpg to what is resident at once).
-template <class T, int D, int G>
-static void step_go_g(const StepArgs &a, hipStream_t st)
+template <class T, int D, int G, bool P>
+static void step_go_gp(const StepArgs &a, hipStream_t st)
 {
     const int grid = a.wpg * a.s.B * a.s.Hkv;
     constexpr int eb = sizeof(typename T::S);
     if (a.unit_slots == step_unit_slots(eb, D, false))
-        hipLaunchKernelGGL((step_kernel<T, D, G, step_rows(eb, D, false)>), dim3(grid), dim3(kBlock),
-                           0, st, a);
+        hipLaunchKernelGGL((step_kernel<T, D, G, step_rows(eb, D, false), P>), dim3(grid),
+                           dim3(kBlock), 0, st, a);
     else
-        hipLaunchKernelGGL((step_kernel<T, D, G, step_rows(eb, D, true)>), dim3(grid), dim3(kBlock),
-                           0, st, a);
+        hipLaunchKernelGGL((step_kernel<T, D, G, step_rows(eb, D, true), P>), dim3(grid),
+                           dim3(kBlock), 0, st, a);
+}
+template <class T, int D, int G>
+static void step_go_g(const StepArgs &a, hipStream_t st)
+{
+    if (a.s.page_table)
+        step_go_gp<T, D, G, true>(a, st);
+    else
+        step_go_gp<T, D, G, false>(a, st);
 }
 
 template <class T, int D>
@@ -2475,14 +2654,19 @@ static void step_go(const StepArgs &a, hipStream_t st)
 }
 
 // Resident workgroups of both unit sizes' kernels (the smaller count).
+template <class T, int D, int U, bool P>
+static int step_resident_up(const Shape &s)
+{
+    const void *fn = s.G == 1   ? (const void *)step_kernel<T, D, 1, U, P>
+                     : s.G == 2 ? (const void *)step_kernel<T, D, 2, U, P>
+                     : s.G == 4 ? (const void *)step_kernel<T, D, 4, U, P>
+                                : (const void *)step_kernel<T, D, 8, U, P>;
+    return device_cu_count() * resident_per_cu(fn, 0);
+}
 template <class T, int D, int U>
 static int step_resident_u(const Shape &s)
 {
-    const void *fn = s.G == 1   ? (const void *)step_kernel<T, D, 1, U>
-                     : s.G == 2 ? (const void *)step_kernel<T, D, 2, U>
-                     : s.G == 4 ? (const void *)step_kernel<T, D, 4, U>
-                                : (const void *)step_kernel<T, D, 8, U>;
-    return device_cu_count() * resident_per_cu(fn, 0);
+    return s.page_table ? step_resident_up<T, D, U, true>(s) : step_resident_up<T, D, U, false>(s);
 }
 template <class T, int D>
 static void step_resident_go(const Shape &s, int *n)
@@ -2562,6 +2746,31 @@ static void append_go(const StepArgs &a, int32_t pos_offset, hipStream_t st)
 hipError_t launch_append(const StepArgs &a, int32_t pos_offset, hipStream_t st)
 {
     MAC_DISPATCH_TD(append_go, a, pos_offset, st);
+    return hipGetLastError();
+}
+
+template <class T, int D>
+static void append_kv_go(const Shape &s, const void *k_new, const void *v_new,
+                         const void *q_tilde, float *q_out, const int32_t *pos, double base,
+                         void *k_cache, void *v_cache, hipStream_t st)
+{
+    const int nh = s.Hkv + (q_out ? s.Hq : 0);
+    hipLaunchKernelGGL((append_kv_kernel<T, D>), dim3(s.B * nh), dim3(D / 2), 0, st, s, k_new,
+                       v_new, q_tilde, q_out, pos, base, k_cache, v_cache);
+}
+
+hipError_t launch_append_kv(const Shape &s, const void *k_new, const void *v_new,
+                            const void *q_tilde, float *q_out, const int32_t *pos, double base,
+                            void *k_cache, void *v_cache, hipStream_t st)
+{
+    if (s.dtype == MAC_DTYPE_BF16 && s.D == 128)
+        append_kv_go<BF16, 128>(s, k_new, v_new, q_tilde, q_out, pos, base, k_cache, v_cache, st);
+    else if (s.dtype == MAC_DTYPE_BF16 && s.D == 64)
+        append_kv_go<BF16, 64>(s, k_new, v_new, q_tilde, q_out, pos, base, k_cache, v_cache, st);
+    else if (s.dtype == MAC_DTYPE_F32 && s.D == 128)
+        append_kv_go<F32, 128>(s, k_new, v_new, q_tilde, q_out, pos, base, k_cache, v_cache, st);
+    else
+        append_kv_go<F32, 64>(s, k_new, v_new, q_tilde, q_out, pos, base, k_cache, v_cache, st);
     return hipGetLastError();
 }
 

@@ -48,6 +48,8 @@ class mac_params(ctypes.Structure):
         ("sm_scale", ctypes.c_float), ("flags", ctypes.c_int32),
         ("kv_stride_b", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64),
         ("kv_stride_t", ctypes.c_int64), ("front_sink", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+        ("page_table", ctypes.c_void_p),
     ]
 
 
@@ -81,6 +83,8 @@ def load():
                                            _vp, _vp, _vp, _vp]),
         "mac_join_aux": (ctypes.c_int, [_vp, _vp]),
         "mac_bind_epochs": (ctypes.c_int, [_vp, _vp]),
+        "mac_append_kv": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, ctypes.c_double, _vp, _vp,
+                                         _vp]),
         "mac_full_decode": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                            ctypes.c_size_t, _vp]),
         "mac_read_device_status": (ctypes.c_int, [_P, _vp, _vp,
@@ -127,10 +131,13 @@ def _check(fn, rc):
 
 def make_params(batch, n_q_heads, n_kv_heads, head_dim, kv_dtype, ring_k,
                 band_r, kv_capacity, tau, thresh_mode=MAC_THRESH_ONE_MINUS_TAU,
-                sm_scale=0.0, strides=(0, 0, 0), flags=0, front_sink=0) -> mac_params:
+                sm_scale=0.0, strides=(0, 0, 0), flags=0, front_sink=0, page_size=0,
+                max_pages=0, page_table=None) -> mac_params:
+    """page_table: device tensor or address of the [B, max_pages] int32
+    page table when page_size > 0 (the tensor must outlive every call)."""
     return mac_params(batch, n_q_heads, n_kv_heads, head_dim, kv_dtype, ring_k,
                       band_r, kv_capacity, tau, thresh_mode, sm_scale, flags,
-                      *strides, front_sink)
+                      *strides, front_sink, page_size, max_pages, _ptr(page_table))
 
 
 def mac_workspace_bytes(p: mac_params) -> int:
@@ -164,6 +171,13 @@ def mac_decode_step(handle, qtilde, q, k_cache, v_cache, pos, out, out_lse=None,
         handle, _ptr(qtilde), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(pos),
         _ptr(out), _ptr(out_lse), _ptr(match_p), _ptr(match_d2), main_stream,
         aux_stream))
+
+
+def mac_append_kv(p: mac_params, k_new, v_new, pos, rope_base, k_cache, v_cache,
+                  q_tilde=None, q_out=None, stream=None):
+    _check("mac_append_kv", load().mac_append_kv(
+        ctypes.byref(p), _ptr(k_new), _ptr(v_new), _ptr(q_tilde), _ptr(q_out), _ptr(pos),
+        float(rope_base), _ptr(k_cache), _ptr(v_cache), stream))
 
 
 def mac_bind_epochs(handle, epoch):

@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--match-filter", action="store_true",
                     help="exact lower-bound filter of the match (second halves of ring "
                          "rows read only where a hit is still possible)")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="read K/V from a paged pool with pages of this many tokens, "
+                         "shuffled through a page table (0 = dense cache)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--no-profile", action="store_true")
@@ -213,8 +216,29 @@ def main():
     dec_q = to_dev(np.moveaxis(q[:, :, W:], 2, 0))
     pos_np = wl.decode_positions(cfg)
     pos = to_dev(pos_np)
+    paging = {}
+    if args.page_size:
+        # Pages of [Hkv, P, d], each request's pages scattered over the pool
+        # by a seeded shuffle.
+        P = args.page_size
+        npg = -(-cfg.capacity // P)
+        g = torch.Generator().manual_seed(0)
+        table = torch.randperm(B * npg, generator=g).reshape(B, npg).to(torch.int32).to(dev)
+
+        def to_pool(X):
+            pad = npg * P - cfg.capacity
+            Xp = torch.nn.functional.pad(X, (0, 0, 0, pad)) if pad else X
+            Xp = Xp.reshape(B, Hkv, npg, P, d).permute(0, 2, 1, 3, 4).reshape(B * npg, Hkv, P, d)
+            pool = torch.empty_like(Xp)
+            pool[table.reshape(-1).long()] = Xp
+            return pool
+
+        K0, V0 = to_pool(K0), to_pool(V0)
+        torch.cuda.synchronize()
+        paging = dict(page_size=P, max_pages=npg, page_table=table,
+                      strides=(Hkv * P * d, P * d, d))
     p = mac.make_params(B, H, Hkv, d, mac.MAC_DTYPE_F32 if cfg.dtype == "f32" else mac.MAC_DTYPE_BF16,
-                        R, cfg.band_r, cfg.capacity, cfg.tau,
+                        R, cfg.band_r, cfg.capacity, cfg.tau, **paging,
                         flags=(mac.MAC_FLAG_FUSED_APPEND if args.append == "fused" else 0)
                         | (mac.MAC_FLAG_MATCH_FILTER if args.match_filter else 0)
                         | {"auto": 0, "single": mac.MAC_FLAG_SINGLE_LAUNCH,
@@ -367,6 +391,7 @@ def main():
                    "launch": launched or args.launch,
                    "append": args.append,
                    "match_filter": bool(args.match_filter),
+                   "page_size": args.page_size,
                    "layers": NL, "kv_dtype": cfg.dtype,
                    "batch": B, "q_heads": H, "kv_heads": Hkv, "head_dim": d,
                    "context": cfg.ctx, "ring_k": R, "band_r": cfg.band_r, "tau": cfg.tau,

@@ -129,6 +129,20 @@ typedef struct mac_params {
      * [0, t-r], and every step attends [0, min(F, m+1)) exactly with its own
      * query, hit or miss.  0 (the default) is the plain method. */
     int32_t front_sink;
+    /* Paged K/V cache (blog, "Production version": the production kernel
+     * reads the serving engine's BF16 paged KV).  page_size = 0: the dense
+     * layout above.  Otherwise page_size is a power of two >= 16, and row t
+     * of request b, KV head g starts at element
+     *   page_table[b * max_pages + t / page_size] * kv_stride_b
+     *   + g * kv_stride_h + (t % page_size) * kv_stride_t
+     * of k_cache / v_cache (all strides 0: pages of [Hkv, page_size, d]).
+     * page_table is a DEVICE int32 array [B, max_pages] (4-byte aligned),
+     * read on the device at every call, so its contents may change between
+     * calls (and between replays of a captured graph) but not during one;
+     * max_pages * page_size >= kv_capacity; rows must be 16-byte aligned. */
+    int32_t page_size;
+    int32_t max_pages;
+    const int32_t *page_table;
 } mac_params;
 
 /* Ring buffers of one attention layer, caller-allocated device memory:
@@ -239,6 +253,28 @@ mac_status mac_decode_step(mac_handle *h, const void *qtilde, const float *q,
  * main_stream and must stay valid while steps that read it run.
  */
 mac_status mac_bind_epochs(mac_handle *h, const int32_t *epoch);
+
+/*
+ * mac_append_kv -- write the new token of every request into the K/V cache,
+ * with RoPE fused into the K write (blog, "Production version", the fused
+ * KV-RoPE setting), and optionally produce the post-RoPE query.
+ *   k_new, v_new [B, Hkv, d] kv_dtype   key (pre-RoPE) and value of position
+ *                                       pos[b]
+ *   q_tilde [B, Hq, d] kv_dtype, q_out [B, Hq, d] fp32: both NULL, or both
+ *                                       given: q_out = RoPE(q_tilde, pos[b])
+ *   pos [B] int32 (device)              positions outside [0, kv_capacity)
+ *                                       are skipped
+ *   rope_base                           > 0: pair (x[2j], x[2j+1]) rotates by
+ *                                       pos * rope_base^(-2j/d); 0: no
+ *                                       rotation (K is copied)
+ *   k_cache, v_cache                    dense or paged, as in mac_params
+ * The rotation is evaluated in fp64 and rounded once to the K element type
+ * (to fp32 for q_out).  Rows are written with plain stores on `stream`; run
+ * it before the mac_decode_step that attends position pos[b].
+ */
+mac_status mac_append_kv(const mac_params *p, const void *k_new, const void *v_new,
+                         const void *q_tilde, float *q_out, const int32_t *pos,
+                         double rope_base, void *k_cache, void *v_cache, void *stream);
 
 /* Make `stream` wait for the last rectify-append enqueued on the handle. */
 mac_status mac_join_aux(mac_handle *h, void *stream);

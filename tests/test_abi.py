@@ -33,10 +33,27 @@ def test_exports_every_declared_function(lib):
 
 
 def test_struct_layout_matches_header():
-    assert ctypes.sizeof(mac.mac_params) == 80
+    assert ctypes.sizeof(mac.mac_params) == 96
     assert mac.mac_params.kv_stride_b.offset == 48
     assert mac.mac_params.front_sink.offset == 72
+    assert mac.mac_params.page_size.offset == 76
+    assert mac.mac_params.max_pages.offset == 80
+    assert mac.mac_params.page_table.offset == 88
     assert ctypes.sizeof(mac.mac_rings) == 32
+
+
+@pytest.mark.parametrize("kw,ok", [
+    (dict(page_size=16, max_pages=256, page_table=0x1000), True),
+    (dict(page_size=64, max_pages=64, page_table=0x1000), True),
+    (dict(page_size=64, max_pages=63, page_table=0x1000), False),   # pages do not cover T
+    (dict(page_size=8, max_pages=512, page_table=0x1000), False),   # below 16 tokens
+    (dict(page_size=48, max_pages=100, page_table=0x1000), False),  # not a power of two
+    (dict(page_size=64, max_pages=64, page_table=None), False),
+    (dict(page_size=64, max_pages=64, page_table=0x1002), False),   # misaligned table
+    (dict(max_pages=64), False),                                    # table without pages
+])
+def test_paged_params(lib, kw, ok):
+    assert (mac.mac_workspace_bytes(_params(**kw)) > 0) == ok
 
 
 def test_front_sink_bounds(lib):
