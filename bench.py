@@ -229,7 +229,8 @@ def main():
             pad = npg * P - cfg.capacity
             Xp = torch.nn.functional.pad(X, (0, 0, 0, pad)) if pad else X
             Xp = Xp.reshape(B, Hkv, npg, P, d).permute(0, 2, 1, 3, 4).reshape(B * npg, Hkv, P, d)
-            pool = torch.empty_like(Xp)
+            # (with one request the reshape is a strided view: the pool must be dense)
+            pool = torch.empty(Xp.shape, dtype=Xp.dtype, device=Xp.device)
             pool[table.reshape(-1).long()] = Xp
             return pool
 

@@ -31,19 +31,43 @@ def _sample_heads(cfg, sig):
     return sorted(set(cand))
 
 
-@pytest.mark.parametrize("cfg_id,append,launch", [
-    (2, "aux", "single"), (2, "fused", "split"), (3, "fused", "single"), (4, "aux", "single"),
-    (5, "fused", "single"), (5, "aux", "split")])
-def test_fullsize_config(oracle_lib, cfg_id, append, launch):
+def _pool(X, P):
+    """Device [B, Hkv, T, d] -> shuffled pages [pages, Hkv, P, d] and the
+    page table (seeded), as a serving engine would hold them."""
+    B, Hkv, T, d = X.shape
+    npg = -(-T // P)
+    table = torch.randperm(B * npg, generator=torch.Generator().manual_seed(1))
+    table = table.reshape(B, npg).to(torch.int32).to(DEV)
+    Xp = torch.nn.functional.pad(X, (0, 0, 0, npg * P - T))
+    Xp = Xp.reshape(B, Hkv, npg, P, d).permute(0, 2, 1, 3, 4).reshape(B * npg, Hkv, P, d)
+    # (with one request the reshape is a strided view: the pool must be dense)
+    pool = torch.empty(Xp.shape, dtype=Xp.dtype, device=Xp.device)
+    pool[table.reshape(-1).long()] = Xp
+    return pool, table
+
+
+@pytest.mark.parametrize("cfg_id,append,launch,F,P", [
+    (2, "aux", "single", 0, 0), (2, "fused", "split", 0, 0), (3, "fused", "single", 0, 0),
+    (4, "aux", "single", 0, 0), (5, "fused", "single", 0, 0), (5, "aux", "split", 0, 0),
+    (2, "fused", "single", 128, 16), (5, "fused", "split", 64, 64)])
+def test_fullsize_config(oracle_lib, cfg_id, append, launch, F, P):
     cfg = wl.WORKLOADS[cfg_id]
-    print("full-size parity: config %d (%s), append=%s, launch=%s"
-          % (cfg_id, cfg.name, append, launch), flush=True)
+    print("full-size parity: config %d (%s), append=%s, launch=%s, front sink %d, page %d"
+          % (cfg_id, cfg.name, append, launch, F, P), flush=True)
     K, V = wl.gen_kv(cfg)
     qt, q, _, sig = wl.gen_queries(cfg)
     flags = (mac.MAC_FLAG_FUSED_APPEND if append == "fused" else 0) | (
         mac.MAC_FLAG_SPLIT_STAGES if launch == "split" else mac.MAC_FLAG_SINGLE_LAUNCH)
-    p = params_for(cfg, flags=flags)
-    layer = Layer(cfg, K, V, qt, q, params=p).init()
+    kv_dev, paging = None, {}
+    if P:
+        kp, table = _pool(to_dev(K), P)
+        vp, _ = _pool(to_dev(V), P)
+        kv_dev = (kp, vp)
+        Hkv, d = cfg.n_kv_heads, cfg.head_dim
+        paging = dict(page_size=P, max_pages=table.shape[1], page_table=table,
+                      strides=(Hkv * P * d, P * d, d))
+    p = params_for(cfg, flags=flags, front_sink=F, **paging)
+    layer = Layer(cfg, K, V, qt, q, params=p, kv_dev=kv_dev).init()
     gpu = run_steps(layer, cfg.steps, aux=torch.cuda.Stream() if append == "aux" else None)
     print("  gpu steps done", flush=True)
 
@@ -89,7 +113,7 @@ def test_fullsize_config(oracle_lib, cfg_id, append, launch):
     t2 = oracle_lib.threshold2(cfg.head_dim, cfg.tau)
     res = oracle_lib.run_streams(K, V, qt, q, heads, ctx_len=cfg.ctx, n_warm=W,
                                  ring_k=cfg.ring_k, band_r=cfg.band_r, thresh2=t2,
-                                 want_ring=True)
+                                 want_ring=True, front_sink=F)
     print("  oracle streams done: %s" % heads, flush=True)
     qr = layer.q_ring.cpu().float().numpy()
     orr = layer.o_ring.cpu().numpy()
