@@ -139,7 +139,10 @@ typedef struct mac_params {
      * page_table is a DEVICE int32 array [B, max_pages] (4-byte aligned),
      * read on the device at every call, so its contents may change between
      * calls (and between replays of a captured graph) but not during one;
-     * max_pages * page_size >= kv_capacity; rows must be 16-byte aligned. */
+     * max_pages * page_size >= kv_capacity; rows must be 16-byte aligned.
+     * The entries that cover positions 0..pos[b] of a request must name
+     * pages of the pool (the library reads them as given; an entry outside
+     * the pool is an out-of-bounds read). */
     int32_t page_size;
     int32_t max_pages;
     const int32_t *page_table;
