@@ -18,7 +18,7 @@ constexpr int kChunkMin = 1 << kChunkMinShift;
 constexpr int kItemCost = 64;
 // The attention kernel splits the first kStaticPct percent of the work
 // statically; workgroups that finish their share claim the rest item by item.
-constexpr int kStaticPct = 70;
+constexpr int kStaticPct = 40;
 // ... when the plan has at least this many items per workgroup.
 constexpr int kPoolItems = 4;
 constexpr int kMaxItemsPerGroup = 128;

@@ -1859,6 +1859,59 @@ struct ShareIter {
     __device__ int item_index() const { return pt->gbegin[grp] + i; }
 };
 
+// Pool items of the attention kernel's claimed tail are handed out longest
+// first: those of groups cut on a grid coarser than kChunkMin (long ranges,
+// e.g. a missing head's whole context) before the rest, each class in item
+// order, so the last claims are short items and workgroups finish close
+// together.  s_bp[g] (g <= NG) receives the number of coarse-grid pool
+// items in groups below g; returns their total.  Pool items are the items
+// from index `first` on.  Called by the whole workgroup.
+__device__ int pool_big_prefix(const PlanTables &pt, int NG, int r_split, int F, bool sink,
+                               int first, int32_t *s_bp)
+{
+    __shared__ int s_w[kBlock / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    auto big_items = [&](int g) {
+        const int n = pt.gcount[g];
+        if (n == 0)
+            return 0;
+        const int skip = first > pt.gbegin[g] ? first - pt.gbegin[g] : 0;
+        if (skip >= n)
+            return 0;
+        const GroupItems gi(pt.gstart[g], pt.gend[g], r_split, F, sink);
+        return (gi.n_main > 0 && gi.rs.cs > kChunkMinShift) ? n - skip : 0;
+    };
+    const int per = (NG + kBlock - 1) / kBlock;
+    const int lo = tid * per, hi = lo + per < NG ? lo + per : NG;
+    int run = 0;
+    for (int g = lo; g < hi; ++g)
+        run += big_items(g);
+    int x = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o)
+            x += y;
+    }
+    if (lane == 63)
+        s_w[wave] = x;
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int w = 0; w < kBlock / 64; ++w) {
+        before += w < wave ? s_w[w] : 0;
+        total += s_w[w];
+    }
+    int acc = before + x - run;
+    for (int g = lo; g < hi; ++g) {
+        s_bp[g] = acc;
+        acc += big_items(g);
+    }
+    if (tid == 0)
+        s_bp[NG] = total;
+    __syncthreads();
+    return total;
+}
+
 // Plan + attention kernel.  kWarm only renames the instantiation used by
 // the ring warm-up, so kernel profiles separate it from decode steps.
 template <class T, int D, int G, bool kWarm, bool kPaged>
@@ -1896,6 +1949,29 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(AttendSh
         const ShareIter pool(pt, NG, r_split, s.F, with_sink, Ws, INT_MAX);
         dyn_first = pool.valid ? pool.item_index() : pt.total;
     }
+    // Claim c of the pool maps to the c-th coarse-grid item, or, past
+    // those, to the (c - n_big)-th other item (see pool_big_prefix).
+    int32_t *s_bp = plan_lds + (s.B * s.Hq + 5 * NG + 2 + 2 * (kBlock / 64));
+    const int n_big =
+        pooled ? pool_big_prefix(pt, NG, r_split, s.F, with_sink, dyn_first, s_bp) : 0;
+    auto pool_index = [&](int c) {
+        const bool big = c < n_big;
+        const int k = big ? c : c - n_big;
+        // items of the class before group g
+        auto before = [&](int g) {
+            const int pp = pt.gbegin[g] > dyn_first ? pt.gbegin[g] - dyn_first : 0;
+            return big ? s_bp[g] : pp - s_bp[g];
+        };
+        int l = 0, h = NG - 1;  // the first group g with before(g + 1) > k
+        while (l < h) {
+            const int mid = (l + h) >> 1;
+            if (before(mid + 1) > k)
+                h = mid;
+            else
+                l = mid + 1;
+        }
+        return (pt.gbegin[l] > dyn_first ? pt.gbegin[l] : dyn_first) + (k - before(l));
+    };
     // Claims the next pool item for the whole workgroup (one atomic, handed
     // to the other waves through LDS); pt.total when the pool is empty.  A
     // count outside the pool ends the claims.
@@ -1905,7 +1981,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(AttendSh
             const uint32_t pool = (uint32_t)(pt.total - dyn_first);
             const uint32_t c =
                 pooled ? atomicAdd((uint32_t *)&a.w.ctrl[kCtrlClaim], 1u) : pool;
-            s_claim[n_claims & 3] = c < pool ? dyn_first + (int)c : pt.total;
+            s_claim[n_claims & 3] = c < pool ? pool_index((int)c) : pt.total;
         }
         __syncthreads();
         const int it = s_claim[n_claims & 3];
@@ -2489,7 +2565,8 @@ __global__ void ring_reset_kernel(int64_t n_q, S *__restrict__ q_ring,
 size_t plan_lds_bytes(int B, int Hq, int Hkv)
 {
     const size_t BH = (size_t)B * Hq, NG = (size_t)B * Hkv;
-    return 4 * (BH + 5 * NG + 2 + 2 * (kBlock / 64));
+    // the planner's tables, then the claimed tail's prefix (NG + 1)
+    return 4 * (BH + 6 * NG + 3 + 2 * (kBlock / 64));
 }
 
 int device_cu_count()
