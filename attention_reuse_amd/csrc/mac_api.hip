@@ -294,6 +294,19 @@ int32_t mac_partition(int32_t s, int32_t e, int32_t r, int32_t *t0,
     return rs.n;
 }
 
+int32_t mac_group_items(int32_t s, int32_t e, int32_t r, int32_t front_sink, int32_t *t0,
+                        int32_t *t1, int32_t *n_before_split, int32_t cap)
+{
+    if (s < 0 || e < s || r < 0 || cap < 0 || front_sink < 0 || front_sink > kMaxFrontSink)
+        return -1;
+    const GroupItems gi(s, e, r, front_sink, true);
+    for (int i = 0; i < gi.n && i < cap; ++i)
+        gi.item(i, t0[i], t1[i]);
+    if (n_before_split)
+        *n_before_split = gi.n_before_split();
+    return gi.n;
+}
+
 #define MAC_HIP(call)                      \
     do {                                   \
         if ((call) != hipSuccess)          \

@@ -95,6 +95,8 @@ def load():
         "mac_release": (ctypes.c_int, [_vp]),
         "mac_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "mac_chunk_tokens": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32]),
+        "mac_group_items": (ctypes.c_int32, [ctypes.c_int32] * 4 + [
+            ctypes.POINTER(ctypes.c_int32)] * 3 + [ctypes.c_int32]),
         "mac_partition": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32,
                                            ctypes.POINTER(ctypes.c_int32),
@@ -237,3 +239,16 @@ def mac_partition(s: int, e: int, r: int):
     t1 = (ctypes.c_int32 * n)()
     lib.mac_partition(s, e, r, t0, t1, n)
     return list(zip(t0, t1))
+
+
+def mac_group_items(s: int, e: int, r: int, front_sink: int):
+    """([(t0, t1), ...], n_before_split) of a KV group's work items."""
+    lib = load()
+    n = lib.mac_group_items(s, e, r, front_sink, None, None, None, 0)
+    if n < 0:
+        raise ValueError("bad range")
+    t0 = (ctypes.c_int32 * max(n, 1))()
+    t1 = (ctypes.c_int32 * max(n, 1))()
+    nb = ctypes.c_int32()
+    lib.mac_group_items(s, e, r, front_sink, t0, t1, ctypes.byref(nb), n)
+    return list(zip(t0[:n], t1[:n])), nb.value

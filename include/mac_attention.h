@@ -332,6 +332,17 @@ int32_t mac_chunk_tokens(int32_t s, int32_t e);
 int32_t mac_partition(int32_t s, int32_t e, int32_t r, int32_t *t0,
                       int32_t *t1, int32_t cap);
 
+/* The work items of one KV group at decode position e whose heads attend
+ * from s, with band r and front sink F (host mirror of the device planner):
+ * first the partition of [max(s, F), e] as mac_partition cuts it (none when
+ * e < F), then, when F > 0, the sink item [0, min(F, e + 1)).  Writes
+ * min(n, cap) items (host arrays) and, if n_before_split is not NULL, the
+ * number of leading items before the rectify split e - r + 1 (the items
+ * whose partials enter the rectified summary).  Returns n, or -1 on bad
+ * input. */
+int32_t mac_group_items(int32_t s, int32_t e, int32_t r, int32_t front_sink, int32_t *t0,
+                        int32_t *t1, int32_t *n_before_split, int32_t cap);
+
 #ifdef __cplusplus
 }
 #endif

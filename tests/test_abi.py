@@ -169,3 +169,29 @@ def test_partition_covers_range_on_the_grid(lib, s, e, r):
     if s == 0:
         assert items == mac.mac_partition(0, e, r)
     assert lib.mac_partition(5, 4, 0, None, None, 0) == -1
+
+
+@pytest.mark.parametrize("s,e,r,F", [(0, 0, 0, 64), (0, 63, 16, 64), (0, 200, 16, 64),
+                                     (150, 3000, 256, 128), (0, 33000, 256, 128),
+                                     (500, 600, 600, 4096), (0, 5000, 0, 1), (10, 90, 5, 0)])
+def test_group_items_with_front_sink(lib, s, e, r, F):
+    """Main items tile [max(s, F), e] as the plain partition does; the sink
+    item [0, min(F, e + 1)) comes last; the rectify split counts only main
+    items, and the items before it cover exactly [max(s, F), e - r]."""
+    items, nb = mac.mac_group_items(s, e, r, F)
+    ms = max(s, F)
+    main = items[:-1] if F > 0 else items
+    if F > 0:
+        assert items[-1] == (0, min(F, e + 1))
+    if ms <= e:
+        assert main == mac.mac_partition(ms, e, r)
+    else:
+        assert main == []
+    covered = [t for a, b in main[:nb] for t in range(a, b)]
+    assert covered == list(range(ms, max(ms, e - r + 1)))
+    assert nb <= len(main)
+    # F = 0 is the plain partition.
+    if F == 0:
+        assert items == mac.mac_partition(s, e, r)
+    assert lib.mac_group_items(5, 4, 0, 0, None, None, None, 0) == -1
+    assert lib.mac_group_items(0, 4, 0, 4097, None, None, None, 0) == -1
