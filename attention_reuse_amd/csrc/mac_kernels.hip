@@ -934,13 +934,16 @@ __device__ inline void load_cached(const StepArgs &a, int grp, SlotOf &&slot_of,
 }
 
 // Merge of group grp by the NT threads of the calling workgroup: cnt items
-// read from src, the group's range starting at gstart, with the cached
-// summaries (c_l, c_o) from load_cached.  Outputs are handled in pair tasks,
+// read from src, the group's range [gstart, e], with the cached summaries
+// (c_l, c_o) from load_cached; ready is group_ready of the group as every
+// thread read it before this call.  The caller passes e and ready so that
+// the merge does not wait for loads of its own.  Outputs are handled in pair tasks,
 // so the fold is the same for every NT and every source.  lds holds
 // MergeShape::kFloats floats.
 template <class T, int D, int G, int NT, class Src>
-__device__ void merge_group(const StepArgs &a, int grp, int cnt, int gstart, const Src &src,
-                            float *lds, const float (&c_l)[MergePairs<D, G, NT>::NPK],
+__device__ void merge_group(const StepArgs &a, int grp, int cnt, int gstart, int e, bool ready,
+                            const Src &src, float *lds,
+                            const float (&c_l)[MergePairs<D, G, NT>::NPK],
                             const float (&c_o)[MergePairs<D, G, NT>::NPK][2])
 {
     using M = MergeShape<T, D, G>;
@@ -952,12 +955,8 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int gstart, con
     const Shape &s = a.s;
     const int tid = threadIdx.x;
     const int b = grp / s.Hkv, g = grp - b * s.Hkv;
-    const int e = end_of(a, b);
     const int r_split = (a.mode == kPlanInit) ? 0 : s.r;
     const int nA = GroupItems(gstart, e, r_split, s.F, a.mode != kPlanInit).n_before_split();
-    // Read by every thread before the barrier below; thread 0 rewrites the
-    // group's epoch after it.
-    const bool ready = group_ready(a, b, grp);
     // The pre-RoPE queries of the fused append are requested first.
     S qa[NPK][2];
     if (a.append_fused) {
@@ -1158,7 +1157,11 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(StepArgs a)
     const int32_t *dec = a.w.dec_slot + (int64_t)grp * G;
     load_cached<T, D, G, kMergeBlock>(a, grp, [&](int jj) { return dec[jj]; }, c_l, c_o);
     const PlainParts<D, G> src{a.w.part_o, a.w.part_l, (int64_t)a.w.grp_begin[grp]};
-    merge_group<T, D, G, kMergeBlock>(a, grp, cnt, a.w.grp_start[grp], src, lds, c_l, c_o);
+    // The group's epoch is read by every thread before merge_group's
+    // barriers; thread 0 rewrites it after them.
+    const int b = grp / a.s.Hkv;
+    merge_group<T, D, G, kMergeBlock>(a, grp, cnt, a.w.grp_start[grp], end_of(a, b),
+                                      group_ready(a, b, grp), src, lds, c_l, c_o);
 }
 
 // ---------------------------------------------------------------------------
@@ -2398,7 +2401,9 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
     }
     if (merger) {
         const CoherentParts<D, G> src{gpo, gpl};
-        merge_group<T, D, G, kBlock>(a, grp, n, sg, src, lds, c_l, c_o);
+        // e and the readiness read at the start of the launch (the group's
+        // epoch is not rewritten before this merge does it).
+        merge_group<T, D, G, kBlock>(a, grp, n, sg, e, ready, src, lds, c_l, c_o);
         if (threadIdx.x == 0) {
             st_wt(counter, 0u);
             st_wt(counter + kGrpSpan, (uint32_t)(e - sg + 1));
