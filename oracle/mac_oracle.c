@@ -104,6 +104,25 @@ void mac_oracle_summary(int d, const double *q, double scale, const void *K,
 }
 
 /*
+ * Rotary position embedding of one d-vector at position pos ([MAC] "Match
+ * (1)": RoPE is a product of independent 2x2 rotations, so pre-RoPE queries
+ * are compared and post-RoPE ones attend).  Pair j = (x[2j], x[2j+1]) turns
+ * by the angle pos * base^(-2j/d):
+ *   y[2j]   = x[2j] cos(a) - x[2j+1] sin(a),
+ *   y[2j+1] = x[2j] sin(a) + x[2j+1] cos(a).
+ * This is the convention the library's fused KV-RoPE append follows.
+ */
+void mac_oracle_rope(int d, const double *x, long pos, double base, double *y)
+{
+    for (int j = 0; j < d / 2; ++j) {
+        double a = (double)pos * pow(base, -2.0 * j / d);
+        double c = cos(a), sn = sin(a);
+        y[2 * j] = x[2 * j] * c - x[2 * j + 1] * sn;
+        y[2 * j + 1] = x[2 * j] * sn + x[2 * j + 1] * c;
+    }
+}
+
+/*
  * Merge of the summaries of two disjoint token sets ([MAC] "Decomposable
  * representation of attention": summaries of disjoint sets add, S = S_a + S_b,
  * Z = Z_a + Z_b; [MAC] "Complete": done in the log domain with a running max;

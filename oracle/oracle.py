@@ -68,6 +68,9 @@ def load():
         lib.mac_oracle_merge.argtypes = [
             ctypes.c_int, _dp, ctypes.c_double, _dp, ctypes.c_double, _dp, _dp]
         lib.mac_oracle_merge.restype = None
+        lib.mac_oracle_rope.argtypes = [ctypes.c_int, _dp, ctypes.c_long, ctypes.c_double,
+                                        _dp]
+        lib.mac_oracle_rope.restype = None
         lib.mac_oracle_unmerge.argtypes = lib.mac_oracle_merge.argtypes
         lib.mac_oracle_unmerge.restype = None
         lib.mac_oracle_stream.argtypes = [
@@ -127,6 +130,15 @@ def summary(q, K, V, a: int, e: int, scale: float | None = None):
                            _dtype_code(K), rs, int(a), int(e), _ptr(o),
                            ctypes.byref(lse))
     return o, lse.value
+
+
+def rope(x, pos: int, base: float) -> np.ndarray:
+    """RoPE of the d-vector x (any float dtype) at position pos, fp64."""
+    lib = load()
+    x = np.ascontiguousarray(x, np.float64)
+    y = np.zeros_like(x)
+    lib.mac_oracle_rope(x.shape[0], _ptr(x), int(pos), float(base), _ptr(y))
+    return y
 
 
 def merge(oa, la, ob, lb):

@@ -2,7 +2,7 @@
 blog, "Production version: one fused persistent BF16 kernel": the production
 kernel reads the serving engine's paged BF16 KV, with RoPE fused into the KV
 write).  Paged runs must equal dense runs on the same data bit for bit; the
-append is checked against RoPE written out in numpy (fp64)."""
+append is checked against the oracle's RoPE (fp64), rounded once."""
 import math
 
 import numpy as np
@@ -109,9 +109,10 @@ def test_paged_full_decode_equals_dense(dtype, d, P):
     assert np.array_equal(outs[0], outs[2]) and np.array_equal(outs[1], outs[3])
 
 
-def _rope_expect(x, pos, base, dtype, to_fp32=False):
-    """Rotation in fp64, then one rounding (bf16 via round-to-odd fp32)."""
-    y = wl.rope(wl.from_storage(x)[:, None, :], np.array([pos]), base)[:, 0, :]
+def _rope_expect(oracle_lib, x, pos, base, dtype, to_fp32=False):
+    """The oracle's rotation (fp64), then one rounding (bf16 via
+    round-to-odd fp32)."""
+    y = np.stack([oracle_lib.rope(r, int(pos), base) for r in wl.from_storage(x)])
     if to_fp32:
         return y.astype(np.float32)
     if dtype == "f32":
@@ -125,7 +126,7 @@ def _rope_expect(x, pos, base, dtype, to_fp32=False):
 
 
 @pytest.mark.parametrize("dtype,d,P", [("bf16", 128, 0), ("bf16", 128, 16), ("f32", 64, 64)])
-def test_append_kv_fuses_rope(dtype, d, P):
+def test_append_kv_fuses_rope(oracle_lib, dtype, d, P):
     cfg = _cfg(dtype=dtype, head_dim=d, n_q_heads=8, n_kv_heads=2, ctx=300, steps=4)
     rng = np.random.default_rng(9)
     B, Hkv, Hq, T = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.capacity
@@ -166,7 +167,7 @@ def test_append_kv_fuses_rope(dtype, d, P):
     for b in range(B):
         mask[b, :, pos[b]] = True
         for g in range(Hkv):
-            want = _rope_expect(kn[b, g][None], pos[b], base, dtype)[0]
+            want = _rope_expect(oracle_lib, kn[b, g][None], pos[b], base, dtype)[0]
             got = Kc[b, g, pos[b]]
             if dtype == "f32":
                 np.testing.assert_array_max_ulp(got, want, maxulp=1)
@@ -175,7 +176,7 @@ def test_append_kv_fuses_rope(dtype, d, P):
                 assert (got == want).mean() > 0.99
             assert np.array_equal(Vc[b, g, pos[b]], vn[b, g])
         for h in range(Hq):
-            want = _rope_expect(qn[b, h][None], pos[b], base, dtype, to_fp32=True)[0]
+            want = _rope_expect(oracle_lib, qn[b, h][None], pos[b], base, dtype, to_fp32=True)[0]
             np.testing.assert_array_max_ulp(qo[b, h].cpu().numpy(), want, maxulp=1)
     # Every other row is untouched.
     assert np.array_equal(Kc[~mask], K0[~mask]) and np.array_equal(Vc[~mask], K0[~mask])
