@@ -2,6 +2,8 @@
 "Production version: one fused persistent BF16 kernel", match-scan item):
 with the filter the step's decisions, outputs and rings are those of the
 full scan bit for bit, in both kernel forms."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -71,3 +73,35 @@ def test_filter_cold_ring_and_forms_agree():
     for k in ("out", "lse", "p", "d2"):
         assert np.array_equal(a[k], b[k]), k
     assert (a["p"][0] == -1).all() and np.isinf(a["d2"][0]).all()
+
+
+def test_filter_lockstep_against_oracle(oracle_lib):
+    """With the filter, decisions and outputs against the oracle directly
+    (match_d2 is compared on hits only: on a miss the filter may report a
+    farther row, always at or above the threshold)."""
+    from mac_harness import tolerance_check
+    cfg = _cfg(batch=1, ctx=1500, steps=24, ring_k=128, band_r=32)
+    gpu = _run(cfg, mac.MAC_FLAG_SPLIT_STAGES | FILTER)
+    K, V = wl.gen_kv(cfg)
+    qt, q, _, _ = wl.gen_queries(cfg)
+    W = cfg.n_warm
+    t2 = oracle_lib.threshold2(cfg.head_dim, cfg.tau)
+    n_hit = n_cmp = 0
+    for h in range(cfg.n_q_heads):
+        o = oracle_lib.run_stream(K[0, h // cfg.group], V[0, h // cfg.group], qt[0, h, :W],
+                                  q[0, h, :W], qt[0, h, W:], q[0, h, W:], ctx_len=cfg.ctx,
+                                  ring_k=cfg.ring_k, band_r=cfg.band_r, thresh2=t2)
+        for s in range(cfg.steps):
+            g_p, o_p = int(gpu["p"][s, 0, h]), int(o["p"][s])
+            if o["exempt"][s] and g_p != o_p:
+                break  # a tie or threshold case: later steps may legitimately differ
+            assert g_p == o_p, (h, s)
+            ok, err = tolerance_check(cfg, gpu["out"][s, 0, h], o["out"][s])
+            assert ok, (h, s, err)
+            if o["hit"][s]:
+                n_hit += 1
+                assert abs(math.sqrt(gpu["d2"][s, 0, h]) - o["dist"][s]) < 1e-3
+            else:
+                assert gpu["d2"][s, 0, h] >= _t2(cfg)
+            n_cmp += 1
+    assert n_cmp > 0.9 * cfg.n_q_heads * cfg.steps and 0.2 * n_cmp < n_hit < n_cmp
