@@ -180,3 +180,26 @@ def test_append_kv_fuses_rope(oracle_lib, dtype, d, P):
             np.testing.assert_array_max_ulp(qo[b, h].cpu().numpy(), want, maxulp=1)
     # Every other row is untouched.
     assert np.array_equal(Kc[~mask], K0[~mask]) and np.array_equal(Vc[~mask], K0[~mask])
+
+
+@pytest.mark.parametrize("flags", [mac.MAC_FLAG_SINGLE_LAUNCH, mac.MAC_FLAG_SPLIT_STAGES | mac.MAC_FLAG_FUSED_APPEND])
+def test_features_together_equal_plain_run(flags):
+    """Paged K/V, the match filter, a front sink and epoch restarts at once:
+    outputs, decisions and rings equal those of a dense, unfiltered run with
+    the same sink and epochs, bit for bit (match_d2 on hits)."""
+    from test_gpu_sink_epoch import _epoch_schedule, _run
+    cfg = _cfg(steps=18)
+    ep = _epoch_schedule(cfg.steps, cfg.batch)
+    dense, paged = _layers(cfg, 32, "NHD", flags, 64)
+    paged.p.flags |= mac.MAC_FLAG_MATCH_FILTER
+    a = _run(dense.init(), cfg.steps, ep, aux=torch.cuda.Stream())
+    b = _run(paged.init(), cfg.steps, ep, aux=torch.cuda.Stream())
+    hit = a["p"] >= 0
+    assert 0.2 < hit.mean() < 0.98
+    for k in ("out", "lse", "p"):
+        assert np.array_equal(a[k], b[k]), k
+    assert np.array_equal(a["d2"][hit], b["d2"][hit])
+    for x, y in zip(_rings(dense), _rings(paged)):
+        assert np.array_equal(x, y)
+    dense.release()
+    paged.release()
