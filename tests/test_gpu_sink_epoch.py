@@ -207,14 +207,16 @@ def test_forms_bitwise_with_sink_and_epochs():
             assert np.array_equal(x, y)
 
 
-def test_epoch_gating_inside_captured_graph():
-    """A decode step captured once in a HIP graph and replayed: epochs bumped
-    on the device between replays take effect in the graph, and every
-    replay equals the same step run eagerly on a second layer."""
+@pytest.mark.parametrize("flags", [FUSED, FUSED | SPLIT])
+def test_epoch_gating_inside_captured_graph(flags):
+    """A decode step captured once in a HIP graph and replayed (one launch,
+    or three kernels): epochs bumped on the device between replays take
+    effect in the graph, and every replay equals the same step run eagerly
+    on a second layer."""
     cfg = _cfg(batch=2, steps=12, sigma=(0.02, 0.1))
     K, V = wl.gen_kv(cfg)
     qt, q, _, _ = wl.gen_queries(cfg)
-    p = params_for(cfg, flags=FUSED, front_sink=64)
+    p = params_for(cfg, flags=flags, front_sink=64)
     ep_sched = _epoch_schedule(cfg.steps, cfg.batch)
     ref_layer = Layer(cfg, K, V, qt, q, params=p).init()
     eager = _run(ref_layer, cfg.steps, ep_sched)
