@@ -57,6 +57,7 @@ WsLayout ws_layout(int B, int Hq, int Hkv, int D, int K, int T, int dtype, bool 
     L.rect_l = take(BH * 4);
     L.ring_epoch = take(BG * 4);
     L.restart = take(BG * 4);
+    L.app_pos = take(BG * 4);
     // The single-launch regions come last, so the layout without them is a
     // prefix of the layout with them.
     L.skeys = L.grp_sync = 0;
@@ -86,6 +87,7 @@ WsPtrs ws_ptrs(void *base, const WsLayout &L)
     w.rect_l = (float *)(c + L.rect_l);
     w.ring_epoch = (int32_t *)(c + L.ring_epoch);
     w.restart = (int32_t *)(c + L.restart);
+    w.app_pos = (int32_t *)(c + L.app_pos);
     w.skeys = L.skeys ? (unsigned long long *)(c + L.skeys) : nullptr;
     w.grp_sync = L.grp_sync ? (uint32_t *)(c + L.grp_sync) : nullptr;
     return w;
@@ -98,7 +100,11 @@ using namespace mac;
 // match, attend (+plan), merge, append, single launch
 constexpr int kStages = MAC_PROFILE_STAGES;
 
+// Marks a live handle; mac_release clears it before freeing.
+constexpr uint64_t kHandleMagic = 0x4d41432d48414e44ull;
+
 struct mac_handle {
+    uint64_t magic = kHandleMagic;
     mac_params p;
     Shape s;
     WsLayout L;
@@ -117,6 +123,11 @@ struct mac_handle {
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// A handle made by mac_init_rings and not yet released.  (A released
+// handle's memory is freed; its cleared mark is what a stale pointer most
+// likely still shows, but reading it is not guaranteed.)
+static bool handle_ok(const mac_handle *h) { return h && h->magic == kHandleMagic; }
+
 // Host-side validation of the parameter block; fills the kernel shape.
 static mac_status check_params(const mac_params *p, Shape *s)
 {
@@ -131,7 +142,8 @@ static mac_status check_params(const mac_params *p, Shape *s)
         !isfinite(p->tau) || !isfinite(p->sm_scale) || p->sm_scale < 0.f ||
         p->front_sink < 0 || p->front_sink > kMaxFrontSink ||
         (p->thresh_mode != MAC_THRESH_ONE_MINUS_TAU &&
-         p->thresh_mode != MAC_THRESH_TAU))
+         p->thresh_mode != MAC_THRESH_TAU) ||
+        p->max_context < 0 || p->min_context < 0)
         return MAC_ERR_INVALID_ARG;
     const int G = p->n_q_heads / p->n_kv_heads;
     if ((p->head_dim != 64 && p->head_dim != 128) ||
@@ -181,6 +193,9 @@ static mac_status check_params(const mac_params *p, Shape *s)
     const int eb = elem_bytes(p->kv_dtype);
     if ((st * eb) % 16 || (sh * eb) % 16 || (sb * eb) % 16)
         return MAC_ERR_MISALIGNED;
+    // Entry refused above the maximum context (0: no limit).
+    if (p->max_context > 0 && p->kv_capacity > p->max_context)
+        return MAC_ERR_CONTEXT_TOO_LONG;
     if (s) {
         const int d = p->head_dim;
         const double scale = p->sm_scale != 0.f ? (double)p->sm_scale
@@ -198,6 +213,7 @@ static mac_status check_params(const mac_params *p, Shape *s)
         s->r = p->band_r;
         s->T = p->kv_capacity;
         s->F = p->front_sink;
+        s->min_ctx = p->min_context;
         s->page_shift = paged ? shift : 0;
         s->max_pages = paged ? p->max_pages : 0;
         s->page_table = paged ? p->page_table : nullptr;
@@ -274,6 +290,10 @@ const char *mac_status_string(mac_status s)
         return "workspace too small";
     case MAC_ERR_MISALIGNED:
         return "buffer or row not 16-byte aligned";
+    case MAC_ERR_CONTEXT_TOO_LONG:
+        return "kv_capacity exceeds max_context";
+    case MAC_ERR_NOT_INITIALIZED:
+        return "handle not initialised by mac_init_rings (or released)";
     }
     return "unknown status";
 }
@@ -499,7 +519,9 @@ mac_status mac_decode_step(mac_handle *h, const void *qtilde, const float *q,
                            int32_t *match_p, float *match_d2,
                            void *main_stream, void *aux_stream)
 {
-    if (!h || !qtilde || !q || !k_cache || !v_cache || !pos || !out)
+    if (!handle_ok(h))
+        return MAC_ERR_NOT_INITIALIZED;
+    if (!qtilde || !q || !k_cache || !v_cache || !pos || !out)
         return MAC_ERR_INVALID_ARG;
     if (!aligned16(qtilde) || !aligned16(q) || !aligned16(k_cache) ||
         !aligned16(v_cache))
@@ -597,7 +619,9 @@ mac_status mac_append_kv(const mac_params *p, const void *k_new, const void *v_n
 
 mac_status mac_bind_epochs(mac_handle *h, const int32_t *epoch)
 {
-    if (!h || (epoch && ((uintptr_t)epoch & 3u)))
+    if (!handle_ok(h))
+        return MAC_ERR_NOT_INITIALIZED;
+    if (epoch && ((uintptr_t)epoch & 3u))
         return MAC_ERR_INVALID_ARG;
     h->epoch = epoch;
     return MAC_OK;
@@ -605,8 +629,8 @@ mac_status mac_bind_epochs(mac_handle *h, const int32_t *epoch)
 
 mac_status mac_join_aux(mac_handle *h, void *stream)
 {
-    if (!h)
-        return MAC_ERR_INVALID_ARG;
+    if (!handle_ok(h))
+        return MAC_ERR_NOT_INITIALIZED;
     MAC_HIP(hipStreamWaitEvent((hipStream_t)stream, h->ev_aux, 0));
     return MAC_OK;
 }
@@ -644,7 +668,9 @@ mac_status mac_read_device_status(const mac_params *p, void *workspace,
 
 mac_status mac_profile_start(mac_handle *h, int32_t n_steps)
 {
-    if (!h || n_steps < 0)
+    if (!handle_ok(h))
+        return MAC_ERR_NOT_INITIALIZED;
+    if (n_steps < 0)
         return MAC_ERR_INVALID_ARG;
     for (hipEvent_t e : h->prof)
         (void)hipEventDestroy(e);
@@ -660,7 +686,9 @@ mac_status mac_profile_start(mac_handle *h, int32_t n_steps)
 
 mac_status mac_profile_read(mac_handle *h, double ms[MAC_PROFILE_STAGES], int32_t *n)
 {
-    if (!h || !ms || !n)
+    if (!handle_ok(h))
+        return MAC_ERR_NOT_INITIALIZED;
+    if (!ms || !n)
         return MAC_ERR_INVALID_ARG;
     for (int k = 0; k < kStages; ++k)
         ms[k] = 0.0;
@@ -684,10 +712,22 @@ mac_status mac_profile_read(mac_handle *h, double ms[MAC_PROFILE_STAGES], int32_
     return MAC_OK;
 }
 
+mac_status mac_stream_read(const void *buf, size_t bytes, float *sink, int32_t grid,
+                           void *stream)
+{
+    if (!buf || !sink || grid < 1 || bytes < 16)
+        return MAC_ERR_INVALID_ARG;
+    if (!aligned16(buf) || ((uintptr_t)sink & 3u))
+        return MAC_ERR_MISALIGNED;
+    MAC_HIP(launch_stream_read(buf, bytes, sink, grid, (hipStream_t)stream));
+    return MAC_OK;
+}
+
 mac_status mac_release(mac_handle *h)
 {
-    if (!h)
-        return MAC_ERR_INVALID_ARG;
+    if (!handle_ok(h))
+        return MAC_ERR_NOT_INITIALIZED;
+    h->magic = 0;
     if (h->ev_main)
         (void)hipEventDestroy(h->ev_main);
     if (h->ev_aux)

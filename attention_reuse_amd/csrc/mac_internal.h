@@ -106,7 +106,12 @@ constexpr int kSingleLaunchMaxGroups = 16;
 // per line, so heads must not share one.
 constexpr int kKeyStride = 16;
 constexpr unsigned long long kSyncMagic = 0x4d41432d53594e43ull;
-enum { kSyncDone = 0, kSyncMagicWord = 1, kSyncSticky = 2 };
+// Synchronisation words: the done counter, the initialised marker, the
+// latched time-outs (cleared when read), and the broken mark: set with a
+// time-out, cleared only by the ring reset; a single launch that finds it
+// set computes nothing and writes NaN outputs, so a handle whose counters a
+// time-out left inconsistent fails visibly until it is re-initialised.
+enum { kSyncDone = 0, kSyncMagicWord = 1, kSyncSticky = 2, kSyncBroken = 3 };
 
 // Key words per group of the single launch: one per match unit, at least
 // one per workgroup, never more than kMaxSingleUnits.
@@ -231,7 +236,7 @@ struct GroupItems {
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WsLayout {
     size_t keys, ctx, dec_slot, grp_begin, grp_count, grp_start, ctrl, sync,
-        part_o, part_l, rect_o, rect_l, ring_epoch, restart, skeys, grp_sync, total;
+        part_o, part_l, rect_o, rect_l, ring_epoch, restart, app_pos, skeys, grp_sync, total;
     int64_t max_items;
     int32_t nsplit;
 };
@@ -251,6 +256,7 @@ enum { kCtrlItems = 0, kCtrlStatus = 1, kCtrlClaim = 2 };
 struct Shape {
     int32_t B, Hq, Hkv, G, D, dtype, K, r, T;
     int32_t F;                    // front sink: leading positions never reused
+    int32_t min_ctx;              // positions below it find no match candidate
     // Paged K/V (page_table non-null): row t of request b, KV head g at
     // b's page page_table[b * max_pages + (t >> page_shift)], element
     // offset page * kv_sb + g * kv_sh + (t mod page size) * kv_st.
@@ -275,6 +281,10 @@ struct WsPtrs {
     // [B * Hkv] 1 where the latest step's merge found the group not ready:
     // the separate append kernel then restarts the group's position ring
     int32_t *restart;
+    // [B * Hkv] the position the latest step's merge appended for each KV
+    // group (-1: nothing to append), so that the separate append kernel never
+    // reads the caller's position array on the auxiliary stream
+    int32_t *app_pos;
     // single launch only (null otherwise): tagged split keys, per-group
     // arrival counters
     unsigned long long *skeys;
@@ -357,6 +367,9 @@ hipError_t launch_ring_reset(const Shape &s, void *q_ring, float *o_ring,
                              float *lse_ring, int32_t *pos_ring, const WsPtrs &w,
                              int64_t n_tag, hipStream_t st);
 int device_cu_count();
+// Streaming read of a buffer (bandwidth measurement); sink holds grid floats.
+hipError_t launch_stream_read(const void *buf, size_t bytes, float *sink, int grid,
+                              hipStream_t st);
 // K and V of position pos[b] into the cache, K rotated by RoPE (base > 0),
 // and q_out = RoPE(q_tilde) when q_out is non-null.
 hipError_t launch_append_kv(const Shape &s, const void *k_new, const void *v_new,

@@ -495,6 +495,7 @@ __device__ PlanTables plan_tables(const StepArgs &a, int32_t *lds, bool publish)
             a.w.grp_count[grp] = s_gcount[grp];
             a.w.grp_start[grp] = s_gstart[grp];
             if (s_gcount[grp] == 0) {
+                a.w.app_pos[grp] = -1;  // nothing to append
                 // No item, so no merge will run: the outputs are written here.
                 const int b = grp / s.Hkv, g = grp - b * s.Hkv;
                 const bool bad = !end_ok(a, s_gend[grp]);
@@ -601,7 +602,8 @@ __device__ inline unsigned long long match_finish(const StepArgs &a, int m, bool
 {
     constexpr int EPL = T::EPL, LPR = D / EPL, RPB = kBlock / LPR;
     const Shape &s = a.s;
-    const bool m_ok = ready && m >= 0 && m < s.T;
+    // Below the minimum context a request does not reuse: no candidate.
+    const bool m_ok = ready && m >= 0 && m < s.T && m >= s.min_ctx;
     float qv[EPL];
     unpack<T>(ml.q, qv);
     // This lane's share of each row's squared distance.
@@ -1133,10 +1135,14 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int gstart, int
     // restarts with this step's entry, here or in the append kernel.
     if (!ready && tid == 0)
         a.w.ring_epoch[grp] = a.epoch[b];
-    if (a.append_fused)
+    if (a.append_fused) {
         ring_append_pos(a, grp, e, !ready, tid, NT);
-    else if (tid == 0)
+    } else if (tid == 0) {
+        // For the append kernel: the group's restart flag and position (it
+        // never reads the caller's arrays, which main_stream may overwrite).
         a.w.restart[grp] = ready ? 0 : 1;
+        a.w.app_pos[grp] = e;
+    }
 }
 
 // Merge kernel: one workgroup of kMergeBlock threads per KV group, from the
@@ -2131,6 +2137,28 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(AttendSh
     }
 }
 
+// NaN outputs, an empty staged summary and nothing to append for the G
+// heads of group grp (query heads bh0 ...), written by the calling
+// workgroup: a position out of range, or a single launch that cannot trust
+// its counters.
+template <int D, int G>
+__device__ inline void group_invalid(const StepArgs &a, int grp, int bh0)
+{
+    for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
+        const int bh = bh0 + idx / D;
+        if (a.out)
+            a.out[(int64_t)bh * D + idx % D] = NAN;
+        a.w.rect_o[(int64_t)bh * D + idx % D] = 0.f;
+        if (idx % D == 0) {
+            if (a.out_lse)
+                a.out_lse[bh] = NAN;
+            a.w.rect_l[bh] = -INFINITY;
+        }
+    }
+    if (threadIdx.x == 0)
+        a.w.app_pos[grp] = -1;
+}
+
 // Single-launch key words (see mac_internal.h): bits 31..24 of the low word
 // carry the tag's low byte instead of 0xff (positions are below 2^24).
 __device__ inline unsigned long long key_tagged(unsigned long long key, uint32_t tag8)
@@ -2278,6 +2306,14 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
     // before the group can complete and its merge restart the rings.
     const bool ready = group_ready(a, b, grp);
     const unsigned long long done = sync[kSyncDone];
+    // An earlier launch on this workspace gave up waiting, so the counters
+    // may be inconsistent: every launch until the ring reset writes NaN
+    // outputs and computes nothing (no workgroup waits, so none can time out).
+    if (sync[kSyncBroken] != 0) {
+        if (loc == 0)
+            group_invalid<D, G>(a, grp, bh0);
+        return;
+    }
     uint32_t *counter = a.w.grp_sync + (int64_t)grp * kGrpStride;
     const int span_prev = (int)counter[kGrpSpan];
     int uj, ufirst;
@@ -2315,6 +2351,17 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
     if (threadIdx.x < 64)
         ok = poll_keys(a, kw + (loc % kKeyReps) * rep_stride, tag8, s_keys);
     ok = block_and(ok);
+    if (!ok) {
+        // The group's keys never all arrived: its outputs are invalid, and
+        // the workspace is marked broken until the ring reset (this group's
+        // counter and the done counter no longer follow the protocol).
+        group_invalid<D, G>(a, grp, bh0);
+        if (threadIdx.x == 0) {
+            atomicOr(&sync[kSyncSticky], (unsigned long long)MAC_DEV_SYNC_TIMEOUT);
+            atomicOr(&sync[kSyncBroken], 1ull);
+        }
+        return;
+    }
 
     // Plan of the group.  Head j's key is the minimum over its units (exact
     // in any order), taken by the 64 / G lanes j * 64 / G, ... of wave 0;
@@ -2412,22 +2459,10 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepArgs a)
     }
     if (n == 0 && loc == 0) {
         // Position out of range: NaN outputs, nothing appended.
-        for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
-            const int bh = bh0 + idx / D;
-            if (a.out)
-                a.out[(int64_t)bh * D + idx % D] = NAN;
-            a.w.rect_o[(int64_t)bh * D + idx % D] = 0.f;
-            if (idx % D == 0) {
-                if (a.out_lse)
-                    a.out_lse[bh] = NAN;
-                a.w.rect_l[bh] = -INFINITY;
-            }
-        }
+        group_invalid<D, G>(a, grp, bh0);
         if (threadIdx.x == 0)
             atomicAdd(&sync[kSyncDone], done_add);
     }
-    if (!ok && threadIdx.x == 0)
-        atomicOr(&sync[kSyncSticky], (unsigned long long)MAC_DEV_SYNC_TIMEOUT);
 }
 
 // ---------------------------------------------------------------------------
@@ -2439,8 +2474,11 @@ __global__ __launch_bounds__(D) void append_kernel(StepArgs a, int32_t pos_offse
     using S = typename T::S;
     const Shape &s = a.s;
     const int bh = blockIdx.x, b = bh / s.Hq, h = bh - b * s.Hq;
+    const int grp = b * s.Hkv + h / s.G;
     const int dim = threadIdx.x;
-    const int t = a.pos[b] + pos_offset;
+    // Decode steps append at the position the merge recorded for the group
+    // (-1: none); the warm-up at the workspace's prompt positions.
+    const int t = kWarm ? a.pos[b] + pos_offset : a.w.app_pos[grp];
     if (t < 0 || t >= s.T)
         return;
     const int slot = t % s.K;
@@ -2451,7 +2489,6 @@ __global__ __launch_bounds__(D) void append_kernel(StepArgs a, int32_t pos_offse
         a.lse_ring[(int64_t)bh * s.K + slot] = a.w.rect_l[bh] * kLn2;
     if (h % s.G == 0) {
         // The merge of the step recorded whether the group restarts.
-        const int grp = b * s.Hkv + h / s.G;
         ring_append_pos(a, grp, t, !kWarm && a.w.restart[grp] != 0, dim, D);
     }
 }
@@ -2562,7 +2599,45 @@ __global__ void ring_reset_kernel(int64_t n_q, S *__restrict__ q_ring,
         ctrl[i0] = 0;
 }
 
+// Streaming read of n16 16-byte words (a measurement of the achievable read
+// bandwidth, the denominator the decode kernels are compared with): each
+// thread keeps kReadUnroll loads in flight, folds every word into one value,
+// and stores it only when it equals a value the data never produces, so no
+// load can be dropped and nothing is written in practice.
+constexpr int kReadUnroll = 8;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(kBlock) void stream_read_kernel(const u32x4 *__restrict__ p,
+                                                              int64_t n16, float *sink)
+{
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (kReadUnroll - 1) * stride < n16; i += kReadUnroll * stride) {
+        u32x4 v[kReadUnroll];
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u)
+            v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u)
+            acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 v = p[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == 0x7fc00123u)
+        sink[blockIdx.x] = __uint_as_float(acc);
+}
+
 }  // namespace
+
+hipError_t launch_stream_read(const void *buf, size_t bytes, float *sink, int grid,
+                              hipStream_t st)
+{
+    hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(kBlock), 0, st,
+                       (const u32x4 *)buf, (int64_t)(bytes / 16), sink);
+    return hipGetLastError();
+}
 
 // ---------------------------------------------------------------------------
 // Launchers with (dtype, D, G) dispatch.

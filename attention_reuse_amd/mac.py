@@ -28,7 +28,10 @@ MAC_FLAG_SINGLE_LAUNCH = 4
 MAC_FLAG_MATCH_FILTER = 8
 STATUS = {0: "MAC_OK", -1: "MAC_ERR_INVALID_ARG", -2: "MAC_ERR_UNSUPPORTED",
           -3: "MAC_ERR_HIP", -4: "MAC_ERR_WORKSPACE_TOO_SMALL",
-          -5: "MAC_ERR_MISALIGNED"}
+          -5: "MAC_ERR_MISALIGNED", -6: "MAC_ERR_CONTEXT_TOO_LONG",
+          -7: "MAC_ERR_NOT_INITIALIZED"}
+MAC_ERR_CONTEXT_TOO_LONG = -6
+MAC_ERR_NOT_INITIALIZED = -7
 STAGES = ("match", "attend", "merge", "append", "step")
 
 
@@ -49,7 +52,8 @@ class mac_params(ctypes.Structure):
         ("kv_stride_b", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64),
         ("kv_stride_t", ctypes.c_int64), ("front_sink", ctypes.c_int32),
         ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32),
-        ("page_table", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p), ("max_context", ctypes.c_int32),
+        ("min_context", ctypes.c_int32),
     ]
 
 
@@ -93,6 +97,7 @@ def load():
         "mac_profile_read": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_double),
                                             ctypes.POINTER(ctypes.c_int32)]),
         "mac_release": (ctypes.c_int, [_vp]),
+        "mac_stream_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, ctypes.c_int32, _vp]),
         "mac_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "mac_chunk_tokens": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32]),
         "mac_group_items": (ctypes.c_int32, [ctypes.c_int32] * 4 + [
@@ -134,12 +139,13 @@ def _check(fn, rc):
 def make_params(batch, n_q_heads, n_kv_heads, head_dim, kv_dtype, ring_k,
                 band_r, kv_capacity, tau, thresh_mode=MAC_THRESH_ONE_MINUS_TAU,
                 sm_scale=0.0, strides=(0, 0, 0), flags=0, front_sink=0, page_size=0,
-                max_pages=0, page_table=None) -> mac_params:
+                max_pages=0, page_table=None, max_context=0, min_context=0) -> mac_params:
     """page_table: device tensor or address of the [B, max_pages] int32
     page table when page_size > 0 (the tensor must outlive every call)."""
     return mac_params(batch, n_q_heads, n_kv_heads, head_dim, kv_dtype, ring_k,
                       band_r, kv_capacity, tau, thresh_mode, sm_scale, flags,
-                      *strides, front_sink, page_size, max_pages, _ptr(page_table))
+                      *strides, front_sink, page_size, max_pages, _ptr(page_table),
+                      max_context, min_context)
 
 
 def mac_workspace_bytes(p: mac_params) -> int:
@@ -215,6 +221,11 @@ def mac_profile_read(handle):
     n = ctypes.c_int32()
     _check("mac_profile_read", load().mac_profile_read(handle, ms, ctypes.byref(n)))
     return dict(zip(STAGES, list(ms))), n.value
+
+
+def mac_stream_read(buf, n_bytes, sink, grid, stream=None):
+    _check("mac_stream_read", load().mac_stream_read(_ptr(buf), int(n_bytes), _ptr(sink),
+                                                     int(grid), stream))
 
 
 def mac_release(handle):

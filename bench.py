@@ -36,7 +36,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=32)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--config", type=int, default=2, choices=sorted(wl.WORKLOADS))
+    # Default: the largest workload on one GPU (8 requests x 128K context,
+    # 4 GiB of K/V per layer).
+    ap.add_argument("--config", type=int, default=3, choices=sorted(wl.WORKLOADS))
     ap.add_argument("--layers", type=int, default=0,
                     help="layer copies per step (0 = enough to overflow the Infinity Cache)")
     ap.add_argument("--mode", choices=("mac", "full"), default="mac")
@@ -54,6 +56,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--no-full", action="store_true",
+                    help="skip the same-run full-decode comparison")
+    ap.add_argument("--graph", action="store_true",
+                    help="time HIP-graph replays of the steps (one graph per step, all "
+                         "layers; needs --append fused) instead of eager launches")
     ap.add_argument("--json-out", default="")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (the "
@@ -134,43 +141,49 @@ def algorithmic_bytes(cfg, match_p, m, second_halves=None):
 
 
 def cpu_baseline(cfg, K, V, qt, q, budget_s):
-    """The CPU oracle, as is, on a bounded sample of the same workload."""
+    """The CPU oracle, as is, on a bounded sample of the same workload: at
+    most one (request, head) stream per thread, spread over the requests and
+    heads, for as many decode steps as the time budget allows."""
     from oracle import oracle as orc
 
     orc.build()
-    threads = min(16, os.cpu_count() or 1)
+    nproc = os.cpu_count() or 1
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = nproc
+    threads = max(1, min(16, avail))
     t2 = orc.threshold2(cfg.head_dim, cfg.tau)
     W = cfg.n_warm
-    # Calibrate on one stream and a few steps, then size the sample.
-    probe_steps = min(8, cfg.steps)
+    all_heads = [(b, h) for b in range(cfg.batch) for h in range(cfg.n_q_heads)]
+    stride = max(1, len(all_heads) // threads)
+    heads = all_heads[::stride][:threads]
 
-    def run(heads, n_steps):
+    def run(n_steps):
         res = orc.run_streams(K, V, qt, q, heads, ctx_len=cfg.ctx, n_warm=W,
                               ring_k=cfg.ring_k, band_r=cfg.band_r, thresh2=t2,
                               n_steps=n_steps, threads=threads)
-        warm = sum(r["warm_seconds"] for r in res.values())
-        return res, warm
+        return sum(r["warm_seconds"] for r in res.values())
 
+    # Calibrate on a few steps, then size the sample to the budget.
+    probe = min(4, cfg.steps)
     t0 = time.perf_counter()
-    _, warm = run([(0, 0)], probe_steps)
-    per_step = max(1e-6, (time.perf_counter() - t0 - warm) / probe_steps)
-    all_heads = [(b, h) for b in range(cfg.batch) for h in range(cfg.n_q_heads)]
-    n_steps = int(min(cfg.steps, max(4, budget_s * threads / per_step / len(all_heads))))
-    heads = all_heads
-    if n_steps == 4 and per_step * 4 * len(all_heads) > budget_s * threads:
-        nh = max(threads, int(budget_s * threads / (per_step * 4)))
-        heads = all_heads[::max(1, len(all_heads) // nh)][:nh]
+    warm = run(probe)
+    per_step = max(1e-6, (time.perf_counter() - t0 - warm / threads) / probe)
+    n_steps = int(min(cfg.steps, max(probe, budget_s / per_step)))
     t0 = time.perf_counter()
-    res, warm = run(heads, n_steps)
+    warm = run(n_steps)
     wall = time.perf_counter() - t0
     # Warm-summary evaluation (lazy, off the per-step path) is excluded,
     # spread over the threads that ran it.
     step_time = max(1e-9, wall - warm / threads)
     value = len(heads) * n_steps / step_time
-    return dict(value=value, unit="heads*layers/s", cores=threads, kind="oracle",
+    return dict(value=value, unit="heads*layers/s", cores=threads, nproc=nproc,
+                kind="oracle",
                 sample="%d (request, head) streams x %d decode steps of %s, fp64 C "
-                       "oracle, %d threads, lazy warm summaries (%.1f s) excluded"
-                % (len(heads), n_steps, cfg.name, threads, warm))
+                       "oracle, %d threads on %d host cores, lazy warm summaries "
+                       "(%.1f CPU-s) excluded" % (len(heads), n_steps, cfg.name, threads,
+                                                   avail, warm))
 
 
 def main():
@@ -281,17 +294,35 @@ def main():
 
     match_rec = torch.full((cfg.steps, NL, B, H), -1, dtype=torch.int32, device=dev)
 
-    def step(s, record=True):
+    def step_on(s, sid, record=True):
         for li, L in enumerate(layers):
             if args.mode == "mac":
                 mac.mac_decode_step(L["h"], dec_qt[s], dec_q[s], L["K"], L["V"], pos[s],
                                     L["out"], None, match_rec[s, li] if record else None,
-                                    None, st, aux.cuda_stream)
+                                    None, sid, aux.cuda_stream)
             else:
                 mac.mac_full_decode(p, dec_q[s], L["K"], L["V"], pos[s], L["out"], None,
-                                    L["ws"], wsb, st)
+                                    L["ws"], wsb, sid)
+
+    def step(s, record=True):
+        step_on(s, st, record)
 
     reset_rings()
+    graphs = None
+    if args.graph:
+        # One graph per timed step, captured before anything runs (capture
+        # does not execute), replayed in order after the eager warm-up.
+        if args.append != "fused" and args.mode == "mac":
+            sys.exit("--graph needs --append fused")
+        graphs = []
+        cap = torch.cuda.Stream()
+        with torch.cuda.stream(cap):
+            for s in range(args.warmup, args.warmup + args.steps):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    step_on(s, cap.cuda_stream)
+                graphs.append(g)
+        torch.cuda.synchronize()
     for s in range(args.warmup):
         step(s)
     for L in layers:
@@ -299,8 +330,11 @@ def main():
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for s in range(args.warmup, args.warmup + args.steps):
-        step(s)
+    for i, s in enumerate(range(args.warmup, args.warmup + args.steps)):
+        if graphs:
+            graphs[i].replay()
+        else:
+            step(s)
     for L in layers:
         mac.mac_join_aux(L["h"], st)
     e1.record(stream)
@@ -373,6 +407,46 @@ def main():
                         peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4),
                         traffic=None)
 
+    # Same run: exact full decode of the same layers and positions (the
+    # baseline MAC is measured against), and the achievable streaming-read
+    # bandwidth of the device (a read-only kernel over a buffer far larger
+    # than the Infinity Cache).
+    full_ms = None
+    if args.mode == "mac" and not args.no_full:
+        fws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        nf = min(args.steps, 8)
+        for s in range(args.warmup, args.warmup + 2):
+            for L in layers:
+                mac.mac_full_decode(p, dec_q[s], L["K"], L["V"], pos[s], L["out"], None,
+                                    fws, wsb, st)
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for s in range(args.warmup, args.warmup + nf):
+            for L in layers:
+                mac.mac_full_decode(p, dec_q[s], L["K"], L["V"], pos[s], L["out"], None,
+                                    fws, wsb, st)
+        f1.record(stream)
+        torch.cuda.synchronize()
+        full_ms = f0.elapsed_time(f1) / nf
+        del fws
+    read_gbs = None
+    if not args.no_full:
+        nbytes = 4 << 30
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        grid = 8 * torch.cuda.get_device_properties(0).multi_processor_count
+        sink = torch.empty(grid, device=dev)
+        times = []
+        for it in range(6):
+            r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            r0.record(stream)
+            mac.mac_stream_read(buf, nbytes, sink, grid, st)
+            r1.record(stream)
+            torch.cuda.synchronize()
+            if it:
+                times.append(r0.elapsed_time(r1))
+        read_gbs = nbytes / (sorted(times)[len(times) // 2] * 1e-3) / 1e9
+        del buf
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(cfg, K, V, qt, q, args.cpu_seconds)
@@ -386,7 +460,10 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32",
+        # K/V, queries and the logits' MFMA operands in the workload's type;
+        # accumulation, softmax and summaries in fp32.
+        "dtype": cfg.dtype,
+        "accum_dtype": "f32",
         "data": "synthetic (seeded N(0,1) K/V, prototype+noise query stream)",
         "config": {"workload": cfg.name, "mode": args.mode,
                    "launch": launched or args.launch,
@@ -404,6 +481,12 @@ def main():
         "hit_rate": round(per["hits"] / (n_ls * B * H), 4),
         "group_miss_rate": round(per["group_miss"] / (n_ls * B * Hkv), 4),
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()} if stage_ms else None,
+        "timing": "graph replay" if graphs else "eager launches",
+        "full_decode_ms_per_step": round(full_ms, 4) if full_ms else None,
+        "speedup_vs_full_decode": round(full_ms / ms_per_step, 3) if full_ms else None,
+        "achievable_read_gbs": round(read_gbs, 1) if read_gbs else None,
+        "step_frac_of_achievable": (round(alg_step / (ms_per_step * 1e-3) / 1e9 / read_gbs, 4)
+                                    if read_gbs else None),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

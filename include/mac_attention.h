@@ -49,7 +49,10 @@ typedef enum mac_status {
     MAC_ERR_UNSUPPORTED = -2,         /* head_dim / dtype / group not built */
     MAC_ERR_HIP = -3,                 /* a HIP runtime call failed          */
     MAC_ERR_WORKSPACE_TOO_SMALL = -4, /* ws_bytes < mac_workspace_bytes()   */
-    MAC_ERR_MISALIGNED = -5           /* a buffer or row not 16-B aligned   */
+    MAC_ERR_MISALIGNED = -5,          /* a buffer or row not 16-B aligned   */
+    MAC_ERR_CONTEXT_TOO_LONG = -6,    /* kv_capacity > max_context          */
+    MAC_ERR_NOT_INITIALIZED = -7      /* handle NULL, released, or not made
+                                         by mac_init_rings                  */
 } mac_status;
 
 /* Element type of the K/V cache, of the pre-RoPE queries and of the query
@@ -101,9 +104,11 @@ enum {
 enum {
     MAC_DEV_BAD_POSITION = 1, /* some m outside [0, kv_capacity)            */
     MAC_DEV_SYNC_TIMEOUT = 2  /* a single-launch step gave up waiting for
-                                 workgroups that never became resident: its
-                                 outputs are not valid, and the handle must
-                                 be re-initialised with mac_init_rings      */
+                                 workgroups that never became resident: the
+                                 waiting groups' outputs are NaN, and every
+                                 later single-launch step on the workspace
+                                 writes NaN outputs and leaves the rings
+                                 untouched until mac_init_rings resets it  */
 };
 
 typedef struct mac_params {
@@ -146,6 +151,21 @@ typedef struct mac_params {
     int32_t page_size;
     int32_t max_pages;
     const int32_t *page_table;
+    /* Context limits (blog, "Production version: one fused persistent BF16
+     * kernel": its settings block turns reuse off below a minimum generated
+     * context, and its graph-safe readiness item refuses entry above a
+     * maximum context).
+     * max_context >= 0: 0 means no limit; otherwise every call whose
+     * kv_capacity exceeds it returns MAC_ERR_CONTEXT_TOO_LONG on the host,
+     * before any launch.
+     * min_context >= 0: a request at position m < min_context finds no
+     * match candidate (decided on the device per request and step, so it
+     * holds inside captured graphs): the step is exact full attention
+     * (match_p -1, match_d2 +inf) and its rectify-append still writes slot
+     * m mod K, so reuse can start as soon as m reaches the limit.  0 (the
+     * default) never blocks. */
+    int32_t max_context;
+    int32_t min_context;
 } mac_params;
 
 /* Ring buffers of one attention layer, caller-allocated device memory:
@@ -226,7 +246,9 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
  * unused.  The append reads qtilde: when it runs on aux_stream, work that
  * overwrites qtilde must be ordered after mac_join_aux (or after a later
  * mac_decode_step on the handle) on the stream that does it; the other
- * inputs are read on main_stream only.  Returns without a host
+ * inputs (pos and epoch included: the merge keeps a copy of each request's
+ * position in the workspace for the append) are read on main_stream only,
+ * so main_stream may overwrite them as soon as the call returns.  Returns without a host
  * synchronisation, so a steady-state step
  * can be captured into a HIP graph (join aux_stream back with mac_join_aux
  * first).  Calls on one handle must not overlap; handles are independent,
@@ -311,6 +333,15 @@ mac_status mac_read_device_status(const mac_params *p, void *workspace,
 enum { MAC_PROFILE_STAGES = 5 };
 mac_status mac_profile_start(mac_handle *h, int32_t n_steps);
 mac_status mac_profile_read(mac_handle *h, double ms[MAC_PROFILE_STAGES], int32_t *n);
+
+/* Streaming read of bytes (rounded down to 16) of the device buffer buf by
+ * `grid` workgroups, enqueued on `stream` (measurement of the achievable HBM
+ * read bandwidth that the decode kernels are compared with).  sink: device
+ * floats [grid], written only in the practically impossible case that the
+ * data folds to one particular value (it keeps the loads from being
+ * optimised away).  buf 16-byte aligned. */
+mac_status mac_stream_read(const void *buf, size_t bytes, float *sink, int32_t grid,
+                           void *stream);
 
 /* Free the handle and its events (not the caller's buffers). */
 mac_status mac_release(mac_handle *h);

@@ -218,6 +218,11 @@ void mac_oracle_unmerge(int d, const double *ow, double lw, const double *op,
  * minus the band, i.e. it covers [F, m-r] (empty when m-r < F).  F = 0 is
  * the plain method.
  *
+ * Minimum context ([MAC], same section, its settings block: reuse is off
+ * below a minimum context): at a position m < min_context the step looks at
+ * no candidate, so it is a miss (exact full attention, dist = +inf), and
+ * its rectify-append still fills slot m mod K.  0 never blocks.
+ *
  * Ready/epoch gating ([MAC], same section, its graph-safe readiness
  * item): restart[s] != 0 marks a ring that is not ready or was invalidated
  * before step s.  Its contents are dropped (every slot empty), so the step
@@ -233,6 +238,7 @@ typedef struct {
     double thresh2;  /* squared-distance threshold T2 (the fp32 value) */
     double exempt;   /* decision-exemption band on distances (1e-4) */
     long front_sink; /* F: leading positions kept out of every summary */
+    long min_context; /* positions below it do not reuse (no candidate) */
 } mac_oracle_cfg;
 
 /*
@@ -330,7 +336,7 @@ int mac_oracle_stream(const mac_oracle_cfg *c, const void *K, const void *V,
         int kb = -1;
         double Db = INFINITY, D2 = INFINITY;
         long pb = -1;
-        for (int k = 0; k < Kr; ++k) {
+        for (int k = 0; k < Kr && m >= c->min_context; ++k) {
             if (pos[k] < m - Kr || pos[k] > m - 1)
                 continue;
             double D = 0.0;

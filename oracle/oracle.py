@@ -38,6 +38,7 @@ class _Cfg(ctypes.Structure):
         ("thresh2", ctypes.c_double),
         ("exempt", ctypes.c_double),
         ("front_sink", ctypes.c_long),
+        ("min_context", ctypes.c_long),
     ]
 
 
@@ -166,7 +167,8 @@ def unmerge(ow, lw, op, lp):
 def run_stream(K, V, qt_warm, q_warm, qt_dec, q_dec, *, ctx_len: int,
                ring_k: int, band_r: int, thresh2: float, n_steps: int | None = None,
                scale: float | None = None, exempt: float = 1e-4,
-               want_ring: bool = False, front_sink: int = 0, restart=None):
+               want_ring: bool = False, front_sink: int = 0, restart=None,
+               min_context: int = 0):
     """Run MAC decode steps for one (request, query head) stream.
 
     K, V: [T, d] of the head's KV group.  qt_warm: [W, d] pre-RoPE warm
@@ -174,7 +176,9 @@ def run_stream(K, V, qt_warm, q_warm, qt_dec, q_dec, *, ctx_len: int,
     q_warm: [W, d] float32 post-RoPE.  qt_dec / q_dec: [S, d] for decode
     positions ctx_len + s.  front_sink: F leading positions kept out of
     every summary.  restart: optional [S] flags, nonzero where the ring is
-    dropped before that step (not ready / invalidated).
+    dropped before that step (not ready / invalidated).  min_context:
+    positions below it look at no candidate (exact attention, still
+    appended).
     """
     lib = load()
     d = K.shape[1]
@@ -190,7 +194,7 @@ def run_stream(K, V, qt_warm, q_warm, qt_dec, q_dec, *, ctx_len: int,
     S = qt_dec.shape[0] if n_steps is None else int(n_steps)
     cfg = _Cfg(d, ring_k, band_r, dt, int(ctx_len), W, S,
                (1.0 / math.sqrt(d)) if scale is None else scale,
-               float(thresh2), exempt, int(front_sink))
+               float(thresh2), exempt, int(front_sink), int(min_context))
     rst = None
     if restart is not None:
         rst = np.ascontiguousarray(restart, np.int32)
@@ -228,7 +232,7 @@ def run_stream(K, V, qt_warm, q_warm, qt_dec, q_dec, *, ctx_len: int,
 def run_streams(K, V, qt, q, heads, *, ctx_len: int, n_warm: int, ring_k: int,
                 band_r: int, thresh2: float, n_steps: int | None = None,
                 threads: int | None = None, want_ring: bool = False,
-                front_sink: int = 0, restart=None):
+                front_sink: int = 0, restart=None, min_context: int = 0):
     """Run many (b, h) streams in parallel threads (ctypes drops the GIL).
 
     K, V: [B, Hkv, T, d]; qt, q: [B, Hq, W+S, d] (warm part first).
@@ -246,7 +250,8 @@ def run_streams(K, V, qt, q, heads, *, ctx_len: int, n_warm: int, ring_k: int,
             K[b, g], V[b, g], qt[b, h, :W], q[b, h, :W], qt[b, h, W:],
             q[b, h, W:], ctx_len=ctx_len, ring_k=ring_k, band_r=band_r,
             thresh2=thresh2, n_steps=n_steps, want_ring=want_ring,
-            front_sink=front_sink, restart=None if restart is None else restart[b])
+            front_sink=front_sink, restart=None if restart is None else restart[b],
+            min_context=min_context)
 
     heads = list(heads)
     nt = threads or min(len(heads), os.cpu_count() or 1, 16)

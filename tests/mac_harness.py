@@ -108,12 +108,13 @@ def tolerance_check(cfg, got, ref):
     return bool(err <= 3e-3), float(err)
 
 
-def lockstep_compare(cfg, gpu, orc, b, h, n_steps):
-    """Compare one (b, h) stream.  Decisions must match exactly except at
-    points the oracle marks exempt (within 1e-4 of the threshold or of a
-    tie); after a disagreement at an exempt point the stream's later steps
-    are not compared (its ring state legitimately differs).  Returns
-    (n_compared, n_exempt, diverged_at or None)."""
+def lockstep_compare(cfg, gpu, orc, b, h, n_steps, allow_diverge=False):
+    """Compare one (b, h) stream.  Decisions must match exactly; at points
+    the oracle marks exempt (within 1e-4 of the threshold or of a tie)
+    several decisions are correct, and a disagreement there fails unless
+    allow_diverge is set: then it is printed with its distances and the
+    stream's later steps are not compared (its ring state legitimately
+    differs).  Returns (n_compared, n_exempt, diverged_at or None)."""
     n_ex = 0
     for s in range(n_steps):
         g_hit = gpu["p"][s, b, h] >= 0
@@ -123,6 +124,12 @@ def lockstep_compare(cfg, gpu, orc, b, h, n_steps):
         if orc["exempt"][s]:
             n_ex += 1
             if (g_hit, g_p) != (o_hit, o_p):
+                msg = ("exempt decision disagreement b=%d h=%d step=%d gpu=(%s,%d) "
+                       "oracle=(%s,%d) dist=%.7f runner-up=%.7f gpu d2=%.7g" % (
+                           b, h, s, g_hit, g_p, o_hit, o_p, orc["dist"][s], orc["dist2"][s],
+                           gpu["d2"][s, b, h]))
+                assert allow_diverge, msg
+                print("  " + msg, flush=True)
                 return s, n_ex, s
         else:
             assert (g_hit, g_p) == (o_hit, o_p), (

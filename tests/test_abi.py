@@ -33,12 +33,14 @@ def test_exports_every_declared_function(lib):
 
 
 def test_struct_layout_matches_header():
-    assert ctypes.sizeof(mac.mac_params) == 96
+    assert ctypes.sizeof(mac.mac_params) == 104
     assert mac.mac_params.kv_stride_b.offset == 48
     assert mac.mac_params.front_sink.offset == 72
     assert mac.mac_params.page_size.offset == 76
     assert mac.mac_params.max_pages.offset == 80
     assert mac.mac_params.page_table.offset == 88
+    assert mac.mac_params.max_context.offset == 96
+    assert mac.mac_params.min_context.offset == 100
     assert ctypes.sizeof(mac.mac_rings) == 32
 
 
@@ -56,6 +58,32 @@ def test_paged_params(lib, kw, ok):
     assert (mac.mac_workspace_bytes(_params(**kw)) > 0) == ok
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(max_context=4096), 0), (dict(max_context=0), 0), (dict(max_context=4095), -6),
+    (dict(max_context=131072, kv_capacity=262144 + 512), -6), (dict(max_context=-1), -1),
+    (dict(min_context=2048), 0), (dict(min_context=1 << 30), 0), (dict(min_context=-5), -1),
+])
+def test_context_limits(lib, kw, status):
+    """max_context refuses a handle or call whose KV capacity exceeds it, on
+    the host before any launch; min_context only has to be non-negative
+    (it is applied on the device per request)."""
+    p = _params(**kw)
+    rc = lib.mac_full_decode(ctypes.byref(p), 0x1000, 0x2000, 0x3000, 0x4000,
+                             None, None, None, 0, None)
+    assert rc == (status if status != 0 else -1)
+    assert (mac.mac_workspace_bytes(p) > 0) == (status == 0)
+    if status != 0:
+        # Refused before any device call (no handle is made).
+        rings = mac.mac_rings(0x1000, 0x2000, 0x3000, 0x4000)
+        h = ctypes.c_void_p()
+        ctx = (ctypes.c_int32 * 2)(4096, 4096)
+        rc = lib.mac_init_rings(ctypes.byref(p), ctypes.byref(rings), 0x6000, 1 << 40,
+                                None, None, 0, ctx, None, None, None, ctypes.byref(h))
+        assert rc == status and not h.value
+    out = (ctypes.c_size_t * 4)()
+    assert lib.mac_ring_bytes(ctypes.byref(p), out) == status
+
+
 def test_front_sink_bounds(lib):
     assert mac.mac_workspace_bytes(_params(front_sink=4096)) > 0
     assert mac.mac_workspace_bytes(_params(front_sink=4097)) == 0
@@ -65,6 +93,8 @@ def test_front_sink_bounds(lib):
 def test_status_strings_and_chunk(lib):
     assert mac.mac_status_string(0) == "ok"
     assert "workspace" in mac.mac_status_string(-4)
+    assert "max_context" in mac.mac_status_string(-6)
+    assert "mac_init_rings" in mac.mac_status_string(-7)
     assert mac.mac_chunk_tokens(0, 63) == 64
     assert mac.mac_chunk_tokens(0, 64 * 128 - 1) == 64
     assert mac.mac_chunk_tokens(0, 64 * 128) == 128
@@ -119,7 +149,7 @@ def test_pointer_validation_happens_before_any_device_call(lib):
     assert rc == -4
     # Decode step with a NULL handle.
     assert lib.mac_decode_step(None, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000,
-                               0x1000, None, None, None, None, None) == -1
+                               0x1000, None, None, None, None, None) == -7
     # Init: more warm positions than ring slots, and a prompt shorter than W.
     rings = mac.mac_rings(0x1000, 0x2000, 0x3000, 0x4000)
     h = ctypes.c_void_p()
@@ -133,8 +163,10 @@ def test_pointer_validation_happens_before_any_device_call(lib):
                             0x7000, 0x8000, 512, ctx, 0x9000, 0xa000, None,
                             ctypes.byref(h))
     assert rc == -1
-    assert lib.mac_release(None) == -1
-    assert lib.mac_profile_start(None, 3) == -1
+    assert lib.mac_release(None) == -7
+    assert lib.mac_profile_start(None, 3) == -7
+    assert lib.mac_join_aux(None, None) == -7
+    assert lib.mac_bind_epochs(None, None) == -7
     f = ctypes.c_int32()
     assert lib.mac_read_device_status(ctypes.byref(p), None, None, ctypes.byref(f)) == -1
 

@@ -46,14 +46,19 @@ def _pool(X, P):
     return pool, table
 
 
-@pytest.mark.parametrize("cfg_id,append,launch,F,P", [
-    (2, "aux", "single", 0, 0), (2, "fused", "split", 0, 0), (3, "fused", "single", 0, 0),
-    (4, "aux", "single", 0, 0), (5, "fused", "single", 0, 0), (5, "aux", "split", 0, 0),
-    (2, "fused", "single", 128, 16), (5, "fused", "split", 64, 64)])
-def test_fullsize_config(oracle_lib, cfg_id, append, launch, F, P):
+TAU = 1  # mac.MAC_THRESH_TAU: distance < tau * sqrt(2d)
+
+
+@pytest.mark.parametrize("cfg_id,append,launch,F,P,mode", [
+    (2, "aux", "single", 0, 0, 0), (2, "fused", "split", 0, 0, 0),
+    (3, "fused", "single", 0, 0, 0), (3, "fused", "split", 0, 0, 0),
+    (4, "aux", "single", 0, 0, 0), (5, "fused", "single", 0, 0, 0),
+    (5, "aux", "split", 0, 0, 0), (5, "aux", "split", 0, 0, TAU),
+    (2, "fused", "single", 128, 16, 0), (5, "fused", "split", 64, 64, 0)])
+def test_fullsize_config(oracle_lib, cfg_id, append, launch, F, P, mode):
     cfg = wl.WORKLOADS[cfg_id]
-    print("full-size parity: config %d (%s), append=%s, launch=%s, front sink %d, page %d"
-          % (cfg_id, cfg.name, append, launch, F, P), flush=True)
+    print("full-size parity: config %d (%s), append=%s, launch=%s, front sink %d, page %d, "
+          "threshold mode %d" % (cfg_id, cfg.name, append, launch, F, P, mode), flush=True)
     K, V = wl.gen_kv(cfg)
     qt, q, _, sig = wl.gen_queries(cfg)
     flags = (mac.MAC_FLAG_FUSED_APPEND if append == "fused" else 0) | (
@@ -66,7 +71,7 @@ def test_fullsize_config(oracle_lib, cfg_id, append, launch, F, P):
         Hkv, d = cfg.n_kv_heads, cfg.head_dim
         paging = dict(page_size=P, max_pages=table.shape[1], page_table=table,
                       strides=(Hkv * P * d, P * d, d))
-    p = params_for(cfg, flags=flags, front_sink=F, **paging)
+    p = params_for(cfg, flags=flags, front_sink=F, thresh_mode=mode, **paging)
     layer = Layer(cfg, K, V, qt, q, params=p, kv_dev=kv_dev).init()
     gpu = run_steps(layer, cfg.steps, aux=torch.cuda.Stream() if append == "aux" else None)
     print("  gpu steps done", flush=True)
@@ -80,11 +85,23 @@ def test_fullsize_config(oracle_lib, cfg_id, append, launch, F, P):
     del vals
     assert gpu["out"].min() >= vmin - 1e-3 and gpu["out"].max() <= vmax + 1e-3
     rate = float((gpu["p"] >= 0).mean())
-    print("  hit rate %.4f" % rate, flush=True)
-    if cfg_id == 5:
+    grp_miss = float((gpu["p"].reshape(cfg.steps, cfg.batch, cfg.n_kv_heads, cfg.group) < 0)
+                     .any(axis=3).mean())
+    print("  hit rate %.4f, KV groups with a missing head %.4f" % (rate, grp_miss), flush=True)
+    if cfg_id == 5 and mode == 0:
         assert 0.6 < rate < 0.97
     else:
         assert rate > 0.95
+    # Match gaps m - p of the hits: the long-context workload with rare
+    # prototype switches reaches back across most of the K = 1024 window.
+    pos_all = wl.decode_positions(cfg)
+    gaps = (pos_all[:, :, None] - gpu["p"])[gpu["p"] >= 0]
+    pct = np.percentile(gaps, [50, 90, 99, 100])
+    print("  match gap m - p: median %d, p90 %d, p99 %d, max %d"
+          % tuple(int(x) for x in pct), flush=True)
+    assert gaps.min() >= 1 and gaps.max() <= cfg.ring_k
+    if cfg_id == 4:
+        assert gaps.max() > 512
 
     # Every miss head equals the full decode bit for bit.
     ws = torch.empty(layer.ws_bytes, dtype=torch.uint8, device=DEV)
@@ -110,7 +127,7 @@ def test_fullsize_config(oracle_lib, cfg_id, append, launch, F, P):
     # Sampled streams against the oracle in lock step.
     heads = _sample_heads(cfg, sig)
     W, nw = layer.n_warm, cfg.n_warm
-    t2 = oracle_lib.threshold2(cfg.head_dim, cfg.tau)
+    t2 = oracle_lib.threshold2(cfg.head_dim, cfg.tau, mode=mode)
     res = oracle_lib.run_streams(K, V, qt, q, heads, ctx_len=cfg.ctx, n_warm=W,
                                  ring_k=cfg.ring_k, band_r=cfg.band_r, thresh2=t2,
                                  want_ring=True, front_sink=F)
@@ -121,7 +138,9 @@ def test_fullsize_config(oracle_lib, cfg_id, append, launch, F, P):
     pr = layer.pos_ring.cpu().numpy()
     diverged = 0
     for (b, h), o in res.items():
-        n, ex, div = lockstep_compare(cfg, gpu, o, b, h, cfg.steps)
+        # At most one sampled stream may leave lock step, at an exempt point
+        # (printed with its distances by lockstep_compare).
+        n, ex, div = lockstep_compare(cfg, gpu, o, b, h, cfg.steps, allow_diverge=True)
         if div is not None:
             diverged += 1
             print("  stream (%d,%d) left lock step at exempt step %d" % (b, h, div), flush=True)

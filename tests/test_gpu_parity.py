@@ -88,23 +88,26 @@ def test_full_decode_any_workspace_contents():
         assert np.array_equal(o, outs[0])
 
 
-def _lockstep(oracle_lib, cfg, layer=None, heads=None, n_warm=None, want_ring=True):
+def _lockstep(oracle_lib, cfg, layer=None, heads=None, n_warm=None, want_ring=True,
+              thresh_mode=0, min_context=0, flags=0):
     K, V, qt, q = _inputs(cfg)
-    layer = layer or Layer(cfg, K, V, qt, q, n_warm=n_warm)
+    layer = layer or Layer(cfg, K, V, qt, q, n_warm=n_warm,
+                           params=params_for(cfg, thresh_mode=thresh_mode,
+                                             min_context=min_context, flags=flags))
     layer.init()
     aux = torch.cuda.Stream()
     gpu = run_steps(layer, cfg.steps, aux=aux)
     heads = heads or [(b, h) for b in range(cfg.batch) for h in range(cfg.n_q_heads)]
     W = layer.n_warm
     nw = cfg.n_warm
-    t2 = oracle_lib.threshold2(cfg.head_dim, cfg.tau)
+    t2 = oracle_lib.threshold2(cfg.head_dim, cfg.tau, mode=thresh_mode)
     res = {}
     for (b, h) in heads:
         g = h // cfg.group
         res[(b, h)] = oracle_lib.run_stream(
             K[b, g], V[b, g], qt[b, h, nw - W:nw], q[b, h, nw - W:nw], qt[b, h, nw:],
             q[b, h, nw:], ctx_len=cfg.ctx, ring_k=cfg.ring_k, band_r=cfg.band_r,
-            thresh2=t2, want_ring=want_ring)
+            thresh2=t2, want_ring=want_ring, min_context=min_context)
     stats = dict(hits=0, steps=0, exempt=0, diverged=0)
     qr = layer.q_ring.cpu().float().numpy() if want_ring else None
     orr = layer.o_ring.cpu().numpy() if want_ring else None
@@ -299,3 +302,92 @@ def test_bad_position_is_flagged_not_faulted():
     after = layer.pos_ring.cpu().numpy()
     assert np.array_equal(after[1], before[1])          # no append for request 1
     assert mac.mac_read_device_status(layer.p, layer.ws) == 0
+
+
+@pytest.mark.parametrize("flags", [0, mac.MAC_FLAG_SPLIT_STAGES])
+def test_lockstep_tau_threshold_rule(oracle_lib, flags):
+    """The acceptance rule distance < tau * sqrt(2d) (MAC_THRESH_TAU; the
+    paper summary's "Core method" form) against the oracle's threshold in
+    the same mode, with per-head noise chosen so that both hits and misses
+    occur under it, one launch and three kernels."""
+    cfg = _cfg(batch=2, ctx=1500, steps=24, ring_k=128, band_r=48, sigma=(0.3, 0.9), seed=11)
+    _, _, st, _ = _lockstep(oracle_lib, cfg, thresh_mode=mac.MAC_THRESH_TAU, flags=flags)
+    rate = st["hits"] / st["steps"]
+    assert st["diverged"] == 0 and 0.2 < rate < 0.95, rate
+
+
+@pytest.mark.parametrize("flags", [0, mac.MAC_FLAG_SPLIT_STAGES | mac.MAC_FLAG_FUSED_APPEND])
+def test_lockstep_min_context(oracle_lib, flags):
+    """Reuse off below the minimum context, decided on the device per
+    request: positions cross the limit during the run (requests at
+    different positions too), and the blocked steps still fill the rings."""
+    cfg = _cfg(batch=2, ctx=1200, steps=24, ring_k=64, band_r=16, sigma=(0.02, 0.2), seed=2)
+    lim = cfg.ctx + 10
+    gpu, res, st, _ = _lockstep(oracle_lib, cfg, min_context=lim, flags=flags)
+    s0 = lim - cfg.ctx
+    assert (gpu["p"][:s0] == -1).all() and np.isinf(gpu["d2"][:s0]).all()
+    assert (gpu["p"][s0:] >= 0).mean() > 0.5
+    assert st["diverged"] == 0
+
+
+def test_aux_append_ignores_pos_overwritten_after_the_call():
+    """The rectify-append on the auxiliary stream appends at the position
+    the step's merge recorded, not at whatever the caller's position array
+    holds when the append runs: here main_stream overwrites the array right
+    after every call while the auxiliary stream is held back by other work,
+    and the rings and outputs still equal the fused append's."""
+    cfg = _cfg(batch=2, steps=10, sigma=(0.02, 0.5))
+    K, V, qt, q = _inputs(cfg)
+    ref_layer = Layer(cfg, K, V, qt, q, params=params_for(cfg, flags=mac.MAC_FLAG_FUSED_APPEND))
+    ref = run_steps(ref_layer.init(), cfg.steps)
+    ref_rings = [t.cpu().float().numpy() for t in
+                 (ref_layer.q_ring, ref_layer.o_ring, ref_layer.lse_ring, ref_layer.pos_ring)]
+    ref_layer.release()
+    for flags in (0, mac.MAC_FLAG_SPLIT_STAGES):
+        layer = Layer(cfg, K, V, qt, q, params=params_for(cfg, flags=flags)).init()
+        aux = torch.cuda.Stream()
+        ms = torch.cuda.current_stream()
+        pos_all = torch.from_numpy(wl.decode_positions(cfg)).to(DEV)
+        pos = torch.empty(cfg.batch, dtype=torch.int32, device=DEV)
+        out = torch.empty((cfg.steps, cfg.batch, cfg.n_q_heads, cfg.head_dim), device=DEV)
+        busy = torch.empty(1 << 24, device=DEV)
+        for s in range(cfg.steps):
+            with torch.cuda.stream(aux):
+                for _ in range(4):  # keeps the auxiliary stream busy
+                    busy.mul_(1.0001)
+            pos.copy_(pos_all[s])
+            mac.mac_decode_step(layer.handle, layer.dec_qt[s], layer.dec_q[s], layer.K,
+                                layer.V, pos, out[s], None, None, None, ms.cuda_stream,
+                                aux.cuda_stream)
+            pos.add_(1)  # a valid but different position, before the append runs
+        mac.mac_join_aux(layer.handle, ms.cuda_stream)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref["out"]), flags
+        rings = [t.cpu().float().numpy() for t in
+                 (layer.q_ring, layer.o_ring, layer.lse_ring, layer.pos_ring)]
+        for x, y in zip(rings, ref_rings):
+            assert np.array_equal(x, y), flags
+        layer.release()
+
+
+def test_full_decode_long_range_matches_oracle(oracle_lib):
+    """One request at a 128K-token range (131001 tokens): the split-KV grid
+    is 1024 tokens (128 cells), checked against the oracle head by head."""
+    cfg = _cfg(batch=1, ctx=131000, steps=2, ring_k=64, band_r=16)
+    K, V = wl.gen_kv(cfg)
+    qt, q, _, _ = wl.gen_queries(cfg)
+    assert mac.mac_chunk_tokens(0, cfg.ctx) == 1024 and mac.mac_chunk_tokens(0, 131072) == 2048
+    p = params_for(cfg)
+    ws_b = mac.mac_workspace_bytes(p)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=DEV)
+    m = np.array([cfg.ctx], np.int32)
+    qq = q[:, :, cfg.n_warm]
+    out = torch.empty((1, cfg.n_q_heads, cfg.head_dim), device=DEV)
+    lse = torch.empty((1, cfg.n_q_heads), device=DEV)
+    mac.mac_full_decode(p, to_dev(qq), to_dev(K), to_dev(V), to_dev(m), out, lse, ws, ws_b,
+                        torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_lib.full_decode(qq, K, V, m)
+    ok, err = tolerance_check(cfg, out.cpu().numpy(), ref_o)
+    assert ok, err
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_l, atol=1e-4)

@@ -269,26 +269,94 @@ def test_hit_path_piecewise_closed_form(oracle_lib, kw):
         np.testing.assert_allclose(res["out"], ref, atol=2e-6, rtol=0)
 
 
+EXEMPT = 1e-4  # decision-exemption band on distances (the parity rule)
+
+
+def _brute_match(cfg, qv, s, t2):
+    """Brute force of step s's match from the stored pre-RoPE queries qv
+    [W+S, d] (warm part first): every candidate position's squared distance,
+    the decision, the runner-up distance and the exemption flag."""
+    W, L = cfg.n_warm, cfg.ctx
+    m = L + s
+    cand = [t for t in range(max(L - W, m - cfg.ring_k), m)]
+    D = {t: float(((qv[W + s] - qv[t - (L - W)]) ** 2).sum()) for t in cand}
+    if not cand:
+        return dict(hit=False, p=-1, dist=math.inf, dist2=math.inf, exempt=False)
+    best = min(cand, key=lambda t: (D[t], -t))
+    others = [D[t] for t in cand if t != best]
+    d1 = math.sqrt(D[best])
+    d2 = math.sqrt(min(others)) if others else math.inf
+    # Several decisions are correct when the nearest distance lies within the
+    # band of the threshold, or the runner-up lies within it of the nearest.
+    exempt = abs(d1 - math.sqrt(t2)) < EXEMPT or (d2 - d1) < EXEMPT
+    hit = D[best] < t2
+    return dict(hit=hit, p=best if hit else -1, dist=d1, dist2=d2, exempt=exempt)
+
+
+def _check_decisions(cfg, res, qt, t2, steps=None):
+    qv = wl.from_storage(qt)
+    n_ex = 0
+    for s in range(cfg.steps if steps is None else steps):
+        ref = _brute_match(cfg, qv, s, t2)
+        assert bool(res["hit"][s]) == ref["hit"], s
+        assert res["p"][s] == ref["p"], s
+        assert res["dist"][s] == ref["dist"] or abs(res["dist"][s] - ref["dist"]) < 1e-12, s
+        assert (res["dist2"][s] == ref["dist2"]
+                or abs(res["dist2"][s] - ref["dist2"]) < 1e-12), (s, res["dist2"][s], ref["dist2"])
+        assert bool(res["exempt"][s]) == ref["exempt"], s
+        n_ex += ref["exempt"]
+    return n_ex
+
+
 @pytest.mark.parametrize("kw", [dict(), dict(dtype="bf16", ring_k=5),
                                 dict(n_protos=2, sigma=(0.3, 0.3), ring_k=12)])
 def test_match_decisions_brute_force(oracle_lib, kw):
     """Nearest pre-RoPE query among the last K positions, ties to the larger
-    position, accepted when the squared distance is below the threshold."""
+    position, accepted when the squared distance is below the threshold; the
+    runner-up distance and the exemption flag against brute force too."""
     cfg = _small(**kw)
     t2 = oracle_lib.threshold2(cfg.head_dim, cfg.tau)
     for h in range(cfg.n_q_heads):
         res, K, V, qt, q = _stream(oracle_lib, cfg, h=h)
-        qv = wl.from_storage(qt)
-        W, L = cfg.n_warm, cfg.ctx
-        for s in range(cfg.steps):
-            m = L + s
-            cand = [t for t in range(max(L - W, m - cfg.ring_k), m)]
-            D = {t: float(((qv[W + s] - qv[t - (L - W)]) ** 2).sum()) for t in cand}
-            best = min(cand, key=lambda t: (D[t], -t))
-            hit = D[best] < t2
-            assert bool(res["hit"][s]) == hit
-            assert res["p"][s] == (best if hit else -1)
-            assert abs(res["dist"][s] - math.sqrt(D[best])) < 1e-12
+        n_ex = _check_decisions(cfg, res, qt, t2)
+        # These streams are far from every tie and from the threshold.
+        assert n_ex < cfg.steps // 2
+
+
+def test_exemption_near_ties_and_threshold(oracle_lib):
+    """Both exemption cases against brute force.  An exact repeat (one
+    prototype, no noise) puts every candidate at distance 0: each step is a
+    tie.  A threshold set just above / below a step's nearest squared distance
+    puts that distance within the band of the threshold."""
+    cfg = _small(n_protos=1, sigma=(0.0, 0.0), switch_p=0.0, steps=8)
+    t2 = oracle_lib.threshold2(cfg.head_dim, cfg.tau)
+    res, K, V, qt, q = _stream(oracle_lib, cfg)
+    assert _check_decisions(cfg, res, qt, t2) == cfg.steps
+    assert (res["dist2"] == 0.0).all()
+    # Threshold proximity: noise keeps candidates apart (no ties).
+    cfg = _small(n_protos=2, sigma=(0.3, 0.3), steps=6, ring_k=12)
+    K, V = wl.gen_kv(cfg)
+    qt, q, _, _ = wl.gen_queries(cfg)
+    qv = wl.from_storage(qt[0, 0])
+    near = _brute_match(cfg, qv, 0, 1e30)
+    for delta in (+3e-5, -3e-5, +5e-3):
+        t2 = (near["dist"] + delta) ** 2
+        res, *_ = _stream(oracle_lib, cfg, thresh2=t2)
+        _check_decisions(cfg, res, qt[0, 0], t2)
+        assert bool(res["exempt"][0]) == (abs(delta) < EXEMPT or near["dist2"] - near["dist"] < EXEMPT)
+        assert bool(res["hit"][0]) == (delta > 0)
+
+
+def test_exemption_cold_ring(oracle_lib):
+    """No candidate (cold ring, first step): a miss, both distances +inf,
+    nothing exempt."""
+    cfg = _small(steps=3)
+    t2 = oracle_lib.threshold2(cfg.head_dim, cfg.tau)
+    res, *_ = _stream(oracle_lib, cfg, W=0)
+    assert not res["hit"][0] and res["dist"][0] == math.inf
+    assert res["dist2"][0] == math.inf and not res["exempt"][0]
+    # Second step: exactly one candidate, so no runner-up.
+    assert res["dist2"][1] == math.inf and math.isfinite(res["dist"][1])
 
 
 def _ring_trace_rows():
@@ -329,3 +397,39 @@ def test_nan_slot_never_selected(oracle_lib):
                                 q[0, 0, W:], ctx_len=cfg.ctx, ring_k=cfg.ring_k,
                                 band_r=cfg.band_r, thresh2=1e9, n_steps=1)
     assert not res["hit"][0] and res["dist"][0] == math.inf
+
+
+def test_min_context_blocks_reuse_below_the_limit(oracle_lib):
+    """Reuse is off below the minimum context: with the limit above every
+    position the stream equals the forced miss (threshold 0) exactly, rings
+    included; with the limit crossed mid-run, the steps below it look at no
+    candidate, the later ones follow the brute-force match over a ring that
+    the blocked steps kept filling, and every output follows the piecewise
+    closed form."""
+    cfg = _small(steps=24)
+    t2 = oracle_lib.threshold2(cfg.head_dim, cfg.tau)
+    blocked, *_ = _stream(oracle_lib, cfg, want_ring=True, min_context=cfg.ctx + cfg.steps)
+    miss, *_ = _stream(oracle_lib, cfg, thresh2=0.0, want_ring=True)
+    assert not blocked["hit"].any() and (blocked["dist"] == math.inf).all()
+    assert not blocked["exempt"].any()
+    for k in ("out", "lse", "ring_pos", "ring_q", "ring_o", "ring_lse"):
+        assert np.array_equal(blocked[k], miss[k]), k
+    lim = cfg.ctx + 9
+    for h in range(cfg.n_q_heads):
+        res, K, V, qt, q = _stream(oracle_lib, cfg, h=h, min_context=lim)
+        s0 = lim - cfg.ctx
+        assert not res["hit"][:s0].any() and (res["dist"][:s0] == math.inf).all()
+        qv = wl.from_storage(qt)
+        for s in range(s0, cfg.steps):
+            ref = _brute_match(cfg, qv, s, t2)
+            assert (bool(res["hit"][s]), int(res["p"][s])) == (ref["hit"], ref["p"]), s
+            assert bool(res["exempt"][s]) == ref["exempt"]
+        assert res["hit"][s0:].any()
+        ref = _owner_closed_form(cfg, res, q, K, V)
+        np.testing.assert_allclose(res["out"], ref, atol=2e-6, rtol=0)
+        # Below the limit each output is full attention (torch softmax).
+        for s in range(s0):
+            m = cfg.ctx + s
+            full, _ = _softmax_attend(q[cfg.n_warm + s], K[:m + 1], V[:m + 1],
+                                      1 / math.sqrt(cfg.head_dim))
+            np.testing.assert_allclose(res["out"][s], full, atol=1e-12)
