@@ -294,6 +294,8 @@ const char *mac_status_string(mac_status s)
         return "kv_capacity exceeds max_context";
     case MAC_ERR_NOT_INITIALIZED:
         return "handle not initialised by mac_init_rings (or released)";
+    case MAC_ERR_SCRATCH_TOO_SMALL:
+        return "shape needs more than the static scratch (MAC_NOALLOC_SCRATCH_BYTES, 48 MiB)";
     }
     return "unknown status";
 }
@@ -346,6 +348,31 @@ static StepArgs base_args(const Shape &s, const WsLayout &L, const WsPtrs &w)
     return a;
 }
 
+// Full decode into the workspace at ws (laid out without the single-launch
+// regions): the plan + attention kernel, then the merge.
+static mac_status full_decode_on(const Shape &s, void *ws, const float *q, const void *k_cache,
+                                 const void *v_cache, const int32_t *pos, float *out,
+                                 float *out_lse, hipStream_t st)
+{
+    const WsLayout L = ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T, s.dtype, false);
+    StepArgs a = base_args(s, L, ws_ptrs(ws, L));
+    a.mode = kPlanFull;
+    // A caller's workspace may be fresh: full decode splits its (regular)
+    // work statically and claims nothing.
+    a.dyn_pool = 0;
+    a.pos = pos;
+    a.q = q;
+    a.q_sh = s.D;
+    a.q_sb = (int64_t)s.Hq * s.D;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.out = out;
+    a.out_lse = out_lse;
+    MAC_HIP(launch_attend(a, st));
+    MAC_HIP(launch_merge(a, st));
+    return MAC_OK;
+}
+
 mac_status mac_full_decode(const mac_params *p, const float *q,
                            const void *k_cache, const void *v_cache,
                            const int32_t *pos, float *out, float *out_lse,
@@ -364,24 +391,29 @@ mac_status mac_full_decode(const mac_params *p, const float *q,
     // that precede the single-launch ones.
     if (ws_bytes < layout_for(p, s).total)
         return MAC_ERR_WORKSPACE_TOO_SMALL;
-    const WsLayout L = ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T, s.dtype, false);
-    StepArgs a = base_args(s, L, ws_ptrs(workspace, L));
-    a.mode = kPlanFull;
-    // A caller's workspace may be fresh: full decode splits its (regular)
-    // work statically and claims nothing.
-    a.dyn_pool = 0;
-    a.pos = pos;
-    a.q = q;
-    a.q_sh = s.D;
-    a.q_sb = (int64_t)s.Hq * s.D;
-    a.k = k_cache;
-    a.v = v_cache;
-    a.out = out;
-    a.out_lse = out_lse;
-    hipStream_t st = (hipStream_t)stream;
-    MAC_HIP(launch_attend(a, st));
-    MAC_HIP(launch_merge(a, st));
-    return MAC_OK;
+    return full_decode_on(s, workspace, q, k_cache, v_cache, pos, out, out_lse,
+                          (hipStream_t)stream);
+}
+
+mac_status mac_full_decode_noalloc(const mac_params *p, const float *q,
+                                   const void *k_cache, const void *v_cache,
+                                   const int32_t *pos, float *out, float *out_lse,
+                                   void *stream)
+{
+    Shape s;
+    mac_status rc = check_params(p, &s);
+    if (rc != MAC_OK)
+        return rc;
+    if (!q || !k_cache || !v_cache || !pos || !out)
+        return MAC_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return MAC_ERR_MISALIGNED;
+    if (ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T, s.dtype, false).total >
+        MAC_NOALLOC_SCRATCH_BYTES)
+        return MAC_ERR_SCRATCH_TOO_SMALL;
+    void *scr = nullptr;
+    MAC_HIP(noalloc_scratch(&scr));
+    return full_decode_on(s, scr, q, k_cache, v_cache, pos, out, out_lse, (hipStream_t)stream);
 }
 
 mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,

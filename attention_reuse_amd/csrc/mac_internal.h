@@ -367,6 +367,9 @@ hipError_t launch_ring_reset(const Shape &s, void *q_ring, float *o_ring,
                              float *lse_ring, int32_t *pos_ring, const WsPtrs &w,
                              int64_t n_tag, hipStream_t st);
 int device_cu_count();
+// Address of this device's static scratch (MAC_NOALLOC_SCRATCH_BYTES), looked
+// up once per device with that device current.
+hipError_t noalloc_scratch(void **ptr);
 // Streaming read of a buffer (bandwidth measurement); sink holds grid floats.
 hipError_t launch_stream_read(const void *buf, size_t bytes, float *sink, int grid,
                               hipStream_t st);

@@ -45,6 +45,7 @@
 // 16 columns), which removes most of the VALU work per token.
 #include <math.h>
 
+#include <mutex>
 #include <utility>
 
 #include "mac_attention.h"
@@ -2630,6 +2631,35 @@ __global__ __launch_bounds__(kBlock) void stream_read_kernel(const u32x4 *__rest
 }
 
 }  // namespace
+
+// Workspace of the entry points that allocate nothing: one array per GPU
+// (each device holds its own copy, at its own address).  Host code never
+// passes `scratch` itself to a kernel -- on the host the name is only a
+// stand-in; kernels get the device address that noalloc_scratch looked up.
+static __device__ __align__(256) unsigned char scratch[MAC_NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void **ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_stream_read(const void *buf, size_t bytes, float *sink, int grid,
                               hipStream_t st)

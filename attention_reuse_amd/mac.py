@@ -29,9 +29,11 @@ MAC_FLAG_MATCH_FILTER = 8
 STATUS = {0: "MAC_OK", -1: "MAC_ERR_INVALID_ARG", -2: "MAC_ERR_UNSUPPORTED",
           -3: "MAC_ERR_HIP", -4: "MAC_ERR_WORKSPACE_TOO_SMALL",
           -5: "MAC_ERR_MISALIGNED", -6: "MAC_ERR_CONTEXT_TOO_LONG",
-          -7: "MAC_ERR_NOT_INITIALIZED"}
+          -7: "MAC_ERR_NOT_INITIALIZED", -8: "MAC_ERR_SCRATCH_TOO_SMALL"}
 MAC_ERR_CONTEXT_TOO_LONG = -6
 MAC_ERR_NOT_INITIALIZED = -7
+MAC_ERR_SCRATCH_TOO_SMALL = -8
+MAC_NOALLOC_SCRATCH_BYTES = 48 << 20
 STAGES = ("match", "attend", "merge", "append", "step")
 
 
@@ -91,6 +93,7 @@ def load():
                                          _vp]),
         "mac_full_decode": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                            ctypes.c_size_t, _vp]),
+        "mac_full_decode_noalloc": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
         "mac_read_device_status": (ctypes.c_int, [_P, _vp, _vp,
                                                   ctypes.POINTER(ctypes.c_int32)]),
         "mac_profile_start": (ctypes.c_int, [_vp, ctypes.c_int32]),
@@ -202,6 +205,13 @@ def mac_full_decode(p: mac_params, q, k_cache, v_cache, pos, out, out_lse,
     _check("mac_full_decode", load().mac_full_decode(
         ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(pos),
         _ptr(out), _ptr(out_lse), _ptr(workspace), int(ws_bytes), stream))
+
+
+def mac_full_decode_noalloc(p: mac_params, q, k_cache, v_cache, pos, out, out_lse,
+                            stream=None):
+    _check("mac_full_decode_noalloc", load().mac_full_decode_noalloc(
+        ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(pos), _ptr(out),
+        _ptr(out_lse), stream))
 
 
 def mac_read_device_status(p: mac_params, workspace, stream=None) -> int:

@@ -51,9 +51,17 @@ typedef enum mac_status {
     MAC_ERR_WORKSPACE_TOO_SMALL = -4, /* ws_bytes < mac_workspace_bytes()   */
     MAC_ERR_MISALIGNED = -5,          /* a buffer or row not 16-B aligned   */
     MAC_ERR_CONTEXT_TOO_LONG = -6,    /* kv_capacity > max_context          */
-    MAC_ERR_NOT_INITIALIZED = -7      /* handle NULL, released, or not made
+    MAC_ERR_NOT_INITIALIZED = -7,     /* handle NULL, released, or not made
                                          by mac_init_rings                  */
+    MAC_ERR_SCRATCH_TOO_SMALL = -8    /* the shape needs more than the
+                                         library's static scratch
+                                         (MAC_NOALLOC_SCRATCH_BYTES)        */
 } mac_status;
+
+/* Size of the device scratch that mac_full_decode_noalloc uses instead of a
+ * workspace: one static array per GPU, held from the library's first use on
+ * that GPU until the process ends. */
+#define MAC_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
 
 /* Element type of the K/V cache, of the pre-RoPE queries and of the query
  * ring.  Post-RoPE queries, outputs and summaries are always fp32. */
@@ -316,6 +324,26 @@ mac_status mac_full_decode(const mac_params *p, const float *q,
                            const void *k_cache, const void *v_cache,
                            const int32_t *pos, float *out, float *out_lse,
                            void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * mac_full_decode_noalloc -- mac_full_decode without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Arguments and results as mac_full_decode, bit for bit (the same kernels on
+ * the same partition).  The partials live in a static device array of
+ * MAC_NOALLOC_SCRATCH_BYTES per GPU, inside the library; shapes whose
+ * mac_full_decode workspace (without the single-launch regions) exceeds it
+ * return MAC_ERR_SCRATCH_TOO_SMALL before any launch.  The call allocates
+ * nothing: the first call on a device (with that device current) only looks
+ * up the array's address.  Every call on one GPU shares that GPU's array, so
+ * calls that overlap on one GPU (concurrent streams, threads) race and must
+ * be serialised by the caller; calls on different GPUs are independent.
+ * Device-side position errors give NaN outputs and are not reported.
+ */
+mac_status mac_full_decode_noalloc(const mac_params *p, const float *q,
+                                   const void *k_cache, const void *v_cache,
+                                   const int32_t *pos, float *out, float *out_lse,
+                                   void *stream);
 
 /* Read (with a synchronisation of `stream`) and clear the device status
  * flags (MAC_DEV_*) of a workspace laid out for p: MAC_DEV_BAD_POSITION of

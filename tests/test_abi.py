@@ -227,3 +227,20 @@ def test_group_items_with_front_sink(lib, s, e, r, F):
         assert items == mac.mac_partition(s, e, r)
     assert lib.mac_group_items(5, 4, 0, 0, None, None, None, 0) == -1
     assert lib.mac_group_items(0, 4, 0, 4097, None, None, None, 0) == -1
+
+
+def test_noalloc_full_decode_rejects_before_any_device_call(lib):
+    """The allocation-free full decode checks its arguments and the scratch
+    size on the host: a shape needing more than the static scratch is
+    refused with its own status, before any launch."""
+    big = _params(batch=48)   # 384 KV groups: ~100 MiB of partials
+    assert mac.mac_workspace_bytes(big) > mac.MAC_NOALLOC_SCRATCH_BYTES
+    rc = lib.mac_full_decode_noalloc(ctypes.byref(big), 0x1000, 0x2000, 0x3000, 0x4000,
+                                     0x5000, None, None)
+    assert rc == mac.MAC_ERR_SCRATCH_TOO_SMALL
+    assert "scratch" in mac.mac_status_string(rc)
+    p = _params()
+    assert lib.mac_full_decode_noalloc(ctypes.byref(p), 0x1000, 0x2000, 0x3000, 0x4000,
+                                       None, None, None) == -1
+    assert lib.mac_full_decode_noalloc(ctypes.byref(p), 0x1004, 0x2000, 0x3000, 0x4000,
+                                       0x5000, None, None) == -5
