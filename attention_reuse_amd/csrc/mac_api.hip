@@ -30,6 +30,12 @@ static int64_t single_tag_words(int B, int Hkv)
     return (int64_t)kKeyReps * B * Hkv * kMaxSingleUnits;
 }
 
+// 64-bit words of the single launch's two pool sets.
+static int64_t single_pool_words(int B, int Hkv)
+{
+    return 2 * ((int64_t)kPoolLine + (int64_t)B * Hkv * kItemsPerGroupMax);
+}
+
 WsLayout ws_layout(int B, int Hq, int Hkv, int D, int K, int T, int dtype, bool single)
 {
     WsLayout L;
@@ -43,7 +49,8 @@ WsLayout ws_layout(int B, int Hq, int Hkv, int D, int K, int T, int dtype, bool 
         return o;
     };
     const size_t BH = (size_t)B * Hq, BG = (size_t)B * Hkv;
-    L.keys = take(BH * kKeyStride * sizeof(unsigned long long));
+    // Two sets of per-head match keys (the two-kernel form alternates them).
+    L.keys = take(2 * BH * kKeyStride * sizeof(unsigned long long));
     L.ctx = take((size_t)B * 4);
     L.dec_slot = take(BH * 4);
     L.grp_begin = take(BG * 4);
@@ -60,10 +67,12 @@ WsLayout ws_layout(int B, int Hq, int Hkv, int D, int K, int T, int dtype, bool 
     L.app_pos = take(BG * 4);
     // The single-launch regions come last, so the layout without them is a
     // prefix of the layout with them.
-    L.skeys = L.grp_sync = 0;
+    L.skeys = L.grp_sync = L.pool = L.gplan = 0;
     if (single) {
         L.skeys = take(single_tag_words(B, Hkv) * sizeof(unsigned long long));
         L.grp_sync = take(BG * kGrpStride * sizeof(uint32_t));
+        L.pool = take(single_pool_words(B, Hkv) * sizeof(unsigned long long));
+        L.gplan = take(BG * kPlanWords * sizeof(int32_t));
     }
     L.total = off;
     return L;
@@ -90,6 +99,8 @@ WsPtrs ws_ptrs(void *base, const WsLayout &L)
     w.app_pos = (int32_t *)(c + L.app_pos);
     w.skeys = L.skeys ? (unsigned long long *)(c + L.skeys) : nullptr;
     w.grp_sync = L.grp_sync ? (uint32_t *)(c + L.grp_sync) : nullptr;
+    w.pool = L.pool ? (unsigned long long *)(c + L.pool) : nullptr;
+    w.gplan = L.gplan ? (int32_t *)(c + L.gplan) : nullptr;
     return w;
 }
 
@@ -112,7 +123,7 @@ struct mac_handle {
     void *ws;
     mac_rings rings;
     bool fused_append;
-    bool split_stages;
+    int form;  // kFormThree, kFormOne or kFormTwo
     int32_t wpg, upg, nkw, done_shift, unit_slots, nsplit;  // single-launch geometry
     const int32_t *epoch = nullptr;  // bound by mac_bind_epochs
     hipEvent_t ev_main = nullptr, ev_aux = nullptr;
@@ -137,8 +148,10 @@ static mac_status check_params(const mac_params *p, Shape *s)
         p->n_q_heads % p->n_kv_heads != 0 || p->ring_k < 1 ||
         p->band_r < 0 || p->kv_capacity < 1 ||
         (p->flags & ~(MAC_FLAG_FUSED_APPEND | MAC_FLAG_SPLIT_STAGES |
-                      MAC_FLAG_SINGLE_LAUNCH | MAC_FLAG_MATCH_FILTER)) != 0 ||
-        (p->flags & MAC_FLAG_SPLIT_STAGES && p->flags & MAC_FLAG_SINGLE_LAUNCH) ||
+                      MAC_FLAG_SINGLE_LAUNCH | MAC_FLAG_MATCH_FILTER |
+                      MAC_FLAG_TWO_STAGES)) != 0 ||
+        __builtin_popcount(p->flags & (MAC_FLAG_SPLIT_STAGES | MAC_FLAG_SINGLE_LAUNCH |
+                                       MAC_FLAG_TWO_STAGES)) > 1 ||
         !isfinite(p->tau) || !isfinite(p->sm_scale) || p->sm_scale < 0.f ||
         p->front_sink < 0 || p->front_sink > kMaxFrontSink ||
         (p->thresh_mode != MAC_THRESH_ONE_MINUS_TAU &&
@@ -214,6 +227,8 @@ static mac_status check_params(const mac_params *p, Shape *s)
         s->T = p->kv_capacity;
         s->F = p->front_sink;
         s->min_ctx = p->min_context;
+        s->cmin = (int64_t)p->batch * p->n_kv_heads > kSingleLaunchMaxGroups ? kChunkMinShiftWide
+                                                                              : kChunkMinShift;
         s->page_shift = paged ? shift : 0;
         s->max_pages = paged ? p->max_pages : 0;
         s->page_table = paged ? p->page_table : nullptr;
@@ -234,19 +249,32 @@ static bool single_launch_supported(const Shape &s)
            s.G * single_min_nsplit(s.K, s.dtype, s.D) <= kMaxSingleUnits;
 }
 
-// Whether a handle for p may run the single launch: not forced to three
-// kernels, at most kSingleLaunchMaxGroups KV groups unless forced, and
-// positions that the tagged keys encode.
-static bool single_launch_form(const mac_params *p, const Shape &s)
+// The forms of a step: match, plan + attention and merge as three kernels;
+// all in one launch; the match kernel, then plan, attention and merge in one.
+enum { kFormThree = 0, kFormOne = 1, kFormTwo = 2 };
+
+// The form a handle for p runs, before the residency check of
+// mac_init_rings: the one its flags force, else one launch for at most
+// kSingleLaunchMaxGroups KV groups and three kernels above, where shapes
+// allow.  The one- and two-kernel forms need positions that the tagged keys
+// and pool entries encode; the one-launch form also needs the group's match
+// units to fit its LDS.
+static int step_form(const mac_params *p, const Shape &s)
 {
-    if (p->flags & MAC_FLAG_SPLIT_STAGES || !single_launch_supported(s))
-        return false;
-    return (p->flags & MAC_FLAG_SINGLE_LAUNCH) || s.B * s.Hkv <= kSingleLaunchMaxGroups;
+    if (p->flags & MAC_FLAG_SPLIT_STAGES)
+        return kFormThree;
+    if (p->flags & MAC_FLAG_TWO_STAGES)
+        return s.T <= kSingleMaxPositions ? kFormTwo : kFormThree;
+    if (!single_launch_supported(s))
+        return kFormThree;
+    return (p->flags & MAC_FLAG_SINGLE_LAUNCH) || s.B * s.Hkv <= kSingleLaunchMaxGroups
+               ? kFormOne
+               : kFormThree;
 }
 
 static WsLayout layout_for(const mac_params *p, const Shape &s)
 {
-    return ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T, s.dtype, single_launch_form(p, s));
+    return ws_layout(s.B, s.Hq, s.Hkv, s.D, s.K, s.T, s.dtype, step_form(p, s) != kFormThree);
 }
 
 extern "C" {
@@ -300,28 +328,47 @@ const char *mac_status_string(mac_status s)
     return "unknown status";
 }
 
-int32_t mac_chunk_tokens(int32_t s, int32_t e)
+// log2 of a valid minimum chunk (a power of two in [64, 2^20]), else -1.
+static int chunk_shift_of(int32_t min_chunk)
 {
-    return (s < 0 || e < s) ? -1 : RangeSplit::chunk_for(s, e);
+    for (int sh = kChunkMinShift; sh <= 20; ++sh)
+        if (min_chunk == (1 << sh))
+            return sh;
+    return -1;
 }
 
-int32_t mac_partition(int32_t s, int32_t e, int32_t r, int32_t *t0,
+int32_t mac_min_chunk_tokens(const mac_params *p)
+{
+    Shape s;
+    return check_params(p, &s) == MAC_OK ? 1 << s.cmin : -1;
+}
+
+int32_t mac_chunk_tokens(int32_t s, int32_t e, int32_t min_chunk)
+{
+    const int cm = chunk_shift_of(min_chunk);
+    return (s < 0 || e < s || cm < 0) ? -1 : RangeSplit::chunk_for(s, e, cm);
+}
+
+int32_t mac_partition(int32_t s, int32_t e, int32_t r, int32_t min_chunk, int32_t *t0,
                       int32_t *t1, int32_t cap)
 {
-    if (s < 0 || e < s || r < 0 || cap < 0)
+    const int cm = chunk_shift_of(min_chunk);
+    if (s < 0 || e < s || r < 0 || cap < 0 || cm < 0)
         return -1;
-    const RangeSplit rs(s, e, r);
+    const RangeSplit rs(s, e, r, RangeSplit::chunk_shift_for(s, e, cm));
     for (int i = 0; i < rs.n && i < cap; ++i)
         rs.item(i, t0[i], t1[i]);
     return rs.n;
 }
 
-int32_t mac_group_items(int32_t s, int32_t e, int32_t r, int32_t front_sink, int32_t *t0,
-                        int32_t *t1, int32_t *n_before_split, int32_t cap)
+int32_t mac_group_items(int32_t s, int32_t e, int32_t r, int32_t front_sink, int32_t min_chunk,
+                        int32_t *t0, int32_t *t1, int32_t *n_before_split, int32_t cap)
 {
-    if (s < 0 || e < s || r < 0 || cap < 0 || front_sink < 0 || front_sink > kMaxFrontSink)
+    const int cm = chunk_shift_of(min_chunk);
+    if (s < 0 || e < s || r < 0 || cap < 0 || front_sink < 0 || front_sink > kMaxFrontSink ||
+        cm < 0)
         return -1;
-    const GroupItems gi(s, e, r, front_sink, true);
+    const GroupItems gi(s, e, r, front_sink, true, cm);
     for (int i = 0; i < gi.n && i < cap; ++i)
         gi.item(i, t0[i], t1[i]);
     if (n_before_split)
@@ -433,7 +480,8 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
     if (!aligned16(rings->q_ring) || !aligned16(rings->o_ring) ||
         !aligned16(workspace))
         return MAC_ERR_MISALIGNED;
-    if ((p->flags & MAC_FLAG_SINGLE_LAUNCH) && !single_launch_supported(s))
+    if (((p->flags & MAC_FLAG_SINGLE_LAUNCH) && !single_launch_supported(s)) ||
+        ((p->flags & MAC_FLAG_TWO_STAGES) && s.T > kSingleMaxPositions))
         return MAC_ERR_UNSUPPORTED;
     const WsLayout L = layout_for(p, s);
     if (ws_bytes < L.total)
@@ -463,8 +511,8 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
     h->ws = workspace;
     h->rings = *rings;
     h->fused_append = (p->flags & MAC_FLAG_FUSED_APPEND) != 0;
-    h->split_stages = !single_launch_form(p, s);
-    if (!h->split_stages) {
+    h->form = step_form(p, s);
+    if (h->form != kFormThree) {
         // wpg workgroups per KV group, all resident at once, each with at
         // least one key word to store.
         const int NG = s.B * s.Hkv;
@@ -474,8 +522,10 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
         // the group's ring rows with it, the large size otherwise.
         const int eb = elem_bytes(s.dtype);
         const int64_t want = h->wpg > 0 ? ((int64_t)s.G * s.K + h->wpg - 1) / h->wpg : 1;
-        h->unit_slots = want <= step_unit_slots(eb, s.D, false) ? step_unit_slots(eb, s.D, false)
-                                                                 : step_unit_slots(eb, s.D, true);
+        int size = 0;
+        while (size < kUnitSizes - 1 && want > step_unit_slots(eb, s.D, size))
+            ++size;
+        h->unit_slots = step_unit_slots(eb, s.D, size);
         h->nsplit = (s.K + h->unit_slots - 1) / h->unit_slots;
         h->upg = s.G * h->nsplit;
         h->nkw = h->upg > h->wpg ? h->upg : h->wpg;
@@ -484,11 +534,11 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
             ++sh;
         h->done_shift = sh;
         if (h->wpg < 1) {
-            if (p->flags & MAC_FLAG_SINGLE_LAUNCH) {
+            if (p->flags & (MAC_FLAG_SINGLE_LAUNCH | MAC_FLAG_TWO_STAGES)) {
                 delete h;
                 return MAC_ERR_UNSUPPORTED;
             }
-            h->split_stages = true;
+            h->form = kFormThree;
         }
     }
     if (hipEventCreateWithFlags(&h->ev_main, hipEventDisableTiming) != hipSuccess ||
@@ -497,8 +547,9 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
         return MAC_ERR_HIP;
     }
     const int64_t n_tag = L.skeys ? single_tag_words(s.B, s.Hkv) : 0;
+    const int64_t n_pool = L.pool ? single_pool_words(s.B, s.Hkv) : 0;
     if (launch_ring_reset(s, rings->q_ring, rings->o_ring, rings->lse_ring,
-                          rings->pos_ring, w, n_tag, st) != hipSuccess) {
+                          rings->pos_ring, w, n_tag, n_pool, st) != hipSuccess) {
         mac_release(h);
         return MAC_ERR_HIP;
     }
@@ -589,8 +640,11 @@ mac_status mac_decode_step(mac_handle *h, const void *qtilde, const float *q,
     a.upg = h->upg;
     a.nkw = h->nkw;
     a.done_shift = h->done_shift;
-    a.nsplit = h->split_stages ? h->L.nsplit : h->nsplit;
+    a.nsplit = h->form == kFormOne ? h->nsplit : h->L.nsplit;
+    a.key_parity = h->form == kFormTwo ? 1 : 0;
+    a.group_only = h->form == kFormTwo ? 1 : 0;
     a.unit_slots = h->unit_slots;
+    a.pool_cap = s.B * s.Hkv * kItemsPerGroupMax;
 
     const bool prof = h->prof_n < h->prof_cap;
     hipEvent_t *pe = prof ? &h->prof[(size_t)h->prof_n * kStages * 2] : nullptr;
@@ -607,10 +661,13 @@ mac_status mac_decode_step(mac_handle *h, const void *qtilde, const float *q,
     // the rings are read and the workspace is reused.
     if (split)
         MAC_HIP(hipStreamWaitEvent(ms, h->ev_aux, 0));
-    if (h->split_stages) {
+    if (h->form == kFormThree) {
         MAC_STAGE(0, ms, launch_match(a, ms));
         MAC_STAGE(1, ms, launch_attend(a, ms));
         MAC_STAGE(2, ms, launch_merge(a, ms));
+    } else if (h->form == kFormTwo) {
+        MAC_STAGE(0, ms, launch_match(a, ms));
+        MAC_STAGE(4, ms, launch_step(a, ms));
     } else {
         MAC_STAGE(4, ms, launch_step(a, ms));
     }
@@ -726,8 +783,8 @@ mac_status mac_profile_read(mac_handle *h, double ms[MAC_PROFILE_STAGES], int32_
         ms[k] = 0.0;
     MAC_HIP(hipDeviceSynchronize());
     // Stages that ran (and recorded their events) on this handle.
-    bool ran[kStages] = {h->split_stages, h->split_stages, h->split_stages, !h->fused_append,
-                         !h->split_stages};
+    const bool three = h->form == kFormThree;
+    bool ran[kStages] = {h->form != kFormOne, three, three, !h->fused_append, !three};
     for (int i = 0; i < h->prof_n; ++i)
         for (int k = 0; k < kStages; ++k) {
             if (!ran[k])

@@ -8,11 +8,15 @@
 namespace mac {
 
 // Work items: a KV group's token range [s, e] is cut on an absolute grid of
-// C tokens, C = kChunkMin * 2^k the smallest such that the range spans at
-// most kMaxItemsPerGroup grid cells.  C depends only on the group's own
-// range, so a head that misses sees exactly the items of a full decode.
+// C tokens, C = Cmin * 2^k the smallest such that the range spans at most
+// kMaxItemsPerGroup grid cells.  C depends only on the group's own range
+// and on the shape's minimum Cmin, so a head that misses sees exactly the
+// items of a full decode of the same shape.  Cmin is 64 tokens for layers
+// of at most kSingleLaunchMaxGroups KV groups (parallelism inside a group
+// matters) and 128 above (each workgroup then holds its whole share of a
+// hit range in flight at once).
 constexpr int kChunkMinShift = 6;
-constexpr int kChunkMin = 1 << kChunkMinShift;
+constexpr int kChunkMinShiftWide = 7;
 // Work of an item in the attention kernel's balanced split: its tokens plus
 // this many (the per-item cost of combining rows and storing the partial).
 constexpr int kItemCost = 64;
@@ -61,23 +65,29 @@ __host__ __device__ constexpr int match_rows_per_load(int elem_bytes, int D)
 {
     return 4096 / (elem_bytes * D);
 }
-// Match units of the single launch come in two sizes: `large` ones of 16
-// loads per lane (at most 256 slots) and small ones of 4 (at most 64
-// slots).  Each size is its own kernel instantiation, so every load of a
-// unit is issued without a branch.
-__host__ __device__ constexpr int step_rows(int elem_bytes, int D, bool large)
+// Match units of the single launch come in two sizes (0, 1): 4 or 16 loads
+// per lane, at most 64 or 256 slots.  The host picks the smallest size whose
+// unit covers a workgroup's share of its group's ring rows.  (A unit of 32
+// loads per lane would request 512 slots at once, but its registers bring
+// the bf16 d = 128 kernel to one wave per SIMD, halving the resident grid.)
+// Each size is its own kernel instantiation, so every load of a unit is
+// issued without a branch.
+constexpr int kUnitSizes = 2;
+__host__ __device__ constexpr int step_unit_loads(int size) { return size == 0 ? 4 : 16; }
+__host__ __device__ constexpr int step_unit_cap(int size) { return size == 0 ? 64 : 256; }
+__host__ __device__ constexpr int step_rows(int elem_bytes, int D, int size)
 {
-    return (large ? 16 : 4) * match_rows_per_load(elem_bytes, D) <= (large ? 256 : 64)
-               ? (large ? 16 : 4)
-               : (large ? 256 : 64) / match_rows_per_load(elem_bytes, D);
+    return step_unit_loads(size) * match_rows_per_load(elem_bytes, D) <= step_unit_cap(size)
+               ? step_unit_loads(size)
+               : step_unit_cap(size) / match_rows_per_load(elem_bytes, D);
 }
-__host__ __device__ constexpr int step_unit_slots(int elem_bytes, int D, bool large)
+__host__ __device__ constexpr int step_unit_slots(int elem_bytes, int D, int size)
 {
-    return step_rows(elem_bytes, D, large) * match_rows_per_load(elem_bytes, D);
+    return step_rows(elem_bytes, D, size) * match_rows_per_load(elem_bytes, D);
 }
 __host__ __device__ constexpr int single_slots(int elem_bytes, int D)
 {
-    return step_unit_slots(elem_bytes, D, true);
+    return step_unit_slots(elem_bytes, D, kUnitSizes - 1);
 }
 // Match units per group of the single launch are at most this many (the
 // host falls back to three kernels beyond).
@@ -94,6 +104,24 @@ constexpr int kGrpStride = 16;
 constexpr int kGrpSpan = 1;
 // Largest position the tagged keys encode.
 constexpr int32_t kSingleMaxPositions = 1 << 24;
+// Cross-group pool of the single launch.  A group whose range is cut on a
+// grid coarser than the shape's minimum (a long range: a head missed) keeps
+// one item per workgroup of its own and publishes the rest; every workgroup
+// claims pool items of any group once its own work is done.  Two sets of
+// pool words, used by launches of alternating parity (the launch whose last
+// group completes resets the other set for the next launch).  Per set: a
+// header of kPoolLine words -- [kPoolState] = groups planned << 32 |
+// entries published (one atomic add per group), [kPoolHead] = entries
+// claimed --
+// then one 64-bit entry per published item: (1 + launch epoch) << 32 |
+// group << 8 | item.
+constexpr int kPoolLine = 32;
+enum { kPoolState = 0, kPoolHead = 16 };  // on separate 128-byte lines
+// Per-group plan record of the single launch, kPlanWords int32 apart:
+// position, range start, item count, readiness, then the G per-head codes;
+// written by the group's first workgroup before it publishes pool entries.
+constexpr int kPlanWords = 16;
+enum { kPlanE = 0, kPlanStart = 1, kPlanN = 2, kPlanReady = 3, kPlanCodes = 4 };
 // Synchronisation line of the workspace (64-bit words).
 constexpr int kLineU64 = 16;
 constexpr int kSyncWords = kLineU64;
@@ -122,16 +150,20 @@ enum { kSyncDone = 0, kSyncMagicWord = 1, kSyncSticky = 2, kSyncBroken = 3 };
 struct RangeSplit {
     // C = 1 << cs; divisions by C are shifts.
     int s, e, cs, c_first, n_grid, sp, has_sp, j_sp, n;
-    __host__ __device__ static int chunk_shift_for(int s_, int e_)
+    // Shift of the smallest C = 2^cmin * 2^k with at most kMaxItemsPerGroup
+    // grid cells over [s_, e_].
+    __host__ __device__ static int chunk_shift_for(int s_, int e_, int cmin)
     {
         const int span = e_ - s_ + 1;
         int cs = 0;
-        while ((kChunkMin << cs) < span && (((span - 1) >> cs) >> kChunkMinShift) + 1 > kMaxItemsPerGroup)
+        while ((1 << (cmin + cs)) < span && (((span - 1) >> cs) >> cmin) + 1 > kMaxItemsPerGroup)
             ++cs;
-        return cs + kChunkMinShift;
+        return cs + cmin;
     }
-    __host__ __device__ static int chunk_for(int s_, int e_) { return 1 << chunk_shift_for(s_, e_); }
-    __host__ __device__ RangeSplit(int s_, int e_, int r) { init(s_, e_, r, chunk_shift_for(s_, e_)); }
+    __host__ __device__ static int chunk_for(int s_, int e_, int cmin)
+    {
+        return 1 << chunk_shift_for(s_, e_, cmin);
+    }
     // The same cuts with the chunk C = 1 << cs_ given.
     __host__ __device__ RangeSplit(int s_, int e_, int r, int cs_) { init(s_, e_, r, cs_); }
     __host__ __device__ void init(int s_, int e_, int r, int cs_)
@@ -191,15 +223,16 @@ struct RangeSplit {
 struct GroupItems {
     RangeSplit rs;
     int ms, n_main, sink_end, n;
-    __host__ __device__ GroupItems() : rs(0, 0, 0), ms(0), n_main(0), sink_end(0), n(0) {}
-    // cs >= 0 forces the grid (1 << cs), as RangeSplit's second constructor.
-    __host__ __device__ GroupItems(int s, int e, int r, int F, bool sink, int cs = -1) : rs(0, 0, 0)
+    __host__ __device__ GroupItems() : rs(0, 0, 0, kChunkMinShift), ms(0), n_main(0), sink_end(0), n(0) {}
+    // cmin: the shape's minimum grid shift; cs >= 0 forces the grid (1 << cs).
+    __host__ __device__ GroupItems(int s, int e, int r, int F, bool sink, int cmin, int cs = -1)
+        : rs(0, 0, 0, kChunkMinShift)
     {
         ms = s > F ? s : F;
         n_main = 0;
         if (ms <= e) {
             if (cs < 0)
-                rs.init(ms, e, r, RangeSplit::chunk_shift_for(ms, e));
+                rs.init(ms, e, r, RangeSplit::chunk_shift_for(ms, e, cmin));
             else
                 rs.init(ms, e, r, cs);
             n_main = rs.n;
@@ -236,7 +269,8 @@ struct GroupItems {
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WsLayout {
     size_t keys, ctx, dec_slot, grp_begin, grp_count, grp_start, ctrl, sync,
-        part_o, part_l, rect_o, rect_l, ring_epoch, restart, app_pos, skeys, grp_sync, total;
+        part_o, part_l, rect_o, rect_l, ring_epoch, restart, app_pos, skeys, grp_sync, pool,
+        gplan, total;
     int64_t max_items;
     int32_t nsplit;
 };
@@ -257,6 +291,7 @@ struct Shape {
     int32_t B, Hq, Hkv, G, D, dtype, K, r, T;
     int32_t F;                    // front sink: leading positions never reused
     int32_t min_ctx;              // positions below it find no match candidate
+    int32_t cmin;                 // shift of the minimum work-item grid
     // Paged K/V (page_table non-null): row t of request b, KV head g at
     // b's page page_table[b * max_pages + (t >> page_shift)], element
     // offset page * kv_sb + g * kv_sh + (t mod page size) * kv_st.
@@ -286,9 +321,11 @@ struct WsPtrs {
     // reads the caller's position array on the auxiliary stream
     int32_t *app_pos;
     // single launch only (null otherwise): tagged split keys, per-group
-    // arrival counters
+    // arrival counters, the two pool sets, per-group plan records
     unsigned long long *skeys;
     uint32_t *grp_sync;
+    unsigned long long *pool;
+    int32_t *gplan;
 };
 
 // Everything the kernels of one call read or write.
@@ -326,6 +363,15 @@ struct StepArgs {
     // nsplit), key words per group, log2 of the done increment per launch,
     // ring slots per match unit
     int32_t wpg, upg, nkw, done_shift, unit_slots;
+    // single launch: pool entries per set (B * Hkv * kItemsPerGroupMax)
+    int32_t pool_cap;
+    // per-head match keys: 0 = set 0 (three kernels: the merge kernel resets
+    // them); 1 = set (launch epoch & 1) of the two sets (match kernel, then
+    // the group kernel, whose first workgroup clears the other set)
+    int32_t key_parity;
+    // the one-launch kernel without its match phase: the group kernel of
+    // the two-kernel form (keys from the match kernel)
+    int32_t group_only;
     // attention kernel: 1 = the last (100 - kStaticPct)% of the work is a pool
     // claimed through ctrl[kCtrlClaim], which must then read 0 at the launch
     // (the ring reset and every merge kernel leave it so); 0 = all of the
@@ -358,14 +404,24 @@ hipError_t launch_step(const StepArgs &a, hipStream_t st);
 // Workgroups of the single-launch kernel for this shape that the device
 // holds resident at once (0 if unknown).
 int step_resident_workgroups(const Shape &s);
+// The two above for one (K/V dtype, head dim) each (mac_step_*.hip).
+void launch_step_bf16_128(const StepArgs &a, hipStream_t st);
+void launch_step_bf16_64(const StepArgs &a, hipStream_t st);
+void launch_step_f32_128(const StepArgs &a, hipStream_t st);
+void launch_step_f32_64(const StepArgs &a, hipStream_t st);
+int step_resident_bf16_128(const Shape &s);
+int step_resident_bf16_64(const Shape &s);
+int step_resident_f32_128(const Shape &s);
+int step_resident_f32_64(const Shape &s);
 // Rectify-append from the workspace staging into the rings; the position of
 // request b is pos[b] + pos_offset.
 hipError_t launch_append(const StepArgs &a, int32_t pos_offset, hipStream_t st);
 // Empties the rings, resets the synchronisation words and clears the first
-// n_tag words of each single-launch tagged region present in w.
+// n_tag words of the single-launch tagged keys and the n_pool words of its
+// pool sets (when present in w).
 hipError_t launch_ring_reset(const Shape &s, void *q_ring, float *o_ring,
                              float *lse_ring, int32_t *pos_ring, const WsPtrs &w,
-                             int64_t n_tag, hipStream_t st);
+                             int64_t n_tag, int64_t n_pool, hipStream_t st);
 int device_cu_count();
 // Address of this device's static scratch (MAC_NOALLOC_SCRATCH_BYTES), looked
 // up once per device with that device current.

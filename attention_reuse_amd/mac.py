@@ -26,6 +26,7 @@ MAC_FLAG_FUSED_APPEND = 1
 MAC_FLAG_SPLIT_STAGES = 2
 MAC_FLAG_SINGLE_LAUNCH = 4
 MAC_FLAG_MATCH_FILTER = 8
+MAC_FLAG_TWO_STAGES = 16
 STATUS = {0: "MAC_OK", -1: "MAC_ERR_INVALID_ARG", -2: "MAC_ERR_UNSUPPORTED",
           -3: "MAC_ERR_HIP", -4: "MAC_ERR_WORKSPACE_TOO_SMALL",
           -5: "MAC_ERR_MISALIGNED", -6: "MAC_ERR_CONTEXT_TOO_LONG",
@@ -102,14 +103,12 @@ def load():
         "mac_release": (ctypes.c_int, [_vp]),
         "mac_stream_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, ctypes.c_int32, _vp]),
         "mac_status_string": (ctypes.c_char_p, [ctypes.c_int]),
-        "mac_chunk_tokens": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32]),
-        "mac_group_items": (ctypes.c_int32, [ctypes.c_int32] * 4 + [
+        "mac_min_chunk_tokens": (ctypes.c_int32, [_P]),
+        "mac_chunk_tokens": (ctypes.c_int32, [ctypes.c_int32] * 3),
+        "mac_group_items": (ctypes.c_int32, [ctypes.c_int32] * 5 + [
             ctypes.POINTER(ctypes.c_int32)] * 3 + [ctypes.c_int32]),
-        "mac_partition": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32,
-                                           ctypes.c_int32,
-                                           ctypes.POINTER(ctypes.c_int32),
-                                           ctypes.POINTER(ctypes.c_int32),
-                                           ctypes.c_int32]),
+        "mac_partition": (ctypes.c_int32, [ctypes.c_int32] * 4 + [
+            ctypes.POINTER(ctypes.c_int32)] * 2 + [ctypes.c_int32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -246,30 +245,34 @@ def mac_status_string(status: int) -> str:
     return load().mac_status_string(status).decode()
 
 
-def mac_chunk_tokens(s: int, e: int) -> int:
-    return int(load().mac_chunk_tokens(s, e))
+def mac_min_chunk_tokens(p: mac_params) -> int:
+    return int(load().mac_min_chunk_tokens(ctypes.byref(p)))
 
 
-def mac_partition(s: int, e: int, r: int):
+def mac_chunk_tokens(s: int, e: int, min_chunk: int = 64) -> int:
+    return int(load().mac_chunk_tokens(s, e, min_chunk))
+
+
+def mac_partition(s: int, e: int, r: int, min_chunk: int = 64):
     """[(t0, t1), ...] work items of a KV group attending [s, e] with band r."""
     lib = load()
-    n = lib.mac_partition(s, e, r, None, None, 0)
+    n = lib.mac_partition(s, e, r, min_chunk, None, None, 0)
     if n < 0:
         raise ValueError("bad range")
     t0 = (ctypes.c_int32 * n)()
     t1 = (ctypes.c_int32 * n)()
-    lib.mac_partition(s, e, r, t0, t1, n)
+    lib.mac_partition(s, e, r, min_chunk, t0, t1, n)
     return list(zip(t0, t1))
 
 
-def mac_group_items(s: int, e: int, r: int, front_sink: int):
+def mac_group_items(s: int, e: int, r: int, front_sink: int, min_chunk: int = 64):
     """([(t0, t1), ...], n_before_split) of a KV group's work items."""
     lib = load()
-    n = lib.mac_group_items(s, e, r, front_sink, None, None, None, 0)
+    n = lib.mac_group_items(s, e, r, front_sink, min_chunk, None, None, None, 0)
     if n < 0:
         raise ValueError("bad range")
     t0 = (ctypes.c_int32 * max(n, 1))()
     t1 = (ctypes.c_int32 * max(n, 1))()
     nb = ctypes.c_int32()
-    lib.mac_group_items(s, e, r, front_sink, t0, t1, ctypes.byref(nb), n)
+    lib.mac_group_items(s, e, r, front_sink, min_chunk, t0, t1, ctypes.byref(nb), n)
     return list(zip(t0[:n], t1[:n])), nb.value

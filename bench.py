@@ -44,8 +44,9 @@ def parse():
     ap.add_argument("--mode", choices=("mac", "full"), default="mac")
     ap.add_argument("--append", choices=("aux", "fused"), default="fused",
                     help="rectify-append on the auxiliary stream or fused into the merge")
-    ap.add_argument("--launch", choices=("auto", "single", "split"), default="auto",
-                    help="decode step as one launch, as match / attend / merge kernels, "
+    ap.add_argument("--launch", choices=("auto", "single", "two", "split"), default="auto",
+                    help="decode step as one launch, as a match kernel and one launch for "
+                         "plan / attention / merge, as match / attend / merge kernels, "
                          "or the library's choice for the shape")
     ap.add_argument("--match-filter", action="store_true",
                     help="exact lower-bound filter of the match (second halves of ring "
@@ -256,6 +257,7 @@ def main():
                         flags=(mac.MAC_FLAG_FUSED_APPEND if args.append == "fused" else 0)
                         | (mac.MAC_FLAG_MATCH_FILTER if args.match_filter else 0)
                         | {"auto": 0, "single": mac.MAC_FLAG_SINGLE_LAUNCH,
+                           "two": mac.MAC_FLAG_TWO_STAGES,
                            "split": mac.MAC_FLAG_SPLIT_STAGES}[args.launch])
     wsb = mac.mac_workspace_bytes(p)
     stream = torch.cuda.current_stream()
@@ -385,12 +387,14 @@ def main():
     roofline = None
     launched = None
     if stage_ms:
-        launched = "single" if stage_ms["step"] > 0 else "split"
-    if stage_ms and launched == "single":
-        # One kernel moves the match, attention and merge bytes (and the ring
-        # append when fused).
+        launched = ("split" if stage_ms["step"] == 0 else
+                    "two" if stage_ms["match"] > 0 else "single")
+    if stage_ms and launched in ("single", "two"):
+        # One kernel moves the attention and merge bytes (and the ring append
+        # when fused), and the match bytes unless the match kernel ran first.
         dom = "step"
-        per_launch["step"] = sum(per_launch[k] for k in ("match", "attend", "merge")) + (
+        per_launch["step"] = sum(per_launch[k] for k in ("attend", "merge")) + (
+            per_launch["match"] if launched == "single" else 0.0) + (
             per_launch["append"] if args.append == "fused" else 0.0)
     elif stage_ms:
         dom = max(("match", "attend"), key=lambda k: stage_ms[k])

@@ -85,11 +85,15 @@ enum { MAC_THRESH_ONE_MINUS_TAU = 0, MAC_THRESH_TAU = 1 };
  *   2^24, when a KV group's ring match needs more than 256 units of up to
  *   256 slots, or when the device cannot hold one workgroup per KV group
  *   resident).
- * With neither of the last two, the step is one launch when a layer has at
- * most 16 KV groups (batch * n_kv_heads) and the shape is one the single
- * launch handles, where the step is bound by latency, and three kernels
- * otherwise, where it is bound by bandwidth.
- * Both forms give the same results bit for bit.
+ *   MAC_FLAG_TWO_STAGES: mac_decode_step runs the match as one kernel and
+ *   plan, attention and merge as a second (MAC_ERR_UNSUPPORTED from
+ *   mac_init_rings when kv_capacity exceeds 2^24 or the device cannot hold
+ *   one workgroup per KV group resident).
+ * At most one of these three may be set.  With none, the step is one launch
+ * when a layer has at most 16 KV groups (batch * n_kv_heads) and the shape
+ * is one the single launch handles, where the step is bound by latency, and
+ * three kernels otherwise, where it is bound by bandwidth.
+ * All forms give the same results bit for bit.
  *   MAC_FLAG_MATCH_FILTER: exact lower-bound filter of the match (blog,
  *   "Production version: one fused persistent BF16 kernel", the match-scan
  *   item).  The first half of every candidate row is read; the second half
@@ -105,7 +109,8 @@ enum {
     MAC_FLAG_FUSED_APPEND = 1,
     MAC_FLAG_SPLIT_STAGES = 2,
     MAC_FLAG_SINGLE_LAUNCH = 4,
-    MAC_FLAG_MATCH_FILTER = 8
+    MAC_FLAG_MATCH_FILTER = 8,
+    MAC_FLAG_TWO_STAGES = 16
 };
 
 /* Device status flags latched in the workspace. */
@@ -242,9 +247,11 @@ mac_status mac_init_rings(const mac_params *p, const mac_rings *rings,
  * ready (mac_bind_epochs) are computed as misses.
  * Match, amend and complete run on main_stream as one kernel launch whose
  * workgroups are all resident at once (the workgroups of each KV group hand
- * match keys and partial summaries to each other inside the launch), or as
- * three kernels (match, plan + attention, merge); see MAC_FLAG_SPLIT_STAGES
- * for the choice.  The single launch needs kv_capacity <= 2^24.  Other work
+ * match keys and partial summaries to each other inside the launch), as
+ * three kernels (match, plan + attention, merge), or as two (the match
+ * kernel, then plan, attention and merge in one launch whose workgroups are
+ * all resident at once); see MAC_FLAG_SPLIT_STAGES for the choice.  The one-
+ * and two-kernel forms need kv_capacity <= 2^24.  Other work
  * that holds compute units while the launch waits for residency only delays
  * it; a launch that cannot get all its workgroups resident within about a
  * second stops waiting and latches MAC_DEV_SYNC_TIMEOUT.  The rectify-append of the rings runs as another
@@ -353,9 +360,10 @@ mac_status mac_read_device_status(const mac_params *p, void *workspace,
 
 /* Per-kernel timing with HIP events (diagnostics).  mac_profile_start arms
  * recording for the next `n_steps` decode steps of the handle; stages are
- * 0 match, 1 plan + attention, 2 merge (these three 0 for the single
- * launch), 3 rectify-append (0 when fused), 4 the single launch (0 with
- * MAC_FLAG_SPLIT_STAGES).  mac_profile_read synchronises, returns the
+ * 0 match (0 for the single launch), 1 plan + attention and 2 merge (0
+ * unless three kernels run), 3 rectify-append (0 when fused), 4 the single
+ * launch or, in the two-kernel form, its second kernel (0 when three
+ * kernels run).  mac_profile_read synchronises, returns the
  * summed milliseconds per stage in ms[5] and the number of recorded steps
  * in *n, and disarms. */
 enum { MAC_PROFILE_STAGES = 5 };
@@ -376,31 +384,41 @@ mac_status mac_release(mac_handle *h);
 
 const char *mac_status_string(mac_status s);
 
+/* The minimum grid of the split-KV partition for a shape (host mirror of
+ * the device planner): 64 tokens for layers of at most 16 KV groups
+ * (batch * n_kv_heads), 128 above; -1 on invalid parameters.  Every entry
+ * point on the same parameters (decode step in either form, full decode)
+ * cuts ranges on the same grid, so a missing head equals the full decode
+ * bit for bit. */
+int32_t mac_min_chunk_tokens(const mac_params *p);
+
 /* Grid of the split-KV partition for a KV group attending [s, e]: the
- * smallest C = 64 * 2^k with at most 128 grid cells over the range (-1 on
- * bad input). */
-int32_t mac_chunk_tokens(int32_t s, int32_t e);
+ * smallest C = min_chunk * 2^k with at most 128 grid cells over the range
+ * (-1 on bad input; min_chunk a power of two >= 64, as
+ * mac_min_chunk_tokens returns). */
+int32_t mac_chunk_tokens(int32_t s, int32_t e, int32_t min_chunk);
 
 /* The split-KV partition the kernels use for a KV group whose heads attend
  * [s, e] with band r (host mirror of the device planner): item i covers
- * [t0[i], t1[i]); boundaries are s, the multiples of mac_chunk_tokens(s, e)
- * in (s, e], the rectify split e - r + 1 when inside (s, e], and e + 1.
- * With front_sink F > 0 the planner applies this to [max(s, F), e] and
- * adds the sink [0, min(F, e + 1)) as one more item.
- * Writes min(n, cap) items (host arrays) and returns n, or -1 on bad input. */
-int32_t mac_partition(int32_t s, int32_t e, int32_t r, int32_t *t0,
+ * [t0[i], t1[i]); boundaries are s, the multiples of
+ * mac_chunk_tokens(s, e, min_chunk) in (s, e], the rectify split e - r + 1
+ * when inside (s, e], and e + 1.  With front_sink F > 0 the planner applies
+ * this to [max(s, F), e] and adds the sink [0, min(F, e + 1)) as one more
+ * item.  Writes min(n, cap) items (host arrays) and returns n, or -1 on bad
+ * input. */
+int32_t mac_partition(int32_t s, int32_t e, int32_t r, int32_t min_chunk, int32_t *t0,
                       int32_t *t1, int32_t cap);
 
 /* The work items of one KV group at decode position e whose heads attend
- * from s, with band r and front sink F (host mirror of the device planner):
- * first the partition of [max(s, F), e] as mac_partition cuts it (none when
- * e < F), then, when F > 0, the sink item [0, min(F, e + 1)).  Writes
- * min(n, cap) items (host arrays) and, if n_before_split is not NULL, the
- * number of leading items before the rectify split e - r + 1 (the items
- * whose partials enter the rectified summary).  Returns n, or -1 on bad
- * input. */
-int32_t mac_group_items(int32_t s, int32_t e, int32_t r, int32_t front_sink, int32_t *t0,
-                        int32_t *t1, int32_t *n_before_split, int32_t cap);
+ * from s, with band r, front sink F and minimum grid min_chunk (host mirror
+ * of the device planner): first the partition of [max(s, F), e] as
+ * mac_partition cuts it (none when e < F), then, when F > 0, the sink item
+ * [0, min(F, e + 1)).  Writes min(n, cap) items (host arrays) and, if
+ * n_before_split is not NULL, the number of leading items before the
+ * rectify split e - r + 1 (the items whose partials enter the rectified
+ * summary).  Returns n, or -1 on bad input. */
+int32_t mac_group_items(int32_t s, int32_t e, int32_t r, int32_t front_sink, int32_t min_chunk,
+                        int32_t *t0, int32_t *t1, int32_t *n_before_split, int32_t cap);
 
 #ifdef __cplusplus
 }

@@ -104,6 +104,21 @@ def test_status_strings_and_chunk(lib):
     assert mac.mac_chunk_tokens(100, 65536) == 512
     assert mac.mac_chunk_tokens(0, 262399) == 4096
     assert mac.mac_chunk_tokens(5, 4) == -1
+    # A 128-token minimum grid.
+    assert mac.mac_chunk_tokens(0, 127, 128) == 128
+    assert mac.mac_chunk_tokens(0, 128 * 128 - 1, 128) == 128
+    assert mac.mac_chunk_tokens(0, 128 * 128, 128) == 256
+    assert mac.mac_chunk_tokens(0, 65536, 128) == 1024
+    assert mac.mac_chunk_tokens(0, 100, 96) == -1 and mac.mac_chunk_tokens(0, 100, 32) == -1
+
+
+def test_min_chunk_by_shape(lib):
+    """64-token grid up to 16 KV groups per layer, 128 above."""
+    assert mac.mac_min_chunk_tokens(_params(batch=2)) == 64      # 16 groups
+    assert mac.mac_min_chunk_tokens(_params(batch=1)) == 64
+    assert mac.mac_min_chunk_tokens(_params(batch=3)) == 128     # 24 groups
+    assert mac.mac_min_chunk_tokens(_params(batch=16)) == 128
+    assert mac.mac_min_chunk_tokens(_params(batch=0)) == -1
 
 
 def test_workspace_and_ring_sizes(lib):
@@ -122,8 +137,9 @@ def test_workspace_and_ring_sizes(lib):
     (dict(head_dim=96), -2), (dict(kv_dtype=7), -2), (dict(n_q_heads=48, n_kv_heads=3), -2),
     (dict(n_q_heads=30), -1), (dict(ring_k=0), -1), (dict(band_r=-1), -1),
     (dict(batch=0), -1), (dict(kv_capacity=0), -1), (dict(tau=float("nan")), -1),
-    (dict(thresh_mode=2), -1), (dict(strides=(0, 0, 100)), -1), (dict(flags=16), -1),
-    (dict(flags=6), -1), (dict(flags=1), 0), (dict(flags=3), 0), (dict(flags=5), 0),
+    (dict(thresh_mode=2), -1), (dict(strides=(0, 0, 100)), -1), (dict(flags=32), -1),
+    (dict(flags=6), -1), (dict(flags=18), -1), (dict(flags=20), -1), (dict(flags=1), 0),
+    (dict(flags=3), 0), (dict(flags=5), 0), (dict(flags=17), 0), (dict(flags=24), 0),
     (dict(batch=300), -2),
     (dict(strides=(1 << 20, 4096 * 136, 136)), 0), (dict(strides=(1 << 20, 4096 * 132, 132)), -5),
 ])
@@ -178,14 +194,16 @@ def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
         mac.load()
 
 
+@pytest.mark.parametrize("cmin", [64, 128])
 @pytest.mark.parametrize("s,e,r", [(0, 0, 0), (0, 127, 32), (0, 128, 32), (5, 1000, 256),
                                    (300, 1000, 256), (900, 1000, 256), (0, 262399, 256),
                                    (1000, 1000, 0), (0, 500, 1000), (640, 1000, 361)])
-def test_partition_covers_range_on_the_grid(lib, s, e, r):
+def test_partition_covers_range_on_the_grid(lib, s, e, r, cmin):
     """Items tile [s, e] in order; every interior boundary is a multiple of the
     chunk or the rectify split e - r + 1; no item crosses either."""
-    C = mac.mac_chunk_tokens(s, e)
-    items = mac.mac_partition(s, e, r)
+    C = mac.mac_chunk_tokens(s, e, cmin)
+    assert C >= cmin
+    items = mac.mac_partition(s, e, r, cmin)
     assert len(items) <= 130
     assert items[0][0] == s and items[-1][1] == e + 1
     for (a0, a1), (b0, _) in zip(items, items[1:]):
@@ -199,24 +217,26 @@ def test_partition_covers_range_on_the_grid(lib, s, e, r):
             assert t0 % C == 0 or t0 == sp
     # A miss head (s = 0) gets the same items as a full decode.
     if s == 0:
-        assert items == mac.mac_partition(0, e, r)
-    assert lib.mac_partition(5, 4, 0, None, None, 0) == -1
+        assert items == mac.mac_partition(0, e, r, cmin)
+    assert lib.mac_partition(5, 4, 0, cmin, None, None, 0) == -1
+    assert lib.mac_partition(0, 4, 0, 100, None, None, 0) == -1
 
 
+@pytest.mark.parametrize("cmin", [64, 128])
 @pytest.mark.parametrize("s,e,r,F", [(0, 0, 0, 64), (0, 63, 16, 64), (0, 200, 16, 64),
                                      (150, 3000, 256, 128), (0, 33000, 256, 128),
                                      (500, 600, 600, 4096), (0, 5000, 0, 1), (10, 90, 5, 0)])
-def test_group_items_with_front_sink(lib, s, e, r, F):
+def test_group_items_with_front_sink(lib, s, e, r, F, cmin):
     """Main items tile [max(s, F), e] as the plain partition does; the sink
     item [0, min(F, e + 1)) comes last; the rectify split counts only main
     items, and the items before it cover exactly [max(s, F), e - r]."""
-    items, nb = mac.mac_group_items(s, e, r, F)
+    items, nb = mac.mac_group_items(s, e, r, F, cmin)
     ms = max(s, F)
     main = items[:-1] if F > 0 else items
     if F > 0:
         assert items[-1] == (0, min(F, e + 1))
     if ms <= e:
-        assert main == mac.mac_partition(ms, e, r)
+        assert main == mac.mac_partition(ms, e, r, cmin)
     else:
         assert main == []
     covered = [t for a, b in main[:nb] for t in range(a, b)]
@@ -224,9 +244,9 @@ def test_group_items_with_front_sink(lib, s, e, r, F):
     assert nb <= len(main)
     # F = 0 is the plain partition.
     if F == 0:
-        assert items == mac.mac_partition(s, e, r)
-    assert lib.mac_group_items(5, 4, 0, 0, None, None, None, 0) == -1
-    assert lib.mac_group_items(0, 4, 0, 4097, None, None, None, 0) == -1
+        assert items == mac.mac_partition(s, e, r, cmin)
+    assert lib.mac_group_items(5, 4, 0, 0, cmin, None, None, None, 0) == -1
+    assert lib.mac_group_items(0, 4, 0, 4097, cmin, None, None, None, 0) == -1
 
 
 def test_noalloc_full_decode_rejects_before_any_device_call(lib):

@@ -54,15 +54,18 @@ TAU = 1  # mac.MAC_THRESH_TAU: distance < tau * sqrt(2d)
     (3, "fused", "single", 0, 0, 0), (3, "fused", "split", 0, 0, 0),
     (4, "aux", "single", 0, 0, 0), (5, "fused", "single", 0, 0, 0),
     (5, "aux", "split", 0, 0, 0), (5, "aux", "split", 0, 0, TAU),
-    (2, "fused", "single", 128, 16, 0), (5, "fused", "split", 64, 64, 0)])
+    (3, "fused", "two", 0, 0, 0), (5, "aux", "two", 0, 0, 0),
+    (2, "fused", "single", 128, 16, 0), (5, "fused", "split", 64, 64, 0),
+    (5, "fused", "two", 64, 64, 0)])
 def test_fullsize_config(oracle_lib, cfg_id, append, launch, F, P, mode):
     cfg = wl.WORKLOADS[cfg_id]
     print("full-size parity: config %d (%s), append=%s, launch=%s, front sink %d, page %d, "
           "threshold mode %d" % (cfg_id, cfg.name, append, launch, F, P, mode), flush=True)
     K, V = wl.gen_kv(cfg)
     qt, q, _, sig = wl.gen_queries(cfg)
-    flags = (mac.MAC_FLAG_FUSED_APPEND if append == "fused" else 0) | (
-        mac.MAC_FLAG_SPLIT_STAGES if launch == "split" else mac.MAC_FLAG_SINGLE_LAUNCH)
+    flags = (mac.MAC_FLAG_FUSED_APPEND if append == "fused" else 0) | {
+        "split": mac.MAC_FLAG_SPLIT_STAGES, "single": mac.MAC_FLAG_SINGLE_LAUNCH,
+        "two": mac.MAC_FLAG_TWO_STAGES}[launch]
     kv_dev, paging = None, {}
     if P:
         kp, table = _pool(to_dev(K), P)

@@ -187,17 +187,18 @@ def test_forced_miss_is_bitwise_full_decode():
 
 
 def test_run_to_run_deterministic_and_launch_and_append_mode_invariant():
-    """Outputs and rings are bitwise identical run to run, as one launch or
-    three kernels, with the rectify-append on an auxiliary stream, on the
+    """Outputs and rings are bitwise identical run to run, as one launch, two
+    kernels or three, with the rectify-append on an auxiliary stream, on the
     main stream, or fused into the merge."""
     cfg = _cfg(steps=12, sigma=(0.02, 0.5))
     K, V, qt, q = _inputs(cfg)
     runs = []
     split, fused = mac.MAC_FLAG_SPLIT_STAGES, mac.MAC_FLAG_FUSED_APPEND
-    single = mac.MAC_FLAG_SINGLE_LAUNCH
+    single, two = mac.MAC_FLAG_SINGLE_LAUNCH, mac.MAC_FLAG_TWO_STAGES
     for flags, aux in ((single, torch.cuda.Stream()), (single, None),
                        (single | fused, torch.cuda.Stream()), (0, torch.cuda.Stream()),
-                       (split, torch.cuda.Stream()), (split | fused, None), (split, None)):
+                       (split, torch.cuda.Stream()), (split | fused, None), (split, None),
+                       (two, torch.cuda.Stream()), (two | fused, None)):
         print("  flags %d, aux stream %s" % (flags, aux is not None), flush=True)
         layer = Layer(cfg, K, V, qt, q, params=params_for(cfg, flags=flags))
         res = run_steps(layer.init(), cfg.steps, aux=aux)
@@ -218,6 +219,16 @@ def test_lockstep_split_stages(oracle_lib):
     cfg = _cfg(batch=2, ctx=1800, steps=24, ring_k=128, band_r=48, sigma=(0.02, 0.5), seed=7)
     K, V, qt, q = _inputs(cfg)
     layer = Layer(cfg, K, V, qt, q, params=params_for(cfg, flags=mac.MAC_FLAG_SPLIT_STAGES))
+    _lockstep(oracle_lib, cfg, layer=layer)
+
+
+def test_lockstep_two_stages(oracle_lib):
+    """The two-kernel form (match kernel, then one launch for plan,
+    attention and merge) against the oracle, over enough steps that both
+    sets of per-head keys are used many times."""
+    cfg = _cfg(batch=2, ctx=1800, steps=24, ring_k=128, band_r=48, sigma=(0.02, 0.5), seed=9)
+    K, V, qt, q = _inputs(cfg)
+    layer = Layer(cfg, K, V, qt, q, params=params_for(cfg, flags=mac.MAC_FLAG_TWO_STAGES))
     _lockstep(oracle_lib, cfg, layer=layer)
 
 
@@ -304,7 +315,7 @@ def test_bad_position_is_flagged_not_faulted():
     assert mac.mac_read_device_status(layer.p, layer.ws) == 0
 
 
-@pytest.mark.parametrize("flags", [0, mac.MAC_FLAG_SPLIT_STAGES])
+@pytest.mark.parametrize("flags", [0, mac.MAC_FLAG_SPLIT_STAGES, mac.MAC_FLAG_TWO_STAGES])
 def test_lockstep_tau_threshold_rule(oracle_lib, flags):
     """The acceptance rule distance < tau * sqrt(2d) (MAC_THRESH_TAU; the
     paper summary's "Core method" form) against the oracle's threshold in
