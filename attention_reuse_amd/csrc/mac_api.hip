@@ -254,22 +254,24 @@ static bool single_launch_supported(const Shape &s)
 enum { kFormThree = 0, kFormOne = 1, kFormTwo = 2 };
 
 // The form a handle for p runs, before the residency check of
-// mac_init_rings: the one its flags force, else one launch for at most
-// kSingleLaunchMaxGroups KV groups and three kernels above, where shapes
-// allow.  The one- and two-kernel forms need positions that the tagged keys
-// and pool entries encode; the one-launch form also needs the group's match
-// units to fit its LDS.
+// mac_init_rings: the one its flags force, else by the number of KV groups
+// (kSingleLaunchMaxGroups, kTwoStageMaxGroups), where shapes allow.  The
+// one- and two-kernel forms need positions that the tagged keys and pool
+// entries encode; the one-launch form also needs the group's match units to
+// fit its LDS.
 static int step_form(const mac_params *p, const Shape &s)
 {
     if (p->flags & MAC_FLAG_SPLIT_STAGES)
         return kFormThree;
+    const bool two_ok = s.T <= kSingleMaxPositions;
     if (p->flags & MAC_FLAG_TWO_STAGES)
-        return s.T <= kSingleMaxPositions ? kFormTwo : kFormThree;
-    if (!single_launch_supported(s))
-        return kFormThree;
-    return (p->flags & MAC_FLAG_SINGLE_LAUNCH) || s.B * s.Hkv <= kSingleLaunchMaxGroups
-               ? kFormOne
-               : kFormThree;
+        return two_ok ? kFormTwo : kFormThree;
+    if (p->flags & MAC_FLAG_SINGLE_LAUNCH)
+        return kFormOne;  // mac_init_rings rejects shapes it does not handle
+    const int NG = s.B * s.Hkv;
+    if (NG <= kSingleLaunchMaxGroups && single_launch_supported(s))
+        return kFormOne;
+    return two_ok && NG <= kTwoStageMaxGroups ? kFormTwo : kFormThree;
 }
 
 static WsLayout layout_for(const mac_params *p, const Shape &s)

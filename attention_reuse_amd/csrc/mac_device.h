@@ -944,23 +944,29 @@ __device__ inline void load_cached(const StepArgs &a, int grp, SlotOf &&slot_of,
     using MP = MergePairs<D, G, NT>;
     const Shape &s = a.s;
     const int b = grp / s.Hkv, g = grp - b * s.Hkv;
+    // Branch-free: every thread loads and selects afterwards, so that
+    // nothing that uses the values is moved next to the loads, where it
+    // would wait for them (and for every load requested before them).  A
+    // thread with nothing to load reads the first element of the rings, or,
+    // where there are no rings (full decode: every head misses), of the
+    // workspace's rectified summaries, which always exist.
+    const float *lse_src = a.lse_ring ? a.lse_ring : a.w.rect_l;
+    const float *o_src = a.o_ring ? a.o_ring : a.w.rect_o;
 #pragma unroll
     for (int k = 0; k < MP::NPK; ++k) {
         const int pt = threadIdx.x + k * NT;
-        c_l[k] = -INFINITY;
-        c_o[k][0] = c_o[k][1] = 0.f;
-        if (pt < MP::NPAIR) {
-            const int jj = 2 * pt / D, dim = 2 * pt - jj * D;
-            const int bh = b * s.Hq + g * G + jj;
-            const int slot = slot_of(jj);
-            if (slot >= 0) {
-                c_l[k] = a.lse_ring[(int64_t)bh * s.K + slot];
-                const float2 v = *reinterpret_cast<const float2 *>(
-                    a.o_ring + ((int64_t)bh * s.K + slot) * D + dim);
-                c_o[k][0] = v.x;
-                c_o[k][1] = v.y;
-            }
-        }
+        const bool pair = pt < MP::NPAIR;
+        const int pp = pair ? pt : 0;
+        const int jj = 2 * pp / D, dim = 2 * pp - jj * D;
+        const int bh = b * s.Hq + g * G + jj;
+        const int slot = slot_of(jj);
+        const bool use = pair && slot >= 0;
+        const int64_t ri = use ? (int64_t)bh * s.K + slot : 0;
+        const float l = lse_src[ri];
+        const float2 v = *reinterpret_cast<const float2 *>(o_src + (use ? ri * D + dim : 0));
+        c_l[k] = use ? l : -INFINITY;
+        c_o[k][0] = use ? v.x : 0.f;
+        c_o[k][1] = use ? v.y : 0.f;
     }
 }
 
@@ -2537,10 +2543,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
     const GroupItems gi(e_ok ? sg : 0, e_ok ? e : 0, s.r, s.F, true, s.cmin);
     const int n = e_ok ? gi.n : 0;
-    int st0[G];  // the sink item: every head attends all of it
-#pragma unroll
-    for (int j = 0; j < G; ++j)
-        st0[j] = 0;
 
     // Items the group's own workgroups run: all of a hit range; of a range
     // cut on a grid coarser than the minimum (a head missed: a long range),
@@ -2591,17 +2593,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
     }
 
-    // The pool words are read while the partials of this workgroup's last
-    // own item are being stored (and again before a merge), so that the
-    // common case -- nothing published -- costs no wait after the last
-    // item.  A workgroup without an item of its own leaves at once: the
-    // workgroups that ran items take the pool's items (at least one per item
-    // of a group's own workgroups), and idle workgroups polling the pool
-    // words would only slow the counters of the others.
-    // No load is requested between the speculative K/V and the first item's
-    // use of it: the wait for the first item's rows would wait for that
-    // load too (the cached summaries, in particular, are requested by the
-    // merge itself).
+    // A workgroup without an item of its own leaves at once: the workgroups
+    // that ran items take the pool's items (at least one per item of a
+    // group's own workgroups), and idle workgroups polling the pool words
+    // would only slow the counters of the others.
     if (n == 0) {
         // Position out of range: NaN outputs, nothing appended.
         if (loc == 0) {
@@ -2614,139 +2609,155 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     if (loc >= n_own)
         return;
     unsigned long long pst = ~0ull, phd = ~0ull;
-    // The group whose context is loaded: its range, plan and head codes.
-    int cgrp = grp, cn = n, csg = sg, ce = e;
-    bool cready = ready;
-    int ccode[G], cst[G];
+    // Counts an item of group cg (cn items); true when the count completes
+    // the group.
+    auto count_item = [&](int cg, int cn) {
+        if (threadIdx.x == 0)
+            s_last = atomicAdd(a.w.grp_sync + (int64_t)cg * kGrpStride, 1u) == (uint32_t)(cn - 1);
+        __syncthreads();
+        return s_last != 0;
+    };
+    // Merge of group mg, whose last count this workgroup made, with its
+    // cached summaries (c_l, c_o from load_cached); the pool words are read
+    // again meanwhile.  e and the readiness are the values read at the start
+    // of the launch (the group's epoch is not rewritten before this merge
+    // does it).
+    auto merge = [&](int mg, int mn, int msg, int me, bool mready, const float(&c_l)[MP::NPK],
+                     const float(&c_o)[MP::NPK][2]) {
+        if (threadIdx.x == 0) {
+            pst = ld_wt(ps + kPoolState);
+            phd = ld_wt(ps + kPoolHead);
+        }
+        const CoherentParts<D, G> src{a.w.part_o + (int64_t)mg * kItemsPerGroupMax * G * D,
+                                      a.w.part_l + (int64_t)mg * kItemsPerGroupMax * G};
+        merge_group<T, D, G, kBlock>(a, mg, mn, msg, me, mready, src, lds, c_l, c_o);
+        if (threadIdx.x == 0) {
+            uint32_t *counter = a.w.grp_sync + (int64_t)mg * kGrpStride;
+            st_wt(counter, 0u);
+            st_wt(counter + kGrpSpan, (uint32_t)(me - msg + 1));
+            group_complete(a, mg, NG);
+        }
+    };
+
+    // Own items n-1-loc, n-1-loc-wpg, ...: the first usually finds its rows
+    // in the speculative loads, else requests them at once.  Only then are
+    // the cached summaries (in case this workgroup merges the group) and the
+    // pool words requested: loads complete in order, so the first item's
+    // wait for its rows does not wait for them.
+    {
+        ctx.queries_from_lds(s_q, s_qb, s.qscale);
+        float *gpo = a.w.part_o + (int64_t)grp * kItemsPerGroupMax * G * D;
+        float *gpl = a.w.part_l + (int64_t)grp * kItemsPerGroupMax * G;
+        // Attention of own item it, its rows requested; the partial stored
+        // device-coherently, then counted.  The count that completes the
+        // group is the group's last, so a workgroup merges its own group at
+        // most once, after its items.
+        auto own_item = [&](int it, int t0, int t1) {
+            // Token-start bounds by value (a reference chosen at run time
+            // would put both arrays in scratch memory): the sink item is
+            // attended by every head in full.
+            const bool sink_item = gi.is_sink(it);
+            int sti[G];
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-        ccode[j] = s_code[j];
-        cst[j] = st[j];
+            for (int j = 0; j < G; ++j)
+                sti[j] = sink_item ? 0 : st[j];
+            float *po = gpo + (int64_t)it * G * D, *pl = gpl + (int64_t)it * G;
+            item_finish<T, D, G, kPaged>(a, ctx, t0, t1, sti, lds, bufs, [&](int j, int dim, float o, float lg) {
+                st_wt(po + j * D + dim, o);
+                if (dim == 0)
+                    st_wt(pl + j, lg);
+            });
+            wait_vmem();  // this wave's partial stores have completed
+            __syncthreads();
+            return count_item(grp, n);
+        };
+        int t0, t1;
+        gi.item(n - 1 - loc, t0, t1);
+        if (!(spec && t0 == sp_t0 && t1 == sp_t1))
+            item_issue<T, D, G, kPaged>(a, ctx, t0, t1, bufs, false);
+        float c_l[MP::NPK], c_o[MP::NPK][2];
+        load_cached<T, D, G, kBlock>(
+            a, grp, [&](int j) { return code_slot(s_code[j], s.r, s.K); }, c_l, c_o);
+        if (threadIdx.x == 0) {
+            pst = ld_wt(ps + kPoolState);
+            phd = ld_wt(ps + kPoolHead);
+        }
+        // The first item is peeled off the loop, so that its wait for the
+        // rows is its own (the loop's items wait for their just-requested
+        // rows, the newest loads).
+        bool merger = own_item(n - 1 - loc, t0, t1);
+        for (int jj = loc + a.wpg; jj < n_own; jj += a.wpg) {
+            const int it = n - 1 - jj;
+            gi.item(it, t0, t1);
+            item_issue<T, D, G, kPaged>(a, ctx, t0, t1, bufs, false);
+            merger = own_item(it, t0, t1) || merger;
+        }
+        if (merger)
+            merge(grp, n, sg, e, ready, c_l, c_o);
     }
-    GroupItems cgi = gi;
-    int jj = loc;
-    // Attention of item wit of the loaded group (cgrp), its partial stored
-    // device-coherently; the K/V rows are requested here unless `loaded`
-    // (the speculative loads already hold them).  With `pool_words` thread 0
-    // also reads the pool words, during the wait for the stores.
-    auto run_item = [&](int wit, bool loaded, bool pool_words) {
-        // The item context is rebuilt from LDS for every item, so that no
-        // register holds it across a merge.
-        const int cb = cgrp / s.Hkv;
-        ItemCtx<T, D, G, kPaged> ictx(a, cb, cgrp - cb * s.Hkv, true);
+
+    // Pool items of any group, until the pool is drained.
+    for (;;) {
+        const int ent = pool_take(ps, tag32, NG, pst, phd, &s_slot);
+        pst = phd = ~0ull;
+        if (ent < 0) {
+            if (ent == -2 && threadIdx.x == 0) {
+                atomicOr(&sync[kSyncSticky], (unsigned long long)MAC_DEV_SYNC_TIMEOUT);
+                atomicOr(&sync[kSyncBroken], 1ull);
+            }
+            break;
+        }
+        const int wgrp = __builtin_amdgcn_readfirstlane(ent >> 8);
+        const int wit = __builtin_amdgcn_readfirstlane(ent & 0xff);
+        // The item's group: plan record and queries.
+        const int32_t *rec = a.w.gplan + (int64_t)wgrp * kPlanWords;
+        if (threadIdx.x < kPlanCodes + G)
+            s_plan[threadIdx.x] =
+                (int)ld_wt_u32(reinterpret_cast<const uint32_t *>(rec + threadIdx.x));
+        const int b2 = wgrp / s.Hkv, g2 = wgrp - b2 * s.Hkv;
+        QueryStage<D, G> q2;
+        q2.request(a, b2, g2);
+        __syncthreads();  // plan words in LDS; s_q and s_qb free
+        q2.store(s_q);
+        if constexpr (AS::kMfma)
+            q2.store_b(s_qb, s.qscale);
+        const int ce = __builtin_amdgcn_readfirstlane(s_plan[kPlanE]);
+        const int csg = __builtin_amdgcn_readfirstlane(s_plan[kPlanStart]);
+        const int cn = __builtin_amdgcn_readfirstlane(s_plan[kPlanN]);
+        const bool cready = __builtin_amdgcn_readfirstlane(s_plan[kPlanReady]) != 0;
+        int ccode[G], cst[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            ccode[j] = __builtin_amdgcn_readfirstlane(s_plan[kPlanCodes + j]);
+            cst[j] = code_start(ccode[j]);
+        }
+        const GroupItems cgi(csg, ce, s.r, s.F, true, s.cmin);
+        __syncthreads();  // queries in LDS
+        ItemCtx<T, D, G, kPaged> ictx(a, b2, g2, true);
+        ictx.queries_from_lds(s_q, s_qb, s.qscale);
         int t0, t1;
         cgi.item(wit, t0, t1);
-        const int(&sti)[G] = cgi.is_sink(wit) ? st0 : cst;
-        if (!loaded)
-            item_issue<T, D, G, kPaged>(a, ictx, t0, t1, bufs, false);
-        ictx.queries_from_lds(s_q, s_qb, s.qscale);
-        float *po = a.w.part_o + ((int64_t)cgrp * kItemsPerGroupMax + wit) * G * D;
-        float *pl = a.w.part_l + ((int64_t)cgrp * kItemsPerGroupMax + wit) * G;
+        const bool sink_item = cgi.is_sink(wit);
+        int sti[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            sti[j] = sink_item ? 0 : cst[j];
+        item_issue<T, D, G, kPaged>(a, ictx, t0, t1, bufs, false);
+        float *po = a.w.part_o + ((int64_t)wgrp * kItemsPerGroupMax + wit) * G * D;
+        float *pl = a.w.part_l + ((int64_t)wgrp * kItemsPerGroupMax + wit) * G;
         item_finish<T, D, G, kPaged>(a, ictx, t0, t1, sti, lds, bufs, [&](int j, int dim, float o, float lg) {
             st_wt(po + j * D + dim, o);
             if (dim == 0)
                 st_wt(pl + j, lg);
         });
-        if (pool_words && threadIdx.x == 0) {
-            pst = ld_wt(ps + kPoolState);
-            phd = ld_wt(ps + kPoolHead);
-        }
-        wait_vmem();  // this wave's partial stores have completed
+        wait_vmem();
         __syncthreads();
-    };
-    // The first own item runs before the loop: the speculative loads hold its
-    // rows when its bounds are the speculated ones.  Inside the loop every
-    // item requests its own rows, so no K/V register lives across a merge.
-    bool pending = false;  // an item of cgrp was run and is not counted yet
-    if (jj < n_own) {
-        const int wit = n - 1 - jj;
-        jj += a.wpg;
-        int t0, t1;
-        gi.item(wit, t0, t1);
-        run_item(wit, spec && t0 == sp_t0 && t1 == sp_t1, jj >= n_own);
-        pending = true;
-    }
-    for (;;) {
-        if (pending) {
-            uint32_t *counter = a.w.grp_sync + (int64_t)cgrp * kGrpStride;
-            if (threadIdx.x == 0)
-                s_last = atomicAdd(counter, 1u) == (uint32_t)(cn - 1);
-            __syncthreads();
-            if (s_last) {
-                // This count completed the group: merge it, with its cached
-                // summaries, requested with the partials.
-                float c_l[MP::NPK], c_o[MP::NPK][2];
-                load_cached<T, D, G, kBlock>(
-                    a, cgrp, [&](int j) { return code_slot(ccode[j], s.r, s.K); }, c_l, c_o);
-                // Fresh pool words, read while the merge runs.
-                if (threadIdx.x == 0) {
-                    pst = ld_wt(ps + kPoolState);
-                    phd = ld_wt(ps + kPoolHead);
-                }
-                const CoherentParts<D, G> src{
-                    a.w.part_o + (int64_t)cgrp * kItemsPerGroupMax * G * D,
-                    a.w.part_l + (int64_t)cgrp * kItemsPerGroupMax * G};
-                // e and the readiness as read at the start of the launch (the
-                // group's epoch is not rewritten before this merge does it).
-                merge_group<T, D, G, kBlock>(a, cgrp, cn, csg, ce, cready, src, lds, c_l, c_o);
-                if (threadIdx.x == 0) {
-                    st_wt(counter, 0u);
-                    st_wt(counter + kGrpSpan, (uint32_t)(ce - csg + 1));
-                    group_complete(a, cgrp, NG);
-                }
-            }
-            pending = false;
+        if (count_item(wgrp, cn)) {
+            float c_l[MP::NPK], c_o[MP::NPK][2];
+            load_cached<T, D, G, kBlock>(
+                a, wgrp, [&](int j) { return code_slot(ccode[j], s.r, s.K); }, c_l, c_o);
+            merge(wgrp, cn, csg, ce, cready, c_l, c_o);
         }
-        int wgrp, wit;
-        bool last_own = false;
-        if (jj < n_own) {
-            wgrp = grp;
-            wit = n - 1 - jj;
-            jj += a.wpg;
-            last_own = jj >= n_own;
-        } else {
-            const int ent = pool_take(ps, tag32, NG, pst, phd, &s_slot);
-            pst = phd = ~0ull;
-            if (ent < 0) {
-                if (ent == -2 && threadIdx.x == 0) {
-                    atomicOr(&sync[kSyncSticky], (unsigned long long)MAC_DEV_SYNC_TIMEOUT);
-                    atomicOr(&sync[kSyncBroken], 1ull);
-                }
-                break;
-            }
-            wgrp = ent >> 8;
-            wit = ent & 0xff;
-        }
-        wgrp = __builtin_amdgcn_readfirstlane(wgrp);
-        wit = __builtin_amdgcn_readfirstlane(wit);
-        if (wgrp != cgrp) {
-            // A pool item of another group: its plan record and queries.
-            const int32_t *rec = a.w.gplan + (int64_t)wgrp * kPlanWords;
-            if (threadIdx.x < kPlanCodes + G)
-                s_plan[threadIdx.x] =
-                    (int)ld_wt_u32(reinterpret_cast<const uint32_t *>(rec + threadIdx.x));
-            const int b2 = wgrp / s.Hkv, g2 = wgrp - b2 * s.Hkv;
-            QueryStage<D, G> q2;
-            q2.request(a, b2, g2);
-            __syncthreads();  // plan words in LDS; s_q and s_qb free
-            q2.store(s_q);
-            if constexpr (AS::kMfma)
-                q2.store_b(s_qb, s.qscale);
-            cgrp = wgrp;
-            ce = __builtin_amdgcn_readfirstlane(s_plan[kPlanE]);
-            csg = __builtin_amdgcn_readfirstlane(s_plan[kPlanStart]);
-            cn = __builtin_amdgcn_readfirstlane(s_plan[kPlanN]);
-            cready = __builtin_amdgcn_readfirstlane(s_plan[kPlanReady]) != 0;
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                ccode[j] = __builtin_amdgcn_readfirstlane(s_plan[kPlanCodes + j]);
-                cst[j] = code_start(ccode[j]);
-            }
-            cgi = GroupItems(csg, ce, s.r, s.F, true, s.cmin);
-            __syncthreads();  // queries in LDS
-        }
-        run_item(wit, false, last_own);
-        pending = true;
     }
 }
 

@@ -125,10 +125,14 @@ enum { kPlanE = 0, kPlanStart = 1, kPlanN = 2, kPlanReady = 3, kPlanCodes = 4 };
 // Synchronisation line of the workspace (64-bit words).
 constexpr int kLineU64 = 16;
 constexpr int kSyncWords = kLineU64;
-// Default form of the decode step: one launch for at most this many KV
-// groups per layer (latency-bound steps), three kernels above (measured on
-// MI355X: one launch is ahead at 8 groups, behind at 64 and 128).
+// Default form of the decode step: one launch for at most
+// kSingleLaunchMaxGroups KV groups per layer (latency-bound steps), the
+// match kernel and one launch for the rest up to kTwoStageMaxGroups, three
+// kernels above (measured on MI355X: one launch is ahead at 8 groups, two
+// kernels at 64, three at 128, where long missed ranges dominate and the
+// attention kernel's global balanced split wins).
 constexpr int kSingleLaunchMaxGroups = 16;
+constexpr int kTwoStageMaxGroups = 64;
 // Match keys of the three-kernel step are kKeyStride words apart (one
 // 128-byte line per head): the atomic minima of a head's splits serialise
 // per line, so heads must not share one.

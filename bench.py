@@ -62,6 +62,10 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="time HIP-graph replays of the steps (one graph per step, all "
                          "layers; needs --append fused) instead of eager launches")
+    ap.add_argument("--alloc", choices=("pool", "layer"), default="pool",
+                    help="K/V, rings and workspaces of all layers as slices of one "
+                         "allocation each (as a serving engine's KV pool), or one "
+                         "allocation per layer and tensor")
     ap.add_argument("--json-out", default="")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (the "
@@ -265,15 +269,34 @@ def main():
     aux = torch.cuda.Stream()
 
     layers = []
-    for li in range(NL):
-        L = dict(K=K0 if li == 0 else K0.clone(), V=V0 if li == 0 else V0.clone(),
-                 q_ring=torch.zeros((B, H, R, d), dtype=K0.dtype, device=dev),
-                 o_ring=torch.zeros((B, H, R, d), device=dev),
-                 lse_ring=torch.zeros((B, H, R), device=dev),
-                 pos_ring=torch.zeros((B, cfg.n_kv_heads, R), dtype=torch.int32, device=dev),
-                 ws=torch.empty(wsb, dtype=torch.uint8, device=dev),
-                 out=torch.empty((B, H, d), device=dev))
-        layers.append(L)
+    if args.alloc == "pool":
+        # One allocation per kind for all layers; layer li uses slice li.
+        wsb_al = -(-wsb // 256) * 256
+        pools = dict(K=torch.empty((NL,) + tuple(K0.shape), dtype=K0.dtype, device=dev),
+                     V=torch.empty((NL,) + tuple(V0.shape), dtype=V0.dtype, device=dev),
+                     q_ring=torch.zeros((NL, B, H, R, d), dtype=K0.dtype, device=dev),
+                     o_ring=torch.zeros((NL, B, H, R, d), device=dev),
+                     lse_ring=torch.zeros((NL, B, H, R), device=dev),
+                     pos_ring=torch.zeros((NL, B, cfg.n_kv_heads, R), dtype=torch.int32,
+                                          device=dev),
+                     ws=torch.empty((NL, wsb_al), dtype=torch.uint8, device=dev),
+                     out=torch.empty((NL, B, H, d), device=dev))
+        pools["K"][:] = K0
+        pools["V"][:] = V0
+        del K0, V0
+        for li in range(NL):
+            layers.append({k: v[li] for k, v in pools.items()})
+        K0, V0 = layers[0]["K"], layers[0]["V"]
+    else:
+        for li in range(NL):
+            L = dict(K=K0 if li == 0 else K0.clone(), V=V0 if li == 0 else V0.clone(),
+                     q_ring=torch.zeros((B, H, R, d), dtype=K0.dtype, device=dev),
+                     o_ring=torch.zeros((B, H, R, d), device=dev),
+                     lse_ring=torch.zeros((B, H, R), device=dev),
+                     pos_ring=torch.zeros((B, cfg.n_kv_heads, R), dtype=torch.int32, device=dev),
+                     ws=torch.empty(wsb, dtype=torch.uint8, device=dev),
+                     out=torch.empty((B, H, d), device=dev))
+            layers.append(L)
     # Warm the rings of layer 0 from the prompt tail; the other layers copy them.
     L0 = layers[0]
     h0 = mac.mac_init_rings(p, L0["q_ring"], L0["o_ring"], L0["lse_ring"], L0["pos_ring"],

@@ -91,8 +91,9 @@ enum { MAC_THRESH_ONE_MINUS_TAU = 0, MAC_THRESH_TAU = 1 };
  *   one workgroup per KV group resident).
  * At most one of these three may be set.  With none, the step is one launch
  * when a layer has at most 16 KV groups (batch * n_kv_heads) and the shape
- * is one the single launch handles, where the step is bound by latency, and
- * three kernels otherwise, where it is bound by bandwidth.
+ * is one the single launch handles (the step is bound by latency), two
+ * kernels up to 64 KV groups, and three kernels above (bound by bandwidth:
+ * the attention kernel balances all groups' work across the device).
  * All forms give the same results bit for bit.
  *   MAC_FLAG_MATCH_FILTER: exact lower-bound filter of the match (blog,
  *   "Production version: one fused persistent BF16 kernel", the match-scan

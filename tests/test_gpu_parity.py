@@ -213,6 +213,34 @@ def test_run_to_run_deterministic_and_launch_and_append_mode_invariant():
             assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("batch", [8, 16])
+def test_forms_bitwise_equal_many_groups(batch):
+    """Above 16 KV groups (64 and 128: the coarser 128-token grid, the
+    two-kernel default and, with missed heads' long ranges, the cross-group
+    pool) the one-launch, two-kernel and three-kernel forms give the same
+    outputs, matches and rings bit for bit."""
+    cfg = _cfg(batch=batch, ctx=6000, steps=10, ring_k=256, band_r=64, sigma=(0.02, 0.5),
+               seed=11)
+    K, V, qt, q = _inputs(cfg)
+    single, two = mac.MAC_FLAG_SINGLE_LAUNCH, mac.MAC_FLAG_TWO_STAGES
+    split, fused = mac.MAC_FLAG_SPLIT_STAGES, mac.MAC_FLAG_FUSED_APPEND
+    runs = []
+    for flags in (split | fused, two | fused, single | fused, 0):
+        print("  batch %d, flags %d" % (batch, flags), flush=True)
+        layer = Layer(cfg, K, V, qt, q, params=params_for(cfg, flags=flags))
+        res = run_steps(layer.init(), cfg.steps)
+        res["rings"] = [t.cpu().float().numpy() for t in
+                        (layer.q_ring, layer.o_ring, layer.lse_ring, layer.pos_ring)]
+        runs.append(res)
+        layer.release()
+    assert (runs[0]["p"] < 0).any() and (runs[0]["p"] >= 0).any()
+    for r in runs[1:]:
+        for k in ("out", "lse", "p", "d2"):
+            assert np.array_equal(runs[0][k], r[k]), k
+        for x, y in zip(runs[0]["rings"], r["rings"]):
+            assert np.array_equal(x, y)
+
+
 def test_lockstep_split_stages(oracle_lib):
     """The three-kernel form of the step against the oracle (the other
     lockstep tests have at most 16 KV groups, so they run one launch)."""
