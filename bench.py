@@ -48,9 +48,13 @@ def parse():
                     help="decode step as one launch, as a match kernel and one launch for "
                          "plan / attention / merge, as match / attend / merge kernels, "
                          "or the library's choice for the shape")
-    ap.add_argument("--match-filter", action="store_true",
+    ap.add_argument("--match-filter", choices=("auto", "on", "off"), default="auto",
                     help="exact lower-bound filter of the match (second halves of ring "
-                         "rows read only where a hit is still possible)")
+                         "rows read only where a hit is still possible); auto: on where "
+                         "the step runs the match kernel (more than 16 KV groups per "
+                         "layer, or --launch two / split), where the match is bound by "
+                         "bandwidth, off in the one-launch step, where it is bound by "
+                         "latency")
     ap.add_argument("--page-size", type=int, default=0,
                     help="read K/V from a paged pool with pages of this many tokens, "
                          "shuffled through a page table (0 = dense cache)")
@@ -62,6 +66,9 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="time HIP-graph replays of the steps (one graph per step, all "
                          "layers; needs --append fused) instead of eager launches")
+    ap.add_argument("--thresh", choices=("one-minus-tau", "tau"), default="one-minus-tau",
+                    help="acceptance threshold: distance < (1 - tau) sqrt(2d) (default), or "
+                         "< tau sqrt(2d), the other reading of the pages")
     ap.add_argument("--alloc", choices=("pool", "layer"), default="pool",
                     help="K/V, rings and workspaces of all layers as slices of one "
                          "allocation each (as a serving engine's KV pool), or one "
@@ -83,12 +90,22 @@ def default_layers(cfg):
     return int(max(1, min(64, math.ceil(768 * 2 ** 20 / est))))
 
 
+DEVICE_SOURCES = ("mac_device.h", "mac_internal.h", "mac_kernels.hip", "mac_step_impl.h",
+                  "mac_step_bf16_128.hip", "mac_step_bf16_64.hip", "mac_step_f32_128.hip",
+                  "mac_step_f32_64.hip")
+
+
 def source_hash():
     """Hash of the device-code sources the PMC counters were taken on."""
     h = hashlib.sha256()
-    for f in ("mac_kernels.hip", "mac_internal.h"):
+    for f in DEVICE_SOURCES:
         h.update(open(os.path.join(ROOT, "attention_reuse_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
+
+
+def thresh_mode(args):
+    from attention_reuse_amd import mac
+    return mac.MAC_THRESH_TAU if args.thresh == "tau" else mac.MAC_THRESH_ONE_MINUS_TAU
 
 
 def read_traffic(workload_name, kernel):
@@ -145,7 +162,7 @@ def algorithmic_bytes(cfg, match_p, m, second_halves=None):
                 hits=hits, group_miss=int((match_p.reshape(B, Hkv, G) < 0).any(axis=2).sum()))
 
 
-def cpu_baseline(cfg, K, V, qt, q, budget_s):
+def cpu_baseline(cfg, K, V, qt, q, budget_s, mode=0):
     """The CPU oracle, as is, on a bounded sample of the same workload: at
     most one (request, head) stream per thread, spread over the requests and
     heads, for as many decode steps as the time budget allows."""
@@ -158,7 +175,7 @@ def cpu_baseline(cfg, K, V, qt, q, budget_s):
     except AttributeError:
         avail = nproc
     threads = max(1, min(16, avail))
-    t2 = orc.threshold2(cfg.head_dim, cfg.tau)
+    t2 = orc.threshold2(cfg.head_dim, cfg.tau, mode=mode)
     W = cfg.n_warm
     all_heads = [(b, h) for b in range(cfg.batch) for h in range(cfg.n_q_heads)]
     stride = max(1, len(all_heads) // threads)
@@ -218,6 +235,11 @@ def main():
         sys.exit("warmup + steps exceeds the %d decode steps of the workload" % cfg.steps)
     B, H, Hkv, d, R, W = (cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim,
                           cfg.ring_k, cfg.n_warm)
+    if args.match_filter == "auto":
+        args.match_filter = args.launch in ("two", "split") or (
+            args.launch == "auto" and B * Hkv > 16)
+    else:
+        args.match_filter = args.match_filter == "on"
     t_gen = time.perf_counter()
     K, V = wl.gen_kv(cfg)
     qt, q, _, _ = wl.gen_queries(cfg)
@@ -257,7 +279,8 @@ def main():
         paging = dict(page_size=P, max_pages=npg, page_table=table,
                       strides=(Hkv * P * d, P * d, d))
     p = mac.make_params(B, H, Hkv, d, mac.MAC_DTYPE_F32 if cfg.dtype == "f32" else mac.MAC_DTYPE_BF16,
-                        R, cfg.band_r, cfg.capacity, cfg.tau, **paging,
+                        R, cfg.band_r, cfg.capacity, cfg.tau, thresh_mode=thresh_mode(args),
+                        **paging,
                         flags=(mac.MAC_FLAG_FUSED_APPEND if args.append == "fused" else 0)
                         | (mac.MAC_FLAG_MATCH_FILTER if args.match_filter else 0)
                         | {"auto": 0, "single": mac.MAC_FLAG_SINGLE_LAUNCH,
@@ -476,7 +499,7 @@ def main():
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(cfg, K, V, qt, q, args.cpu_seconds)
+        cpu = cpu_baseline(cfg, K, V, qt, q, args.cpu_seconds, mode=thresh_mode(args))
 
     alg_step = sum(per[k] for k in ("match", "attend", "merge", "append")) / args.steps
     value = B * H * NL / (ms_per_step * 1e-3)
@@ -500,6 +523,8 @@ def main():
                    "layers": NL, "kv_dtype": cfg.dtype,
                    "batch": B, "q_heads": H, "kv_heads": Hkv, "head_dim": d,
                    "context": cfg.ctx, "ring_k": R, "band_r": cfg.band_r, "tau": cfg.tau,
+                   "threshold": ("tau*sqrt(2d)" if args.thresh == "tau"
+                                 else "(1-tau)*sqrt(2d)"),
                    "parallelism": "1 GPU"},
         "kv_gb_per_step": round(per["kv"] / args.steps / 1e9, 4),
         "full_kv_gb_per_step": round(per["full_kv"] / args.steps / 1e9, 4),
