@@ -408,8 +408,11 @@ def main():
     n_ls = args.steps * NL
     per_launch = {k: v / n_ls for k, v in per.items()}
 
-    # Per-stage kernel durations with HIP events, on the stream each stage
-    # runs on, over a second pass of the same steps.
+    # Per-kernel durations: HIP events recorded by the library around each
+    # kernel, on the stream it runs on, in a second pass over the same steps
+    # from the same ring state.  (Recorded inside the timed pass, the events
+    # would add about 2 us of gap per record to the timed step: 20% at the
+    # default workload.)
     stage_ms = None
     if not args.no_profile and args.mode == "mac":
         reset_rings()
@@ -533,7 +536,9 @@ def main():
         "hit_rate": round(per["hits"] / (n_ls * B * H), 4),
         "group_miss_rate": round(per["group_miss"] / (n_ls * B * Hkv), 4),
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()} if stage_ms else None,
-        "timing": "graph replay" if graphs else "eager launches",
+        "timing": ("graph replay" if graphs else "eager launches") + (
+            "; per-kernel HIP events from a second eager pass of the same steps"
+            if stage_ms else ""),
         "full_decode_ms_per_step": round(full_ms, 4) if full_ms else None,
         "speedup_vs_full_decode": round(full_ms / ms_per_step, 3) if full_ms else None,
         "achievable_read_gbs": round(read_gbs, 1) if read_gbs else None,
