@@ -2393,6 +2393,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     using AS = AttendShape<T, D, G>;
     using MS = MergeShape<T, D, G>;
     using MP = MergePairs<D, G, kBlock>;
+    // The cross-group pool is part of the group kernel of the two-kernel
+    // form only.  In the one-launch kernel (the default up to 16 KV groups)
+    // its state cost every hit step more than it saved on the missed ones
+    // (measured at 8 groups), so there a group runs all its items itself.
+    constexpr bool kPool = !kMatch;
     constexpr int kFloats = AS::kFloats > MS::kFloats ? AS::kFloats : MS::kFloats;
     __shared__ float lds[kFloats];
     __shared__ unsigned long long s_keys[kMaxSingleUnits];
@@ -2544,16 +2549,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const GroupItems gi(e_ok ? sg : 0, e_ok ? e : 0, s.r, s.F, true, s.cmin);
     const int n = e_ok ? gi.n : 0;
 
-    // Items the group's own workgroups run: all of a hit range; of a range
-    // cut on a grid coarser than the minimum (a head missed: a long range),
-    // one per workgroup -- the items nearest the end -- while the rest go to
-    // the launch's pool, where any workgroup that has finished its own work
-    // claims them.  The group's first workgroup publishes: the plan record
-    // (completed before the entries are written), then the entries, and in
-    // any case counts the group as planned.
+    // Items the group's own workgroups run: all of a hit range; with the
+    // pool, of a range cut on a grid coarser than the minimum (a head missed:
+    // a long range), one per workgroup -- the items nearest the end -- while
+    // the rest go to the launch's pool, where any workgroup that has
+    // finished its own work claims them.  The group's first workgroup
+    // publishes: the plan record (completed before the entries are written),
+    // then the entries, and in any case counts the group as planned.
     const uint32_t tag32 = (uint32_t)(E + 1);
     unsigned long long *ps = pool_set(a, E);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (kPool && blockIdx.x == 0 && threadIdx.x == 0) {
         // The other pool set, which no workgroup of this launch touches (the
         // previous launch on this workspace, which used it, has ended), is
         // cleared for the next launch.
@@ -2562,8 +2567,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         st_wt(nxt + kPoolHead, 0ull);
     }
     const bool coarse = n > 0 && gi.n_main > 0 && gi.rs.cs > s.cmin;
-    const int n_own = coarse && n > a.wpg ? a.wpg : n;
-    if (loc == 0) {
+    const int n_own = kPool && coarse && n > a.wpg ? a.wpg : n;
+    if (kPool && loc == 0) {
         const int n_pool = n - n_own;
         if (n_pool > 0) {
             int32_t *rec = a.w.gplan + (int64_t)grp * kPlanWords;
@@ -2624,7 +2629,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     // does it).
     auto merge = [&](int mg, int mn, int msg, int me, bool mready, const float(&c_l)[MP::NPK],
                      const float(&c_o)[MP::NPK][2]) {
-        if (threadIdx.x == 0) {
+        if (kPool && threadIdx.x == 0) {
             pst = ld_wt(ps + kPoolState);
             phd = ld_wt(ps + kPoolHead);
         }
@@ -2678,7 +2683,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         float c_l[MP::NPK], c_o[MP::NPK][2];
         load_cached<T, D, G, kBlock>(
             a, grp, [&](int j) { return code_slot(s_code[j], s.r, s.K); }, c_l, c_o);
-        if (threadIdx.x == 0) {
+        if (kPool && threadIdx.x == 0) {
             pst = ld_wt(ps + kPoolState);
             phd = ld_wt(ps + kPoolHead);
         }
@@ -2696,6 +2701,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             merge(grp, n, sg, e, ready, c_l, c_o);
     }
 
+    if constexpr (!kPool)
+        return;
     // Pool items of any group, until the pool is drained.
     for (;;) {
         const int ent = pool_take(ps, tag32, NG, pst, phd, &s_slot);
