@@ -13,10 +13,11 @@ namespace mac {
 // and on the shape's minimum Cmin, so a head that misses sees exactly the
 // items of a full decode of the same shape.  Cmin is 64 tokens for layers
 // of at most kSingleLaunchMaxGroups KV groups (parallelism inside a group
-// matters) and 128 above (each workgroup then holds its whole share of a
-// hit range in flight at once).
+// matters) and 256 above (measured at 64 groups, 8 workgroups each: fewer,
+// longer items stream within one workgroup instead of running as two
+// items one after the other, and the merge folds fewer partials).
 constexpr int kChunkMinShift = 6;
-constexpr int kChunkMinShiftWide = 7;
+constexpr int kChunkMinShiftWide = 8;
 // Work of an item in the attention kernel's balanced split: its tokens plus
 // this many (the per-item cost of combining rows and storing the partial).
 constexpr int kItemCost = 64;

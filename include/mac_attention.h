@@ -387,7 +387,7 @@ const char *mac_status_string(mac_status s);
 
 /* The minimum grid of the split-KV partition for a shape (host mirror of
  * the device planner): 64 tokens for layers of at most 16 KV groups
- * (batch * n_kv_heads), 128 above; -1 on invalid parameters.  Every entry
+ * (batch * n_kv_heads), 256 above; -1 on invalid parameters.  Every entry
  * point on the same parameters (decode step in either form, full decode)
  * cuts ranges on the same grid, so a missing head equals the full decode
  * bit for bit. */

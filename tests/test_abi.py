@@ -113,11 +113,11 @@ def test_status_strings_and_chunk(lib):
 
 
 def test_min_chunk_by_shape(lib):
-    """64-token grid up to 16 KV groups per layer, 128 above."""
+    """64-token grid up to 16 KV groups per layer, 256 above."""
     assert mac.mac_min_chunk_tokens(_params(batch=2)) == 64      # 16 groups
     assert mac.mac_min_chunk_tokens(_params(batch=1)) == 64
-    assert mac.mac_min_chunk_tokens(_params(batch=3)) == 128     # 24 groups
-    assert mac.mac_min_chunk_tokens(_params(batch=16)) == 128
+    assert mac.mac_min_chunk_tokens(_params(batch=3)) == 256     # 24 groups
+    assert mac.mac_min_chunk_tokens(_params(batch=16)) == 256
     assert mac.mac_min_chunk_tokens(_params(batch=0)) == -1
 
 
@@ -194,7 +194,7 @@ def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
         mac.load()
 
 
-@pytest.mark.parametrize("cmin", [64, 128])
+@pytest.mark.parametrize("cmin", [64, 128, 256])
 @pytest.mark.parametrize("s,e,r", [(0, 0, 0), (0, 127, 32), (0, 128, 32), (5, 1000, 256),
                                    (300, 1000, 256), (900, 1000, 256), (0, 262399, 256),
                                    (1000, 1000, 0), (0, 500, 1000), (640, 1000, 361)])
@@ -222,7 +222,7 @@ def test_partition_covers_range_on_the_grid(lib, s, e, r, cmin):
     assert lib.mac_partition(0, 4, 0, 100, None, None, 0) == -1
 
 
-@pytest.mark.parametrize("cmin", [64, 128])
+@pytest.mark.parametrize("cmin", [64, 128, 256])
 @pytest.mark.parametrize("s,e,r,F", [(0, 0, 0, 64), (0, 63, 16, 64), (0, 200, 16, 64),
                                      (150, 3000, 256, 128), (0, 33000, 256, 128),
                                      (500, 600, 600, 4096), (0, 5000, 0, 1), (10, 90, 5, 0)])

@@ -15,7 +15,7 @@ if torch.cuda.is_available():
     from mac_harness import (DEV, Layer, lockstep_compare, params_for, to_dev,
                              tolerance_check)
 
-SPLIT, FUSED, SINGLE = 2, 1, 4
+SPLIT, FUSED, SINGLE, TWO = 2, 1, 4, 16
 
 
 def _cfg(**kw):
@@ -207,12 +207,14 @@ def test_forms_bitwise_with_sink_and_epochs():
             assert np.array_equal(x, y)
 
 
-@pytest.mark.parametrize("flags", [FUSED, FUSED | SPLIT])
+@pytest.mark.parametrize("flags", [FUSED, FUSED | SPLIT, FUSED | TWO])
 def test_epoch_gating_inside_captured_graph(flags):
     """A decode step captured once in a HIP graph and replayed (one launch,
-    or three kernels): epochs bumped on the device between replays take
+    two kernels or three): epochs bumped on the device between replays take
     effect in the graph, and every replay equals the same step run eagerly
-    on a second layer."""
+    on a second layer.  The two-kernel form alternates its key sets and
+    pool sets by the launch epoch counted on the device, so replays of one
+    captured launch stay correct."""
     cfg = _cfg(batch=2, steps=12, sigma=(0.02, 0.1))
     K, V = wl.gen_kv(cfg)
     qt, q, _, _ = wl.gen_queries(cfg)
