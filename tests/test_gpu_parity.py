@@ -382,7 +382,7 @@ def test_aux_append_ignores_pos_overwritten_after_the_call():
     ref_rings = [t.cpu().float().numpy() for t in
                  (ref_layer.q_ring, ref_layer.o_ring, ref_layer.lse_ring, ref_layer.pos_ring)]
     ref_layer.release()
-    for flags in (0, mac.MAC_FLAG_SPLIT_STAGES):
+    for flags in (0, mac.MAC_FLAG_SPLIT_STAGES, mac.MAC_FLAG_TWO_STAGES):
         layer = Layer(cfg, K, V, qt, q, params=params_for(cfg, flags=flags)).init()
         aux = torch.cuda.Stream()
         ms = torch.cuda.current_stream()
