@@ -262,6 +262,18 @@ __device__ inline bool end_ok(const StepArgs &a, int e)
     return e < a.s.T && (a.mode == kPlanInit || e >= 0);
 }
 
+// Load of a word that is the same for the whole workgroup and was written
+// before the launch began, as a scalar load: such loads are issued back to
+// back and waited for together, where plain loads of memory that the kernel
+// also writes become vector loads, each waited for before the branch that
+// uses it.  The scalar cache is invalidated at launch, so the value is the
+// one of the launch's start or a later one.
+template <class V>
+__device__ inline V ld_uniform(const V *p)
+{
+    return *(const __attribute__((address_space(4))) V *)p;
+}
+
 // Whether KV group grp (of request b) may reuse its rings: always when the
 // caller binds no epochs, else when the request's epoch is non-negative and
 // equals the one the group's rings were built for.  A group that is not
@@ -270,10 +282,11 @@ __device__ inline bool end_ok(const StepArgs &a, int e)
 // (see ring_append_pos).
 __device__ inline bool group_ready(const StepArgs &a, int b, int grp)
 {
-    if (!a.epoch)
-        return true;
-    const int32_t ep = a.epoch[b];
-    return ep >= 0 && a.w.ring_epoch[grp] == ep;
+    // Both words are requested without a branch (with no epochs bound the
+    // first reads the group's own word, and the result is true).
+    const int32_t built = ld_uniform(a.w.ring_epoch + grp);
+    const int32_t ep = ld_uniform(a.epoch ? a.epoch + b : a.w.ring_epoch + grp);
+    return !a.epoch || (ep >= 0 && built == ep);
 }
 
 // Position-ring update of the rectify-append of KV group grp at position e,
@@ -944,29 +957,34 @@ __device__ inline void load_cached(const StepArgs &a, int grp, SlotOf &&slot_of,
     using MP = MergePairs<D, G, NT>;
     const Shape &s = a.s;
     const int b = grp / s.Hkv, g = grp - b * s.Hkv;
-    // Branch-free: every thread loads and selects afterwards, so that
-    // nothing that uses the values is moved next to the loads, where it
-    // would wait for them (and for every load requested before them).  A
-    // thread with nothing to load reads the first element of the rings, or,
-    // where there are no rings (full decode: every head misses), of the
-    // workspace's rectified summaries, which always exist.
-    const float *lse_src = a.lse_ring ? a.lse_ring : a.w.rect_l;
-    const float *o_src = a.o_ring ? a.o_ring : a.w.rect_o;
+    // Branch-free: the group's G heads' rings as buffers, and a thread with
+    // nothing to load reads at the buffers' size, which returns zeros
+    // without a memory access (so do all reads where there are no rings:
+    // full decode, every head missed).  A plain load whose value is selected
+    // afterwards was turned into a conditional load, and the merge's rescale
+    // of the lse moved next to it, where it waited for every load requested
+    // before it (the first item's K/V rows among them).
+    const int64_t h0 = (int64_t)b * s.Hq + g * G;
+    const uint32_t n_l = a.lse_ring ? (uint32_t)(G * s.K) * 4u : 0u;
+    const uint32_t n_o = a.o_ring ? (uint32_t)(G * s.K * D) * 4u : 0u;
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+        a.lse_ring ? a.lse_ring + h0 * s.K : nullptr, (short)0, (int)n_l, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        a.o_ring ? a.o_ring + h0 * s.K * D : nullptr, (short)0, (int)n_o, 0x00020000);
 #pragma unroll
     for (int k = 0; k < MP::NPK; ++k) {
         const int pt = threadIdx.x + k * NT;
         const bool pair = pt < MP::NPAIR;
         const int pp = pair ? pt : 0;
         const int jj = 2 * pp / D, dim = 2 * pp - jj * D;
-        const int bh = b * s.Hq + g * G + jj;
         const int slot = slot_of(jj);
         const bool use = pair && slot >= 0;
-        const int64_t ri = use ? (int64_t)bh * s.K + slot : 0;
-        const float l = lse_src[ri];
-        const float2 v = *reinterpret_cast<const float2 *>(o_src + (use ? ri * D + dim : 0));
-        c_l[k] = use ? l : -INFINITY;
-        c_o[k][0] = use ? v.x : 0.f;
-        c_o[k][1] = use ? v.y : 0.f;
+        const uint32_t ri = (uint32_t)(jj * s.K + slot);
+        const uint32_t l = __builtin_amdgcn_raw_buffer_load_b32(rl, use ? ri * 4u : n_l, 0, 0);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(ro, use ? (ri * D + dim) * 4u : n_o, 0, 0);
+        c_l[k] = use ? __uint_as_float(l) : -INFINITY;
+        c_o[k][0] = __uint_as_float(v[0]);
+        c_o[k][1] = __uint_as_float(v[1]);
     }
 }
 
@@ -2412,41 +2430,60 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int b = grp / s.Hkv, g = grp - b * s.Hkv;
     const int bh0 = b * s.Hq + g * G;
     unsigned long long *sync = a.w.sync;
-    // Requested first, so that waiting for them waits for nothing else.  The
-    // done counter is read with a plain load: its value from earlier
-    // launches is visible at kernel start, and the increments of this
-    // launch's groups leave floor(done / 2^s) unchanged until this
-    // workgroup's own group completes.
-    const int e = a.pos[b];
-    // Read before this workgroup's keys are stored (they depend on it), so
-    // before the group can complete and its merge restart the rings.
+    // Entry.  The words of the launch's start (position, counters, the
+    // group's previous span, readiness) are scalar loads, requested together
+    // with the vector loads that need none of them (the first match unit's
+    // ring rows, the queries, the group kernel's key words of both sets);
+    // the first wait is for the scalar words.  The done counter's value from
+    // earlier launches is visible at kernel start, and the increments of
+    // this launch's groups leave floor(done / 2^s) unchanged until this
+    // workgroup's own group completes.  Readiness is read before this
+    // workgroup's keys are stored (they depend on it), so before the group
+    // can complete and its merge restart the rings.
+    const int e = ld_uniform(a.pos + b);
+    const unsigned long long done = ld_uniform(sync + kSyncDone);
+    const unsigned long long broken = ld_uniform(sync + kSyncBroken);
+    const int span_prev = (int)ld_uniform(a.w.grp_sync + (int64_t)grp * kGrpStride + kGrpSpan);
     const bool ready = group_ready(a, b, grp);
-    const unsigned long long done = sync[kSyncDone];
-    // An earlier launch on this workspace gave up waiting, so the counters
-    // may be inconsistent: every launch until the ring reset writes NaN
-    // outputs and computes nothing (no workgroup waits, so none can time out).
-    if (sync[kSyncBroken] != 0) {
-        if (loc == 0)
-            group_invalid<D, G>(a, grp, bh0);
-        return;
-    }
-    const int span_prev = (int)a.w.grp_sync[(int64_t)grp * kGrpStride + kGrpSpan];
-    const unsigned long long E = done >> a.done_shift;
     // The group's queries and K/V row pointers do not depend on the plan.
     QueryStage<D, G> qs;
     ItemCtx<T, D, G, kPaged> ctx(a, b, g, true);
     unsigned long long hkey = ~0ull;  // group kernel: head's key (lanes j * 64 / G)
+    unsigned long long hkey1 = ~0ull;
+    int uj = 0, ufirst = 0;
+    MatchLoads<T, D, U> ml;
+    if constexpr (kMatch) {
+        single_unit(a, loc, uj, ufirst);
+        match_issue<T, D, U>(a, ufirst, bh0 + uj, ml);
+        qs.request(a, b, g);
+    } else {
+        // The match kernel finished every key of set E & 1; the words of
+        // both sets (the workspace always holds two) are requested, so that
+        // the request does not wait for E.
+        qs.request(a, b, g);
+        if (threadIdx.x < 64 && threadIdx.x % (64 / G) == 0) {
+            const int64_t o = (int64_t)(bh0 + threadIdx.x / (64 / G)) * kKeyStride;
+            hkey = a.w.keys[o];
+            hkey1 = a.w.keys[(int64_t)s.B * s.Hq * kKeyStride + o];
+        }
+    }
+    // Keeps the done counter's load with the others: without a use here it
+    // is moved past the branch below and waited for on its own.
+    __asm__ volatile("" ::"s"(done));
+    // An earlier launch on this workspace gave up waiting, so the counters
+    // may be inconsistent: every launch until the ring reset writes NaN
+    // outputs and computes nothing (no workgroup waits, so none can time out).
+    if (broken != 0) {
+        if (loc == 0)
+            group_invalid<D, G>(a, grp, bh0);
+        return;
+    }
+    const unsigned long long E = done >> a.done_shift;
     int sp_t0 = 0, sp_t1 = 0;
     bool spec = false;
     ItemBufs<T, D, G> bufs;
     bool ok = true;
     if constexpr (kMatch) {
-        int uj, ufirst;
-        single_unit(a, loc, uj, ufirst);
-        MatchLoads<T, D, U> ml;
-        match_issue<T, D, U>(a, ufirst, bh0 + uj, ml);
-        qs.request(a, b, g);
-
         unsigned long long *klds = reinterpret_cast<unsigned long long *>(lds);
         const int64_t rep_stride = (int64_t)NG * a.nkw;
         unsigned long long *kw = a.w.skeys + (int64_t)grp * a.nkw;
@@ -2474,23 +2511,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             ok = poll_keys(a, kw + (loc % kKeyReps) * rep_stride, tag8, s_keys);
         ok = block_and(ok);
     } else {
-        // Group kernel: the match kernel has finished every key (set E & 1).
-        // The first workgroup clears the other set for the next launch's
-        // match (the launches that used it have ended).
+        // Group kernel.  The first workgroup clears the other key set for the
+        // next launch's match (the launches that used it have ended).
         if (blockIdx.x == 0) {
             unsigned long long *nxt = key_set(a, E + 1);
             for (int i = threadIdx.x; i < s.B * s.Hq; i += kBlock)
                 nxt[(int64_t)i * kKeyStride] = ~0ull;
         }
-        if (threadIdx.x < 64 && threadIdx.x % (64 / G) == 0)
-            hkey = key_set(a, E)[(int64_t)(bh0 + threadIdx.x / (64 / G)) * kKeyStride];
-        qs.request(a, b, g);
-        spec = spec_item(a, e, loc, span_prev, sp_t0, sp_t1);
-        if (spec)
-            item_issue<T, D, G, kPaged>(a, ctx, sp_t0, sp_t1, bufs, false);
+        if (a.key_parity && (E & 1))
+            hkey = hkey1;
+        // The queries, requested before the scalar words, have arrived by
+        // now.  Stored before the speculative K/V is requested: a wait for
+        // them after a conditional request was a wait for every load.
         qs.store(s_q);
         if constexpr (AS::kMfma)
             qs.store_b(s_qb, s.qscale);
+        spec = spec_item(a, e, loc, span_prev, sp_t0, sp_t1);
+        if (spec)
+            item_issue<T, D, G, kPaged>(a, ctx, sp_t0, sp_t1, bufs, false);
     }
     if (!ok) {
         // The group's keys never all arrived: its outputs are invalid, and
