@@ -803,6 +803,24 @@ mac_status mac_profile_read(mac_handle *h, double ms[MAC_PROFILE_STAGES], int32_
     return MAC_OK;
 }
 
+mac_status mac_timeline_read(mac_handle *h, void *host, size_t bytes)
+{
+    if (!handle_ok(h))
+        return MAC_ERR_NOT_INITIALIZED;
+    if (!host)
+        return MAC_ERR_INVALID_ARG;
+    const Shape &s = h->s;
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess)
+        e = s.dtype == MAC_DTYPE_BF16 && s.D == 128  ? timeline_read_bf16_128(host, bytes)
+            : s.dtype == MAC_DTYPE_BF16              ? timeline_read_bf16_64(host, bytes)
+            : s.D == 128                             ? timeline_read_f32_128(host, bytes)
+                                                     : timeline_read_f32_64(host, bytes);
+    if (e == hipErrorNotSupported)
+        return MAC_ERR_UNSUPPORTED;
+    return e == hipSuccess ? MAC_OK : MAC_ERR_HIP;
+}
+
 mac_status mac_stream_read(const void *buf, size_t bytes, float *sink, int32_t grid,
                            void *stream)
 {

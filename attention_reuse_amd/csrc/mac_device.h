@@ -59,6 +59,50 @@
 namespace mac {
 namespace {
 
+// Opt-in timeline of the step kernel, in a separate build of the library
+// (MAC_TIMELINE defined; the default build compiles the marks to nothing).
+// Thread 0 of workgroup w writes the 100 MHz real-time counter (a mark) or
+// a count (a note) to word w * kTimelineSlots + slot of its source file's
+// array; a launch overwrites the words its workgroups reach.  Slot meanings
+// are listed with mac_timeline_read in the public header.
+constexpr int kTimelineSlots = 32, kTimelineWgs = 4096;
+enum TimelineSlot : int {
+    kTlEntry = 0,         // workgroup start
+    kTlKeys = 1,          // match keys stored (one launch) / queries staged (group kernel)
+    kTlSpec = 2,          // speculative K/V requested
+    kTlPlanned = 3,       // group planned (head decisions in LDS)
+    kTlPublished = 4,     // items counted, pool entries published
+    kTlItem = 5,          // first own item begins (rows requested)
+    kTlItemComputed = 6,  // first own item's blocks computed
+    kTlItemStored = 7,    // its partial stored (write-through complete)
+    kTlItemCounted = 8,   // its count on the group counter done
+    kTlOwnDone = 9,       // all own items done
+    kTlMergeEnd = 10,     // merge of the own group done (its merger only)
+    kTlExit = 11,         // end of a workgroup that ran items
+    kTlExitIdle = 12,     // end of a workgroup without own items
+    kTlPoolFirst = 13,    // first pool item claimed
+    kTlMergeBegin = 20,   // merge of a group begins (its merger)
+    kTlMergeWeights = 21, // item weights formed (few items) / list A folded
+    kTlMergeSummed = 22,  // both lists' partials summed
+    kTlMergeWritten = 23, // outputs and ring entries written (stores issued)
+    kTlNoteItems = 16,    // note: the group's item count
+    kTlNoteOwn = 17,      // note: items its own workgroups run
+    kTlNoteSpec = 18,     // note: first item from the speculative rows (1), re-requested (2), none (0)
+    kTlNotePool = 19,     // note: pool items this workgroup ran
+};
+#ifdef MAC_TIMELINE
+__device__ unsigned long long timeline_words[kTimelineWgs * kTimelineSlots];
+#define MAC_NOTE(slot, v)                                                                  \
+    do {                                                                                   \
+        if (threadIdx.x == 0 && blockIdx.x < kTimelineWgs)                                 \
+            timeline_words[blockIdx.x * kTimelineSlots + (slot)] = (unsigned long long)(v); \
+    } while (0)
+#define MAC_MARK(slot) MAC_NOTE(slot, __builtin_amdgcn_s_memrealtime())
+#else
+#define MAC_NOTE(slot, v) ((void)0)
+#define MAC_MARK(slot) ((void)0)
+#endif
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -282,11 +326,12 @@ __device__ inline V ld_uniform(const V *p)
 // (see ring_append_pos).
 __device__ inline bool group_ready(const StepArgs &a, int b, int grp)
 {
-    // Both words are requested without a branch (with no epochs bound the
-    // first reads the group's own word, and the result is true).
+    if (!a.epoch)
+        return true;
+    // Both words requested together (the second does not wait for the first).
+    const int32_t ep = ld_uniform(a.epoch + b);
     const int32_t built = ld_uniform(a.w.ring_epoch + grp);
-    const int32_t ep = ld_uniform(a.epoch ? a.epoch + b : a.w.ring_epoch + grp);
-    return !a.epoch || (ep >= 0 && built == ep);
+    return ep >= 0 && built == ep;
 }
 
 // Position-ring update of the rectify-append of KV group grp at position e,
@@ -713,12 +758,18 @@ __global__ __launch_bounds__(kBlock) void match_kernel(StepArgs a)
     __shared__ unsigned long long sm[kBlock / 64];
     constexpr int U = kSlotsPerSplit / (kBlock / (D / T::EPL));
     const int bh = blockIdx.y, b = bh / a.s.Hq;
-    const bool ready = group_ready(a, b, b * a.s.Hkv + (bh - b * a.s.Hq) / a.s.G);
     MatchLoads<T, D, U> ml;
     match_issue<T, D, U>(a, blockIdx.x * kSlotsPerSplit, bh, ml);
-    const unsigned long long best = match_finish<T, D, U>(a, a.pos[b], ready, ml, sm);
+    // Scalar words after the rows are requested (a wait for any scalar load
+    // waits for all of them).  The done counter selects the key set; read
+    // here, in flight with the rows, rather than after the reduction, where
+    // it was a further round trip of every workgroup.
+    const unsigned long long done = ld_uniform(a.w.sync + kSyncDone);
+    const bool ready = group_ready(a, b, b * a.s.Hkv + (bh - b * a.s.Hq) / a.s.G);
+    __asm__ volatile("" ::"s"(done));
+    const unsigned long long best = match_finish<T, D, U>(a, ld_uniform(a.pos + b), ready, ml, sm);
     if (threadIdx.x == 0 && best != ~0ull)
-        atomicMin(&key_set(a, a.w.sync[kSyncDone] >> a.done_shift)[bh * kKeyStride], best);
+        atomicMin(&key_set(a, done >> a.done_shift)[bh * kKeyStride], best);
 }
 
 // ---------------------------------------------------------------------------
@@ -1012,6 +1063,7 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int gstart, int
     const int b = grp / s.Hkv, g = grp - b * s.Hkv;
     const int r_split = (a.mode == kPlanInit) ? 0 : s.r;
     const int nA = GroupItems(gstart, e, r_split, s.F, a.mode != kPlanInit, s.cmin).n_before_split();
+    MAC_MARK(kTlMergeBegin);
     // The pre-RoPE queries of the fused append are requested first.
     S qa[NPK][2];
     if (a.append_fused) {
@@ -1051,6 +1103,7 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int gstart, int
                 src.template span<FPL>(i < cnt ? i : cnt - 1, f0, ov[u]);
         }
         fold_weights<MD, G>(lv, cnt, nA, lds);
+        MAC_MARK(kTlMergeWeights);
         const float *s_w = lds + G * MD, *s_hl = s_w + G * MD, *s_inv = s_hl + 2 * G;
         float *s_sum = lds + 2 * G * MD + 4 * G;  // [4 waves][2 lists][G * D]
         if (loader) {
@@ -1136,8 +1189,11 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int gstart, int
                 res_o[list][k][1] = fo[1];
             }
             __syncthreads();
+            if (list == 0)
+                MAC_MARK(kTlMergeWeights);
         }
     }
+    MAC_MARK(kTlMergeSummed);
 
     // R = C (+) A, out = R (+) Bt.  Results are held until every thread has
     // read its cached summary (and the group's epoch), since the fused
@@ -1185,6 +1241,7 @@ __device__ void merge_group(const StepArgs &a, int grp, int cnt, int gstart, int
                 a.w.rect_l[bh] = rec_l[k];
         }
     }
+    MAC_MARK(kTlMergeWritten);
     // A group that was not ready adopts the request's epoch; its ring
     // restarts with this step's entry, here or in the append kernel.
     if (!ready && tid == 0)
@@ -2429,6 +2486,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int grp = blockIdx.x / a.wpg, loc = blockIdx.x - grp * a.wpg;
     const int b = grp / s.Hkv, g = grp - b * s.Hkv;
     const int bh0 = b * s.Hq + g * G;
+    MAC_MARK(kTlEntry);
     unsigned long long *sync = a.w.sync;
     // Entry.  The words of the launch's start (position, counters, the
     // group's previous span, readiness) are scalar loads, requested together
@@ -2497,6 +2555,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             match_issue<T, D, U>(a, ufirst, bh0 + uj, ml);
             store_unit_key(kw, rep_stride, u, match_finish<T, D, U>(a, e, ready, ml, klds), tag8);
         }
+        MAC_MARK(kTlKeys);
         // Speculative K/V, requested once the keys are out: loads complete in
         // order, so requests made earlier would hold back the match (and the
         // first poll of the keys).  They are in flight while the other units'
@@ -2507,6 +2566,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         spec = spec_item(a, e, loc, span_prev, sp_t0, sp_t1);
         if (spec)
             item_issue<T, D, G, kPaged>(a, ctx, sp_t0, sp_t1, bufs, false);
+        MAC_MARK(kTlSpec);
         if (threadIdx.x < 64)
             ok = poll_keys(a, kw + (loc % kKeyReps) * rep_stride, tag8, s_keys);
         ok = block_and(ok);
@@ -2526,9 +2586,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         qs.store(s_q);
         if constexpr (AS::kMfma)
             qs.store_b(s_qb, s.qscale);
+        MAC_MARK(kTlKeys);
         spec = spec_item(a, e, loc, span_prev, sp_t0, sp_t1);
         if (spec)
             item_issue<T, D, G, kPaged>(a, ctx, sp_t0, sp_t1, bufs, false);
+        MAC_MARK(kTlSpec);
     }
     if (!ok) {
         // The group's keys never all arrived: its outputs are invalid, and
@@ -2569,6 +2631,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
     }
     __syncthreads();
+    MAC_MARK(kTlPlanned);
     int st[G];
     int sg = e;
 #pragma unroll
@@ -2577,9 +2640,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         sg = st[j] < sg ? st[j] : sg;
     }
     if (grp == 0 && loc == 0 && threadIdx.x == 0) {
+        // Scalar loads: a vector load here would wait for every load this
+        // workgroup has in flight (its speculative K/V among them).
         int bad = 0;
         for (int bb = 0; bb < s.B; ++bb) {
-            const int eb = a.pos[bb];
+            const int eb = ld_uniform(a.pos + bb);
             bad |= !(eb >= 0 && eb < s.T);
         }
         a.w.ctrl[kCtrlStatus] = bad ? MAC_DEV_BAD_POSITION : 0;
@@ -2640,6 +2705,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     // that ran items take the pool's items (at least one per item of a
     // group's own workgroups), and idle workgroups polling the pool words
     // would only slow the counters of the others.
+    MAC_MARK(kTlPublished);
+    MAC_NOTE(kTlNoteItems, n);
+    MAC_NOTE(kTlNoteOwn, n_own);
     if (n == 0) {
         // Position out of range: NaN outputs, nothing appended.
         if (loc == 0) {
@@ -2649,8 +2717,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
         return;
     }
-    if (loc >= n_own)
+    if (loc >= n_own) {
+        MAC_MARK(kTlExitIdle);
         return;
+    }
     unsigned long long pst = ~0ull, phd = ~0ull;
     // Counts an item of group cg (cn items); true when the count completes
     // the group.
@@ -2710,9 +2780,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                 if (dim == 0)
                     st_wt(pl + j, lg);
             });
+            const bool first = it == n - 1 - loc;
+            if (first)
+                MAC_MARK(kTlItemComputed);
             wait_vmem();  // this wave's partial stores have completed
             __syncthreads();
-            return count_item(grp, n);
+            if (first)
+                MAC_MARK(kTlItemStored);
+            const bool last = count_item(grp, n);
+            if (first)
+                MAC_MARK(kTlItemCounted);
+            return last;
         };
         int t0, t1;
         gi.item(n - 1 - loc, t0, t1);
@@ -2728,6 +2806,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         // The first item is peeled off the loop, so that its wait for the
         // rows is its own (the loop's items wait for their just-requested
         // rows, the newest loads).
+        MAC_NOTE(kTlNoteSpec, !spec ? 0 : (t0 == sp_t0 && t1 == sp_t1) ? 1 : 2);
+        MAC_MARK(kTlItem);
         bool merger = own_item(n - 1 - loc, t0, t1);
         for (int jj = loc + a.wpg; jj < n_own; jj += a.wpg) {
             const int it = n - 1 - jj;
@@ -2735,13 +2815,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             item_issue<T, D, G, kPaged>(a, ctx, t0, t1, bufs, false);
             merger = own_item(it, t0, t1) || merger;
         }
-        if (merger)
+        MAC_MARK(kTlOwnDone);
+        if (merger) {
             merge(grp, n, sg, e, ready, c_l, c_o);
+            MAC_MARK(kTlMergeEnd);
+        }
     }
 
-    if constexpr (!kPool)
+    if constexpr (!kPool) {
+        MAC_MARK(kTlExit);
         return;
+    }
     // Pool items of any group, until the pool is drained.
+    int n_taken = 0;
     for (;;) {
         const int ent = pool_take(ps, tag32, NG, pst, phd, &s_slot);
         pst = phd = ~0ull;
@@ -2752,6 +2838,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             }
             break;
         }
+        if (n_taken++ == 0)
+            MAC_MARK(kTlPoolFirst);
         const int wgrp = __builtin_amdgcn_readfirstlane(ent >> 8);
         const int wit = __builtin_amdgcn_readfirstlane(ent & 0xff);
         // The item's group: plan record and queries.
@@ -2804,6 +2892,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             merge(wgrp, cn, csg, ce, cready, c_l, c_o);
         }
     }
+    MAC_MARK(kTlExit);
+    MAC_NOTE(kTlNotePool, n_taken);
 }
 
 // ---------------------------------------------------------------------------

@@ -418,6 +418,12 @@ int step_resident_bf16_128(const Shape &s);
 int step_resident_bf16_64(const Shape &s);
 int step_resident_f32_128(const Shape &s);
 int step_resident_f32_64(const Shape &s);
+// Copies of the step kernels' timeline words (library built with
+// MAC_TIMELINE; hipErrorNotSupported otherwise), one per source file.
+hipError_t timeline_read_bf16_128(void *host, size_t bytes);
+hipError_t timeline_read_bf16_64(void *host, size_t bytes);
+hipError_t timeline_read_f32_128(void *host, size_t bytes);
+hipError_t timeline_read_f32_64(void *host, size_t bytes);
 // Rectify-append from the workspace staging into the rings; the position of
 // request b is pos[b] + pos_offset.
 hipError_t launch_append(const StepArgs &a, int32_t pos_offset, hipStream_t st);

@@ -82,6 +82,21 @@ static void step_resident_go(const Shape &s, int *n)
     *n = a < b ? (a < c ? a : c) : (b < c ? b : c);
 }
 
+// This source file's timeline words (the step kernels of its dtype and
+// head dim write them); hipErrorNotSupported in the default build.
+static hipError_t timeline_copy(void *host, size_t bytes)
+{
+#ifdef MAC_TIMELINE
+    constexpr size_t cap = sizeof(unsigned long long) * kTimelineWgs * kTimelineSlots;
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(timeline_words), bytes < cap ? bytes : cap, 0,
+                               hipMemcpyDeviceToHost);
+#else
+    (void)host;
+    (void)bytes;
+    return hipErrorNotSupported;
+#endif
+}
+
 }  // namespace
 }  // namespace mac
 
@@ -96,5 +111,9 @@ static void step_resident_go(const Shape &s, int *n)
         int n = 0;                                                     \
         step_resident_go<T, D>(s, &n);                                 \
         return n;                                                      \
+    }                                                                  \
+    hipError_t timeline_read_##NAME(void *host, size_t bytes)          \
+    {                                                                  \
+        return timeline_copy(host, bytes);                             \
     }                                                                  \
     }

@@ -100,6 +100,7 @@ def load():
         "mac_profile_start": (ctypes.c_int, [_vp, ctypes.c_int32]),
         "mac_profile_read": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_double),
                                             ctypes.POINTER(ctypes.c_int32)]),
+        "mac_timeline_read": (ctypes.c_int, [_vp, _vp, ctypes.c_size_t]),
         "mac_release": (ctypes.c_int, [_vp]),
         "mac_stream_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, ctypes.c_int32, _vp]),
         "mac_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -230,6 +231,20 @@ def mac_profile_read(handle):
     n = ctypes.c_int32()
     _check("mac_profile_read", load().mac_profile_read(handle, ms, ctypes.byref(n)))
     return dict(zip(STAGES, list(ms))), n.value
+
+
+TIMELINE_WGS = 4096
+TIMELINE_SLOTS = 32
+
+
+def mac_timeline_read(handle):
+    """The step kernels' timeline words as a list of TIMELINE_WGS lists of
+    TIMELINE_SLOTS ints (a library built with MAC_TIMELINE only)."""
+    n = TIMELINE_WGS * TIMELINE_SLOTS
+    buf = (ctypes.c_uint64 * n)()
+    _check("mac_timeline_read", load().mac_timeline_read(handle, buf, ctypes.sizeof(buf)))
+    w = list(buf)
+    return [w[i * TIMELINE_SLOTS:(i + 1) * TIMELINE_SLOTS] for i in range(TIMELINE_WGS)]
 
 
 def mac_stream_read(buf, n_bytes, sink, grid, stream=None):

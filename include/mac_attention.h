@@ -371,6 +371,30 @@ enum { MAC_PROFILE_STAGES = 5 };
 mac_status mac_profile_start(mac_handle *h, int32_t n_steps);
 mac_status mac_profile_read(mac_handle *h, double ms[MAC_PROFILE_STAGES], int32_t *n);
 
+/* Per-workgroup timeline of the step kernel (diagnostics).  Only a library
+ * built with MAC_TIMELINE defined records it (attention_reuse_amd/build.py
+ * --timeline makes libmac_attention_timeline.so); the default build returns
+ * MAC_ERR_UNSUPPORTED.  Synchronises the device, then copies up to `bytes`
+ * bytes of the timeline words of the step kernels of h's K/V dtype and head
+ * dim to host memory `host` (caller-owned): 4096 workgroups x 32 uint64
+ * words, word w * 32 + slot, each written by the latest launch whose
+ * workgroup w reached it (earlier launches' values remain elsewhere).
+ * Marks hold the 100 MHz device real-time counter:
+ *   0 workgroup start; 1 match keys stored (one launch) or queries staged
+ *   (group kernel of the two-kernel form); 2 speculative K/V requested;
+ *   3 group planned; 4 items counted and pool entries published; 5 first
+ *   own item begins; 6 its blocks computed; 7 its partial stored; 8 its
+ *   count done; 9 all own items done; 10 merge of the own group done (its
+ *   merger only); 11 end of a workgroup that ran items; 12 end of a
+ *   workgroup without own items; 13 first pool item claimed; in the merge
+ *   of a group, by its merger: 20 begins, 21 item weights formed (up to 24
+ *   items for G <= 4, 12 otherwise) or the first list folded, 22 both lists
+ *   summed, 23 outputs and ring entries written (stores issued).
+ * Notes hold counts: 16 the group's items; 17 items of its own workgroups;
+ * 18 first item from the speculative rows (1), re-requested (2), none (0);
+ * 19 pool items run by this workgroup. */
+mac_status mac_timeline_read(mac_handle *h, void *host, size_t bytes);
+
 /* Streaming read of bytes (rounded down to 16) of the device buffer buf by
  * `grid` workgroups, enqueued on `stream` (measurement of the achievable HBM
  * read bandwidth that the decode kernels are compared with).  sink: device

@@ -264,3 +264,26 @@ def test_noalloc_full_decode_rejects_before_any_device_call(lib):
                                        None, None, None) == -1
     assert lib.mac_full_decode_noalloc(ctypes.byref(p), 0x1004, 0x2000, 0x3000, 0x4000,
                                        0x5000, None, None) == -5
+
+
+def test_timeline_summary_reads_the_latest_launch():
+    """The timeline tool's host summary: workgroups of the latest launch are
+    those that started within 20 us of its last start, and a point counts
+    only when it was written after the workgroup's own start."""
+    from attention_reuse_amd import timeline as tl
+    W = [[0] * 32 for _ in range(8)]
+    for w in range(4):                      # an earlier launch
+        W[w][0], W[w][11] = 1000 + w, 5000
+    for w in range(4, 8):                   # the latest launch: entries 100 us later
+        W[w][0] = 11000 + 10 * w
+        W[w][3] = W[w][0] + 300             # planned 3 us after start
+        W[w][4] = W[w][0] + 400
+        W[w][16], W[w][17] = 7, 7
+    W[7][11] = 900                          # stale: before this launch's start
+    lines = tl.summarize(W)
+    assert lines[0].endswith(": 4")
+    planned = [l for l in lines if l.startswith("group planned")][0].split()
+    # planned 3.0, 3.1, 3.2, 3.3 us after the first start: min 3.0, median 3.2
+    assert planned[2] == "4" and float(planned[3]) == 3.0 and float(planned[5]) == 3.2
+    end = [l for l in lines if l.startswith("end (ran items)")][0].split()
+    assert end[3] == "0"
