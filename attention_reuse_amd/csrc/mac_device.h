@@ -186,10 +186,11 @@ __device__ inline float dpp(float v)
 template <int W>
 __device__ inline float row_sum(float v)
 {
-    static_assert(W == 8 || W == 16 || W == 32, "row width");
+    static_assert(W == 4 || W == 8 || W == 16 || W == 32, "row width");
     v += dpp<kDppQuadXor1>(v);
     v += dpp<kDppQuadXor2>(v);
-    v += dpp<kDppHalfMirror>(v);
+    if (W >= 8)
+        v += dpp<kDppHalfMirror>(v);
     if (W >= 16)
         v += dpp<kDppRowMirror>(v);
     if (W == 32)
@@ -749,15 +750,117 @@ __device__ inline unsigned long long match_finish(const StepArgs &a, int m, bool
     return best;
 }
 
+// Filtered match of one unit in half rows (match kernel, filter on).  A
+// row's D dims are two halves of H = LPR / 2 lanes; a pass gives each H-lane
+// group one row's half, so every lane of a load carries data (the row
+// geometry of match_issue leaves half the lanes of the first pass idle) and
+// the unit takes half the load instructions.  The sums are those of the
+// full-row scan bit for bit: row_sum<LPR> is row_sum<H> over each half
+// followed by one addition of the two halves, so the first half's
+// row_sum<H> is the filter's lower bound and first + second is the row's
+// distance, with each lane's products over the same 8 (or 4) dims in the
+// same order.  Key and validity as match_finish.  The scalar words (the
+// position, readiness and the done counter, returned in *done) are read
+// after the rows are requested.
+template <class T, int D>
+__device__ inline unsigned long long match_halves(const StepArgs &a, int first, int bh,
+                                                  unsigned long long *done, unsigned long long *sm)
+{
+    using S = typename T::S;
+    constexpr int EPL = T::EPL, LPR = D / EPL, H = LPR / 2, RPH = kBlock / H;
+    constexpr int UH = kSlotsPerSplit / RPH;
+    static_assert(UH >= 1 && UH * RPH == kSlotsPerSplit, "half-row unit shape");
+    const Shape &s = a.s;
+    const int b = bh / s.Hq, h = bh - b * s.Hq;
+    const int lane = threadIdx.x % H, row = threadIdx.x / H;
+    const S *qp = (const S *)a.qtilde + b * a.qt_sb + h * a.qt_sh + lane * EPL;
+    const uint4 q0 = load16(qp), q1 = load16(qp + D / 2);
+    const uint32_t oob = (uint32_t)s.K * D * sizeof(S);
+    const __amdgpu_buffer_rsrc_t ring = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<S *>((const S *)a.q_ring + (int64_t)bh * s.K * D), (short)0, (int)oob,
+        0x00020000);
+    const int32_t *pr = a.pos_ring + ((int64_t)b * s.Hkv + h / s.G) * s.K;
+    uint4 raw[UH];
+    int pos[UH];
+#pragma unroll
+    for (int u = 0; u < UH; ++u) {
+        const int k = match_slot<UH>(a, first, u, RPH, row);
+        raw[u] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(ring, (uint32_t)(k * D + lane * EPL) * sizeof(S), 0, 0));
+        pos[u] = pr[k];
+    }
+    *done = ld_uniform(a.w.sync + kSyncDone);
+    const int m = ld_uniform(a.pos + b);
+    const bool ready = group_ready(a, b, b * s.Hkv + h / s.G);
+    __asm__ volatile("" ::"s"(*done));
+    const bool m_ok = ready && m >= 0 && m < s.T && m >= s.min_ctx;
+    auto lane_d2 = [&](const uint4 &qv4, const uint4 &rv4) {
+        float qv[EPL], rv[EPL];
+        unpack<T>(qv4, qv);
+        unpack<T>(rv4, rv);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const float df = qv[e] - rv[e];
+            acc = fmaf(df, df, acc);
+        }
+        return acc;
+    };
+    const float lb_max = s.thresh2 * kFilterMargin;
+    float h0[UH];
+    bool keep[UH];
+    uint4 raw2[UH];
+#pragma unroll
+    for (int u = 0; u < UH; ++u) {
+        h0[u] = row_sum<H>(lane_d2(q0, raw[u]));
+        const int pu = pos[u];
+        keep[u] = h0[u] < lb_max && m_ok && pu >= 0 && pu >= m - s.K && pu <= m - 1;
+        const int k = match_slot<UH>(a, first, u, RPH, row);
+        const uint32_t off = keep[u] ? (uint32_t)(k * D + D / 2 + lane * EPL) * sizeof(S) : oob;
+        raw2[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ring, off, 0, 0));
+    }
+    unsigned long long best = ~0ull;
+#pragma unroll
+    for (int u = 0; u < UH; ++u) {
+        const float acc = h0[u] + row_sum<H>(lane_d2(q1, raw2[u]));
+        uint32_t bits = __float_as_uint(acc);
+        if (acc != acc)
+            bits = 0x7f800000u;  // NaN distance counts as +inf
+        const unsigned long long key =
+            ((unsigned long long)bits << 32) | (0xffffffffu - (uint32_t)pos[u]);
+        best = umin64(best, keep[u] ? key : ~0ull);
+    }
+#pragma unroll
+    for (int off = H; off < 64; off <<= 1)
+        best = umin64(best, shfl_xor_u64(best, off));
+    if ((threadIdx.x & 63) == 0)
+        sm[threadIdx.x >> 6] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int i = 1; i < kBlock / 64; ++i)
+            best = umin64(best, sm[i]);
+    }
+    return best;
+}
+
 // Match kernel.  Grid (nsplit, B*Hq).  The head's key is the minimum over
 // its splits (exact and order-independent), folded with a 64-bit atomic
 // minimum; read by the next kernel, reset to ~0 by the merge of the step.
-template <class T, int D>
+template <class T, int D, bool kHalves>
 __global__ __launch_bounds__(kBlock) void match_kernel(StepArgs a)
 {
     __shared__ unsigned long long sm[kBlock / 64];
     constexpr int U = kSlotsPerSplit / (kBlock / (D / T::EPL));
     const int bh = blockIdx.y, b = bh / a.s.Hq;
+    if constexpr (kHalves) {
+        // Filter on: half rows (the same keys as the full-row scan).
+        unsigned long long done;
+        const unsigned long long best = match_halves<T, D>(a, blockIdx.x * kSlotsPerSplit, bh, &done, sm);
+        if (threadIdx.x == 0 && best != ~0ull)
+            atomicMin(&key_set(a, done >> a.done_shift)[bh * kKeyStride], best);
+        return;
+    }
     MatchLoads<T, D, U> ml;
     match_issue<T, D, U>(a, blockIdx.x * kSlotsPerSplit, bh, ml);
     // Scalar words after the rows are requested (a wait for any scalar load

@@ -84,8 +84,12 @@ int device_cu_count()
 template <class T, int D>
 static void match_go(const StepArgs &a, hipStream_t st)
 {
-    hipLaunchKernelGGL((match_kernel<T, D>), dim3(a.nsplit, a.s.B * a.s.Hq), dim3(kBlock), 0,
-                       st, a);
+    if (a.match_filter)
+        hipLaunchKernelGGL((match_kernel<T, D, true>), dim3(a.nsplit, a.s.B * a.s.Hq),
+                           dim3(kBlock), 0, st, a);
+    else
+        hipLaunchKernelGGL((match_kernel<T, D, false>), dim3(a.nsplit, a.s.B * a.s.Hq),
+                           dim3(kBlock), 0, st, a);
 }
 
 hipError_t launch_match(const StepArgs &a, hipStream_t st)
