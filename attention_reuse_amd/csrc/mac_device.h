@@ -754,7 +754,9 @@ __device__ inline unsigned long long match_finish(const StepArgs &a, int m, bool
 // row's D dims are two halves of H = LPR / 2 lanes; a pass gives each H-lane
 // group one row's half, so every lane of a load carries data (the row
 // geometry of match_issue leaves half the lanes of the first pass idle) and
-// the unit takes half the load instructions.  The sums are those of the
+// the unit takes half the load instructions.  A workgroup takes
+// kSlotsPerHalvesSplit slots (128: measured 10.1 us against 10.6 us with 64
+// and 10.2 us with 256 at the 128K batch-8 workload).  The sums are those of the
 // full-row scan bit for bit: row_sum<LPR> is row_sum<H> over each half
 // followed by one addition of the two halves, so the first half's
 // row_sum<H> is the filter's lower bound and first + second is the row's
@@ -768,8 +770,8 @@ __device__ inline unsigned long long match_halves(const StepArgs &a, int first, 
 {
     using S = typename T::S;
     constexpr int EPL = T::EPL, LPR = D / EPL, H = LPR / 2, RPH = kBlock / H;
-    constexpr int UH = kSlotsPerSplit / RPH;
-    static_assert(UH >= 1 && UH * RPH == kSlotsPerSplit, "half-row unit shape");
+    constexpr int UH = kSlotsPerHalvesSplit / RPH;
+    static_assert(UH >= 1 && UH * RPH == kSlotsPerHalvesSplit, "half-row unit shape");
     const Shape &s = a.s;
     const int b = bh / s.Hq, h = bh - b * s.Hq;
     const int lane = threadIdx.x % H, row = threadIdx.x / H;
@@ -856,7 +858,7 @@ __global__ __launch_bounds__(kBlock) void match_kernel(StepArgs a)
     if constexpr (kHalves) {
         // Filter on: half rows (the same keys as the full-row scan).
         unsigned long long done;
-        const unsigned long long best = match_halves<T, D>(a, blockIdx.x * kSlotsPerSplit, bh, &done, sm);
+        const unsigned long long best = match_halves<T, D>(a, blockIdx.x * kSlotsPerHalvesSplit, bh, &done, sm);
         if (threadIdx.x == 0 && best != ~0ull)
             atomicMin(&key_set(a, done >> a.done_shift)[bh * kKeyStride], best);
         return;

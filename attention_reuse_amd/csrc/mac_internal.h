@@ -29,6 +29,8 @@ constexpr int kPoolItems = 4;
 constexpr int kMaxItemsPerGroup = 128;
 // Ring slots scanned by one match workgroup.
 constexpr int kSlotsPerSplit = 64;
+// Ring slots per workgroup of the filtered (half-row) match kernel.
+constexpr int kSlotsPerHalvesSplit = 128;
 // Single launch: workgroups 0 .. kSpecMax-1 of a group may request the K/V
 // of their item before the match has decided the group's range: the item
 // they would run if the range kept the span it had at the group's previous

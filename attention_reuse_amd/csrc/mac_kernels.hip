@@ -85,7 +85,9 @@ template <class T, int D>
 static void match_go(const StepArgs &a, hipStream_t st)
 {
     if (a.match_filter)
-        hipLaunchKernelGGL((match_kernel<T, D, true>), dim3(a.nsplit, a.s.B * a.s.Hq),
+        hipLaunchKernelGGL((match_kernel<T, D, true>),
+                           dim3((a.s.K + kSlotsPerHalvesSplit - 1) / kSlotsPerHalvesSplit,
+                                a.s.B * a.s.Hq),
                            dim3(kBlock), 0, st, a);
     else
         hipLaunchKernelGGL((match_kernel<T, D, false>), dim3(a.nsplit, a.s.B * a.s.Hq),

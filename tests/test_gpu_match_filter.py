@@ -43,7 +43,10 @@ def _t2(cfg):
 
 
 @pytest.mark.parametrize("kw", [dict(), dict(dtype="f32", head_dim=64, n_q_heads=8, n_kv_heads=2),
-                                dict(head_dim=64), dict(dtype="f32", n_q_heads=8, n_kv_heads=2)])
+                                dict(head_dim=64), dict(dtype="f32", n_q_heads=8, n_kv_heads=2),
+                                # ring sizes that end inside a match unit: a multiple of 4
+                                # (positions in 16-byte loads) and one that is not
+                                dict(ring_k=252), dict(ring_k=250)])
 @pytest.mark.parametrize("form", [mac.MAC_FLAG_SPLIT_STAGES, mac.MAC_FLAG_SINGLE_LAUNCH])
 def test_filter_keeps_results_bitwise(kw, form):
     """Mixed hits and misses, every head dim and dtype: the filtered step
