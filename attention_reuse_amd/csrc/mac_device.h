@@ -810,7 +810,7 @@ __device__ inline unsigned long long match_halves(const StepArgs &a, int first, 
     };
     const float lb_max = s.thresh2 * kFilterMargin;
     float h0[UH];
-    bool keep[UH];
+    bool keep[UH], any[UH];
     uint4 raw2[UH];
 #pragma unroll
     for (int u = 0; u < UH; ++u) {
@@ -819,11 +819,19 @@ __device__ inline unsigned long long match_halves(const StepArgs &a, int first, 
         keep[u] = h0[u] < lb_max && m_ok && pu >= 0 && pu >= m - s.K && pu <= m - 1;
         const int k = match_slot<UH>(a, first, u, RPH, row);
         const uint32_t off = keep[u] ? (uint32_t)(k * D + D / 2 + lane * EPL) * sizeof(S) : oob;
-        raw2[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ring, off, 0, 0));
+        // A wave none of whose rows can still hit skips the second half:
+        // no load instruction (an out-of-range one still costs address
+        // processing) and no distance.
+        any[u] = __builtin_amdgcn_ballot_w64(keep[u]) != 0;
+        raw2[u] = make_uint4(0u, 0u, 0u, 0u);
+        if (any[u])
+            raw2[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ring, off, 0, 0));
     }
     unsigned long long best = ~0ull;
 #pragma unroll
     for (int u = 0; u < UH; ++u) {
+        if (!any[u])
+            continue;
         const float acc = h0[u] + row_sum<H>(lane_d2(q1, raw2[u]));
         uint32_t bits = __float_as_uint(acc);
         if (acc != acc)
