@@ -85,6 +85,9 @@ enum TimelineSlot : int {
     kTlMergeWeights = 21, // item weights formed (few items) / list A folded
     kTlMergeSummed = 22,  // both lists' partials summed
     kTlMergeWritten = 23, // outputs and ring entries written (stores issued)
+    kTlOwnQueries = 24,   // own-items block: queries read from LDS
+    kTlOwnBounds = 25,    // first item's bounds computed
+    kTlOwnRows = 26,      // its rows requested (or found speculated)
     kTlNoteItems = 16,    // note: the group's item count
     kTlNoteOwn = 17,      // note: items its own workgroups run
     kTlNoteSpec = 18,     // note: first item from the speculative rows (1), re-requested (2), none (0)
@@ -2872,6 +2875,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     // wait for its rows does not wait for them.
     {
         ctx.queries_from_lds(s_q, s_qb, s.qscale);
+        MAC_MARK(kTlOwnQueries);
         float *gpo = a.w.part_o + (int64_t)grp * kItemsPerGroupMax * G * D;
         float *gpl = a.w.part_l + (int64_t)grp * kItemsPerGroupMax * G;
         // Attention of own item it, its rows requested; the partial stored
@@ -2907,8 +2911,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         };
         int t0, t1;
         gi.item(n - 1 - loc, t0, t1);
+        MAC_MARK(kTlOwnBounds);
         if (!(spec && t0 == sp_t0 && t1 == sp_t1))
             item_issue<T, D, G, kPaged>(a, ctx, t0, t1, bufs, false);
+        MAC_MARK(kTlOwnRows);
         float c_l[MP::NPK], c_o[MP::NPK][2];
         load_cached<T, D, G, kBlock>(
             a, grp, [&](int j) { return code_slot(s_code[j], s.r, s.K); }, c_l, c_o);

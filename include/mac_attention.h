@@ -389,7 +389,9 @@ mac_status mac_profile_read(mac_handle *h, double ms[MAC_PROFILE_STAGES], int32_
  *   workgroup without own items; 13 first pool item claimed; in the merge
  *   of a group, by its merger: 20 begins, 21 item weights formed (up to 24
  *   items for G <= 4, 12 otherwise) or the first list folded, 22 both lists
- *   summed, 23 outputs and ring entries written (stores issued).
+ *   summed, 23 outputs and ring entries written (stores issued); in the
+ *   own-items block before the first item: 24 queries read from LDS, 25
+ *   the item's bounds computed, 26 its rows requested (or speculated).
  * Notes hold counts: 16 the group's items; 17 items of its own workgroups;
  * 18 first item from the speculative rows (1), re-requested (2), none (0);
  * 19 pool items run by this workgroup. */
