@@ -88,6 +88,7 @@ enum TimelineSlot : int {
     kTlOwnQueries = 24,   // own-items block: queries read from LDS
     kTlOwnBounds = 25,    // first item's bounds computed
     kTlOwnRows = 26,      // its rows requested (or found speculated)
+    kTlBlocksDone = 27,   // an item's blocks done, before the cross-row combine (latest item)
     kTlNoteItems = 16,    // note: the group's item count
     kTlNoteOwn = 17,      // note: items its own workgroups run
     kTlNoteSpec = 18,     // note: first item from the speculative rows (1), re-requested (2), none (0)
@@ -2029,6 +2030,7 @@ __device__ inline void item_finish(const StepArgs &a, const ItemCtx<T, D, G, kPa
                 load_block<T, D, G, LPR, RPB, NB, kPaged>(bufB, ctx.rows, s, base + 3 * TPB, t1, row);
         }
     }
+    MAC_MARK(kTlBlocksDone);
     item_combine<T, D, G>(ia, lds, row, lane, sink);
 }
 
