@@ -793,8 +793,15 @@ __device__ inline unsigned long long match_halves(const StepArgs &a, int first, 
         const int k = match_slot<UH>(a, first, u, RPH, row);
         raw[u] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(ring, (uint32_t)(k * D + lane * EPL) * sizeof(S), 0, 0));
-        pos[u] = pr[k];
     }
+    // The row group's UH positions in one load instruction (lane u of the
+    // group reads row u's), handed to the other lanes when the bound is
+    // formed: one instruction instead of UH (each costs address processing
+    // for the whole wave).
+    static_assert(UH <= H, "one position per lane of a half row");
+    int pv = 0;
+    if (lane < UH)
+        pv = pr[match_slot<UH>(a, first, lane, RPH, row)];
     *done = ld_uniform(a.w.sync + kSyncDone);
     const int m = ld_uniform(a.pos + b);
     const bool ready = group_ready(a, b, b * s.Hkv + h / s.G);
@@ -819,6 +826,7 @@ __device__ inline unsigned long long match_halves(const StepArgs &a, int first, 
 #pragma unroll
     for (int u = 0; u < UH; ++u) {
         h0[u] = row_sum<H>(lane_d2(q0, raw[u]));
+        pos[u] = __shfl(pv, ((int)(threadIdx.x & 63) & ~(H - 1)) + u, 64);
         const int pu = pos[u];
         keep[u] = h0[u] < lb_max && m_ok && pu >= 0 && pu >= m - s.K && pu <= m - 1;
         const int k = match_slot<UH>(a, first, u, RPH, row);
