@@ -758,7 +758,9 @@ __device__ inline unsigned long long match_finish(const StepArgs &a, int m, bool
 // row's D dims are two halves of H = LPR / 2 lanes; a pass gives each H-lane
 // group one row's half, so every lane of a load carries data (the row
 // geometry of match_issue leaves half the lanes of the first pass idle) and
-// the unit takes half the load instructions.  A workgroup takes
+// the unit takes half the row load instructions; the time of this kernel
+// follows its load instructions, each of which costs address processing for
+// the whole wave whether or not a lane reads memory.  A workgroup takes
 // kSlotsPerHalvesSplit slots (128: measured 10.1 us against 10.6 us with 64
 // and 10.2 us with 256 at the 128K batch-8 workload).  The sums are those of the
 // full-row scan bit for bit: row_sum<LPR> is row_sum<H> over each half
@@ -866,9 +868,11 @@ __device__ inline unsigned long long match_halves(const StepArgs &a, int first, 
     return best;
 }
 
-// Match kernel.  Grid (nsplit, B*Hq).  The head's key is the minimum over
-// its splits (exact and order-independent), folded with a 64-bit atomic
-// minimum; read by the next kernel, reset to ~0 by the merge of the step.
+// Match kernel.  Grid (nsplit, B*Hq) of kSlotsPerSplit-slot full-row splits,
+// or, with the filter (kHalves), (ceil(K / kSlotsPerHalvesSplit), B*Hq) of
+// half-row splits.  The head's key is the minimum over its splits (exact
+// and order-independent), folded with a 64-bit atomic minimum; read by the
+// next kernel, reset to ~0 by the merge of the step.
 template <class T, int D, bool kHalves>
 __global__ __launch_bounds__(kBlock) void match_kernel(StepArgs a)
 {
