@@ -89,6 +89,8 @@ enum TimelineSlot : int {
     kTlOwnBounds = 25,    // first item's bounds computed
     kTlOwnRows = 26,      // its rows requested (or found speculated)
     kTlBlocksDone = 27,   // an item's blocks done, before the cross-row combine (latest item)
+    kTlCombineRows = 28,  // the workgroup's rows of that item in LDS (latest item)
+    kTlCombineSums = 29,  // that item's per-head weights and sums formed (latest item)
     kTlNoteItems = 16,    // note: the group's item count
     kTlNoteOwn = 17,      // note: items its own workgroups run
     kTlNoteSpec = 18,     // note: first item from the speculative rows (1), re-requested (2), none (0)
@@ -165,6 +167,22 @@ __device__ inline void unpack<BF16>(const uint4 &v, float *f)
 __device__ inline uint4 load16(const void *p)
 {
     return *reinterpret_cast<const uint4 *>(p);
+}
+// The same with the non-temporal hint (nt): the line is not kept in the
+// caches for reuse.
+__device__ inline uint4 load16_nt(const void *p)
+{
+    typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+    const u4v x = __builtin_nontemporal_load(reinterpret_cast<const u4v *>(p));
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
+template <bool kNt>
+__device__ inline uint4 load16_kv(const void *p)
+{
+    if constexpr (kNt)
+        return load16_nt(p);
+    else
+        return load16(p);
 }
 
 // v_exp_f32 / v_log_f32 (base 2) without library range wrappers; the
@@ -1517,8 +1535,9 @@ struct BlockPages {
     }
 };
 
-// load_block with row t at element offset off(t) from the lane's column.
-template <class T, int D, int G, int LPR, int RPB, int NB, class Off>
+// load_block with row t at element offset off(t) from the lane's column;
+// kNt: loads with the non-temporal hint.
+template <class T, int D, int G, int LPR, int RPB, int NB, bool kNt = false, class Off>
 __device__ inline void load_block_at(KvBlock<T, G, T::EPL, NB> &kv, const KvRows<T> &rows,
                                      int base, int t1, int row, Off &&off)
 {
@@ -1535,12 +1554,12 @@ __device__ inline void load_block_at(KvBlock<T, G, T::EPL, NB> &kv, const KvRows
         const int64_t ok = off(tk);
 #pragma unroll
         for (int kk = 0; kk < NB; ++kk)
-            kv.k[kk] = load16(kb + ok + 32 * kk);
+            kv.k[kk] = load16_kv<kNt>(kb + ok + 32 * kk);
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             int t = base + i * RPB + row;
             t = t < t1 ? t : t1 - 1;
-            kv.v[i] = load16(vb + off(t));
+            kv.v[i] = load16_kv<kNt>(vb + off(t));
         }
     } else {
 #pragma unroll
@@ -1548,8 +1567,8 @@ __device__ inline void load_block_at(KvBlock<T, G, T::EPL, NB> &kv, const KvRows
             int t = base + i * RPB + row;
             t = t < t1 ? t : t1 - 1;
             const int64_t o = off(t);
-            kv.k[i] = load16(kb + o);
-            kv.v[i] = load16(vb + o);
+            kv.k[i] = load16_kv<kNt>(kb + o);
+            kv.v[i] = load16_kv<kNt>(vb + o);
         }
     }
 }
@@ -1558,18 +1577,18 @@ __device__ inline void load_block_at(KvBlock<T, G, T::EPL, NB> &kv, const KvRows
 // t1 - 1 of the item instead, which the block computation masks (its logit
 // is -inf, its probability exactly 0).  No branch separates the loads, so
 // the compiler can wait for each block on its own.
-template <class T, int D, int G, int LPR, int RPB, int NB, bool kPaged>
+template <class T, int D, int G, int LPR, int RPB, int NB, bool kPaged, bool kNt = false>
 __device__ inline void load_block(KvBlock<T, G, T::EPL, NB> &kv, const KvRows<T> &rows,
                                   const Shape &s, int base, int t1, int row)
 {
     if constexpr (kPaged) {
         const BlockPages<RPB * NB> bp(s, rows.table, base, t1);
-        load_block_at<T, D, G, LPR, RPB, NB>(kv, rows, base, t1, row,
-                                             [&](int t) { return bp.offset(s, t); });
+        load_block_at<T, D, G, LPR, RPB, NB, kNt>(kv, rows, base, t1, row,
+                                                  [&](int t) { return bp.offset(s, t); });
     } else {
         const int64_t st = s.kv_st;
-        load_block_at<T, D, G, LPR, RPB, NB>(kv, rows, base, t1, row,
-                                             [&](int t) { return (int64_t)t * st; });
+        load_block_at<T, D, G, LPR, RPB, NB, kNt>(kv, rows, base, t1, row,
+                                                  [&](int t) { return (int64_t)t * st; });
     }
 }
 
@@ -1970,6 +1989,7 @@ __device__ inline void item_combine(const ItemAcc<T, D, G> &ia, float *lds, int 
         for (int e = 0; e < EPL; ++e)
             sm_acc[(row * G + j) * D + lane * EPL + e] = ia.acc[j][e];
     __syncthreads();
+    MAC_MARK(kTlCombineRows);
     // Row weights c[rr][j] = 2^(m[rr][j] - M_j), one per thread; then head
     // j's total sum L_j = sum_rr c[rr][j] * l[rr][j] in row order.
     float *sm_c = sm_acc + RPB * G * D;  // [RPB][G]
@@ -1995,6 +2015,7 @@ __device__ inline void item_combine(const ItemAcc<T, D, G> &ia, float *lds, int 
         sm_hd[threadIdx.x] = Ls;
     }
     __syncthreads();
+    MAC_MARK(kTlCombineSums);
     for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
         const int j = idx / D, dim = idx - j * D;
         const float ls = sm_hd[j];
@@ -2292,12 +2313,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(AttendSh
             return;
         const int lb = ld.grp / s.Hkv, lg = ld.grp - lb * s.Hkv;
         if constexpr (kPaged)
-            load_block_at<T, D, G, LPR, RPB, NB>(buf, kv_rows<T, D, G, true>(a, lb, lg), ld_base,
-                                                 ld.t1, row,
-                                                 [&](int t) { return pages.offset(s, t); });
+            load_block_at<T, D, G, LPR, RPB, NB, true>(buf, kv_rows<T, D, G, true>(a, lb, lg),
+                                                       ld_base, ld.t1, row,
+                                                       [&](int t) { return pages.offset(s, t); });
         else
-            load_block<T, D, G, LPR, RPB, NB, false>(buf, kv_rows<T, D, G, false>(a, lb, lg), s,
-                                                     ld_base, ld.t1, row);
+            load_block<T, D, G, LPR, RPB, NB, false, true>(
+                buf, kv_rows<T, D, G, false>(a, lb, lg), s, ld_base, ld.t1, row);
         ld_base += TPB;
         if (ld_base >= ld.t1) {
             if (ld.valid && ld.hi != INT_MAX)

@@ -29,6 +29,7 @@ MARKS = [(0, "workgroup start"), (1, "keys stored / queries staged"),
          (4, "items published"), (24, "own items: queries in regs"),
          (25, "first item's bounds"), (26, "first item's rows requested"),
          (5, "first item begins"), (27, "item blocks done (latest)"),
+         (28, "item rows in LDS (latest)"), (29, "item weights and sums (latest)"),
          (6, "first item computed"),
          (7, "first partial stored"), (8, "first item counted"), (9, "own items done"),
          (20, "merge begins"), (21, "merge: weights / list A"),

@@ -392,7 +392,8 @@ mac_status mac_profile_read(mac_handle *h, double ms[MAC_PROFILE_STAGES], int32_
  *   summed, 23 outputs and ring entries written (stores issued); in the
  *   own-items block before the first item: 24 queries read from LDS, 25
  *   the item's bounds computed, 26 its rows requested (or speculated);
- *   27 an item's blocks done, before their cross-row combine (the latest
+ *   27 an item's blocks done, before their cross-row combine, and 28 the
+ *   row states of all the workgroup's waves in LDS (both for the latest
  *   item of the workgroup).
  * Notes hold counts: 16 the group's items; 17 items of its own workgroups;
  * 18 first item from the speculative rows (1), re-requested (2), none (0);
