@@ -427,6 +427,8 @@ __device__ inline bool block_or(bool p) { return !block_and(!p); }
 // Cache-policy operand of the buffer-load builtins selecting sc1 (device
 // coherence, as the agent-scope atomic accesses above use).
 constexpr int kCacheSc1 = 16;
+// ... and the non-temporal hint (nt): lines not kept for reuse.
+constexpr int kCacheNt = 2;
 
 // s_waitcnt vmcnt(0): this wave's loads and stores have completed (a
 // write-through store is then visible to every XCD).  Encoding (gfx9):
@@ -787,7 +789,11 @@ __device__ inline unsigned long long match_finish(const StepArgs &a, int m, bool
 // distance, with each lane's products over the same 8 (or 4) dims in the
 // same order.  Key and validity as match_finish.  The scalar words (the
 // position, readiness and the done counter, returned in *done) are read
-// after the rows are requested.
+// after the rows are requested.  The ring rows are loaded with the
+// non-temporal hint: a ring this kernel serves (more than 16 KV groups)
+// outgrows the caches before its next step reads it, and the step's K/V
+// that follows found more of its data cached (0.3 us less match and 0.45
+// us less group kernel per launch at the 128K batch-8 workload).
 template <class T, int D>
 __device__ inline unsigned long long match_halves(const StepArgs &a, int first, int bh,
                                                   unsigned long long *done, unsigned long long *sm)
@@ -812,7 +818,8 @@ __device__ inline unsigned long long match_halves(const StepArgs &a, int first, 
     for (int u = 0; u < UH; ++u) {
         const int k = match_slot<UH>(a, first, u, RPH, row);
         raw[u] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(ring, (uint32_t)(k * D + lane * EPL) * sizeof(S), 0, 0));
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(ring, (uint32_t)(k * D + lane * EPL) * sizeof(S), 0,
+                                                         kCacheNt));
     }
     // The row group's UH positions in one load instruction (lane u of the
     // group reads row u's), handed to the other lanes when the bound is
@@ -857,7 +864,8 @@ __device__ inline unsigned long long match_halves(const StepArgs &a, int first, 
         any[u] = __builtin_amdgcn_ballot_w64(keep[u]) != 0;
         raw2[u] = make_uint4(0u, 0u, 0u, 0u);
         if (any[u])
-            raw2[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ring, off, 0, 0));
+            raw2[u] = __builtin_bit_cast(uint4,
+                                         __builtin_amdgcn_raw_buffer_load_b128(ring, off, 0, kCacheNt));
     }
     unsigned long long best = ~0ull;
 #pragma unroll
