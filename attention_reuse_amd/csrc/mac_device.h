@@ -791,9 +791,9 @@ __device__ inline unsigned long long match_finish(const StepArgs &a, int m, bool
 // position, readiness and the done counter, returned in *done) are read
 // after the rows are requested.  The ring rows are loaded with the
 // non-temporal hint: a ring this kernel serves (more than 16 KV groups)
-// outgrows the caches before its next step reads it, and the step's K/V
-// that follows found more of its data cached (0.3 us less match and 0.45
-// us less group kernel per launch at the 128K batch-8 workload).
+// outgrows the caches before its next step reads it (measured: 0.3 us less
+// match, and 0.45 us less in the group kernel that follows, per launch at
+// the 128K batch-8 workload).
 template <class T, int D>
 __device__ inline unsigned long long match_halves(const StepArgs &a, int first, int bh,
                                                   unsigned long long *done, unsigned long long *sm)
